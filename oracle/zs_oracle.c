@@ -1,0 +1,234 @@
+/*
+ * zs_oracle.c -- plain, slow, obviously correct CPU oracle for one rank's
+ * share of the sharded mixed-precision AdamW step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The product path
+ * (the HIP library) never calls it and shares no code with it.
+ *
+ * Sources (page titles as printed on the pages):
+ *  - "Chapter 9: Distributed Training and Data Parallelism", section 9.2.2
+ *    (Adam): first moment, second moment, bias correction, update with the
+ *    epsilon added after the square root.
+ *  - same page, section 9.2.1 and 9.4.2: fp32 master copy plus two fp32
+ *    moments per parameter (12 bytes), low-precision parameter and gradient.
+ *  - same page, section 9.3.5 (reduce-scatter: rank r receives the sum over
+ *    ranks of chunk r) and section 9.4.2 (ZeRO-1/2 training step:
+ *    reduce-scatter the gradients, update only the owned shard, all-gather).
+ *  - "Lecture 7: Parallelism I -- collectives, data parallelism and ZeRO"
+ *    (CS336 notes), section 7 (16 bytes per parameter under mixed-precision
+ *    AdamW: bf16 parameter, bf16 gradient, fp32 master, fp32 m, fp32 v) and
+ *    section 8.1 (FlatZeRO1: all parameters concatenated into one flat
+ *    vector, split evenly; exercise 1(e): pad with zeros until divisible).
+ *
+ * Every floating-point operation is IEEE-754 binary32 with round-to-nearest-
+ * even, evaluated one operation at a time in the order written below.  Build
+ * with -ffp-contract=off and without fast-math so that no multiply-add is
+ * fused and denormals are kept.  The bias-correction denominators are formed
+ * once per call in binary64 and rounded once to binary32.
+ *
+ * Readings taken where the pages are silent (each is listed with its reason
+ * in the design notes of the repository):
+ *  - "AdamW" is named but its decay is not written out: decoupled decay
+ *    coupled to the learning rate, w <- w*(1 - lr*wd) on decayed elements,
+ *    then w <- w - lr*u, both using the pre-step w.
+ *  - the k gradient partials are SUMMED (reduce-scatter delivers a sum), in
+ *    a fixed left fold j = 0..k-1, then multiplied by grad_scale.
+ *  - the step counter t starts at 1.
+ *  - fp32 -> bf16 is round-to-nearest-even on the 16 dropped bits; every NaN
+ *    becomes the canonical quiet NaN 0x7FC0.
+ *  - element i takes the weight-decay flag of the LAST segment-table entry
+ *    whose start is <= i (entries sorted non-decreasing, first start 0).
+ *
+ * Parity pins (all in the CPU test suite): page examples for the reduce
+ * (reduce-scatter exercise, ring demo), closed forms for step 1, constant
+ * and zero gradients, the t -> infinity limit of bias correction, exact
+ * power-of-two scaling, the library AdamW of torch (CPU, float64) for the
+ * update formula, torch's bf16 conversion over all 2^32 inputs, and the
+ * sharding invariant against the unsharded routine.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+/* Same field layout as the product's segment and hyper-parameter structs
+ * (an interface both sides must agree on), declared here independently. */
+typedef struct {
+    int64_t start;   /* element offset inside the buffer the call covers */
+    int32_t wd_on;   /* non-zero: decoupled weight decay applies */
+    int32_t reserved;
+} zo_segment;
+
+typedef struct {
+    float lr, beta1, beta2, eps, weight_decay, grad_scale;
+} zo_hparams;
+
+enum { ZO_OK = 0, ZO_ERR_INVALID = 2 };
+
+static float bf16_to_f32(uint16_t h)
+{
+    uint32_t u = ((uint32_t)h) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* fp32 -> bf16, round to nearest, ties to even, done by looking at the 16
+ * bits that are dropped.  NaN -> 0x7FC0.  Finite values whose rounding
+ * carries past the largest bf16 become infinity (the carry walks into the
+ * exponent field), which is what round-to-nearest requires. */
+uint16_t zs_oracle_bf16_rne(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)0x7FC0u;
+    uint32_t hi = u >> 16;
+    uint32_t lo = u & 0xffffu;
+    if (lo > 0x8000u || (lo == 0x8000u && (hi & 1u)))
+        hi += 1u;
+    return (uint16_t)hi;
+}
+
+void zs_oracle_bf16_rne_array(const float *x, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = zs_oracle_bf16_rne(x[i]);
+}
+
+/* Per-call scalars of the update, shared by both routines below. */
+typedef struct {
+    float c1, c2, bc1, bc2, df;
+} zo_scalars;
+
+static int hparams_ok(const zo_hparams *hp)
+{
+    if (!hp) return 0;
+    if (!isfinite(hp->lr) || !isfinite(hp->beta1) || !isfinite(hp->beta2) ||
+        !isfinite(hp->eps) || !isfinite(hp->weight_decay) ||
+        !isfinite(hp->grad_scale))
+        return 0;
+    if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f)) return 0;
+    if (!(hp->beta2 >= 0.0f && hp->beta2 < 1.0f)) return 0;
+    if (hp->eps < 0.0f) return 0;
+    return 1;
+}
+
+static zo_scalars make_scalars(const zo_hparams *hp, int64_t t)
+{
+    zo_scalars s;
+    s.c1 = 1.0f - hp->beta1;
+    s.c2 = 1.0f - hp->beta2;
+    s.bc1 = (float)(1.0 - pow((double)hp->beta1, (double)t));
+    s.bc2 = (float)(1.0 - pow((double)hp->beta2, (double)t));
+    float lrwd = hp->lr * hp->weight_decay;
+    s.df = 1.0f - lrwd;
+    return s;
+}
+
+/* Moments, bias correction, update and decay for one element.  g is the
+ * already-reduced fp32 gradient. */
+static void adamw_element(float *w, float *m, float *v, float g, int decay,
+                          const zo_hparams *hp, const zo_scalars *s)
+{
+    float m_prev = *m, v_prev = *v, w_prev = *w;
+
+    float a = hp->beta1 * m_prev;
+    float b = s->c1 * g;
+    float m_new = a + b;
+
+    float gg = g * g;
+    float c = hp->beta2 * v_prev;
+    float d = s->c2 * gg;
+    float v_new = c + d;
+
+    float m_hat = m_new / s->bc1;
+    float v_hat = v_new / s->bc2;
+    float denom = sqrtf(v_hat) + hp->eps;
+    float u = m_hat / denom;
+
+    float w_dec = decay ? (w_prev * s->df) : w_prev;
+    float step = hp->lr * u;
+    float w_new = w_dec - step;
+
+    *m = m_new;
+    *v = v_new;
+    *w = w_new;
+}
+
+/*
+ * One rank's shard step.  Host pointers, n elements of the shard:
+ *   master, m, v : fp32 [n], updated in place
+ *   param_bf16   : bf16 [n] (raw 16-bit patterns), written only
+ *   grads[j]     : bf16 [n] for j < k, the k partial gradients
+ *   segs[nseg]   : weight-decay segment table of this shard
+ * Returns 0 on success, 2 on an invalid argument (nothing written).
+ */
+int zs_oracle_shard_step(float *master, float *m, float *v, uint16_t *param_bf16,
+                         const uint16_t *const *grads, int k, int64_t n,
+                         const zo_segment *segs, int32_t nseg,
+                         const zo_hparams *hp, int64_t step)
+{
+    if (k < 1 || n < 0 || step < 1 || !hparams_ok(hp)) return ZO_ERR_INVALID;
+    if (nseg < 1 || !segs || segs[0].start != 0) return ZO_ERR_INVALID;
+    for (int32_t s = 1; s < nseg; ++s)
+        if (segs[s].start < segs[s - 1].start) return ZO_ERR_INVALID;
+    if (n == 0) return ZO_OK;
+    if (!master || !m || !v || !param_bf16 || !grads) return ZO_ERR_INVALID;
+    for (int j = 0; j < k; ++j)
+        if (!grads[j]) return ZO_ERR_INVALID;
+
+    zo_scalars sc = make_scalars(hp, step);
+
+    int32_t seg = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        while (seg + 1 < nseg && segs[seg + 1].start <= i)
+            ++seg;
+        int decay = segs[seg].wd_on != 0;
+
+        /* reduce: left fold of the k partials, then the scale */
+        float g = bf16_to_f32(grads[0][i]);
+        for (int j = 1; j < k; ++j)
+            g = g + bf16_to_f32(grads[j][i]);
+        g = g * hp->grad_scale;
+
+        adamw_element(&master[i], &m[i], &v[i], g, decay, hp, &sc);
+        param_bf16[i] = zs_oracle_bf16_rne(master[i]);
+    }
+    return ZO_OK;
+}
+
+/*
+ * AdamW over an unsharded buffer with an already-reduced fp32 gradient and a
+ * per-element decay mask (one byte per element, non-zero = decay).  This is
+ * the plain optimizer the sharded step must reproduce: the concatenation of
+ * every rank's shard step equals this routine run over the whole padded
+ * buffer on the fold-summed gradient.
+ */
+int zs_oracle_adamw_unsharded(float *w, float *m, float *v, uint16_t *param_bf16,
+                              const float *g, const uint8_t *decay_mask,
+                              int64_t n, const zo_hparams *hp, int64_t step)
+{
+    if (n < 0 || step < 1 || !hparams_ok(hp)) return ZO_ERR_INVALID;
+    if (n == 0) return ZO_OK;
+    if (!w || !m || !v || !param_bf16 || !g || !decay_mask) return ZO_ERR_INVALID;
+    zo_scalars sc = make_scalars(hp, step);
+    for (int64_t i = 0; i < n; ++i) {
+        float gi = g[i] * hp->grad_scale;
+        adamw_element(&w[i], &m[i], &v[i], gi, decay_mask[i] != 0, hp, &sc);
+        param_bf16[i] = zs_oracle_bf16_rne(w[i]);
+    }
+    return ZO_OK;
+}
+
+/* The four per-call scalars, exposed so that tests can pin them to the
+ * closed forms (c1 = 1-b1, bias corrections, decay factor). */
+void zs_oracle_scalars(const zo_hparams *hp, int64_t step, float out[5])
+{
+    zo_scalars s = make_scalars(hp, step);
+    out[0] = s.c1;
+    out[1] = s.c2;
+    out[2] = s.bc1;
+    out[3] = s.bc2;
+    out[4] = s.df;
+}
