@@ -1,0 +1,162 @@
+/*
+ * zs.h -- C ABI of libzs: one rank's share of the sharded mixed-precision
+ * AdamW step (ZeRO-1 "update only my shard"), fused into one HBM pass on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What one call computes, for every element i of the rank's shard [0, n):
+ *
+ *   g   = (((f32(G[0][i]) + f32(G[1][i])) + ...) + f32(G[k-1][i])) * grad_scale
+ *   m'  = beta1*m + (1-beta1)*g
+ *   v'  = beta2*v + (1-beta2)*(g*g)
+ *   u   = (m'/bc1) / (sqrt(v'/bc2) + eps),   bc1 = 1-beta1^t, bc2 = 1-beta2^t
+ *   w'  = (decay(i) ? w*(1 - lr*wd) : w) - lr*u
+ *   master[i] = w', m[i] = m', v[i] = v', param_bf16[i] = bf16_rne(w')
+ *
+ * Sources (page titles as printed):
+ *  - "Chapter 9: Distributed Training and Data Parallelism", section 9.2.2
+ *    (Adam moments, bias correction, update with epsilon outside the root);
+ *    section 9.3.5 (reduce-scatter hands rank r the SUM of chunk r over all
+ *    ranks); section 9.4.2 (ZeRO-1/2 step: reduce-scatter the gradients,
+ *    update the owned shard of optimizer state and parameters, all-gather
+ *    the parameters).
+ *  - "Lecture 7: Parallelism I -- collectives, data parallelism and ZeRO"
+ *    (CS336 notes), section 7 (mixed-precision AdamW keeps 16 bytes per
+ *    parameter: bf16 weight, bf16 gradient, fp32 master, fp32 m, fp32 v) and
+ *    section 8.1 (FlatZeRO1: one flat buffer split evenly across ranks; the
+ *    rank's k partials are the inputs of its reduce-scatter chunk).
+ *
+ * Numerics: IEEE binary32, round to nearest even, one operation at a time in
+ * the order above (no fused multiply-add), correctly rounded divide and
+ * square root, denormals kept.  bc1, bc2 are formed on the host in binary64
+ * as 1 - pow(beta, t) and rounded once; (1-beta1), (1-beta2) and
+ * (1 - lr*wd) are formed in binary32.  bf16_rne is round-to-nearest-even on
+ * the 16 dropped bits; every NaN becomes 0x7FC0.  "AdamW" decay is read as
+ * decoupled and lr-coupled, applied to the pre-step weight.
+ *
+ * Threading: zs_init/zs_fini must not race with other calls.  After
+ * zs_init the library holds no mutable state, so zs_shard_step may be
+ * called concurrently from several threads and on several streams.
+ */
+#ifndef ZS_H_
+#define ZS_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZS_MAX_K 16           /* most gradient partials one call sums */
+#define ZS_MAX_SEGMENTS 65536 /* most entries in one segment table */
+
+typedef enum {
+    ZS_OK = 0,
+    ZS_ERR_NOT_INITIALIZED = 1, /* zs_init not called, or zs_fini called */
+    ZS_ERR_INVALID_ARGUMENT = 2,/* bad pointer, size, k, step or hparams */
+    ZS_ERR_MISALIGNED = 3,      /* a buffer base is not 16-byte aligned */
+    ZS_ERR_TOO_MANY_SEGMENTS = 4,
+    ZS_ERR_DEVICE = 5,          /* a HIP call failed; see zs_last_device_error */
+    ZS_ERR_ALIASING = 6         /* output ranges overlap each other or an input */
+} zs_status;
+
+/* Optimizer hyper-parameters.  beta1, beta2 in [0, 1); eps >= 0; all finite.
+ * grad_scale multiplies the summed gradient (1.0 = plain sum). */
+typedef struct {
+    float lr, beta1, beta2, eps, weight_decay, grad_scale;
+} zs_hparams;
+
+/* One entry of a weight-decay segment table.  start is an element offset
+ * inside the shard.  Element i takes wd_on of the LAST entry whose
+ * start <= i.  Entries must be sorted by start (non-decreasing) and the
+ * first must have start == 0.  Entries with start >= n are ignored.
+ * 16 bytes per entry, 8-byte aligned. */
+typedef struct {
+    int64_t start;
+    int32_t wd_on;    /* non-zero: decoupled weight decay applies */
+    int32_t reserved; /* must be 0 */
+} zs_segment;
+
+/* segs is a DEVICE pointer (device memory the caller owns) to count
+ * entries; the table is read by the kernel and never written.  Because it
+ * lives on the device the library does not check its order: an unsorted
+ * table gives unspecified decay flags but every read stays inside
+ * segs[0 .. count-1]. */
+typedef struct {
+    const zs_segment *segs;
+    int32_t count;
+    int32_t reserved;
+} zs_seg_table;
+
+/* Launch geometry override, for tuning and for determinism tests.  Zero in a
+ * field selects the library default.  Results never depend on it. */
+typedef struct {
+    int32_t chunk_tiles;  /* 2048-element tiles per workgroup (1..4096) */
+    int32_t nontemporal;  /* 0 = default, 1 = streaming (non-temporal) loads/stores, 2 = cached */
+    int32_t reserved[2];
+} zs_launch_cfg;
+
+/* Prepare the library for one device: records its compute-unit count and
+ * checks that it is a gfx950 part.  Idempotent for the same ordinal.
+ * Returns ZS_OK, ZS_ERR_INVALID_ARGUMENT (no such device) or
+ * ZS_ERR_DEVICE (HIP error, or the device is not gfx950). */
+int zs_init(int device_ordinal);
+
+/*
+ * Enqueue one shard step on `stream` (a hipStream_t; NULL = the null
+ * stream).  Asynchronous: returns once the kernel is enqueued; faults during
+ * execution surface at the caller's next synchronisation of the stream.
+ *
+ *   master, m, v : DEVICE fp32 [n], read and updated in place
+ *   param_bf16   : DEVICE bf16 [n] (raw 16-bit patterns), written only
+ *   grads        : HOST array of k DEVICE pointers, each bf16 [n], read only;
+ *                  partial j is added in the order j = 0, 1, ..., k-1
+ *   k            : 1 .. ZS_MAX_K
+ *   n            : elements in the shard, >= 0 (n == 0: ZS_OK, nothing enqueued)
+ *   seg_table    : HOST struct describing the device-resident table above
+ *   hparams      : HOST struct, read during the call only
+ *   step         : the optimizer step t >= 1 used in the bias correction
+ *
+ * All buffers are owned by the caller; the library allocates nothing and
+ * keeps no pointer after returning.  Every base pointer (master, m, v,
+ * param_bf16, each grads[j]) must be 16-byte aligned, and the segment table
+ * 8-byte aligned.  The byte ranges of master, m, v and param_bf16 must not
+ * overlap each other or any grads[j] (partials may alias one another).
+ *
+ * Errors are reported synchronously with nothing enqueued:
+ * ZS_ERR_NOT_INITIALIZED, ZS_ERR_INVALID_ARGUMENT (null pointer, k or n out
+ * of range, step < 1, non-finite or out-of-range hparams, count < 1),
+ * ZS_ERR_TOO_MANY_SEGMENTS, ZS_ERR_MISALIGNED, ZS_ERR_ALIASING.  A launch
+ * failure returns ZS_ERR_DEVICE.
+ */
+int zs_shard_step(float *master, float *m, float *v, uint16_t *param_bf16,
+                  const uint16_t *const *grads, int k, int64_t n,
+                  const zs_seg_table *seg_table, const zs_hparams *hparams,
+                  int64_t step, void *stream);
+
+/* zs_shard_step with an explicit launch geometry (cfg may be NULL).  Same
+ * arguments, results and errors; a cfg field out of range returns
+ * ZS_ERR_INVALID_ARGUMENT.  Outputs are bitwise identical for every cfg. */
+int zs_shard_step_cfg(float *master, float *m, float *v, uint16_t *param_bf16,
+                      const uint16_t *const *grads, int k, int64_t n,
+                      const zs_seg_table *seg_table, const zs_hparams *hparams,
+                      int64_t step, void *stream, const zs_launch_cfg *cfg);
+
+/* Release what zs_init recorded.  Later calls return ZS_ERR_NOT_INITIALIZED
+ * until zs_init is called again.  Always returns ZS_OK. */
+int zs_fini(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char *zs_status_string(int status);
+
+/* The last hipError_t seen by the library on the calling thread (0 = none). */
+int zs_last_device_error(void);
+
+/* Bytes one zs_shard_step call moves through HBM, by the algorithm:
+ * n * (12 + 2k) read + n * 14 written.  For reporting only. */
+int64_t zs_algorithmic_bytes(int k, int64_t n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZS_H_ */

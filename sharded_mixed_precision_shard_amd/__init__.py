@@ -1,0 +1,186 @@
+"""Python binding of libzs (include/zs.h): one rank's fused ZeRO-shard AdamW step.
+
+Argument marshalling only: every step of the path runs in the HIP library.
+Device buffers may be given as torch tensors (their ``data_ptr()`` is used)
+or as plain integer device addresses.  There is no CPU fallback: if
+``libzs.so`` has not been built, importing the library raises.
+
+Entry points keep the C names: :func:`zs_init`, :func:`zs_shard_step`,
+:func:`zs_shard_step_cfg`, :func:`zs_fini`, :func:`zs_status_string`,
+:func:`zs_last_device_error`, :func:`zs_algorithmic_bytes`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libzs.so")
+
+ZS_MAX_K = 16
+ZS_MAX_SEGMENTS = 65536
+
+ZS_OK = 0
+ZS_ERR_NOT_INITIALIZED = 1
+ZS_ERR_INVALID_ARGUMENT = 2
+ZS_ERR_MISALIGNED = 3
+ZS_ERR_TOO_MANY_SEGMENTS = 4
+ZS_ERR_DEVICE = 5
+ZS_ERR_ALIASING = 6
+
+# Symbols declared in include/zs.h.
+EXPORTS = ("zs_init", "zs_shard_step", "zs_shard_step_cfg", "zs_fini", "zs_status_string",
+           "zs_last_device_error", "zs_algorithmic_bytes")
+
+
+class ZsHparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("grad_scale", ctypes.c_float)]
+
+
+class ZsSegment(ctypes.Structure):
+    _fields_ = [("start", ctypes.c_int64), ("wd_on", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class ZsSegTable(ctypes.Structure):
+    _fields_ = [("segs", ctypes.c_void_p), ("count", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class ZsLaunchCfg(ctypes.Structure):
+    _fields_ = [("chunk_tiles", ctypes.c_int32), ("nontemporal", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 2)]
+
+
+class ZsError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d, hip error %d)" % (
+            where, zs_status_string(status), status, zs_last_device_error()))
+
+
+_lib = None
+
+
+def load_library():
+    """Load libzs.so; raise if it is missing (no fallback of any kind)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libzs.so is not built (expected at %s); run "
+                          "__graft_entry__.build() first" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    lib.zs_init.argtypes = [ctypes.c_int]
+    lib.zs_init.restype = ctypes.c_int
+    step_args = [P, P, P, P, P, ctypes.c_int, ctypes.c_int64, P, P, ctypes.c_int64, P]
+    lib.zs_shard_step.argtypes = step_args
+    lib.zs_shard_step.restype = ctypes.c_int
+    lib.zs_shard_step_cfg.argtypes = step_args + [P]
+    lib.zs_shard_step_cfg.restype = ctypes.c_int
+    lib.zs_fini.argtypes = []
+    lib.zs_fini.restype = ctypes.c_int
+    lib.zs_status_string.argtypes = [ctypes.c_int]
+    lib.zs_status_string.restype = ctypes.c_char_p
+    lib.zs_last_device_error.argtypes = []
+    lib.zs_last_device_error.restype = ctypes.c_int
+    lib.zs_algorithmic_bytes.argtypes = [ctypes.c_int, ctypes.c_int64]
+    lib.zs_algorithmic_bytes.restype = ctypes.c_int64
+    _lib = lib
+    return lib
+
+
+def _addr(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return int(x.data_ptr())
+    raise TypeError("expected a tensor with data_ptr() or an integer address, got %r" % type(x))
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        return 0
+    if isinstance(stream, int):
+        return stream
+    if hasattr(stream, "cuda_stream"):
+        return int(stream.cuda_stream)
+    raise TypeError("stream must be None, an int hipStream_t or a torch stream")
+
+
+def hparams(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, grad_scale=1.0):
+    return ZsHparams(lr, beta1, beta2, eps, weight_decay, grad_scale)
+
+
+def seg_table(segs, count=None) -> ZsSegTable:
+    """Describe a device-resident table.  ``segs`` is a device tensor of int64
+    pairs [count, 2] = (start, wd_on | reserved << 32) or an address."""
+    if count is None:
+        count = int(segs.shape[0])
+    return ZsSegTable(_addr(segs), int(count), 0)
+
+
+def zs_init(device_ordinal: int = 0) -> int:
+    return load_library().zs_init(int(device_ordinal))
+
+
+def zs_fini() -> int:
+    return load_library().zs_fini()
+
+
+def zs_status_string(status: int) -> str:
+    return load_library().zs_status_string(int(status)).decode()
+
+
+def zs_last_device_error() -> int:
+    return load_library().zs_last_device_error()
+
+
+def zs_algorithmic_bytes(k: int, n: int) -> int:
+    return load_library().zs_algorithmic_bytes(int(k), int(n))
+
+
+def _marshal(master, m, v, param_bf16, grads, k, seg_table_, hparams_):
+    if k is None:
+        k = len(grads)
+    gp = (ctypes.c_void_p * max(len(grads), 1))(*[_addr(g) for g in grads])
+    st = seg_table_ if isinstance(seg_table_, ZsSegTable) else seg_table(seg_table_)
+    return (ctypes.c_void_p(_addr(master)), ctypes.c_void_p(_addr(m)), ctypes.c_void_p(_addr(v)),
+            ctypes.c_void_p(_addr(param_bf16)), ctypes.cast(gp, ctypes.c_void_p), int(k), st,
+            hparams_, gp)
+
+
+def zs_shard_step(master, m, v, param_bf16, grads, k, n, seg_table_, hparams_, step,
+                  stream=None, check=True) -> int:
+    """Enqueue one shard step (see include/zs.h).  Raises ZsError on a
+    non-zero status when ``check`` is true; returns the status otherwise."""
+    pm, pmm, pv, pp, pg, kk, st, hp, keep = _marshal(master, m, v, param_bf16, grads, k,
+                                                     seg_table_, hparams_)
+    rc = load_library().zs_shard_step(pm, pmm, pv, pp, pg, kk, int(n), ctypes.byref(st),
+                                      ctypes.byref(hp), int(step),
+                                      ctypes.c_void_p(_stream_handle(stream)))
+    del keep
+    if check and rc != ZS_OK:
+        raise ZsError(rc, "zs_shard_step")
+    return rc
+
+
+def zs_shard_step_cfg(master, m, v, param_bf16, grads, k, n, seg_table_, hparams_, step,
+                      stream=None, chunk_tiles=0, nontemporal=0, check=True) -> int:
+    """zs_shard_step with an explicit launch geometry (results never change)."""
+    pm, pmm, pv, pp, pg, kk, st, hp, keep = _marshal(master, m, v, param_bf16, grads, k,
+                                                     seg_table_, hparams_)
+    cfg = ZsLaunchCfg(int(chunk_tiles), int(nontemporal), (ctypes.c_int32 * 2)(0, 0))
+    rc = load_library().zs_shard_step_cfg(pm, pmm, pv, pp, pg, kk, int(n), ctypes.byref(st),
+                                          ctypes.byref(hp), int(step),
+                                          ctypes.c_void_p(_stream_handle(stream)),
+                                          ctypes.byref(cfg))
+    del keep
+    if check and rc != ZS_OK:
+        raise ZsError(rc, "zs_shard_step_cfg")
+    return rc

@@ -1,0 +1,55 @@
+"""Build the gfx950 shared library ``libzs.so`` from ``csrc/zs_step.hip``.
+
+hipcc cross-compiles for gfx950 without a GPU, so this runs anywhere the
+ROCm toolchain is installed.  The library is built in-tree, next to this file.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+REPO_DIR = os.path.dirname(PKG_DIR)
+INCLUDE_DIR = os.path.join(REPO_DIR, "include")
+SRC = os.path.join(PKG_DIR, "csrc", "zs_step.hip")
+LIB = os.path.join(PKG_DIR, "libzs.so")
+
+ARCH = "gfx950"
+
+# Numerics flags: no fused multiply-add contraction, IEEE divide and square
+# root, denormals kept.  Packed fp32 instructions are disabled.
+HIPCC_FLAGS = [
+    "--offload-arch=" + ARCH,
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-ffp-contract=off",
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-fno-gpu-flush-denormals-to-zero",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+]
+
+
+def hipcc() -> str:
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found; the ROCm toolchain is required to build libzs.so")
+    return path
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libzs.so (always recompiles).  Returns the library path."""
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE_DIR, "-o", tmp, SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,479 @@
+// zs_step.hip -- fused reduce + AdamW + bf16-cast shard step for gfx950,
+// and the C ABI declared in include/zs.h.
+//
+// One rank's share of the ZeRO-1 optimizer step ("Chapter 9: Distributed
+// Training and Data Parallelism", section 9.4.2; "Lecture 7: Parallelism I",
+// section 8.1): sum the k bf16 gradient partials the reduce-scatter delivers
+// for this rank's chunk, run mixed-precision AdamW (section 9.2.2 of the
+// first page) on the fp32 master, m and v, and write the bf16 parameter copy
+// that the all-gather would broadcast.
+//
+// The work is purely elementwise and bandwidth bound (about 0.5 flop per HBM
+// byte), so there is no MFMA here.  Design for CDNA4:
+//   * each lane owns 8 consecutive elements of a 2048-element workgroup
+//     tile: one 16-byte load per bf16 partial, two 16-byte loads per fp32
+//     state array, 16-byte stores; every byte is read once and written once;
+//   * each workgroup owns a contiguous chunk of tiles, so its segment cursor
+//     only moves forward;
+//   * the slice of the weight-decay segment table that the chunk touches is
+//     staged in LDS once per workgroup (restaged only if the chunk crosses
+//     more than kLdsSegs entries);
+//   * segment boundaries are resolved per wavefront: a 512-element window
+//     inside one segment takes one wave-uniform flag; only windows that
+//     contain a boundary resolve flags per lane;
+//   * 64-bit element indices throughout (shards exceed 2^31 elements).
+//
+// Numerics follow the header: binary32, no contraction, correctly rounded
+// divide and square root, denormals kept, bf16 round-to-nearest-even with
+// NaN -> 0x7FC0.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "zs.h"
+
+namespace {
+
+constexpr int kThreads = 256;                 // 4 wavefronts of 64 lanes
+constexpr int kVec = 8;                       // elements per lane per tile
+constexpr int kTile = kThreads * kVec;        // 2048 elements per tile
+constexpr int kWave = 64;
+constexpr int kWindow = kWave * kVec;         // 512 elements per wave per tile
+constexpr int kLdsSegs = 1024;                // staged segment entries
+constexpr int kMaxChunkTiles = 4096;
+constexpr int64_t kNoStart = INT64_MAX;       // sentinel past the table end
+
+static_assert(kLdsSegs % kThreads == 0, "staging rounds must be whole");
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct StepArgs {
+    float *master;
+    float *m;
+    float *v;
+    uint16_t *param;
+    const uint16_t *grads[ZS_MAX_K];
+    const zs_segment *segs;
+    int64_t n;
+    int64_t chunk;  // elements per workgroup, a multiple of kTile
+    int32_t nseg;
+    float lr, b1, b2, c1, c2, bc1, bc2, eps, df, gscale;
+};
+
+template <int NT, typename T>
+__device__ __forceinline__ T load(const T *p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+template <int NT, typename T>
+__device__ __forceinline__ void store(T *p, T x) {
+    if constexpr (NT) __builtin_nontemporal_store(x, p);
+    else *p = x;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xffff0000u); }
+
+// Round to nearest even by adding 0x7fff plus the lowest kept bit, then
+// dropping 16 bits; NaN is mapped to the canonical quiet NaN.
+__device__ __forceinline__ uint32_t to_bf16(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    return ((u & 0x7fffffffu) > 0x7f800000u) ? 0x7fc0u : r;
+}
+
+// One element of the update: g is the reduced, scaled gradient.
+__device__ __forceinline__ void adamw(float &w, float &m, float &v, float g, bool decay,
+                                      const StepArgs &a) {
+#pragma clang fp contract(off)
+    const float m1 = a.b1 * m + a.c1 * g;
+    const float v1 = a.b2 * v + a.c2 * (g * g);
+    const float mh = m1 / a.bc1;
+    const float vh = v1 / a.bc2;
+    const float u = mh / (sqrtf(vh) + a.eps);
+    const float wd = decay ? w * a.df : w;
+    w = wd - a.lr * u;
+    m = m1;
+    v = v1;
+}
+
+// Largest s with segs[s].start <= e (0 if none); reads stay in [0, nseg).
+__device__ int32_t last_le(const zs_segment *segs, int32_t nseg, int64_t e) {
+    int32_t lo = 0, hi = nseg - 1;
+    while (lo < hi) {
+        const int32_t mid = lo + (hi - lo + 1) / 2;
+        if (segs[mid].start <= e) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Stage the table entries from the one covering `from` onward into LDS, in
+// rounds of kThreads, stopping after the round that reaches an entry whose
+// start is >= `until`.  Entries past the table end read as kNoStart.
+// Returns the start of the last staged entry: every element e with
+// from <= e < result resolves inside the staged slice.  Block-uniform; all
+// threads must call it.
+__device__ int64_t stage_segments(const StepArgs &a, int64_t from, int64_t until,
+                                  int64_t *s_start, uint8_t *s_flag, int32_t *s_base) {
+    if (threadIdx.x == 0) *s_base = last_le(a.segs, a.nseg, from);
+    __syncthreads();
+    const int64_t base = *s_base;
+    int staged = 0;
+    for (int r = 0; r < kLdsSegs; r += kThreads) {
+        const int j = r + (int)threadIdx.x;
+        const int64_t idx = base + j;
+        int64_t st = kNoStart;
+        uint8_t fl = 0;
+        if (idx < a.nseg) {
+            st = a.segs[idx].start;
+            fl = a.segs[idx].wd_on != 0;
+        }
+        s_start[j] = st;
+        s_flag[j] = fl;
+        staged = r + kThreads;
+        if (__syncthreads_or(st >= until)) break;
+    }
+    return s_start[staged - 1];
+}
+
+template <int K, int NT>
+__global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) {
+    __shared__ int64_t s_start[kLdsSegs];
+    __shared__ uint8_t s_flag[kLdsSegs];
+    __shared__ int32_t s_base;
+
+    const int tid = (int)threadIdx.x;
+    const int wave = tid / kWave;
+    const int64_t c0 = (int64_t)blockIdx.x * a.chunk;
+    if (c0 >= a.n) return;  // block-uniform
+    const int64_t c1 = (c0 + a.chunk < a.n) ? c0 + a.chunk : a.n;
+
+    int64_t lim = stage_segments(a, c0, c1, s_start, s_flag, &s_base);
+    int wc = 0;  // this wave's cursor into the staged slice
+
+    for (int64_t t0 = c0; t0 < c1; t0 += kTile) {
+        const int64_t tend = (t0 + kTile < c1) ? t0 + kTile : c1;
+        bool overflow = false;
+        if (tend > lim) {  // block-uniform: the slice ends inside this tile
+            __syncthreads();
+            lim = stage_segments(a, t0, c1, s_start, s_flag, &s_base);
+            wc = 0;
+            overflow = tend > lim;
+        }
+        const int64_t w0 = t0 + (int64_t)wave * kWindow;
+        if (w0 >= tend) continue;  // wave-uniform
+        const int64_t w1 = (w0 + kWindow < tend) ? w0 + kWindow : tend;
+        const int64_t e = t0 + (int64_t)tid * kVec;
+
+        // Decay flags of this lane's 8 elements, one bit each.
+        uint32_t mask;
+        if (!overflow) {
+            while (s_start[wc + 1] <= w0) ++wc;
+            if (s_start[wc + 1] >= w1) {
+                mask = s_flag[wc] ? 0xffu : 0u;
+            } else {
+                mask = 0;
+                int lc = wc;
+                for (int q = 0; q < kVec; ++q) {
+                    const int64_t eq = e + q;
+                    if (eq >= w1) break;
+                    while (s_start[lc + 1] <= eq) ++lc;
+                    mask |= (uint32_t)s_flag[lc] << q;
+                }
+            }
+        } else {
+            mask = 0;
+            for (int q = 0; q < kVec; ++q) {
+                const int64_t eq = e + q;
+                if (eq >= w1) break;
+                const int32_t s = last_le(a.segs, a.nseg, eq);
+                mask |= (uint32_t)(a.segs[s].wd_on != 0) << q;
+            }
+        }
+
+        if (e + kVec <= a.n) {
+            // Full 8-element group: 16-byte vector traffic only.
+            const f32x4 *pw = reinterpret_cast<const f32x4 *>(a.master + e);
+            const f32x4 *pm = reinterpret_cast<const f32x4 *>(a.m + e);
+            const f32x4 *pv = reinterpret_cast<const f32x4 *>(a.v + e);
+            f32x4 w[2] = {load<NT>(pw), load<NT>(pw + 1)};
+            f32x4 m[2] = {load<NT>(pm), load<NT>(pm + 1)};
+            f32x4 v[2] = {load<NT>(pv), load<NT>(pv + 1)};
+            u32x4 gr[K];
+#pragma unroll
+            for (int j = 0; j < K; ++j)
+                gr[j] = load<NT>(reinterpret_cast<const u32x4 *>(a.grads[j] + e));
+
+            u32x4 pout;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                // dword d of every partial holds elements 2d (low) and 2d+1 (high)
+                float g0 = bf16_lo(gr[0][d]);
+                float g1 = bf16_hi(gr[0][d]);
+#pragma unroll
+                for (int j = 1; j < K; ++j) {
+                    g0 = g0 + bf16_lo(gr[j][d]);
+                    g1 = g1 + bf16_hi(gr[j][d]);
+                }
+                g0 = g0 * a.gscale;
+                g1 = g1 * a.gscale;
+                const int h = d >> 1;         // which f32x4 half
+                const int l = (d & 1) * 2;    // lane inside the f32x4
+                float w0v = w[h][l], m0v = m[h][l], v0v = v[h][l];
+                float w1v = w[h][l + 1], m1v = m[h][l + 1], v1v = v[h][l + 1];
+                adamw(w0v, m0v, v0v, g0, (mask >> (2 * d)) & 1u, a);
+                adamw(w1v, m1v, v1v, g1, (mask >> (2 * d + 1)) & 1u, a);
+                w[h][l] = w0v; m[h][l] = m0v; v[h][l] = v0v;
+                w[h][l + 1] = w1v; m[h][l + 1] = m1v; v[h][l + 1] = v1v;
+                pout[d] = to_bf16(w0v) | (to_bf16(w1v) << 16);
+            }
+            f32x4 *qw = reinterpret_cast<f32x4 *>(a.master + e);
+            f32x4 *qm = reinterpret_cast<f32x4 *>(a.m + e);
+            f32x4 *qv = reinterpret_cast<f32x4 *>(a.v + e);
+            store<NT>(qw, w[0]); store<NT>(qw + 1, w[1]);
+            store<NT>(qm, m[0]); store<NT>(qm + 1, m[1]);
+            store<NT>(qv, v[0]); store<NT>(qv + 1, v[1]);
+            store<NT>(reinterpret_cast<u32x4 *>(a.param + e), pout);
+        } else if (e < a.n) {
+            // Ragged tail of the shard (fewer than 8 elements): scalar traffic.
+            const int cnt = (int)(a.n - e);
+            for (int q = 0; q < cnt; ++q) {
+                const int64_t i = e + q;
+                float g = __uint_as_float((uint32_t)a.grads[0][i] << 16);
+#pragma unroll
+                for (int j = 1; j < K; ++j) g = g + __uint_as_float((uint32_t)a.grads[j][i] << 16);
+                g = g * a.gscale;
+                float wv = a.master[i], mv = a.m[i], vv = a.v[i];
+                adamw(wv, mv, vv, g, (mask >> q) & 1u, a);
+                a.master[i] = wv;
+                a.m[i] = mv;
+                a.v[i] = vv;
+                a.param[i] = (uint16_t)to_bf16(wv);
+            }
+        }
+    }
+}
+
+typedef void (*kernel_fn)(const StepArgs);
+
+template <int K>
+kernel_fn pick_nt(int nt) {
+    return nt ? shard_step_kernel<K, 1> : shard_step_kernel<K, 0>;
+}
+
+kernel_fn pick_kernel(int k, int nt) {
+    switch (k) {
+        case 1: return pick_nt<1>(nt);
+        case 2: return pick_nt<2>(nt);
+        case 3: return pick_nt<3>(nt);
+        case 4: return pick_nt<4>(nt);
+        case 5: return pick_nt<5>(nt);
+        case 6: return pick_nt<6>(nt);
+        case 7: return pick_nt<7>(nt);
+        case 8: return pick_nt<8>(nt);
+        case 9: return pick_nt<9>(nt);
+        case 10: return pick_nt<10>(nt);
+        case 11: return pick_nt<11>(nt);
+        case 12: return pick_nt<12>(nt);
+        case 13: return pick_nt<13>(nt);
+        case 14: return pick_nt<14>(nt);
+        case 15: return pick_nt<15>(nt);
+        case 16: return pick_nt<16>(nt);
+        default: return nullptr;
+    }
+}
+
+// ---------------------------------------------------------------- host side
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+    int ready;
+    int cus;
+};
+
+DeviceInfo g_dev[kMaxDevices];
+int g_initialized = 0;
+thread_local int t_last_hip_error = 0;
+
+int device_error(hipError_t e) {
+    t_last_hip_error = (int)e;
+    return ZS_ERR_DEVICE;
+}
+
+bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    const uintptr_t a1 = a0 + (uintptr_t)abytes, b1 = b0 + (uintptr_t)bbytes;
+    return a0 < b1 && b0 < a1;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int pick_chunk_tiles(int64_t n, int cus) {
+    // Enough workgroups for many rounds of residency on every compute unit,
+    // long enough chunks that the per-workgroup table staging is noise.
+    const int64_t tiles = (n + kTile - 1) / kTile;
+    const int64_t target = (int64_t)cus * 64;
+    int64_t ct = tiles / (target > 0 ? target : 1);
+    if (ct < 1) ct = 1;
+    if (ct > 32) ct = 32;
+    return (int)ct;
+}
+
+int validate_and_launch(float *master, float *m, float *v, uint16_t *param,
+                        const uint16_t *const *grads, int k, int64_t n,
+                        const zs_seg_table *st, const zs_hparams *hp, int64_t step,
+                        void *stream, const zs_launch_cfg *cfg) {
+    if (!g_initialized) return ZS_ERR_NOT_INITIALIZED;
+    if (k < 1 || k > ZS_MAX_K || n < 0 || step < 1 || !st || !hp || !grads)
+        return ZS_ERR_INVALID_ARGUMENT;
+    if (!std::isfinite(hp->lr) || !std::isfinite(hp->beta1) || !std::isfinite(hp->beta2) ||
+        !std::isfinite(hp->eps) || !std::isfinite(hp->weight_decay) ||
+        !std::isfinite(hp->grad_scale))
+        return ZS_ERR_INVALID_ARGUMENT;
+    if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f) ||
+        hp->eps < 0.0f)
+        return ZS_ERR_INVALID_ARGUMENT;
+    if (st->count < 1) return ZS_ERR_INVALID_ARGUMENT;
+    if (st->count > ZS_MAX_SEGMENTS) return ZS_ERR_TOO_MANY_SEGMENTS;
+    int chunk_tiles = 0, nt = 0;
+    if (cfg) {
+        if (cfg->chunk_tiles < 0 || cfg->chunk_tiles > kMaxChunkTiles) return ZS_ERR_INVALID_ARGUMENT;
+        if (cfg->nontemporal < 0 || cfg->nontemporal > 2) return ZS_ERR_INVALID_ARGUMENT;
+        chunk_tiles = cfg->chunk_tiles;
+        nt = cfg->nontemporal == 1 ? 1 : 0;
+    }
+    if (n == 0) return ZS_OK;
+    if (!master || !m || !v || !param || !st->segs) return ZS_ERR_INVALID_ARGUMENT;
+    for (int j = 0; j < k; ++j)
+        if (!grads[j]) return ZS_ERR_INVALID_ARGUMENT;
+    if (!aligned16(master) || !aligned16(m) || !aligned16(v) || !aligned16(param) ||
+        ((uintptr_t)st->segs & 7u))
+        return ZS_ERR_MISALIGNED;
+    for (int j = 0; j < k; ++j)
+        if (!aligned16(grads[j])) return ZS_ERR_MISALIGNED;
+    if (n > INT64_MAX / 4) return ZS_ERR_INVALID_ARGUMENT;
+    const int64_t b4 = n * 4, b2 = n * 2;
+    const void *outs[4] = {master, m, v, param};
+    const int64_t ob[4] = {b4, b4, b4, b2};
+    for (int x = 0; x < 4; ++x) {
+        for (int y = x + 1; y < 4; ++y)
+            if (overlaps(outs[x], ob[x], outs[y], ob[y])) return ZS_ERR_ALIASING;
+        for (int j = 0; j < k; ++j)
+            if (overlaps(outs[x], ob[x], grads[j], b2)) return ZS_ERR_ALIASING;
+    }
+
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return device_error(e);
+    if (dev < 0 || dev >= kMaxDevices || !g_dev[dev].ready) return ZS_ERR_NOT_INITIALIZED;
+
+    StepArgs a;
+    a.master = master;
+    a.m = m;
+    a.v = v;
+    a.param = param;
+    for (int j = 0; j < ZS_MAX_K; ++j) a.grads[j] = j < k ? grads[j] : nullptr;
+    a.segs = st->segs;
+    a.nseg = st->count;
+    a.n = n;
+    a.lr = hp->lr;
+    a.b1 = hp->beta1;
+    a.b2 = hp->beta2;
+    a.c1 = 1.0f - hp->beta1;
+    a.c2 = 1.0f - hp->beta2;
+    a.bc1 = (float)(1.0 - std::pow((double)hp->beta1, (double)step));
+    a.bc2 = (float)(1.0 - std::pow((double)hp->beta2, (double)step));
+    a.eps = hp->eps;
+    {
+        const float lrwd = hp->lr * hp->weight_decay;
+        a.df = 1.0f - lrwd;
+    }
+    a.gscale = hp->grad_scale;
+
+    if (chunk_tiles == 0) chunk_tiles = pick_chunk_tiles(n, g_dev[dev].cus);
+    int64_t chunk = (int64_t)chunk_tiles * kTile;
+    int64_t blocks = (n + chunk - 1) / chunk;
+    while (blocks > 0x7fffffffLL) {  // keep the grid inside the 32-bit limit
+        chunk *= 2;
+        blocks = (n + chunk - 1) / chunk;
+    }
+    a.chunk = chunk;
+
+    kernel_fn fn = pick_kernel(k, nt);
+    void *args[] = {&a};
+    e = hipLaunchKernel((const void *)fn, dim3((unsigned)blocks), dim3(kThreads), args, 0,
+                        (hipStream_t)stream);
+    if (e != hipSuccess) return device_error(e);
+    return ZS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int zs_init(int device_ordinal) {
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    if (e != hipSuccess) return device_error(e);
+    if (device_ordinal < 0 || device_ordinal >= count || device_ordinal >= kMaxDevices)
+        return ZS_ERR_INVALID_ARGUMENT;
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, device_ordinal);
+    if (e != hipSuccess) return device_error(e);
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return ZS_ERR_DEVICE;
+    g_dev[device_ordinal].cus = prop.multiProcessorCount;
+    g_dev[device_ordinal].ready = 1;
+    g_initialized = 1;
+    return ZS_OK;
+}
+
+int zs_shard_step(float *master, float *m, float *v, uint16_t *param_bf16,
+                  const uint16_t *const *grads, int k, int64_t n,
+                  const zs_seg_table *seg_table, const zs_hparams *hparams,
+                  int64_t step, void *stream) {
+    return validate_and_launch(master, m, v, param_bf16, grads, k, n, seg_table, hparams, step,
+                               stream, nullptr);
+}
+
+int zs_shard_step_cfg(float *master, float *m, float *v, uint16_t *param_bf16,
+                      const uint16_t *const *grads, int k, int64_t n,
+                      const zs_seg_table *seg_table, const zs_hparams *hparams,
+                      int64_t step, void *stream, const zs_launch_cfg *cfg) {
+    return validate_and_launch(master, m, v, param_bf16, grads, k, n, seg_table, hparams, step,
+                               stream, cfg);
+}
+
+int zs_fini(void) {
+    for (int d = 0; d < kMaxDevices; ++d) g_dev[d].ready = 0;
+    g_initialized = 0;
+    return ZS_OK;
+}
+
+const char *zs_status_string(int status) {
+    switch (status) {
+        case ZS_OK: return "ok";
+        case ZS_ERR_NOT_INITIALIZED: return "library not initialized for this device";
+        case ZS_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case ZS_ERR_MISALIGNED: return "buffer not 16-byte aligned";
+        case ZS_ERR_TOO_MANY_SEGMENTS: return "segment table too large";
+        case ZS_ERR_DEVICE: return "HIP runtime error";
+        case ZS_ERR_ALIASING: return "output buffers overlap";
+        default: return "unknown status";
+    }
+}
+
+int zs_last_device_error(void) { return t_last_hip_error; }
+
+int64_t zs_algorithmic_bytes(int k, int64_t n) {
+    if (k < 1 || n < 0) return 0;
+    return n * (int64_t)(12 + 2 * k) + n * 14;
+}
+
+}  // extern "C"
