@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark of one rank's fused ZeRO-shard AdamW step on one MI355X.
+
+A step is one zs_shard_step call over the whole shard: sum the k bf16
+partials, AdamW on the fp32 master/m/v, write the bf16 parameter copy.
+Inputs are seeded and synthetic, shaped like the model shards of the
+workload (see synth/layouts.py), resident in HBM before timing starts.
+
+Default workload: the 70B-shaped shard (80 layers, d = 8192, rank 0 of 8,
+8,053,473,280 elements, 1,970 weight-decay segments, k = 2 partials,
+t = 10000...), the largest shard of the set and one of the >= 1e9-element
+shards.  Other workloads: --config {tiny,gpt2-small,7b,175b,70b}.
+
+Prints ONE JSON line on stdout (rank 0): the metric (achieved HBM GB/s by
+the algorithmic byte count, and params/s), the roofline of the kernel
+measured with HIP events on the launch stream, and the CPU oracle timed on
+a bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
+KERNEL_SRC = os.path.join(ROOT, "sharded_mixed_precision_shard_amd", "csrc", "zs_step.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(config: str, launch_key: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source and launch configuration."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(config)
+    if not ent or ent.get("kernel_sha") != kernel_source_hash() or \
+            ent.get("launch") != launch_key:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, seconds: float):
+    """Time the CPU oracle (single thread, as it stands) on a bounded window
+    of the same workload: the first min(n, 2^24) elements of the shard."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    n = min(w.n, 1 << 24)
+    master = synth.host_master(w, 0, n)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    p = np.zeros(n, np.uint16)
+    grads = synth.host_grads(w, w.t0, 0, n)
+    segs = synth.clip_segments(w.shard.segments, 0, n)
+    hp = oracle.hparams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, 1.0)
+    steps = 0
+    elapsed = 0.0
+    t = w.t0
+    while elapsed < seconds or steps == 0:
+        t0 = time.perf_counter()
+        rc = oracle.shard_step(master, m, v, p, grads, segs, hp, t)
+        elapsed += time.perf_counter() - t0
+        assert rc == 0
+        steps += 1
+        t += 1
+    bpe = 26 + 2 * w.k
+    return {
+        "value": round(n * steps * bpe / elapsed / 1e9, 4),
+        "unit": "GB/s",
+        "params_per_s": round(n * steps / elapsed, 1),
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "first %d elements of the %s shard (k=%d, %d segments in the window), "
+                  "%d oracle steps, single-threaded C, %.1f s" % (
+                      n, w.name.split(":")[0].split(" (")[0], w.k, len(segs), steps, elapsed),
+    }
+
+
+def copy_ceiling(torch, nbytes: int):
+    """Device-to-device copy of nbytes with torch (read + write), in GB/s."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    for _ in range(2):
+        dst.copy_(src)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="70b")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU oracle time budget for the cpu_baseline leg (0 = skip)")
+    ap.add_argument("--chunk-tiles", type=int, default=0, help="launch geometry override")
+    ap.add_argument("--nontemporal", type=int, default=0, help="0 default, 1 on, 2 off")
+    ap.add_argument("--copy-gb", type=float, default=8.0,
+                    help="size of the in-run copy-ceiling measurement (0 = skip)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one rank's shard step on ONE GPU; the shard step has no "
+              "cross-GPU work (the reduce-scatter and all-gather around it are not built). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sharded_mixed_precision_shard_amd as zs
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    rc = zs.zs_init(0)
+    if rc != zs.ZS_OK:
+        raise zs.ZsError(rc, "zs_init")
+
+    w = synth.workload(args.config)
+    n, k = w.n, w.k
+    bpe = 26 + 2 * k
+    bytes_per_step = bpe * n
+    assert zs.zs_algorithmic_bytes(k, n) == bytes_per_step
+    log("workload: %s  n=%d k=%d segments=%d bytes/step=%.3f GB" % (
+        w.name, n, k, len(w.shard.segments), bytes_per_step / 1e9))
+
+    copy_gbps = None
+    if args.copy_gb > 0:
+        copy_gbps = copy_ceiling(torch, int(args.copy_gb * 1e9) // 4096 * 4096)
+        log("copy ceiling (torch copy_, %.1f GB): %.1f GB/s" % (args.copy_gb, copy_gbps))
+
+    dev = torch.device("cuda:0")
+    master = torch.empty(n, dtype=torch.float32, device=dev)
+    m = torch.zeros(n, dtype=torch.float32, device=dev)
+    v = torch.zeros(n, dtype=torch.float32, device=dev)
+    param = torch.zeros(n, dtype=torch.int16, device=dev)
+    grads = [torch.empty(n, dtype=torch.int16, device=dev) for _ in range(k)]
+    table = torch.tensor([[s, 1 if f else 0] for s, f in w.shard.segments], dtype=torch.int64,
+                         device=dev)
+    st = zs.seg_table(table)
+    hp = zs.hparams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, 1.0)
+    stream = torch.cuda.current_stream()
+    synth.dev_master(w, master)
+
+    def step(t):
+        if args.chunk_tiles or args.nontemporal:
+            zs.zs_shard_step_cfg(master, m, v, param, grads, k, n, st, hp, t, stream,
+                                 chunk_tiles=args.chunk_tiles, nontemporal=args.nontemporal)
+        else:
+            zs.zs_shard_step(master, m, v, param, grads, k, n, st, hp, t, stream)
+
+    # pre-warm of the moments where the workload asks for it (fresh partials per step)
+    for t in range(1, w.prewarm_steps + 1):
+        synth.dev_grads(w, t, grads)
+        step(t)
+    # the partials of the first measured step stay resident for every timed step
+    synth.dev_grads(w, w.t0, grads)
+    torch.cuda.synchronize()
+
+    t = w.t0
+    for _ in range(args.warmup):
+        step(t)
+        t += 1
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_begin = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(t)
+        ends[i].record(stream)
+        t += 1
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_begin
+    kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_ms = sum(kernel_ms) / len(kernel_ms)
+    log("kernel ms per launch: avg %.4f min %.4f max %.4f" % (avg_ms, min(kernel_ms),
+                                                              max(kernel_ms)))
+
+    value = bytes_per_step * args.steps / elapsed / 1e9
+    achieved = bytes_per_step / (avg_ms * 1e-3) / 1e9
+    launch_key = "chunk_tiles=%d,nontemporal=%d" % (args.chunk_tiles, args.nontemporal)
+    traffic = measured_traffic(args.config, launch_key)
+
+    del master, m, v, param, grads
+    torch.cuda.empty_cache()
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+        log("cpu oracle: %.3f GB/s (%s)" % (cpu["value"], cpu["sample"]))
+
+    out = {
+        "metric": "achieved HBM GB/s (% of peak) and params/s for fused ZeRO-shard AdamW step",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 state, bf16 partials and param",
+        "data": "synthetic (seeded SplitMix64 / Irwin-Hall draws; partials of the first "
+                "measured step kept resident across timed steps)",
+        "config": {
+            "workload": w.name,
+            "shard_params": n,
+            "k_partials": k,
+            "segments": len(w.shard.segments),
+            "bytes_per_param": bpe,
+            "bytes_per_step": bytes_per_step,
+            "first_step_t": w.t0 + args.warmup,
+        },
+        "params_per_s": round(n * args.steps / elapsed, 1),
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "copy_ceiling_gbps": round(copy_gbps, 1) if copy_gbps else None,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": "shard_step_kernel<K=%d>" % k,
+            "avg_launch_ms": round(avg_ms, 4),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

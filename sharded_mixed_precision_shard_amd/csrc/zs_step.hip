@@ -10,16 +10,21 @@
 //
 // The work is purely elementwise and bandwidth bound (about 0.5 flop per HBM
 // byte), so there is no MFMA here.  Design for CDNA4:
-//   * each lane owns 8 consecutive elements of a 2048-element workgroup
-//     tile: one 16-byte load per bf16 partial, two 16-byte loads per fp32
-//     state array, 16-byte stores; every byte is read once and written once;
-//   * each workgroup owns a contiguous chunk of tiles, so its segment cursor
-//     only moves forward;
-//   * the slice of the weight-decay segment table that the chunk touches is
-//     staged in LDS once per workgroup (restaged only if the chunk crosses
-//     more than kLdsSegs entries);
-//   * segment boundaries are resolved per wavefront: a 512-element window
-//     inside one segment takes one wave-uniform flag; only windows that
+//   * a workgroup tile is 2048 elements; wavefront w of the workgroup owns
+//     the 512-element window [512w, 512w + 512) of it, as two 256-element
+//     halves; lane l owns elements 4l..4l+3 of each half.  Every load and
+//     store instruction of a wavefront is then one dense, contiguous run
+//     (1 KB per fp32 array, 512 B per bf16 array) of 16-byte (fp32) or
+//     8-byte (bf16) accesses, and every byte is read once and written once;
+//   * a workgroup owns a contiguous chunk of tiles (one tile by default: the
+//     resident workgroups then sweep memory as one compact front);
+//   * the segment holding the chunk's first element is found by one
+//     wavefront with a 64-way search of the device table (two dependent
+//     loads for up to 4096 entries); a chunk that lies inside one segment
+//     takes a workgroup-uniform decay flag, otherwise the slice of the table
+//     it touches is staged in LDS (restaged if it exceeds kLdsSegs entries);
+//   * segment boundaries inside a staged chunk are resolved per wavefront: a
+//     window inside one segment takes a wave-uniform flag; only windows that
 //     contain a boundary resolve flags per lane;
 //   * 64-bit element indices throughout (shards exceed 2^31 elements).
 //
@@ -38,18 +43,20 @@
 namespace {
 
 constexpr int kThreads = 256;                 // 4 wavefronts of 64 lanes
-constexpr int kVec = 8;                       // elements per lane per tile
-constexpr int kTile = kThreads * kVec;        // 2048 elements per tile
 constexpr int kWave = 64;
-constexpr int kWindow = kWave * kVec;         // 512 elements per wave per tile
+constexpr int kQuad = 4;                      // contiguous elements per lane per half
+constexpr int kHalf = kWave * kQuad;          // 256 elements per half window
+constexpr int kWindow = 2 * kHalf;            // 512 elements per wave per tile
+constexpr int kTile = (kThreads / kWave) * kWindow;  // 2048 elements per tile
 constexpr int kLdsSegs = 1024;                // staged segment entries
 constexpr int kMaxChunkTiles = 4096;
 constexpr int64_t kNoStart = INT64_MAX;       // sentinel past the table end
 
 static_assert(kLdsSegs % kThreads == 0, "staging rounds must be whole");
+static_assert(kTile == 2048, "tile size is part of the launch arithmetic");
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct StepArgs {
     float *master;
@@ -113,17 +120,47 @@ __device__ int32_t last_le(const zs_segment *segs, int32_t nseg, int64_t e) {
     return lo;
 }
 
-// Stage the table entries from the one covering `from` onward into LDS, in
-// rounds of kThreads, stopping after the round that reaches an entry whose
-// start is >= `until`.  Entries past the table end read as kNoStart.
-// Returns the start of the last staged entry: every element e with
-// from <= e < result resolves inside the staged slice.  Block-uniform; all
-// threads must call it.
-__device__ int64_t stage_segments(const StepArgs &a, int64_t from, int64_t until,
-                                  int64_t *s_start, uint8_t *s_flag, int32_t *s_base) {
-    if (threadIdx.x == 0) *s_base = last_le(a.segs, a.nseg, from);
+// The same search done by a whole wavefront, 64 probes per round: each round
+// narrows [lo, hi) to one of 64 sub-ranges, so a table of up to 4096
+// entries takes two dependent loads.  All 64 lanes must be active; every
+// lane returns the same index.  Reads stay in [0, nseg).
+__device__ int32_t wave_last_le(const zs_segment *segs, int32_t nseg, int64_t e) {
+    const int lane = (int)(threadIdx.x % kWave);
+    int32_t lo = 0, hi = nseg;  // answer in [lo, hi)
+    while (hi - lo > 1) {
+        const int32_t step = (hi - lo + kWave - 1) / kWave;
+        const int64_t idx = (int64_t)lo + (int64_t)lane * step;
+        const bool le = idx < hi && segs[idx].start <= e;
+        const uint64_t mask = __ballot(le);
+        const int top = mask ? 63 - __clzll(mask) : 0;
+        lo = lo + top * step;
+        hi = (lo + step < hi) ? lo + step : hi;
+    }
+    return lo;
+}
+
+// Locate the segment of element `from` and either report that [from, until)
+// lies inside it (returns until, *uniform = its decay flag) or stage the
+// table entries from it onward into LDS, in rounds of kThreads, stopping
+// after the round that reaches an entry whose start is >= until; entries
+// past the table end read as kNoStart (*uniform = -1 then).  In the staged
+// case every element e with from <= e < result resolves inside the slice.
+// Block-uniform: all threads must call it.
+__device__ int64_t locate_segments(const StepArgs &a, int64_t from, int64_t until,
+                                   int64_t *s_start, uint8_t *s_flag, int32_t *s_info,
+                                   int *uniform) {
+    if (threadIdx.x < kWave) {
+        const int32_t s = wave_last_le(a.segs, a.nseg, from);
+        if (threadIdx.x == 0) {
+            const int64_t next = s + 1 < a.nseg ? a.segs[s + 1].start : kNoStart;
+            s_info[0] = s;
+            s_info[1] = next >= until ? (a.segs[s].wd_on != 0) : -1;
+        }
+    }
     __syncthreads();
-    const int64_t base = *s_base;
+    const int64_t base = s_info[0];
+    *uniform = s_info[1];
+    if (*uniform >= 0) return until;
     int staged = 0;
     for (int r = 0; r < kLdsSegs; r += kThreads) {
         const int j = r + (int)threadIdx.x;
@@ -142,46 +179,93 @@ __device__ int64_t stage_segments(const StepArgs &a, int64_t from, int64_t until
     return s_start[staged - 1];
 }
 
+// Reduce, update and pack four consecutive elements held as one f32x4 per
+// state array and one u32x2 (4 bf16) per partial.  mask bit q = decay of
+// element q.
+template <int K>
+__device__ __forceinline__ void quad_update(f32x4 &w, f32x4 &m, f32x4 &v, const u32x2 *gr,
+                                            uint32_t mask, const StepArgs &a, u32x2 &pout) {
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+        // dword d of every partial holds elements 2d (low half) and 2d+1 (high half)
+        float g0 = bf16_lo(gr[0][d]);
+        float g1 = bf16_hi(gr[0][d]);
+#pragma unroll
+        for (int j = 1; j < K; ++j) {
+            g0 = g0 + bf16_lo(gr[j][d]);
+            g1 = g1 + bf16_hi(gr[j][d]);
+        }
+        g0 = g0 * a.gscale;
+        g1 = g1 * a.gscale;
+        float w0 = w[2 * d], m0 = m[2 * d], v0 = v[2 * d];
+        float w1 = w[2 * d + 1], m1 = m[2 * d + 1], v1 = v[2 * d + 1];
+        adamw(w0, m0, v0, g0, (mask >> (2 * d)) & 1u, a);
+        adamw(w1, m1, v1, g1, (mask >> (2 * d + 1)) & 1u, a);
+        w[2 * d] = w0; m[2 * d] = m0; v[2 * d] = v0;
+        w[2 * d + 1] = w1; m[2 * d + 1] = m1; v[2 * d + 1] = v1;
+        pout[d] = to_bf16(w0) | (to_bf16(w1) << 16);
+    }
+}
+
+template <int K>
+__device__ __forceinline__ void scalar_update(const StepArgs &a, int64_t i, bool decay) {
+    float g = __uint_as_float((uint32_t)a.grads[0][i] << 16);
+#pragma unroll
+    for (int j = 1; j < K; ++j) g = g + __uint_as_float((uint32_t)a.grads[j][i] << 16);
+    g = g * a.gscale;
+    float wv = a.master[i], mv = a.m[i], vv = a.v[i];
+    adamw(wv, mv, vv, g, decay, a);
+    a.master[i] = wv;
+    a.m[i] = mv;
+    a.v[i] = vv;
+    a.param[i] = (uint16_t)to_bf16(wv);
+}
+
 template <int K, int NT>
 __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) {
     __shared__ int64_t s_start[kLdsSegs];
     __shared__ uint8_t s_flag[kLdsSegs];
-    __shared__ int32_t s_base;
+    __shared__ int32_t s_info[2];
 
     const int tid = (int)threadIdx.x;
+    const int lane = tid % kWave;
     const int wave = tid / kWave;
     const int64_t c0 = (int64_t)blockIdx.x * a.chunk;
     if (c0 >= a.n) return;  // block-uniform
     const int64_t c1 = (c0 + a.chunk < a.n) ? c0 + a.chunk : a.n;
 
-    int64_t lim = stage_segments(a, c0, c1, s_start, s_flag, &s_base);
-    int wc = 0;  // this wave's cursor into the staged slice
+    int uniform;  // decay flag of the whole located range, or -1 when staged
+    int64_t lim = locate_segments(a, c0, c1, s_start, s_flag, s_info, &uniform);
+    int wc = 0;   // this wave's cursor into the staged slice
 
     for (int64_t t0 = c0; t0 < c1; t0 += kTile) {
         const int64_t tend = (t0 + kTile < c1) ? t0 + kTile : c1;
         bool overflow = false;
-        if (tend > lim) {  // block-uniform: the slice ends inside this tile
+        if (tend > lim) {  // block-uniform: the located range ends inside this tile
             __syncthreads();
-            lim = stage_segments(a, t0, c1, s_start, s_flag, &s_base);
+            lim = locate_segments(a, t0, c1, s_start, s_flag, s_info, &uniform);
             wc = 0;
             overflow = tend > lim;
         }
         const int64_t w0 = t0 + (int64_t)wave * kWindow;
         if (w0 >= tend) continue;  // wave-uniform
         const int64_t w1 = (w0 + kWindow < tend) ? w0 + kWindow : tend;
-        const int64_t e = t0 + (int64_t)tid * kVec;
+        const int64_t ea = w0 + (int64_t)lane * kQuad;  // first half: ea .. ea+3
+        const int64_t eb = ea + kHalf;                  // second half: eb .. eb+3
 
-        // Decay flags of this lane's 8 elements, one bit each.
+        // Decay flags of this lane's 8 elements: bits 0-3 for ea+q, 4-7 for eb+q.
         uint32_t mask;
-        if (!overflow) {
+        if (uniform >= 0) {
+            mask = uniform ? 0xffu : 0u;
+        } else if (!overflow) {
             while (s_start[wc + 1] <= w0) ++wc;
             if (s_start[wc + 1] >= w1) {
                 mask = s_flag[wc] ? 0xffu : 0u;
             } else {
                 mask = 0;
                 int lc = wc;
-                for (int q = 0; q < kVec; ++q) {
-                    const int64_t eq = e + q;
+                for (int q = 0; q < 2 * kQuad; ++q) {
+                    const int64_t eq = (q < kQuad ? ea : eb - kQuad) + q;
                     if (eq >= w1) break;
                     while (s_start[lc + 1] <= eq) ++lc;
                     mask |= (uint32_t)s_flag[lc] << q;
@@ -189,72 +273,46 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
             }
         } else {
             mask = 0;
-            for (int q = 0; q < kVec; ++q) {
-                const int64_t eq = e + q;
+            for (int q = 0; q < 2 * kQuad; ++q) {
+                const int64_t eq = (q < kQuad ? ea : eb - kQuad) + q;
                 if (eq >= w1) break;
                 const int32_t s = last_le(a.segs, a.nseg, eq);
                 mask |= (uint32_t)(a.segs[s].wd_on != 0) << q;
             }
         }
 
-        if (e + kVec <= a.n) {
-            // Full 8-element group: 16-byte vector traffic only.
-            const f32x4 *pw = reinterpret_cast<const f32x4 *>(a.master + e);
-            const f32x4 *pm = reinterpret_cast<const f32x4 *>(a.m + e);
-            const f32x4 *pv = reinterpret_cast<const f32x4 *>(a.v + e);
-            f32x4 w[2] = {load<NT>(pw), load<NT>(pw + 1)};
-            f32x4 m[2] = {load<NT>(pm), load<NT>(pm + 1)};
-            f32x4 v[2] = {load<NT>(pv), load<NT>(pv + 1)};
-            u32x4 gr[K];
+        if (w0 + kWindow <= a.n) {
+            // Whole window in range: dense vector traffic only.
+            const f32x4 *pw = reinterpret_cast<const f32x4 *>(a.master);
+            const f32x4 *pm = reinterpret_cast<const f32x4 *>(a.m);
+            const f32x4 *pv = reinterpret_cast<const f32x4 *>(a.v);
+            const int64_t qa = ea / kQuad, qb = eb / kQuad;  // f32x4 / u32x2 indices
+            f32x4 wa = load<NT>(pw + qa), wb = load<NT>(pw + qb);
+            f32x4 ma = load<NT>(pm + qa), mb = load<NT>(pm + qb);
+            f32x4 va = load<NT>(pv + qa), vb = load<NT>(pv + qb);
+            u32x2 ga[K], gb[K];
 #pragma unroll
-            for (int j = 0; j < K; ++j)
-                gr[j] = load<NT>(reinterpret_cast<const u32x4 *>(a.grads[j] + e));
-
-            u32x4 pout;
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                // dword d of every partial holds elements 2d (low) and 2d+1 (high)
-                float g0 = bf16_lo(gr[0][d]);
-                float g1 = bf16_hi(gr[0][d]);
-#pragma unroll
-                for (int j = 1; j < K; ++j) {
-                    g0 = g0 + bf16_lo(gr[j][d]);
-                    g1 = g1 + bf16_hi(gr[j][d]);
-                }
-                g0 = g0 * a.gscale;
-                g1 = g1 * a.gscale;
-                const int h = d >> 1;         // which f32x4 half
-                const int l = (d & 1) * 2;    // lane inside the f32x4
-                float w0v = w[h][l], m0v = m[h][l], v0v = v[h][l];
-                float w1v = w[h][l + 1], m1v = m[h][l + 1], v1v = v[h][l + 1];
-                adamw(w0v, m0v, v0v, g0, (mask >> (2 * d)) & 1u, a);
-                adamw(w1v, m1v, v1v, g1, (mask >> (2 * d + 1)) & 1u, a);
-                w[h][l] = w0v; m[h][l] = m0v; v[h][l] = v0v;
-                w[h][l + 1] = w1v; m[h][l + 1] = m1v; v[h][l + 1] = v1v;
-                pout[d] = to_bf16(w0v) | (to_bf16(w1v) << 16);
+            for (int j = 0; j < K; ++j) {
+                const u32x2 *pg = reinterpret_cast<const u32x2 *>(a.grads[j]);
+                ga[j] = load<NT>(pg + qa);
+                gb[j] = load<NT>(pg + qb);
             }
-            f32x4 *qw = reinterpret_cast<f32x4 *>(a.master + e);
-            f32x4 *qm = reinterpret_cast<f32x4 *>(a.m + e);
-            f32x4 *qv = reinterpret_cast<f32x4 *>(a.v + e);
-            store<NT>(qw, w[0]); store<NT>(qw + 1, w[1]);
-            store<NT>(qm, m[0]); store<NT>(qm + 1, m[1]);
-            store<NT>(qv, v[0]); store<NT>(qv + 1, v[1]);
-            store<NT>(reinterpret_cast<u32x4 *>(a.param + e), pout);
-        } else if (e < a.n) {
-            // Ragged tail of the shard (fewer than 8 elements): scalar traffic.
-            const int cnt = (int)(a.n - e);
-            for (int q = 0; q < cnt; ++q) {
-                const int64_t i = e + q;
-                float g = __uint_as_float((uint32_t)a.grads[0][i] << 16);
-#pragma unroll
-                for (int j = 1; j < K; ++j) g = g + __uint_as_float((uint32_t)a.grads[j][i] << 16);
-                g = g * a.gscale;
-                float wv = a.master[i], mv = a.m[i], vv = a.v[i];
-                adamw(wv, mv, vv, g, (mask >> q) & 1u, a);
-                a.master[i] = wv;
-                a.m[i] = mv;
-                a.v[i] = vv;
-                a.param[i] = (uint16_t)to_bf16(wv);
+            u32x2 pa, pb;
+            quad_update<K>(wa, ma, va, ga, mask & 0xfu, a, pa);
+            quad_update<K>(wb, mb, vb, gb, mask >> 4, a, pb);
+            f32x4 *qw = reinterpret_cast<f32x4 *>(a.master);
+            f32x4 *qm = reinterpret_cast<f32x4 *>(a.m);
+            f32x4 *qv = reinterpret_cast<f32x4 *>(a.v);
+            u32x2 *qp = reinterpret_cast<u32x2 *>(a.param);
+            store<NT>(qw + qa, wa); store<NT>(qw + qb, wb);
+            store<NT>(qm + qa, ma); store<NT>(qm + qb, mb);
+            store<NT>(qv + qa, va); store<NT>(qv + qb, vb);
+            store<NT>(qp + qa, pa); store<NT>(qp + qb, pb);
+        } else {
+            // The shard's last, partial window: element by element.
+            for (int q = 0; q < 2 * kQuad; ++q) {
+                const int64_t i = (q < kQuad ? ea : eb - kQuad) + q;
+                if (i < a.n) scalar_update<K>(a, i, (mask >> q) & 1u);
             }
         }
     }
@@ -316,14 +374,14 @@ bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 int pick_chunk_tiles(int64_t n, int cus) {
-    // Enough workgroups for many rounds of residency on every compute unit,
-    // long enough chunks that the per-workgroup table staging is noise.
-    const int64_t tiles = (n + kTile - 1) / kTile;
-    const int64_t target = (int64_t)cus * 64;
-    int64_t ct = tiles / (target > 0 ? target : 1);
-    if (ct < 1) ct = 1;
-    if (ct > 32) ct = 32;
-    return (int)ct;
+    // One tile per workgroup: the resident workgroups then cover one compact
+    // stretch of every array and sweep through memory together, which
+    // measured best on MI355X for every shard size (longer chunks spread the
+    // active front over more DRAM pages).  The per-workgroup segment search
+    // is two dependent table loads and hides behind the other workgroups.
+    (void)n;
+    (void)cus;
+    return 1;
 }
 
 int validate_and_launch(float *master, float *m, float *v, uint16_t *param,

@@ -18,7 +18,8 @@ import subprocess
 
 import numpy as np
 
-from .layouts import WORKLOADS, Shard, Workload, decay_mask_full, shard_of, workload  # noqa
+from .layouts import (WORKLOADS, Shard, Workload, clip_segments, decay_mask_full,  # noqa
+                      shard_of, workload)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 HOST_LIB = os.path.join(_HERE, "libzs_synth_host.so")

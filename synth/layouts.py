@@ -90,6 +90,19 @@ def shard_of(tensors: List[Tensor], p: int, rank: int) -> Shard:
     return Shard(n=n, index0=lo, valid_end=total, segments=segs, total=total, padded=padded)
 
 
+def clip_segments(segments, lo, hi):
+    """The shard's table restricted to window [lo, hi), rebased to lo."""
+    out = []
+    for i, (s, f) in enumerate(segments):
+        e = segments[i + 1][0] if i + 1 < len(segments) else None
+        if (e is None or e > lo) and s < hi:
+            out.append((max(s, lo) - lo, f))
+    # collapse entries that all start at 0 to the last one (same lookup result)
+    while len(out) > 1 and out[1][0] == 0:
+        out.pop(0)
+    return out
+
+
 def decay_mask_full(tensors: List[Tensor], padded: int):
     """Per-element decay flag of the whole padded flat buffer (numpy uint8)."""
     import numpy as np

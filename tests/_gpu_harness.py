@@ -69,19 +69,6 @@ def segment_tensor(segments, device):
     return t.tensor(rows, dtype=t.int64, device=device)
 
 
-def clip_segments(segments, lo, hi):
-    """The shard's table restricted to window [lo, hi), rebased to lo."""
-    out = []
-    for i, (s, f) in enumerate(segments):
-        e = segments[i + 1][0] if i + 1 < len(segments) else None
-        if (e is None or e > lo) and s < hi:
-            out.append((max(s, lo) - lo, f))
-    # collapse entries that all start at 0 to the last one (same lookup result)
-    while len(out) > 1 and out[1][0] == 0:
-        out.pop(0)
-    return out
-
-
 def oracle_window(w: synth.Workload, lo, hi, steps):
     """Run the oracle over shard elements [lo, hi) for the given optimizer
     steps (inputs regenerated on the host).  Returns (master, m, v, param)."""
@@ -90,7 +77,7 @@ def oracle_window(w: synth.Workload, lo, hi, steps):
     m = np.zeros(n, F32)
     v = np.zeros(n, F32)
     p = np.zeros(n, np.uint16)
-    segs = clip_segments(w.shard.segments, lo, hi)
+    segs = synth.clip_segments(w.shard.segments, lo, hi)
     hp = oracle.hparams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, 1.0)
     for t in steps:
         rc = oracle.shard_step(master, m, v, p, synth.host_grads(w, t, lo, hi), segs, hp, t)
