@@ -400,12 +400,14 @@ int validate_and_launch(float *master, float *m, float *v, uint16_t *param,
         return ZS_ERR_INVALID_ARGUMENT;
     if (st->count < 1) return ZS_ERR_INVALID_ARGUMENT;
     if (st->count > ZS_MAX_SEGMENTS) return ZS_ERR_TOO_MANY_SEGMENTS;
-    int chunk_tiles = 0, nt = 0;
+    // Streaming (non-temporal) loads and stores by default: nothing is
+    // reused, and on MI355X they measured 5-10 % faster than cached access.
+    int chunk_tiles = 0, nt = 1;
     if (cfg) {
         if (cfg->chunk_tiles < 0 || cfg->chunk_tiles > kMaxChunkTiles) return ZS_ERR_INVALID_ARGUMENT;
         if (cfg->nontemporal < 0 || cfg->nontemporal > 2) return ZS_ERR_INVALID_ARGUMENT;
         chunk_tiles = cfg->chunk_tiles;
-        nt = cfg->nontemporal == 1 ? 1 : 0;
+        nt = cfg->nontemporal == 2 ? 0 : 1;
     }
     if (n == 0) return ZS_OK;
     if (!master || !m || !v || !param || !st->segs) return ZS_ERR_INVALID_ARGUMENT;
