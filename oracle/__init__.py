@@ -67,6 +67,10 @@ def _load():
         lib.zs_oracle_bf16_rne_array.restype = None
         lib.zs_oracle_scalars.argtypes = [P, ctypes.c_int64, P]
         lib.zs_oracle_scalars.restype = None
+        lib.zs_oracle_q8_blocks.argtypes = [P, ctypes.c_int64, ctypes.c_int32, P, P]
+        lib.zs_oracle_q8_blocks.restype = ctypes.c_int
+        lib.zs_oracle_q8_dequant.argtypes = [P, P, ctypes.c_int64, ctypes.c_int32, P]
+        lib.zs_oracle_q8_dequant.restype = None
         _lib = lib
     return _lib
 
@@ -149,3 +153,23 @@ def scalars(hp: Hparams, step: int):
 def bf16_to_f32(h: np.ndarray) -> np.ndarray:
     """bf16 bit patterns -> float32 (exact: the 16 low bits are zero)."""
     return (np.asarray(h, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def q8_blocks(x_bf16: np.ndarray, block: int = 256):
+    """Block-wise int8 quantization of bf16 bit patterns -> (q int8[n], scale float32[nb])."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    n = x.shape[0]
+    q = np.zeros(n, dtype=np.int8)
+    sc = np.zeros(max(0, -(-n // block)), dtype=np.float32)
+    rc = _load().zs_oracle_q8_blocks(_ptr(x), n, block, _ptr(q), _ptr(sc) if sc.size else None)
+    if rc != 0:
+        raise ValueError("zs_oracle_q8_blocks: invalid argument")
+    return q, sc
+
+
+def q8_dequant(q: np.ndarray, scale: np.ndarray, block: int = 256) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    scale = np.ascontiguousarray(scale, dtype=np.float32)
+    out = np.empty(q.shape[0], dtype=np.float32)
+    _load().zs_oracle_q8_dequant(_ptr(q), _ptr(scale), q.shape[0], block, _ptr(out))
+    return out

@@ -232,3 +232,59 @@ void zs_oracle_scalars(const zo_hparams *hp, int64_t step, float out[5])
     out[3] = s.bc2;
     out[4] = s.df;
 }
+
+/*
+ * Block-wise symmetric int8 quantization of bf16 values: the payload of a
+ * quantized all-gather ("Chapter 9: Distributed Training and Data
+ * Parallelism", section 9.4.3, ZeRO++: weights converted from 16-bit to INT8
+ * before the all-gather and dequantized after it; block-wise quantization to
+ * limit the loss).  The pages give neither the block size nor the scale
+ * rule; the reading is the plainest one:
+ *   blocks of `block` consecutive elements from element 0 (the last block may
+ *   be shorter); a = max |x| over the block (NaN if any element is NaN);
+ *   scale = a / 127 in binary32; q = clamp(round_half_even(x / scale),
+ *   -127, 127), except that every q of a block whose scale is 0 or not finite
+ *   is 0.  The receiver reconstructs q * scale.
+ */
+int zs_oracle_q8_blocks(const uint16_t *x_bf16, int64_t n, int32_t block, int8_t *q,
+                        float *scale)
+{
+    if (n < 0 || block < 1) return ZO_ERR_INVALID;
+    if (n == 0) return ZO_OK;
+    if (!x_bf16 || !q || !scale) return ZO_ERR_INVALID;
+    int64_t nblocks = (n + block - 1) / block;
+    for (int64_t b = 0; b < nblocks; ++b) {
+        int64_t lo = b * block;
+        int64_t hi = lo + block < n ? lo + block : n;
+        float a = 0.0f;
+        int has_nan = 0;
+        for (int64_t i = lo; i < hi; ++i) {
+            float x = bf16_to_f32(x_bf16[i]);
+            if (isnan(x)) has_nan = 1;
+            else if (fabsf(x) > a) a = fabsf(x);
+        }
+        if (has_nan) a = NAN;
+        float s = a / 127.0f;
+        scale[b] = s;
+        int usable = isfinite(s) && s > 0.0f;
+        for (int64_t i = lo; i < hi; ++i) {
+            if (!usable) {
+                q[i] = 0;
+                continue;
+            }
+            float r = rintf(bf16_to_f32(x_bf16[i]) / s);
+            if (r > 127.0f) r = 127.0f;
+            if (r < -127.0f) r = -127.0f;
+            q[i] = (int8_t)r;
+        }
+    }
+    return ZO_OK;
+}
+
+/* Receiver side of the quantized all-gather: x = q * scale (binary32). */
+void zs_oracle_q8_dequant(const int8_t *q, const float *scale, int64_t n, int32_t block,
+                          float *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = (float)q[i] * scale[i / block];
+}
