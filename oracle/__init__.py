@@ -71,6 +71,13 @@ def _load():
         lib.zs_oracle_q8_blocks.restype = ctypes.c_int
         lib.zs_oracle_q8_dequant.argtypes = [P, P, ctypes.c_int64, ctypes.c_int32, P]
         lib.zs_oracle_q8_dequant.restype = None
+        lib.zs_oracle_shard_step_q8grad.argtypes = [P, P, P, P, P, P, ctypes.c_int,
+                                                    ctypes.c_int64, ctypes.c_int32, P,
+                                                    ctypes.c_int32, P, ctypes.c_int64]
+        lib.zs_oracle_shard_step_q8grad.restype = ctypes.c_int
+        lib.zs_oracle_shard_step_bf16mv.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int64,
+                                                    P, ctypes.c_int32, P, ctypes.c_int64]
+        lib.zs_oracle_shard_step_bf16mv.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -173,3 +180,45 @@ def q8_dequant(q: np.ndarray, scale: np.ndarray, block: int = 256) -> np.ndarray
     out = np.empty(q.shape[0], dtype=np.float32)
     _load().zs_oracle_q8_dequant(_ptr(q), _ptr(scale), q.shape[0], block, _ptr(out))
     return out
+
+
+def shard_step_q8grad(master, m, v, param_bf16, qgrads, qscales, segs, hp: Hparams, step: int,
+                      block: int = 256) -> int:
+    """Oracle step on int8 partials qgrads[j] (int8[n]) with block scales
+    qscales[j] (float32[ceil(n/block)])."""
+    n = master.shape[0]
+    _check(master, np.float32, n, "master")
+    _check(m, np.float32, n, "m")
+    _check(v, np.float32, n, "v")
+    _check(param_bf16, np.uint16, n, "param_bf16")
+    nb = -(-n // block)
+    for q, s in zip(qgrads, qscales):
+        _check(q, np.int8, n, "qgrad")
+        _check(s, np.float32, nb, "qscale")
+    k = len(qgrads)
+    qp = (ctypes.c_void_p * max(k, 1))(*[q.ctypes.data for q in qgrads])
+    sp = (ctypes.c_void_p * max(k, 1))(*[s.ctypes.data for s in qscales])
+    seg_arr = segs if isinstance(segs, ctypes.Array) else segments_array(segs)
+    return _load().zs_oracle_shard_step_q8grad(
+        _ptr(master), _ptr(m), _ptr(v), _ptr(param_bf16), ctypes.cast(qp, ctypes.c_void_p),
+        ctypes.cast(sp, ctypes.c_void_p), k, n, block, ctypes.cast(seg_arr, ctypes.c_void_p),
+        len(seg_arr), ctypes.byref(hp), int(step))
+
+
+def shard_step_bf16mv(master, m_bf16, v_bf16, param_bf16, grads, segs, hp: Hparams,
+                      step: int) -> int:
+    """Oracle step with bf16 moments (uint16 bit patterns, updated in place)."""
+    n = master.shape[0]
+    _check(master, np.float32, n, "master")
+    _check(m_bf16, np.uint16, n, "m")
+    _check(v_bf16, np.uint16, n, "v")
+    _check(param_bf16, np.uint16, n, "param_bf16")
+    for g in grads:
+        _check(g, np.uint16, n, "grad")
+    k = len(grads)
+    gp = (ctypes.c_void_p * max(k, 1))(*[g.ctypes.data for g in grads])
+    seg_arr = segs if isinstance(segs, ctypes.Array) else segments_array(segs)
+    return _load().zs_oracle_shard_step_bf16mv(
+        _ptr(master), _ptr(m_bf16), _ptr(v_bf16), _ptr(param_bf16),
+        ctypes.cast(gp, ctypes.c_void_p), k, n, ctypes.cast(seg_arr, ctypes.c_void_p),
+        len(seg_arr), ctypes.byref(hp), int(step))

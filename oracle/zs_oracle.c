@@ -288,3 +288,84 @@ void zs_oracle_q8_dequant(const int8_t *q, const float *scale, int64_t n, int32_
     for (int64_t i = 0; i < n; ++i)
         out[i] = (float)q[i] * scale[i / block];
 }
+
+static int segs_ok(const zo_segment *segs, int32_t nseg)
+{
+    if (nseg < 1 || !segs || segs[0].start != 0) return 0;
+    for (int32_t s = 1; s < nseg; ++s)
+        if (segs[s].start < segs[s - 1].start) return 0;
+    return 1;
+}
+
+/*
+ * Shard step whose k partials arrive block-quantized to int8 (the quantized
+ * reduce-scatter of "Chapter 9", section 9.4.3): partial j of element i is
+ * q[j][i] * scale[j][i / block], one binary32 rounding; the partials are then
+ * summed in the left fold j = 0..k-1 and multiplied by grad_scale, and the
+ * rest is the ordinary step.
+ */
+int zs_oracle_shard_step_q8grad(float *master, float *m, float *v, uint16_t *param_bf16,
+                                const int8_t *const *q, const float *const *scale, int k,
+                                int64_t n, int32_t block, const zo_segment *segs,
+                                int32_t nseg, const zo_hparams *hp, int64_t step)
+{
+    if (k < 1 || n < 0 || block < 1 || step < 1 || !hparams_ok(hp)) return ZO_ERR_INVALID;
+    if (!segs_ok(segs, nseg)) return ZO_ERR_INVALID;
+    if (n == 0) return ZO_OK;
+    if (!master || !m || !v || !param_bf16 || !q || !scale) return ZO_ERR_INVALID;
+    for (int j = 0; j < k; ++j)
+        if (!q[j] || !scale[j]) return ZO_ERR_INVALID;
+    zo_scalars sc = make_scalars(hp, step);
+    int32_t seg = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        while (seg + 1 < nseg && segs[seg + 1].start <= i)
+            ++seg;
+        int64_t b = i / block;
+        float g = (float)q[0][i] * scale[0][b];
+        for (int j = 1; j < k; ++j) {
+            float t = (float)q[j][i] * scale[j][b];
+            g = g + t;
+        }
+        g = g * hp->grad_scale;
+        adamw_element(&master[i], &m[i], &v[i], g, segs[seg].wd_on != 0, hp, &sc);
+        param_bf16[i] = zs_oracle_bf16_rne(master[i]);
+    }
+    return ZO_OK;
+}
+
+/*
+ * Shard step with the moments kept in bf16 ("Lecture 7: Parallelism I",
+ * section 8.4: everything in BF16 except the fp32 master weights).  m and v
+ * are widened to binary32, updated as in the ordinary step (the weight
+ * update uses the unrounded new moments), then stored rounded to nearest
+ * even (reading: the page does not say how they are rounded).
+ */
+int zs_oracle_shard_step_bf16mv(float *master, uint16_t *m, uint16_t *v, uint16_t *param_bf16,
+                                const uint16_t *const *grads, int k, int64_t n,
+                                const zo_segment *segs, int32_t nseg, const zo_hparams *hp,
+                                int64_t step)
+{
+    if (k < 1 || n < 0 || step < 1 || !hparams_ok(hp)) return ZO_ERR_INVALID;
+    if (!segs_ok(segs, nseg)) return ZO_ERR_INVALID;
+    if (n == 0) return ZO_OK;
+    if (!master || !m || !v || !param_bf16 || !grads) return ZO_ERR_INVALID;
+    for (int j = 0; j < k; ++j)
+        if (!grads[j]) return ZO_ERR_INVALID;
+    zo_scalars sc = make_scalars(hp, step);
+    int32_t seg = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        while (seg + 1 < nseg && segs[seg + 1].start <= i)
+            ++seg;
+        float g = bf16_to_f32(grads[0][i]);
+        for (int j = 1; j < k; ++j)
+            g = g + bf16_to_f32(grads[j][i]);
+        g = g * hp->grad_scale;
+        float mf = bf16_to_f32(m[i]);
+        float vf = bf16_to_f32(v[i]);
+        adamw_element(&master[i], &mf, &vf, g, segs[seg].wd_on != 0, hp, &sc);
+        m[i] = zs_oracle_bf16_rne(mf);
+        v[i] = zs_oracle_bf16_rne(vf);
+        param_bf16[i] = zs_oracle_bf16_rne(master[i]);
+    }
+    return ZO_OK;
+}
