@@ -48,12 +48,13 @@ extern "C" {
 
 #define ZS_MAX_K 16           /* most gradient partials one call sums */
 #define ZS_MAX_SEGMENTS 65536 /* most entries in one segment table */
+#define ZS_Q8_BLOCK 256       /* elements per int8 quantization block */
 
 typedef enum {
     ZS_OK = 0,
     ZS_ERR_NOT_INITIALIZED = 1, /* zs_init not called, or zs_fini called */
     ZS_ERR_INVALID_ARGUMENT = 2,/* bad pointer, size, k, step or hparams */
-    ZS_ERR_MISALIGNED = 3,      /* a buffer base is not 16-byte aligned */
+    ZS_ERR_MISALIGNED = 3,      /* a buffer base is not aligned as documented */
     ZS_ERR_TOO_MANY_SEGMENTS = 4,
     ZS_ERR_DEVICE = 5,          /* a HIP call failed; see zs_last_device_error */
     ZS_ERR_ALIASING = 6         /* output ranges overlap each other or an input */
@@ -141,6 +142,70 @@ int zs_shard_step_cfg(float *master, float *m, float *v, uint16_t *param_bf16,
                       const uint16_t *const *grads, int k, int64_t n,
                       const zs_seg_table *seg_table, const zs_hparams *hparams,
                       int64_t step, void *stream, const zs_launch_cfg *cfg);
+
+/*
+ * zs_shard_step that also writes the block-quantized int8 copy of the new
+ * parameters: the payload of a quantized all-gather ("Chapter 9: Distributed
+ * Training and Data Parallelism", section 9.4.3, ZeRO++: 16-bit weights are
+ * converted to INT8 before the all-gather, halving its volume, and
+ * dequantized after it; quantization is block-wise).  The pages give no
+ * block size or scale rule; the reading used:
+ *   blocks of ZS_Q8_BLOCK consecutive shard elements from element 0 (the
+ *   last block may be shorter); x = the new bf16 parameter as fp32;
+ *   a = max |x| over the block (NaN if any x is NaN); scale = a / 127
+ *   (binary32); q = clamp(round_half_even(x / scale), -127, 127), and q = 0
+ *   for every element of a block whose scale is 0 or not finite.
+ *   The receiver reconstructs x ~ q * scale, |x - q*scale| <= scale / 2.
+ *
+ *   param_q8       : DEVICE int8 [n], written only, 16-byte aligned
+ *   param_q8_scale : DEVICE fp32 [ceil(n / ZS_Q8_BLOCK)], written only,
+ *                    4-byte aligned
+ * Every other argument, the other outputs and the errors are those of
+ * zs_shard_step; the two new ranges must not overlap any other buffer.
+ * Extra HBM traffic: n + 4 * ceil(n / 256) bytes written.
+ */
+int zs_shard_step_q8ag(float *master, float *m, float *v, uint16_t *param_bf16,
+                       int8_t *param_q8, float *param_q8_scale,
+                       const uint16_t *const *grads, int k, int64_t n,
+                       const zs_seg_table *seg_table, const zs_hparams *hparams,
+                       int64_t step, void *stream);
+
+/*
+ * zs_shard_step whose k partials arrive block-quantized to int8, as a
+ * quantized reduce-scatter would deliver them ("Chapter 9", section 9.4.3,
+ * ZeRO++: gradients of the reduce-scatter quantized block-wise).  Partial j
+ * of element i is qgrads[j][i] * qscales[j][i / ZS_Q8_BLOCK], each product
+ * rounded once in binary32; the partials are then summed in the same left
+ * fold j = 0 .. k-1 as zs_shard_step and multiplied by grad_scale.
+ *
+ *   qgrads  : HOST array of k DEVICE pointers, int8 [n], 16-byte aligned
+ *   qscales : HOST array of k DEVICE pointers, fp32 [ceil(n / ZS_Q8_BLOCK)],
+ *             4-byte aligned
+ * Everything else as zs_shard_step.  HBM traffic per element:
+ * 12 + k (1 + 4/256) bytes read, 14 written.
+ */
+int zs_shard_step_q8grad(float *master, float *m, float *v, uint16_t *param_bf16,
+                         const int8_t *const *qgrads, const float *const *qscales, int k,
+                         int64_t n, const zs_seg_table *seg_table, const zs_hparams *hparams,
+                         int64_t step, void *stream);
+
+/*
+ * zs_shard_step with the moments m and v stored as bf16: the "everything in
+ * BF16 except the fp32 master weights" state of "Lecture 7: Parallelism I",
+ * section 8.4 (12 bytes per parameter instead of 16).  Each element's m and
+ * v are widened to fp32, updated exactly as in zs_shard_step (the weight
+ * update uses the unrounded new moments), and stored back rounded to nearest
+ * even (reading: the page does not say how the moments are rounded).
+ *
+ *   m_bf16, v_bf16 : DEVICE bf16 [n], read and updated in place, 16-byte
+ *                    aligned
+ * Everything else as zs_shard_step.  HBM traffic per element: 8 + 2k bytes
+ * read, 10 written.
+ */
+int zs_shard_step_bf16mv(float *master, uint16_t *m_bf16, uint16_t *v_bf16,
+                         uint16_t *param_bf16, const uint16_t *const *grads, int k, int64_t n,
+                         const zs_seg_table *seg_table, const zs_hparams *hparams,
+                         int64_t step, void *stream);
 
 /* Release what zs_init recorded.  Later calls return ZS_ERR_NOT_INITIALIZED
  * until zs_init is called again.  Always returns ZS_OK. */

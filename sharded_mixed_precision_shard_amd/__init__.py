@@ -6,7 +6,8 @@ or as plain integer device addresses.  There is no CPU fallback: if
 ``libzs.so`` has not been built, importing the library raises.
 
 Entry points keep the C names: :func:`zs_init`, :func:`zs_shard_step`,
-:func:`zs_shard_step_cfg`, :func:`zs_fini`, :func:`zs_status_string`,
+:func:`zs_shard_step_cfg`, :func:`zs_shard_step_q8ag`, :func:`zs_shard_step_q8grad`,
+:func:`zs_shard_step_bf16mv`, :func:`zs_fini`, :func:`zs_status_string`,
 :func:`zs_last_device_error`, :func:`zs_algorithmic_bytes`.
 """
 from __future__ import annotations
@@ -19,6 +20,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libzs.so")
 
 ZS_MAX_K = 16
 ZS_MAX_SEGMENTS = 65536
+ZS_Q8_BLOCK = 256
 
 ZS_OK = 0
 ZS_ERR_NOT_INITIALIZED = 1
@@ -29,7 +31,8 @@ ZS_ERR_DEVICE = 5
 ZS_ERR_ALIASING = 6
 
 # Symbols declared in include/zs.h.
-EXPORTS = ("zs_init", "zs_shard_step", "zs_shard_step_cfg", "zs_fini", "zs_status_string",
+EXPORTS = ("zs_init", "zs_shard_step", "zs_shard_step_cfg", "zs_shard_step_q8ag",
+           "zs_shard_step_q8grad", "zs_shard_step_bf16mv", "zs_fini", "zs_status_string",
            "zs_last_device_error", "zs_algorithmic_bytes")
 
 
@@ -81,6 +84,14 @@ def load_library():
     lib.zs_shard_step.restype = ctypes.c_int
     lib.zs_shard_step_cfg.argtypes = step_args + [P]
     lib.zs_shard_step_cfg.restype = ctypes.c_int
+    lib.zs_shard_step_q8ag.argtypes = [P, P, P, P, P, P, P, ctypes.c_int, ctypes.c_int64, P, P,
+                                       ctypes.c_int64, P]
+    lib.zs_shard_step_q8ag.restype = ctypes.c_int
+    lib.zs_shard_step_q8grad.argtypes = [P, P, P, P, P, P, ctypes.c_int, ctypes.c_int64, P, P,
+                                         ctypes.c_int64, P]
+    lib.zs_shard_step_q8grad.restype = ctypes.c_int
+    lib.zs_shard_step_bf16mv.argtypes = step_args
+    lib.zs_shard_step_bf16mv.restype = ctypes.c_int
     lib.zs_fini.argtypes = []
     lib.zs_fini.restype = ctypes.c_int
     lib.zs_status_string.argtypes = [ctypes.c_int]
@@ -184,3 +195,70 @@ def zs_shard_step_cfg(master, m, v, param_bf16, grads, k, n, seg_table_, hparams
     if check and rc != ZS_OK:
         raise ZsError(rc, "zs_shard_step_cfg")
     return rc
+
+
+def _ptr_array(xs):
+    return (ctypes.c_void_p * max(len(xs), 1))(*[_addr(x) for x in xs])
+
+
+def zs_shard_step_q8ag(master, m, v, param_bf16, param_q8, param_q8_scale, grads, k, n,
+                       seg_table_, hparams_, step, stream=None, check=True) -> int:
+    """zs_shard_step that also writes the int8 block-quantized parameter copy
+    (param_q8: int8[n]) and its block scales (float32[ceil(n/256)])."""
+    gp = _ptr_array(grads)
+    st = seg_table_ if isinstance(seg_table_, ZsSegTable) else seg_table(seg_table_)
+    rc = load_library().zs_shard_step_q8ag(
+        ctypes.c_void_p(_addr(master)), ctypes.c_void_p(_addr(m)), ctypes.c_void_p(_addr(v)),
+        ctypes.c_void_p(_addr(param_bf16)), ctypes.c_void_p(_addr(param_q8)),
+        ctypes.c_void_p(_addr(param_q8_scale)), ctypes.cast(gp, ctypes.c_void_p),
+        int(len(grads) if k is None else k), int(n), ctypes.byref(st), ctypes.byref(hparams_),
+        int(step), ctypes.c_void_p(_stream_handle(stream)))
+    if check and rc != ZS_OK:
+        raise ZsError(rc, "zs_shard_step_q8ag")
+    return rc
+
+
+def zs_shard_step_q8grad(master, m, v, param_bf16, qgrads, qscales, k, n, seg_table_, hparams_,
+                         step, stream=None, check=True) -> int:
+    """zs_shard_step on int8 partials qgrads[j] (int8[n]) with block scales
+    qscales[j] (float32[ceil(n/256)])."""
+    qp = _ptr_array(qgrads)
+    sp = _ptr_array(qscales)
+    st = seg_table_ if isinstance(seg_table_, ZsSegTable) else seg_table(seg_table_)
+    rc = load_library().zs_shard_step_q8grad(
+        ctypes.c_void_p(_addr(master)), ctypes.c_void_p(_addr(m)), ctypes.c_void_p(_addr(v)),
+        ctypes.c_void_p(_addr(param_bf16)), ctypes.cast(qp, ctypes.c_void_p),
+        ctypes.cast(sp, ctypes.c_void_p), int(len(qgrads) if k is None else k), int(n),
+        ctypes.byref(st), ctypes.byref(hparams_), int(step),
+        ctypes.c_void_p(_stream_handle(stream)))
+    if check and rc != ZS_OK:
+        raise ZsError(rc, "zs_shard_step_q8grad")
+    return rc
+
+
+def zs_shard_step_bf16mv(master, m_bf16, v_bf16, param_bf16, grads, k, n, seg_table_, hparams_,
+                         step, stream=None, check=True) -> int:
+    """zs_shard_step with bf16 moments m_bf16, v_bf16 (bf16[n], in place)."""
+    pm, pmm, pv, pp, pg, kk, st, hp, keep = _marshal(master, m_bf16, v_bf16, param_bf16, grads,
+                                                     k, seg_table_, hparams_)
+    rc = load_library().zs_shard_step_bf16mv(pm, pmm, pv, pp, pg, kk, int(n), ctypes.byref(st),
+                                             ctypes.byref(hp), int(step),
+                                             ctypes.c_void_p(_stream_handle(stream)))
+    del keep
+    if check and rc != ZS_OK:
+        raise ZsError(rc, "zs_shard_step_bf16mv")
+    return rc
+
+
+def algorithmic_bytes(variant: str, k: int, n: int) -> int:
+    """HBM bytes one call moves by the algorithm, per entry point."""
+    nb = -(-n // ZS_Q8_BLOCK)
+    if variant == "base":
+        return (26 + 2 * k) * n
+    if variant == "q8ag":
+        return (26 + 2 * k) * n + n + 4 * nb
+    if variant == "q8grad":
+        return (12 + k + 14) * n + 4 * k * nb
+    if variant == "bf16mv":
+        return (18 + 2 * k) * n
+    raise ValueError(variant)

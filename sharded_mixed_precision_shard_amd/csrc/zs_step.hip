@@ -60,10 +60,14 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct StepArgs {
     float *master;
-    float *m;
-    float *v;
+    void *m;         // fp32 [n], or bf16 [n] in the bf16-moment variant
+    void *v;
     uint16_t *param;
-    const uint16_t *grads[ZS_MAX_K];
+    int8_t *q8;      // quantized parameter copy (variant with an int8 payload)
+    float *q8_scale;
+    const uint16_t *grads[ZS_MAX_K];   // bf16 partials
+    const int8_t *qgrads[ZS_MAX_K];    // int8 partials (block-quantized variant)
+    const float *qscales[ZS_MAX_K];
     const zs_segment *segs;
     int64_t n;
     int64_t chunk;  // elements per workgroup, a multiple of kTile
@@ -179,49 +183,168 @@ __device__ int64_t locate_segments(const StepArgs &a, int64_t from, int64_t unti
     return s_start[staged - 1];
 }
 
-// Reduce, update and pack four consecutive elements held as one f32x4 per
-// state array and one u32x2 (4 bf16) per partial.  mask bit q = decay of
-// element q.
-template <int K>
-__device__ __forceinline__ void quad_update(f32x4 &w, f32x4 &m, f32x4 &v, const u32x2 *gr,
-                                            uint32_t mask, const StepArgs &a, u32x2 &pout) {
+// Variants of the step, chosen at compile time (bit mask):
+//   kOutQ8  - also write the block-quantized int8 copy of the new parameters
+//             with one fp32 scale per kQ8Block elements (the payload of a
+//             quantized all-gather);
+//   kGradQ8 - the k partials arrive as int8 with one fp32 scale per
+//             kQ8Block elements each (a block-quantized reduce-scatter) and
+//             are dequantized inside the reduce;
+//   kMvBf16 - the moments m and v are stored as bf16 (12 bytes per parameter
+//             of optimizer state plus weight instead of 16).
+constexpr int kOutQ8 = 1;
+constexpr int kGradQ8 = 2;
+constexpr int kMvBf16 = 4;
+constexpr int kQ8Block = ZS_Q8_BLOCK;
+static_assert(kQ8Block == kHalf, "a quantization block is one half window");
+
+__device__ __forceinline__ f32x4 bf16x4_to_f32x4(u32x2 d) {
+    f32x4 r;
+    r[0] = bf16_lo(d[0]);
+    r[1] = bf16_hi(d[0]);
+    r[2] = bf16_lo(d[1]);
+    r[3] = bf16_hi(d[1]);
+    return r;
+}
+
+__device__ __forceinline__ u32x2 f32x4_to_bf16x4(f32x4 x) {
+    u32x2 r;
+    r[0] = to_bf16(x[0]) | (to_bf16(x[1]) << 16);
+    r[1] = to_bf16(x[2]) | (to_bf16(x[3]) << 16);
+    return r;
+}
+
+__device__ __forceinline__ float i8_at(uint32_t word, int byte) {
+    return (float)(int32_t)(int8_t)(uint8_t)(word >> (8 * byte));
+}
+
+// The four reduced gradients of one lane's quad (elements 4 * qi .. +3).
+template <int K, int V, int NT>
+struct QuadGrads {
+    u32x2 bf[(V & kGradQ8) ? 1 : K];   // bf16 partials
+    uint32_t q[(V & kGradQ8) ? K : 1]; // int8 partials (4 per word)
+    float s[(V & kGradQ8) ? K : 1];    // their block scales
+
+    __device__ __forceinline__ void load_from(const StepArgs &a, int64_t qi) {
+        if constexpr (V & kGradQ8) {
+            const int64_t blk = (qi * kQuad) / kQ8Block;
 #pragma unroll
-    for (int d = 0; d < 2; ++d) {
-        // dword d of every partial holds elements 2d (low half) and 2d+1 (high half)
-        float g0 = bf16_lo(gr[0][d]);
-        float g1 = bf16_hi(gr[0][d]);
+            for (int j = 0; j < K; ++j) {
+                q[j] = load<NT>(reinterpret_cast<const uint32_t *>(a.qgrads[j]) + qi);
+                s[j] = a.qscales[j][blk];
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < K; ++j)
+                bf[j] = load<NT>(reinterpret_cast<const u32x2 *>(a.grads[j]) + qi);
+        }
+    }
+
+    // Left fold over the partials of element e (0..3 of the quad), then the scale.
+    __device__ __forceinline__ float reduced(int e, const StepArgs &a) const {
+#pragma clang fp contract(off)
+        float g;
+        if constexpr (V & kGradQ8) {
+            g = i8_at(q[0], e) * s[0];
+#pragma unroll
+            for (int j = 1; j < K; ++j) {
+                const float t = i8_at(q[j], e) * s[j];
+                g = g + t;
+            }
+        } else {
+            const int d = e >> 1;
+            g = (e & 1) ? bf16_hi(bf[0][d]) : bf16_lo(bf[0][d]);
+#pragma unroll
+            for (int j = 1; j < K; ++j) g = g + ((e & 1) ? bf16_hi(bf[j][d]) : bf16_lo(bf[j][d]));
+        }
+        return g * a.gscale;
+    }
+};
+
+// Reduced gradient of one element in the scalar (ragged tail) path.
+template <int K, int V>
+__device__ __forceinline__ float scalar_grad(const StepArgs &a, int64_t i) {
+#pragma clang fp contract(off)
+    float g;
+    if constexpr (V & kGradQ8) {
+        const int64_t blk = i / kQ8Block;
+        g = (float)a.qgrads[0][i] * a.qscales[0][blk];
 #pragma unroll
         for (int j = 1; j < K; ++j) {
-            g0 = g0 + bf16_lo(gr[j][d]);
-            g1 = g1 + bf16_hi(gr[j][d]);
+            const float t = (float)a.qgrads[j][i] * a.qscales[j][blk];
+            g = g + t;
         }
-        g0 = g0 * a.gscale;
-        g1 = g1 * a.gscale;
-        float w0 = w[2 * d], m0 = m[2 * d], v0 = v[2 * d];
-        float w1 = w[2 * d + 1], m1 = m[2 * d + 1], v1 = v[2 * d + 1];
-        adamw(w0, m0, v0, g0, (mask >> (2 * d)) & 1u, a);
-        adamw(w1, m1, v1, g1, (mask >> (2 * d + 1)) & 1u, a);
-        w[2 * d] = w0; m[2 * d] = m0; v[2 * d] = v0;
-        w[2 * d + 1] = w1; m[2 * d + 1] = m1; v[2 * d + 1] = v1;
-        pout[d] = to_bf16(w0) | (to_bf16(w1) << 16);
-    }
-}
-
-template <int K>
-__device__ __forceinline__ void scalar_update(const StepArgs &a, int64_t i, bool decay) {
-    float g = __uint_as_float((uint32_t)a.grads[0][i] << 16);
+    } else {
+        g = __uint_as_float((uint32_t)a.grads[0][i] << 16);
 #pragma unroll
-    for (int j = 1; j < K; ++j) g = g + __uint_as_float((uint32_t)a.grads[j][i] << 16);
-    g = g * a.gscale;
-    float wv = a.master[i], mv = a.m[i], vv = a.v[i];
-    adamw(wv, mv, vv, g, decay, a);
-    a.master[i] = wv;
-    a.m[i] = mv;
-    a.v[i] = vv;
-    a.param[i] = (uint16_t)to_bf16(wv);
+        for (int j = 1; j < K; ++j) g = g + __uint_as_float((uint32_t)a.grads[j][i] << 16);
+    }
+    return g * a.gscale;
 }
 
-template <int K, int NT>
+// Maximum over the 64 lanes of a wavefront (every lane gets it).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+#pragma unroll
+    for (int off = kWave / 2; off >= 1; off >>= 1) {
+        const uint32_t y = (uint32_t)__shfl_xor((int)x, off, kWave);
+        x = x > y ? x : y;
+    }
+    return x;
+}
+
+// Quantize one block (one half window: 64 lanes x 4 bf16 values) to int8.
+// `bits` are the lane's four bf16 values widened to fp32 bit patterns;
+// `valid` marks which of them lie inside the shard.  The block maximum of
+// |x| is taken on the bit patterns (integer order of |x| bits = order of
+// |x|, and every NaN pattern sorts above infinity, so a NaN wins).  All 64
+// lanes must call this together.  Returns the four int8 codes packed in a
+// word; lane 0 stores the scale when the block exists.
+__device__ __forceinline__ uint32_t quantize_block(const uint32_t bits[4], uint32_t valid,
+                                                   const StepArgs &a, int64_t block,
+                                                   bool block_exists) {
+    uint32_t amax = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t ab = bits[e] & 0x7fffffffu;
+        if (((valid >> e) & 1u) && ab > amax) amax = ab;
+    }
+    amax = wave_max_u32(amax);
+    const float scale = __uint_as_float(amax) / 127.0f;
+    const bool usable = scale > 0.0f && scale <= 3.40282347e+38f;
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        int32_t q = 0;
+        if (usable) {
+            float r = __builtin_rintf(__uint_as_float(bits[e]) / scale);
+            r = r > 127.0f ? 127.0f : r;
+            r = r < -127.0f ? -127.0f : r;
+            q = (int32_t)r;
+        }
+        word |= ((uint32_t)q & 0xffu) << (8 * e);
+    }
+    if (block_exists && (threadIdx.x % kWave) == 0) a.q8_scale[block] = scale;
+    return word;
+}
+
+// Reduce, update and pack one lane's quad.  mask bit e = decay of element e.
+template <int K, int V, int NT>
+__device__ __forceinline__ void quad_update(f32x4 &w, f32x4 &m, f32x4 &v,
+                                            const QuadGrads<K, V, NT> &gr, uint32_t mask,
+                                            const StepArgs &a, u32x2 &pout) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float g = gr.reduced(e, a);
+        float we = w[e], me = m[e], ve = v[e];
+        adamw(we, me, ve, g, (mask >> e) & 1u, a);
+        w[e] = we;
+        m[e] = me;
+        v[e] = ve;
+    }
+    pout = f32x4_to_bf16x4(w);
+}
+
+template <int K, int V, int NT>
 __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) {
     __shared__ int64_t s_start[kLdsSegs];
     __shared__ uint8_t s_flag[kLdsSegs];
@@ -283,36 +406,105 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
 
         if (w0 + kWindow <= a.n) {
             // Whole window in range: dense vector traffic only.
-            const f32x4 *pw = reinterpret_cast<const f32x4 *>(a.master);
-            const f32x4 *pm = reinterpret_cast<const f32x4 *>(a.m);
-            const f32x4 *pv = reinterpret_cast<const f32x4 *>(a.v);
-            const int64_t qa = ea / kQuad, qb = eb / kQuad;  // f32x4 / u32x2 indices
+            const int64_t qa = ea / kQuad, qb = eb / kQuad;  // quad indices
+            f32x4 *pw = reinterpret_cast<f32x4 *>(a.master);
             f32x4 wa = load<NT>(pw + qa), wb = load<NT>(pw + qb);
-            f32x4 ma = load<NT>(pm + qa), mb = load<NT>(pm + qb);
-            f32x4 va = load<NT>(pv + qa), vb = load<NT>(pv + qb);
-            u32x2 ga[K], gb[K];
-#pragma unroll
-            for (int j = 0; j < K; ++j) {
-                const u32x2 *pg = reinterpret_cast<const u32x2 *>(a.grads[j]);
-                ga[j] = load<NT>(pg + qa);
-                gb[j] = load<NT>(pg + qb);
+            f32x4 ma, mb, va, vb;
+            if constexpr (V & kMvBf16) {
+                const u32x2 *pm = reinterpret_cast<const u32x2 *>(a.m);
+                const u32x2 *pv = reinterpret_cast<const u32x2 *>(a.v);
+                ma = bf16x4_to_f32x4(load<NT>(pm + qa));
+                mb = bf16x4_to_f32x4(load<NT>(pm + qb));
+                va = bf16x4_to_f32x4(load<NT>(pv + qa));
+                vb = bf16x4_to_f32x4(load<NT>(pv + qb));
+            } else {
+                const f32x4 *pm = reinterpret_cast<const f32x4 *>(a.m);
+                const f32x4 *pv = reinterpret_cast<const f32x4 *>(a.v);
+                ma = load<NT>(pm + qa);
+                mb = load<NT>(pm + qb);
+                va = load<NT>(pv + qa);
+                vb = load<NT>(pv + qb);
             }
+            QuadGrads<K, V, NT> ga, gb;
+            ga.load_from(a, qa);
+            gb.load_from(a, qb);
             u32x2 pa, pb;
-            quad_update<K>(wa, ma, va, ga, mask & 0xfu, a, pa);
-            quad_update<K>(wb, mb, vb, gb, mask >> 4, a, pb);
-            f32x4 *qw = reinterpret_cast<f32x4 *>(a.master);
-            f32x4 *qm = reinterpret_cast<f32x4 *>(a.m);
-            f32x4 *qv = reinterpret_cast<f32x4 *>(a.v);
-            u32x2 *qp = reinterpret_cast<u32x2 *>(a.param);
-            store<NT>(qw + qa, wa); store<NT>(qw + qb, wb);
-            store<NT>(qm + qa, ma); store<NT>(qm + qb, mb);
-            store<NT>(qv + qa, va); store<NT>(qv + qb, vb);
-            store<NT>(qp + qa, pa); store<NT>(qp + qb, pb);
+            quad_update<K, V, NT>(wa, ma, va, ga, mask & 0xfu, a, pa);
+            quad_update<K, V, NT>(wb, mb, vb, gb, mask >> 4, a, pb);
+            store<NT>(pw + qa, wa);
+            store<NT>(pw + qb, wb);
+            if constexpr (V & kMvBf16) {
+                u32x2 *pm = reinterpret_cast<u32x2 *>(a.m);
+                u32x2 *pv = reinterpret_cast<u32x2 *>(a.v);
+                store<NT>(pm + qa, f32x4_to_bf16x4(ma));
+                store<NT>(pm + qb, f32x4_to_bf16x4(mb));
+                store<NT>(pv + qa, f32x4_to_bf16x4(va));
+                store<NT>(pv + qb, f32x4_to_bf16x4(vb));
+            } else {
+                f32x4 *pm = reinterpret_cast<f32x4 *>(a.m);
+                f32x4 *pv = reinterpret_cast<f32x4 *>(a.v);
+                store<NT>(pm + qa, ma);
+                store<NT>(pm + qb, mb);
+                store<NT>(pv + qa, va);
+                store<NT>(pv + qb, vb);
+            }
+            u32x2 *pp = reinterpret_cast<u32x2 *>(a.param);
+            store<NT>(pp + qa, pa);
+            store<NT>(pp + qb, pb);
+            if constexpr (V & kOutQ8) {
+                const uint32_t ba[4] = {pa[0] << 16, pa[0] & 0xffff0000u, pa[1] << 16,
+                                        pa[1] & 0xffff0000u};
+                const uint32_t bb[4] = {pb[0] << 16, pb[0] & 0xffff0000u, pb[1] << 16,
+                                        pb[1] & 0xffff0000u};
+                const int64_t blk = w0 / kQ8Block;
+                const uint32_t qwa = quantize_block(ba, 0xfu, a, blk, true);
+                const uint32_t qwb = quantize_block(bb, 0xfu, a, blk + 1, true);
+                uint32_t *pq = reinterpret_cast<uint32_t *>(a.q8);
+                store<NT>(pq + qa, qwa);
+                store<NT>(pq + qb, qwb);
+            }
         } else {
-            // The shard's last, partial window: element by element.
+            // The shard's last, partial window: element by element (the whole
+            // wavefront stays here together, for the block maxima).
+            uint32_t pbits[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            uint32_t valid = 0;
             for (int q = 0; q < 2 * kQuad; ++q) {
                 const int64_t i = (q < kQuad ? ea : eb - kQuad) + q;
-                if (i < a.n) scalar_update<K>(a, i, (mask >> q) & 1u);
+                if (i >= a.n) continue;
+                valid |= 1u << q;
+                const float g = scalar_grad<K, V>(a, i);
+                float wv = a.master[i], mv, vv;
+                if constexpr (V & kMvBf16) {
+                    mv = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(a.m)[i] << 16);
+                    vv = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(a.v)[i] << 16);
+                } else {
+                    mv = reinterpret_cast<const float *>(a.m)[i];
+                    vv = reinterpret_cast<const float *>(a.v)[i];
+                }
+                adamw(wv, mv, vv, g, (mask >> q) & 1u, a);
+                a.master[i] = wv;
+                if constexpr (V & kMvBf16) {
+                    reinterpret_cast<uint16_t *>(a.m)[i] = (uint16_t)to_bf16(mv);
+                    reinterpret_cast<uint16_t *>(a.v)[i] = (uint16_t)to_bf16(vv);
+                } else {
+                    reinterpret_cast<float *>(a.m)[i] = mv;
+                    reinterpret_cast<float *>(a.v)[i] = vv;
+                }
+                const uint32_t pbf = to_bf16(wv);
+                a.param[i] = (uint16_t)pbf;
+                pbits[q] = pbf << 16;
+            }
+            if constexpr (V & kOutQ8) {
+                const int64_t blk = w0 / kQ8Block;
+                const uint32_t qwa = quantize_block(pbits, valid & 0xfu, a, blk, w0 < a.n);
+                const uint32_t qwb = quantize_block(pbits + 4, valid >> 4, a, blk + 1,
+                                                    w0 + kHalf < a.n);
+                for (int q = 0; q < 2 * kQuad; ++q) {
+                    if (!((valid >> q) & 1u)) continue;
+                    const int64_t i = (q < kQuad ? ea : eb - kQuad) + q;
+                    const uint32_t word = q < kQuad ? qwa : qwb;
+                    a.q8[i] = (int8_t)(uint8_t)(word >> (8 * (q % kQuad)));
+                }
             }
         }
     }
@@ -321,28 +513,34 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
 typedef void (*kernel_fn)(const StepArgs);
 
 template <int K>
-kernel_fn pick_nt(int nt) {
-    return nt ? shard_step_kernel<K, 1> : shard_step_kernel<K, 0>;
+kernel_fn pick_variant(int variant, int nt) {
+    switch (variant) {
+        case 0: return nt ? shard_step_kernel<K, 0, 1> : shard_step_kernel<K, 0, 0>;
+        case kOutQ8: return shard_step_kernel<K, kOutQ8, 1>;
+        case kGradQ8: return shard_step_kernel<K, kGradQ8, 1>;
+        case kMvBf16: return shard_step_kernel<K, kMvBf16, 1>;
+        default: return nullptr;
+    }
 }
 
-kernel_fn pick_kernel(int k, int nt) {
+kernel_fn pick_kernel(int k, int variant, int nt) {
     switch (k) {
-        case 1: return pick_nt<1>(nt);
-        case 2: return pick_nt<2>(nt);
-        case 3: return pick_nt<3>(nt);
-        case 4: return pick_nt<4>(nt);
-        case 5: return pick_nt<5>(nt);
-        case 6: return pick_nt<6>(nt);
-        case 7: return pick_nt<7>(nt);
-        case 8: return pick_nt<8>(nt);
-        case 9: return pick_nt<9>(nt);
-        case 10: return pick_nt<10>(nt);
-        case 11: return pick_nt<11>(nt);
-        case 12: return pick_nt<12>(nt);
-        case 13: return pick_nt<13>(nt);
-        case 14: return pick_nt<14>(nt);
-        case 15: return pick_nt<15>(nt);
-        case 16: return pick_nt<16>(nt);
+        case 1: return pick_variant<1>(variant, nt);
+        case 2: return pick_variant<2>(variant, nt);
+        case 3: return pick_variant<3>(variant, nt);
+        case 4: return pick_variant<4>(variant, nt);
+        case 5: return pick_variant<5>(variant, nt);
+        case 6: return pick_variant<6>(variant, nt);
+        case 7: return pick_variant<7>(variant, nt);
+        case 8: return pick_variant<8>(variant, nt);
+        case 9: return pick_variant<9>(variant, nt);
+        case 10: return pick_variant<10>(variant, nt);
+        case 11: return pick_variant<11>(variant, nt);
+        case 12: return pick_variant<12>(variant, nt);
+        case 13: return pick_variant<13>(variant, nt);
+        case 14: return pick_variant<14>(variant, nt);
+        case 15: return pick_variant<15>(variant, nt);
+        case 16: return pick_variant<16>(variant, nt);
         default: return nullptr;
     }
 }
@@ -371,8 +569,6 @@ bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
     return a0 < b1 && b0 < a1;
 }
 
-bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
-
 int pick_chunk_tiles(int64_t n, int cus) {
     // One tile per workgroup: the resident workgroups then cover one compact
     // stretch of every array and sweep through memory together, which
@@ -384,13 +580,40 @@ int pick_chunk_tiles(int64_t n, int cus) {
     return 1;
 }
 
-int validate_and_launch(float *master, float *m, float *v, uint16_t *param,
-                        const uint16_t *const *grads, int k, int64_t n,
-                        const zs_seg_table *st, const zs_hparams *hp, int64_t step,
-                        void *stream, const zs_launch_cfg *cfg) {
+// One call, whatever the variant: the buffers it reads and writes.
+struct Request {
+    float *master = nullptr;
+    void *m = nullptr;
+    void *v = nullptr;
+    uint16_t *param = nullptr;
+    int8_t *q8 = nullptr;
+    float *q8_scale = nullptr;
+    const uint16_t *const *grads = nullptr;
+    const int8_t *const *qgrads = nullptr;
+    const float *const *qscales = nullptr;
+    int k = 0;
+    int64_t n = 0;
+    const zs_seg_table *st = nullptr;
+    const zs_hparams *hp = nullptr;
+    int64_t step = 0;
+    void *stream = nullptr;
+    const zs_launch_cfg *cfg = nullptr;
+    int variant = 0;
+};
+
+struct Span {
+    const void *p;
+    int64_t bytes;
+    uintptr_t align;
+};
+
+int validate_and_launch(const Request &r) {
     if (!g_initialized) return ZS_ERR_NOT_INITIALIZED;
-    if (k < 1 || k > ZS_MAX_K || n < 0 || step < 1 || !st || !hp || !grads)
+    const bool gq = (r.variant & kGradQ8) != 0;
+    if (r.k < 1 || r.k > ZS_MAX_K || r.n < 0 || r.step < 1 || !r.st || !r.hp)
         return ZS_ERR_INVALID_ARGUMENT;
+    if (gq ? (!r.qgrads || !r.qscales) : !r.grads) return ZS_ERR_INVALID_ARGUMENT;
+    const zs_hparams *hp = r.hp;
     if (!std::isfinite(hp->lr) || !std::isfinite(hp->beta1) || !std::isfinite(hp->beta2) ||
         !std::isfinite(hp->eps) || !std::isfinite(hp->weight_decay) ||
         !std::isfinite(hp->grad_scale))
@@ -398,35 +621,59 @@ int validate_and_launch(float *master, float *m, float *v, uint16_t *param,
     if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f) ||
         hp->eps < 0.0f)
         return ZS_ERR_INVALID_ARGUMENT;
-    if (st->count < 1) return ZS_ERR_INVALID_ARGUMENT;
-    if (st->count > ZS_MAX_SEGMENTS) return ZS_ERR_TOO_MANY_SEGMENTS;
+    if (r.st->count < 1) return ZS_ERR_INVALID_ARGUMENT;
+    if (r.st->count > ZS_MAX_SEGMENTS) return ZS_ERR_TOO_MANY_SEGMENTS;
     // Streaming (non-temporal) loads and stores by default: nothing is
     // reused, and on MI355X they measured 5-10 % faster than cached access.
     int chunk_tiles = 0, nt = 1;
-    if (cfg) {
-        if (cfg->chunk_tiles < 0 || cfg->chunk_tiles > kMaxChunkTiles) return ZS_ERR_INVALID_ARGUMENT;
-        if (cfg->nontemporal < 0 || cfg->nontemporal > 2) return ZS_ERR_INVALID_ARGUMENT;
-        chunk_tiles = cfg->chunk_tiles;
-        nt = cfg->nontemporal == 2 ? 0 : 1;
+    if (r.cfg) {
+        if (r.cfg->chunk_tiles < 0 || r.cfg->chunk_tiles > kMaxChunkTiles)
+            return ZS_ERR_INVALID_ARGUMENT;
+        if (r.cfg->nontemporal < 0 || r.cfg->nontemporal > 2) return ZS_ERR_INVALID_ARGUMENT;
+        chunk_tiles = r.cfg->chunk_tiles;
+        nt = r.cfg->nontemporal == 2 ? 0 : 1;
     }
-    if (n == 0) return ZS_OK;
-    if (!master || !m || !v || !param || !st->segs) return ZS_ERR_INVALID_ARGUMENT;
-    for (int j = 0; j < k; ++j)
-        if (!grads[j]) return ZS_ERR_INVALID_ARGUMENT;
-    if (!aligned16(master) || !aligned16(m) || !aligned16(v) || !aligned16(param) ||
-        ((uintptr_t)st->segs & 7u))
-        return ZS_ERR_MISALIGNED;
-    for (int j = 0; j < k; ++j)
-        if (!aligned16(grads[j])) return ZS_ERR_MISALIGNED;
-    if (n > INT64_MAX / 4) return ZS_ERR_INVALID_ARGUMENT;
-    const int64_t b4 = n * 4, b2 = n * 2;
-    const void *outs[4] = {master, m, v, param};
-    const int64_t ob[4] = {b4, b4, b4, b2};
-    for (int x = 0; x < 4; ++x) {
-        for (int y = x + 1; y < 4; ++y)
-            if (overlaps(outs[x], ob[x], outs[y], ob[y])) return ZS_ERR_ALIASING;
-        for (int j = 0; j < k; ++j)
-            if (overlaps(outs[x], ob[x], grads[j], b2)) return ZS_ERR_ALIASING;
+    if (r.n == 0) return ZS_OK;
+    if (r.n > INT64_MAX / 8) return ZS_ERR_INVALID_ARGUMENT;
+    if (!r.st->segs) return ZS_ERR_INVALID_ARGUMENT;
+    if ((uintptr_t)r.st->segs & 7u) return ZS_ERR_MISALIGNED;
+
+    const int64_t n = r.n;
+    const int64_t nblocks = (n + kQ8Block - 1) / kQ8Block;
+    const int64_t mv_bytes = (r.variant & kMvBf16) ? 2 * n : 4 * n;
+    Span outs[6];
+    int nouts = 0;
+    outs[nouts++] = {r.master, 4 * n, 16};
+    outs[nouts++] = {r.m, mv_bytes, 16};
+    outs[nouts++] = {r.v, mv_bytes, 16};
+    outs[nouts++] = {r.param, 2 * n, 16};
+    if (r.variant & kOutQ8) {
+        outs[nouts++] = {r.q8, n, 16};
+        outs[nouts++] = {r.q8_scale, 4 * nblocks, 4};
+    }
+    Span ins[2 * ZS_MAX_K];
+    int nins = 0;
+    for (int j = 0; j < r.k; ++j) {
+        if (gq) {
+            ins[nins++] = {r.qgrads[j], n, 16};
+            ins[nins++] = {r.qscales[j], 4 * nblocks, 4};
+        } else {
+            ins[nins++] = {r.grads[j], 2 * n, 16};
+        }
+    }
+    for (int x = 0; x < nouts; ++x)
+        if (!outs[x].p) return ZS_ERR_INVALID_ARGUMENT;
+    for (int x = 0; x < nins; ++x)
+        if (!ins[x].p) return ZS_ERR_INVALID_ARGUMENT;
+    for (int x = 0; x < nouts; ++x)
+        if ((uintptr_t)outs[x].p & (outs[x].align - 1)) return ZS_ERR_MISALIGNED;
+    for (int x = 0; x < nins; ++x)
+        if ((uintptr_t)ins[x].p & (ins[x].align - 1)) return ZS_ERR_MISALIGNED;
+    for (int x = 0; x < nouts; ++x) {
+        for (int y = x + 1; y < nouts; ++y)
+            if (overlaps(outs[x].p, outs[x].bytes, outs[y].p, outs[y].bytes)) return ZS_ERR_ALIASING;
+        for (int y = 0; y < nins; ++y)
+            if (overlaps(outs[x].p, outs[x].bytes, ins[y].p, ins[y].bytes)) return ZS_ERR_ALIASING;
     }
 
     int dev = 0;
@@ -435,21 +682,27 @@ int validate_and_launch(float *master, float *m, float *v, uint16_t *param,
     if (dev < 0 || dev >= kMaxDevices || !g_dev[dev].ready) return ZS_ERR_NOT_INITIALIZED;
 
     StepArgs a;
-    a.master = master;
-    a.m = m;
-    a.v = v;
-    a.param = param;
-    for (int j = 0; j < ZS_MAX_K; ++j) a.grads[j] = j < k ? grads[j] : nullptr;
-    a.segs = st->segs;
-    a.nseg = st->count;
+    a.master = r.master;
+    a.m = r.m;
+    a.v = r.v;
+    a.param = r.param;
+    a.q8 = r.q8;
+    a.q8_scale = r.q8_scale;
+    for (int j = 0; j < ZS_MAX_K; ++j) {
+        a.grads[j] = (!gq && j < r.k) ? r.grads[j] : nullptr;
+        a.qgrads[j] = (gq && j < r.k) ? r.qgrads[j] : nullptr;
+        a.qscales[j] = (gq && j < r.k) ? r.qscales[j] : nullptr;
+    }
+    a.segs = r.st->segs;
+    a.nseg = r.st->count;
     a.n = n;
     a.lr = hp->lr;
     a.b1 = hp->beta1;
     a.b2 = hp->beta2;
     a.c1 = 1.0f - hp->beta1;
     a.c2 = 1.0f - hp->beta2;
-    a.bc1 = (float)(1.0 - std::pow((double)hp->beta1, (double)step));
-    a.bc2 = (float)(1.0 - std::pow((double)hp->beta2, (double)step));
+    a.bc1 = (float)(1.0 - std::pow((double)hp->beta1, (double)r.step));
+    a.bc2 = (float)(1.0 - std::pow((double)hp->beta2, (double)r.step));
     a.eps = hp->eps;
     {
         const float lrwd = hp->lr * hp->weight_decay;
@@ -466,12 +719,29 @@ int validate_and_launch(float *master, float *m, float *v, uint16_t *param,
     }
     a.chunk = chunk;
 
-    kernel_fn fn = pick_kernel(k, nt);
+    kernel_fn fn = pick_kernel(r.k, r.variant, nt);
+    if (!fn) return ZS_ERR_INVALID_ARGUMENT;
     void *args[] = {&a};
     e = hipLaunchKernel((const void *)fn, dim3((unsigned)blocks), dim3(kThreads), args, 0,
-                        (hipStream_t)stream);
+                        (hipStream_t)r.stream);
     if (e != hipSuccess) return device_error(e);
     return ZS_OK;
+}
+
+Request base_request(float *master, void *m, void *v, uint16_t *param, int k, int64_t n,
+                     const zs_seg_table *st, const zs_hparams *hp, int64_t step, void *stream) {
+    Request r;
+    r.master = master;
+    r.m = m;
+    r.v = v;
+    r.param = param;
+    r.k = k;
+    r.n = n;
+    r.st = st;
+    r.hp = hp;
+    r.step = step;
+    r.stream = stream;
+    return r;
 }
 
 }  // namespace
@@ -498,16 +768,54 @@ int zs_shard_step(float *master, float *m, float *v, uint16_t *param_bf16,
                   const uint16_t *const *grads, int k, int64_t n,
                   const zs_seg_table *seg_table, const zs_hparams *hparams,
                   int64_t step, void *stream) {
-    return validate_and_launch(master, m, v, param_bf16, grads, k, n, seg_table, hparams, step,
-                               stream, nullptr);
+    Request r = base_request(master, m, v, param_bf16, k, n, seg_table, hparams, step, stream);
+    r.grads = grads;
+    return validate_and_launch(r);
 }
 
 int zs_shard_step_cfg(float *master, float *m, float *v, uint16_t *param_bf16,
                       const uint16_t *const *grads, int k, int64_t n,
                       const zs_seg_table *seg_table, const zs_hparams *hparams,
                       int64_t step, void *stream, const zs_launch_cfg *cfg) {
-    return validate_and_launch(master, m, v, param_bf16, grads, k, n, seg_table, hparams, step,
-                               stream, cfg);
+    Request r = base_request(master, m, v, param_bf16, k, n, seg_table, hparams, step, stream);
+    r.grads = grads;
+    r.cfg = cfg;
+    return validate_and_launch(r);
+}
+
+int zs_shard_step_q8ag(float *master, float *m, float *v, uint16_t *param_bf16,
+                       int8_t *param_q8, float *param_q8_scale,
+                       const uint16_t *const *grads, int k, int64_t n,
+                       const zs_seg_table *seg_table, const zs_hparams *hparams,
+                       int64_t step, void *stream) {
+    Request r = base_request(master, m, v, param_bf16, k, n, seg_table, hparams, step, stream);
+    r.grads = grads;
+    r.q8 = param_q8;
+    r.q8_scale = param_q8_scale;
+    r.variant = kOutQ8;
+    return validate_and_launch(r);
+}
+
+int zs_shard_step_q8grad(float *master, float *m, float *v, uint16_t *param_bf16,
+                         const int8_t *const *qgrads, const float *const *qscales, int k,
+                         int64_t n, const zs_seg_table *seg_table, const zs_hparams *hparams,
+                         int64_t step, void *stream) {
+    Request r = base_request(master, m, v, param_bf16, k, n, seg_table, hparams, step, stream);
+    r.qgrads = qgrads;
+    r.qscales = qscales;
+    r.variant = kGradQ8;
+    return validate_and_launch(r);
+}
+
+int zs_shard_step_bf16mv(float *master, uint16_t *m_bf16, uint16_t *v_bf16,
+                         uint16_t *param_bf16, const uint16_t *const *grads, int k, int64_t n,
+                         const zs_seg_table *seg_table, const zs_hparams *hparams,
+                         int64_t step, void *stream) {
+    Request r = base_request(master, m_bf16, v_bf16, param_bf16, k, n, seg_table, hparams, step,
+                             stream);
+    r.grads = grads;
+    r.variant = kMvBf16;
+    return validate_and_launch(r);
 }
 
 int zs_fini(void) {
@@ -521,7 +829,7 @@ const char *zs_status_string(int status) {
         case ZS_OK: return "ok";
         case ZS_ERR_NOT_INITIALIZED: return "library not initialized for this device";
         case ZS_ERR_INVALID_ARGUMENT: return "invalid argument";
-        case ZS_ERR_MISALIGNED: return "buffer not 16-byte aligned";
+        case ZS_ERR_MISALIGNED: return "buffer not aligned";
         case ZS_ERR_TOO_MANY_SEGMENTS: return "segment table too large";
         case ZS_ERR_DEVICE: return "HIP runtime error";
         case ZS_ERR_ALIASING: return "output buffers overlap";

@@ -28,6 +28,11 @@ DEV_LIB = os.path.join(_HERE, "libzs_synth.so")
 ROLE_MASTER = 1
 ROLE_GRAD = 2
 ROLE_HEAVY = 3
+ROLE_QGRAD = 4    # int8 partial j of step t
+ROLE_QSCALE = 5   # block scales of int8 partial j of step t
+
+Q8_BLOCK = 256
+Q8_SD = 42.0      # standard deviation of the drawn int8 codes (Irwin-Hall / 1560)
 
 
 def build_host() -> str:
@@ -73,6 +78,10 @@ def _host_lib():
             fn.argtypes = [P, I64, U64, U64, I64, I64, ctypes.c_float, ctypes.c_uint32,
                            ctypes.c_float]
             fn.restype = None
+        lib.synth_q8.argtypes = [P, I64, U64, I64, I64]
+        lib.synth_q8.restype = None
+        lib.synth_q8_scales.argtypes = [P, I64, U64, I64, ctypes.c_float]
+        lib.synth_q8_scales.restype = None
         _host = lib
     return _host
 
@@ -88,6 +97,10 @@ def _dev_lib():
             fn.argtypes = [P, I64, U64, U64, I64, I64, ctypes.c_float, ctypes.c_uint32,
                            ctypes.c_float, P]
             fn.restype = ctypes.c_int
+        lib.synth_dev_q8.argtypes = [P, I64, U64, I64, I64, P]
+        lib.synth_dev_q8.restype = ctypes.c_int
+        lib.synth_dev_q8_scales.argtypes = [P, I64, U64, I64, ctypes.c_float, P]
+        lib.synth_dev_q8_scales.restype = ctypes.c_int
         _dev = lib
     return _dev
 
@@ -147,6 +160,40 @@ def host_grads(w: Workload, t: int, lo: int = 0, hi: int = None):
     return out
 
 
+def q8_base_scale(sigma: float) -> np.float32:
+    """Block scale base so that q * scale has about the partials' sigma."""
+    return np.float32(sigma / Q8_SD)
+
+
+def host_q8(n, key, index0, valid_end):
+    out = np.empty(int(n), dtype=np.int8)
+    _host_lib().synth_q8(out.ctypes.data, int(n), key, int(index0), int(valid_end))
+    return out
+
+
+def host_q8_scales(nblocks, skey, block0, base):
+    out = np.empty(int(nblocks), dtype=np.float32)
+    _host_lib().synth_q8_scales(out.ctypes.data, int(nblocks), skey, int(block0),
+                                np.float32(base))
+    return out
+
+
+def host_qgrads(w: Workload, t: int, lo: int = 0, hi: int = None):
+    """Int8 partials of step t for shard elements [lo, hi) (lo a multiple of
+    the block) and the scales of the blocks they cover."""
+    hi = w.n if hi is None else hi
+    if lo % Q8_BLOCK:
+        raise ValueError("window must start on a quantization block")
+    nb = -(-(hi - lo) // Q8_BLOCK)
+    qs, ss = [], []
+    for j in range(w.k):
+        qs.append(host_q8(hi - lo, stream_key(w.seed, ROLE_QGRAD, j, t), w.shard.index0 + lo,
+                          w.shard.valid_end))
+        ss.append(host_q8_scales(nb, stream_key(w.seed, ROLE_QSCALE, j, t), lo // Q8_BLOCK,
+                                 q8_base_scale(w.grad_sigma)))
+    return qs, ss
+
+
 # -------------------------------------------------------------- device side
 
 def _check_dev(out, dtype_name, n):
@@ -195,3 +242,30 @@ def dev_grads(w: Workload, t: int, outs):
         dev_normal_bf16(outs[j], w.n, stream_key(w.seed, ROLE_GRAD, j, t), w.shard.index0,
                         w.shard.valid_end, w.grad_sigma, stream_key(w.seed, ROLE_HEAVY, j, t),
                         w.heavy_p, w.heavy_sigma)
+
+
+def dev_q8(out, n, key, index0, valid_end):
+    import torch
+    if out.dtype != torch.int8 or not out.is_cuda or out.numel() < n:
+        raise ValueError("out must be a device int8 tensor with >= %d elements" % n)
+    rc = _dev_lib().synth_dev_q8(out.data_ptr(), int(n), key, int(index0), int(valid_end),
+                                 _stream())
+    if rc != 0:
+        raise RuntimeError("synth_dev_q8 failed with hip error %d" % rc)
+
+
+def dev_q8_scales(out, nblocks, skey, block0, base):
+    _check_dev(out, "f32", nblocks)
+    rc = _dev_lib().synth_dev_q8_scales(out.data_ptr(), int(nblocks), skey, int(block0),
+                                        np.float32(base), _stream())
+    if rc != 0:
+        raise RuntimeError("synth_dev_q8_scales failed with hip error %d" % rc)
+
+
+def dev_qgrads(w: Workload, t: int, qouts, souts):
+    nb = -(-w.n // Q8_BLOCK)
+    for j in range(w.k):
+        dev_q8(qouts[j], w.n, stream_key(w.seed, ROLE_QGRAD, j, t), w.shard.index0,
+               w.shard.valid_end)
+        dev_q8_scales(souts[j], nb, stream_key(w.seed, ROLE_QSCALE, j, t), 0,
+                      q8_base_scale(w.grad_sigma))

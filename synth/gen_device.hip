@@ -67,6 +67,37 @@ __global__ __launch_bounds__(256) void fill_bf16(uint16_t *out, int64_t n, uint6
     }
 }
 
+__global__ __launch_bounds__(256) void fill_q8(int8_t *out, int64_t n, uint64_t key,
+                                               int64_t index0, int64_t valid_end) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const int64_t gi = index0 + i;
+        int32_t q = 0;
+        if (gi < valid_end) {
+            int32_t s = 0;
+#pragma unroll
+            for (int r = 0; r < 3; ++r) {
+                const uint64_t x = output(key, 3u * (uint64_t)gi + (uint64_t)r);
+                s += (int32_t)(x & 0xffffu) + (int32_t)((x >> 16) & 0xffffu) +
+                     (int32_t)((x >> 32) & 0xffffu) + (int32_t)(x >> 48);
+            }
+            q = (s - 393210) / 1560;
+            q = q > 127 ? 127 : (q < -127 ? -127 : q);
+        }
+        out[i] = (int8_t)q;
+    }
+}
+
+__global__ __launch_bounds__(256) void fill_scales(float *out, int64_t nblocks, uint64_t skey,
+                                                   int64_t block0, float base) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblocks; b += stride) {
+        const uint64_t h = output(skey, (uint64_t)(block0 + b));
+        const float f = (float)(1024u + (uint32_t)(h & 1023u)) * 0.0009765625f;
+        out[b] = base * f;
+    }
+}
+
 unsigned grid_for(int64_t n) {
     int64_t b = (n + 255) / 256;
     if (b > 65536) b = 65536;
@@ -97,6 +128,25 @@ int synth_dev_normal_bf16(uint16_t *out, int64_t n, uint64_t key, uint64_t hkey,
     if (!out) return (int)hipErrorInvalidValue;
     hipLaunchKernelGGL(fill_bf16, dim3(grid_for(n)), dim3(256), 0, (hipStream_t)stream, out, n,
                        key, hkey, index0, valid_end, scale, heavy_thresh, heavy_scale);
+    return (int)hipGetLastError();
+}
+
+// Int8 partials and their block scales (definition in gen_host.c).
+int synth_dev_q8(int8_t *out, int64_t n, uint64_t key, int64_t index0, int64_t valid_end,
+                 void *stream) {
+    if (n <= 0) return 0;
+    if (!out) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(fill_q8, dim3(grid_for(n)), dim3(256), 0, (hipStream_t)stream, out, n, key,
+                       index0, valid_end);
+    return (int)hipGetLastError();
+}
+
+int synth_dev_q8_scales(float *out, int64_t nblocks, uint64_t skey, int64_t block0, float base,
+                        void *stream) {
+    if (nblocks <= 0) return 0;
+    if (!out) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(fill_scales, dim3(grid_for(nblocks)), dim3(256), 0, (hipStream_t)stream,
+                       out, nblocks, skey, block0, base);
     return (int)hipGetLastError();
 }
 

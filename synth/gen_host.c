@@ -102,3 +102,35 @@ void synth_normal_bf16(uint16_t *out, int64_t n, uint64_t key, uint64_t hkey, in
         out[i] = (uint16_t)(u >> 16);
     }
 }
+
+/*
+ * Int8 block-quantized partials, drawn directly (no quantizer involved):
+ * q[i] = clamp(z / 1560, -127, 127) with z the Irwin-Hall integer of element
+ * gi = index0 + i (C division, truncating toward zero; |q| has standard
+ * deviation about 42), 0 past valid_end.  Block b's scale is
+ *   base * ((1024 + (h & 1023)) * 2^-10),  h = output b of the stream keyed
+ * `skey` (one binary32 multiply by an exact factor in [1, 2)).  Blocks are
+ * counted from the shard start (block0 = index of its first block).
+ */
+void synth_q8(int8_t *out, int64_t n, uint64_t key, int64_t index0, int64_t valid_end)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t gi = index0 + i;
+        int32_t q = 0;
+        if (gi < valid_end) {
+            q = irwin_hall_z(key, (uint64_t)gi) / 1560;
+            if (q > 127) q = 127;
+            if (q < -127) q = -127;
+        }
+        out[i] = (int8_t)q;
+    }
+}
+
+void synth_q8_scales(float *out, int64_t nblocks, uint64_t skey, int64_t block0, float base)
+{
+    for (int64_t b = 0; b < nblocks; ++b) {
+        uint64_t h = synth_output(skey, (uint64_t)(block0 + b));
+        float f = (float)(1024u + (uint32_t)(h & 1023u)) * 0.0009765625f;
+        out[b] = base * f;
+    }
+}

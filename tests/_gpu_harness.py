@@ -22,43 +22,80 @@ def torch():
     return _t
 
 
-class DeviceShard:
-    """Device buffers of one rank's shard for a synth Workload."""
+VARIANTS = ("base", "q8ag", "q8grad", "bf16mv")
 
-    def __init__(self, w: synth.Workload, device="cuda:0"):
+
+class DeviceShard:
+    """Device buffers of one rank's shard for a synth Workload, for one of the
+    entry points: base (zs_shard_step), q8ag (also the int8 parameter copy),
+    q8grad (int8 partials) or bf16mv (bf16 moments)."""
+
+    def __init__(self, w: synth.Workload, variant="base", device="cuda:0"):
         t = torch()
         self.w = w
+        self.variant = variant
         n = w.n
+        nb = -(-n // zs.ZS_Q8_BLOCK)
         dev = t.device(device)
+        mv_dtype = t.int16 if variant == "bf16mv" else t.float32
         self.master = t.empty(n, dtype=t.float32, device=dev)
-        self.m = t.zeros(n, dtype=t.float32, device=dev)
-        self.v = t.zeros(n, dtype=t.float32, device=dev)
+        self.m = t.zeros(n, dtype=mv_dtype, device=dev)
+        self.v = t.zeros(n, dtype=mv_dtype, device=dev)
         self.param = t.zeros(n, dtype=t.int16, device=dev)
-        self.grads = [t.empty(n, dtype=t.int16, device=dev) for _ in range(w.k)]
+        self.grads = self.qgrads = self.qscales = self.q8 = self.q8s = None
+        if variant == "q8grad":
+            self.qgrads = [t.empty(n, dtype=t.int8, device=dev) for _ in range(w.k)]
+            self.qscales = [t.empty(nb, dtype=t.float32, device=dev) for _ in range(w.k)]
+        else:
+            self.grads = [t.empty(n, dtype=t.int16, device=dev) for _ in range(w.k)]
+        if variant == "q8ag":
+            self.q8 = t.zeros(n, dtype=t.int8, device=dev)
+            self.q8s = t.zeros(nb, dtype=t.float32, device=dev)
         self.table = segment_tensor(w.shard.segments, dev)
         synth.dev_master(w, self.master)
 
     def fill_grads(self, step):
-        synth.dev_grads(self.w, step, self.grads)
+        if self.variant == "q8grad":
+            synth.dev_qgrads(self.w, step, self.qgrads, self.qscales)
+        else:
+            synth.dev_grads(self.w, step, self.grads)
 
     def step(self, t_step, **cfg):
         t = torch()
         w = self.w
         hp = zs.hparams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, 1.0)
-        if cfg:
+        st = zs.seg_table(self.table)
+        s = t.cuda.current_stream()
+        if self.variant == "q8ag":
+            zs.zs_shard_step_q8ag(self.master, self.m, self.v, self.param, self.q8, self.q8s,
+                                  self.grads, w.k, w.n, st, hp, t_step, s)
+        elif self.variant == "q8grad":
+            zs.zs_shard_step_q8grad(self.master, self.m, self.v, self.param, self.qgrads,
+                                    self.qscales, w.k, w.n, st, hp, t_step, s)
+        elif self.variant == "bf16mv":
+            zs.zs_shard_step_bf16mv(self.master, self.m, self.v, self.param, self.grads, w.k,
+                                    w.n, st, hp, t_step, s)
+        elif cfg:
             zs.zs_shard_step_cfg(self.master, self.m, self.v, self.param, self.grads, w.k, w.n,
-                                 zs.seg_table(self.table), hp, t_step,
-                                 t.cuda.current_stream(), **cfg)
+                                 st, hp, t_step, s, **cfg)
         else:
-            zs.zs_shard_step(self.master, self.m, self.v, self.param, self.grads, w.k, w.n,
-                             zs.seg_table(self.table), hp, t_step, t.cuda.current_stream())
+            zs.zs_shard_step(self.master, self.m, self.v, self.param, self.grads, w.k, w.n, st,
+                             hp, t_step, s)
 
     def window(self, lo, hi):
-        return (self.master[lo:hi].cpu().numpy(), self.m[lo:hi].cpu().numpy(),
-                self.v[lo:hi].cpu().numpy(), self.param[lo:hi].cpu().numpy().view(np.uint16))
+        """(master, m, v, param[, q8, q8 scales of the covered blocks]) on [lo, hi)."""
+        mv = (lambda x: x[lo:hi].cpu().numpy().view(np.uint16)) if self.variant == "bf16mv" \
+            else (lambda x: x[lo:hi].cpu().numpy())
+        out = (self.master[lo:hi].cpu().numpy(), mv(self.m), mv(self.v),
+               self.param[lo:hi].cpu().numpy().view(np.uint16))
+        if self.variant == "q8ag":
+            b0, b1 = lo // zs.ZS_Q8_BLOCK, -(-hi // zs.ZS_Q8_BLOCK)
+            out = out + (self.q8[lo:hi].cpu().numpy(), self.q8s[b0:b1].cpu().numpy())
+        return out
 
     def free(self):
-        for name in ("master", "m", "v", "param", "grads", "table"):
+        for name in ("master", "m", "v", "param", "grads", "qgrads", "qscales", "q8", "q8s",
+                     "table"):
             setattr(self, name, None)
         torch().cuda.empty_cache()
 
@@ -69,19 +106,33 @@ def segment_tensor(segments, device):
     return t.tensor(rows, dtype=t.int64, device=device)
 
 
-def oracle_window(w: synth.Workload, lo, hi, steps):
+def oracle_window(w: synth.Workload, lo, hi, steps, variant="base"):
     """Run the oracle over shard elements [lo, hi) for the given optimizer
-    steps (inputs regenerated on the host).  Returns (master, m, v, param)."""
+    steps (inputs regenerated on the host), with the arithmetic of `variant`.
+    Quantized variants need lo on a block boundary and hi on one or at n."""
     n = hi - lo
     master = synth.host_master(w, lo, hi)
-    m = np.zeros(n, F32)
-    v = np.zeros(n, F32)
+    mv_dtype = np.uint16 if variant == "bf16mv" else F32
+    m = np.zeros(n, mv_dtype)
+    v = np.zeros(n, mv_dtype)
     p = np.zeros(n, np.uint16)
     segs = synth.clip_segments(w.shard.segments, lo, hi)
     hp = oracle.hparams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, 1.0)
     for t in steps:
-        rc = oracle.shard_step(master, m, v, p, synth.host_grads(w, t, lo, hi), segs, hp, t)
+        if variant == "q8grad":
+            qs, ss = synth.host_qgrads(w, t, lo, hi)
+            rc = oracle.shard_step_q8grad(master, m, v, p, qs, ss, segs, hp, t)
+        elif variant == "bf16mv":
+            rc = oracle.shard_step_bf16mv(master, m, v, p, synth.host_grads(w, t, lo, hi), segs,
+                                          hp, t)
+        else:
+            rc = oracle.shard_step(master, m, v, p, synth.host_grads(w, t, lo, hi), segs, hp, t)
         assert rc == 0
+    if variant == "q8ag":
+        if lo % zs.ZS_Q8_BLOCK or (hi % zs.ZS_Q8_BLOCK and hi != w.n):
+            raise ValueError("q8ag windows must be whole quantization blocks")
+        q, s = oracle.q8_blocks(p, zs.ZS_Q8_BLOCK)
+        return master, m, v, p, q, s
     return master, m, v, p
 
 
@@ -94,10 +145,23 @@ def bf16_ulp_distance(a, b):
 
 
 def assert_parity(got, ref, where=""):
-    """|d| <= 1e-6 * max(1, |x|) on master, m, v; <= 1 bf16 ulp on the param.
-    NaN must meet NaN.  Returns True if every output is bitwise equal."""
+    """|d| <= 1e-6 * max(1, |x|) on fp32 master, m, v; <= 1 bf16 ulp on the
+    param (and on m, v when they are bf16); int8 codes and their scales of the
+    quantized parameter copy, when present, exactly (NaN meets NaN).
+    Returns True if every output is bitwise equal."""
     bitwise = True
+    for name, g, r in zip(("m", "v"), got[1:3], ref[1:3]):
+        if g.dtype == np.uint16:
+            d = bf16_ulp_distance(g, r)
+            assert d.max(initial=0) <= 1, "%s %s: %d bf16 ulp" % (where, name, int(d.max()))
+            bitwise &= bool(np.array_equal(g, r))
+    if len(got) > 4:
+        assert np.array_equal(got[4], ref[4]), "%s q8: %d codes differ" % (
+            where, int((got[4] != ref[4]).sum()))
+        assert np.array_equal(got[5], ref[5], equal_nan=True), "%s q8 scales differ" % where
     for name, g, r in zip(("master", "m", "v"), got[:3], ref[:3]):
+        if g.dtype == np.uint16:
+            continue
         gd, rd = g.astype(np.float64), r.astype(np.float64)
         nan_g, nan_r = np.isnan(gd), np.isnan(rd)
         assert np.array_equal(nan_g, nan_r), "%s %s: NaN pattern differs" % (where, name)
@@ -117,11 +181,20 @@ def assert_parity(got, ref, where=""):
     return bitwise
 
 
-def boundary_windows(w: synth.Workload, size, max_boundaries=64, n_random=4, seed=0):
+def boundary_windows(w: synth.Workload, size, max_boundaries=64, n_random=4, seed=0, align=1):
     """Windows [lo, hi) of the shard: first, last (ragged tail), ones that
-    straddle segment boundaries, and random ones.  Deduplicated, sorted."""
+    straddle segment boundaries, and random ones.  Deduplicated, sorted.
+    With align > 1 every window starts on a multiple of align and has a
+    multiple of align elements, except a last window that ends at n."""
     n = w.n
     size = min(size, n)
+    if align > 1:
+        out = set()
+        for lo, hi in boundary_windows(w, size, max_boundaries, n_random, seed):
+            a = lo // align * align
+            b = min(n, -(-hi // align) * align)
+            out.add((a, b))
+        return sorted(out)
     starts = {0, max(0, n - size)}
     bounds = [s for s, _ in w.shard.segments[1:]]
     if len(bounds) > max_boundaries:

@@ -1,0 +1,214 @@
+"""GPU parity of the step variants (through the C ABI) against the oracle:
+the int8 all-gather payload (zs_shard_step_q8ag), int8 block-quantized
+partials (zs_shard_step_q8grad) and bf16 moments (zs_shard_step_bf16mv).
+Same bar as the ordinary step; int8 codes and scales must match exactly."""
+import numpy as np
+import pytest
+
+import oracle
+import sharded_mixed_precision_shard_amd as zs
+import synth
+from tests import _gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+F32 = np.float32
+BLOCK = zs.ZS_Q8_BLOCK
+SIZES = [1, 7, 255, 256, 257, 511, 512, 513, 2047, 2049, 4096, 10007, 65539]
+
+
+@pytest.fixture(scope="module")
+def gpu():
+    import torch
+    assert torch.cuda.is_available()
+    torch.cuda.set_device(0)
+    assert zs.zs_init(0) == zs.ZS_OK
+    yield torch
+    torch.cuda.synchronize()
+
+
+def _dev(torch, a):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16).copy()).cuda()
+    return torch.from_numpy(a.copy()).cuda()
+
+
+def _segments(rng, n):
+    segs, a = [], 0
+    while a < n:
+        segs.append((a, bool(rng.random() < 0.5)))
+        a += int(rng.integers(1, 8)) if rng.random() < 0.4 else int(rng.integers(8, 3000))
+    return segs
+
+
+def _bf16_partials(rng, k, n, sigma=1e-2):
+    return [(rng.normal(0, sigma, n).astype(F32).view(np.uint32) >> 16).astype(np.uint16)
+            for _ in range(k)]
+
+
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("k", [1, 2, 5])
+def test_q8ag_matches_oracle(gpu, n, k):
+    torch = gpu
+    rng = np.random.default_rng(100 + n * 7 + k)
+    segs = _segments(rng, n)
+    w0 = rng.normal(0, 0.02, n).astype(F32)
+    ref = [w0.copy(), np.zeros(n, F32), np.zeros(n, F32), np.zeros(n, np.uint16)]
+    dw, dm, dv = _dev(torch, w0), _dev(torch, ref[1]), _dev(torch, ref[2])
+    dp = torch.zeros(n, dtype=torch.int16, device="cuda")
+    nb = -(-n // BLOCK)
+    dq = torch.full((n,), 99, dtype=torch.int8, device="cuda")
+    ds = torch.full((nb,), -1.0, dtype=torch.float32, device="cuda")
+    table = H.segment_tensor(segs, "cuda")
+    for t in (1, 2, 3):
+        gs = _bf16_partials(rng, k, n)
+        if t == 3 and n > 300:
+            gs[0][n // 2] = 0x7FC0  # a NaN partial poisons one element and its block
+        zs.zs_shard_step_q8ag(dw, dm, dv, dp, dq, ds, [_dev(torch, g) for g in gs], k, n,
+                              zs.seg_table(table), zs.hparams(), t, torch.cuda.current_stream())
+        assert oracle.shard_step(*ref, gs, segs, oracle.hparams(), t) == 0
+    torch.cuda.synchronize()
+    q, s = oracle.q8_blocks(ref[3], BLOCK)
+    got = (dw.cpu().numpy(), dm.cpu().numpy(), dv.cpu().numpy(),
+           dp.cpu().numpy().view(np.uint16), dq.cpu().numpy(), ds.cpu().numpy())
+    H.assert_parity(got, tuple(ref) + (q, s), "q8ag n=%d k=%d" % (n, k))
+    if n > 300:
+        assert np.isnan(got[5][(n // 2) // BLOCK])
+
+
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("k", [1, 3, 8])
+def test_q8grad_matches_oracle(gpu, n, k):
+    torch = gpu
+    rng = np.random.default_rng(200 + n * 7 + k)
+    segs = _segments(rng, n)
+    nb = -(-n // BLOCK)
+    w0 = rng.normal(0, 0.02, n).astype(F32)
+    ref = [w0.copy(), np.zeros(n, F32), np.zeros(n, F32), np.zeros(n, np.uint16)]
+    dw, dm, dv = _dev(torch, w0), _dev(torch, ref[1]), _dev(torch, ref[2])
+    dp = torch.zeros(n, dtype=torch.int16, device="cuda")
+    table = H.segment_tensor(segs, "cuda")
+    for t in (1, 2, 3):
+        qs = [rng.integers(-127, 128, n).astype(np.int8) for _ in range(k)]
+        ss = [(rng.random(nb) * 1e-4).astype(F32) for _ in range(k)]
+        zs.zs_shard_step_q8grad(dw, dm, dv, dp, [_dev(torch, q) for q in qs],
+                                [_dev(torch, s) for s in ss], k, n, zs.seg_table(table),
+                                zs.hparams(), t, torch.cuda.current_stream())
+        assert oracle.shard_step_q8grad(*ref, qs, ss, segs, oracle.hparams(), t) == 0
+    torch.cuda.synchronize()
+    got = (dw.cpu().numpy(), dm.cpu().numpy(), dv.cpu().numpy(),
+           dp.cpu().numpy().view(np.uint16))
+    H.assert_parity(got, ref, "q8grad n=%d k=%d" % (n, k))
+
+
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("k", [1, 2, 8])
+def test_bf16mv_matches_oracle(gpu, n, k):
+    torch = gpu
+    rng = np.random.default_rng(300 + n * 7 + k)
+    segs = _segments(rng, n)
+    w0 = rng.normal(0, 0.02, n).astype(F32)
+    ref = [w0.copy(), np.zeros(n, np.uint16), np.zeros(n, np.uint16), np.zeros(n, np.uint16)]
+    dw = _dev(torch, w0)
+    dm = torch.zeros(n, dtype=torch.int16, device="cuda")
+    dv = torch.zeros(n, dtype=torch.int16, device="cuda")
+    dp = torch.zeros(n, dtype=torch.int16, device="cuda")
+    table = H.segment_tensor(segs, "cuda")
+    for t in range(1, 11):
+        gs = _bf16_partials(rng, k, n, 1e-3)
+        zs.zs_shard_step_bf16mv(dw, dm, dv, dp, [_dev(torch, g) for g in gs], k, n,
+                                zs.seg_table(table), zs.hparams(), t,
+                                torch.cuda.current_stream())
+        assert oracle.shard_step_bf16mv(*ref, gs, segs, oracle.hparams(), t) == 0
+    torch.cuda.synchronize()
+    got = (dw.cpu().numpy(), dm.cpu().numpy().view(np.uint16), dv.cpu().numpy().view(np.uint16),
+           dp.cpu().numpy().view(np.uint16))
+    H.assert_parity(got, ref, "bf16mv n=%d k=%d" % (n, k))
+
+
+def test_variant_argument_errors(gpu):
+    torch = gpu
+    n = 1024
+    f = [torch.zeros(n, dtype=torch.float32, device="cuda") for _ in range(3)]
+    p = torch.zeros(n, dtype=torch.int16, device="cuda")
+    g = [torch.zeros(n, dtype=torch.int16, device="cuda")]
+    q = torch.zeros(n, dtype=torch.int8, device="cuda")
+    s = torch.zeros(4, dtype=torch.float32, device="cuda")
+    st = zs.seg_table(H.segment_tensor([(0, True)], "cuda"))
+    hp = zs.hparams()
+    ok = zs.ZS_OK
+    assert zs.zs_shard_step_q8ag(*f, p, q, s, g, 1, n, st, hp, 1, None, check=False) == ok
+    assert zs.zs_shard_step_q8ag(*f, p, 0, s, g, 1, n, st, hp, 1, None, check=False) == \
+        zs.ZS_ERR_INVALID_ARGUMENT
+    assert zs.zs_shard_step_q8ag(*f, p, q.data_ptr() + 4, s, g, 1, n - 8, st, hp, 1, None,
+                                 check=False) == zs.ZS_ERR_MISALIGNED
+    assert zs.zs_shard_step_q8ag(*f, p, q, s.data_ptr() + 2, g, 1, n, st, hp, 1, None,
+                                 check=False) == zs.ZS_ERR_MISALIGNED
+    assert zs.zs_shard_step_q8ag(*f, p, p, s, g, 1, n, st, hp, 1, None, check=False) == \
+        zs.ZS_ERR_ALIASING
+    assert zs.zs_shard_step_q8ag(*f, p, q, f[0], g, 1, n, st, hp, 1, None, check=False) == \
+        zs.ZS_ERR_ALIASING
+    assert zs.zs_shard_step_q8grad(*f, p, [q], [s], 1, n, st, hp, 1, None, check=False) == ok
+    assert zs.zs_shard_step_q8grad(*f, p, [q], [0], 1, n, st, hp, 1, None, check=False) == \
+        zs.ZS_ERR_INVALID_ARGUMENT
+    assert zs.zs_shard_step_q8grad(*f, p, [q], [s], 1, n, st, hp, 0, None, check=False) == \
+        zs.ZS_ERR_INVALID_ARGUMENT
+    assert zs.zs_shard_step_q8grad(*f, p, [f[0]], [s], 1, n, st, hp, 1, None, check=False) == \
+        zs.ZS_ERR_ALIASING
+    mb = torch.zeros(n, dtype=torch.int16, device="cuda")
+    vb = torch.zeros(n, dtype=torch.int16, device="cuda")
+    assert zs.zs_shard_step_bf16mv(f[0], mb, vb, p, g, 1, n, st, hp, 1, None, check=False) == ok
+    assert zs.zs_shard_step_bf16mv(f[0], mb, mb, p, g, 1, n, st, hp, 1, None, check=False) == \
+        zs.ZS_ERR_ALIASING
+    torch.cuda.synchronize()
+
+
+def test_device_int8_generator_matches_host(gpu):
+    torch = gpu
+    n, nb = 100_003, 400
+    key = synth.stream_key(5, synth.ROLE_QGRAD, 2, 7)
+    skey = synth.stream_key(5, synth.ROLE_QSCALE, 2, 7)
+    dq = torch.empty(n, dtype=torch.int8, device="cuda")
+    ds = torch.empty(nb, dtype=torch.float32, device="cuda")
+    synth.dev_q8(dq, n, key, 777, 90_000)
+    synth.dev_q8_scales(ds, nb, skey, 3, synth.q8_base_scale(1e-3))
+    torch.cuda.synchronize()
+    assert np.array_equal(dq.cpu().numpy(), synth.host_q8(n, key, 777, 90_000))
+    assert np.array_equal(ds.cpu().numpy(),
+                          synth.host_q8_scales(nb, skey, 3, synth.q8_base_scale(1e-3)))
+
+
+def _large_variant(torch, name, variant, window, max_boundaries):
+    w = synth.workload(name)
+    free, _ = torch.cuda.mem_get_info()
+    per = {"base": 14 + 2 * w.k, "q8ag": 15 + 2 * w.k, "q8grad": 14 + w.k,
+           "bf16mv": 10 + 2 * w.k}[variant]
+    if free < w.n * per + (2 << 30):
+        pytest.skip("needs %.1f GB of free device memory" % (w.n * per / 1e9))
+    print("%s %s: n=%d k=%d" % (name, variant, w.n, w.k), flush=True)
+    ds = H.DeviceShard(w, variant)
+    ts = list(range(1, w.prewarm_steps + 1)) + w.step_ts()
+    for t in ts:
+        ds.fill_grads(t)
+        ds.step(t)
+    torch.cuda.synchronize()
+    wins = H.boundary_windows(w, window, max_boundaries=max_boundaries, n_random=3, seed=2,
+                              align=BLOCK)
+    got = [ds.window(lo, hi) for lo, hi in wins]
+    ds.free()
+    for (lo, hi), g in zip(wins, got):
+        H.assert_parity(g, H.oracle_window(w, lo, hi, ts, variant),
+                        "%s %s [%d,%d)" % (name, variant, lo, hi))
+
+
+@pytest.mark.parametrize("variant", ["q8ag", "q8grad", "bf16mv"])
+def test_variants_on_70b_shard_windows(gpu, variant):
+    """The full 70B-shaped rank-0 shard (8.05e9 elements, 1970 segments,
+    t = 10000..10002) in each variant's default launch, compared on windows
+    around segment boundaries and at the ragged ends."""
+    _large_variant(gpu, "70b", variant, 1 << 14, 48)
+
+
+@pytest.mark.parametrize("variant", ["q8ag", "q8grad", "bf16mv"])
+def test_variants_on_gpt2_shard_windows(gpu, variant):
+    _large_variant(gpu, "gpt2-small", variant, 1 << 14, 30)

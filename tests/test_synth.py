@@ -70,3 +70,16 @@ def test_decay_off_for_biases_and_norms():
         assert wd == (name.split(".")[-1].startswith("w") or name in ("wpe", "wte"))
     for name, _, wd in transformer_12d2(2, 64, n_heads=4):
         assert wd == (".w_" in name)
+
+
+def test_int8_partials_and_scales():
+    key = synth.stream_key(3, synth.ROLE_QGRAD, 1, 2)
+    q = synth.host_q8(1 << 18, key, 1000, 1000 + (1 << 18) - 50)
+    assert q.dtype == np.int8 and abs(q[:-50].astype(np.float64).std() - synth.Q8_SD) < 1.0
+    assert not q[-50:].any()  # padding
+    win = synth.host_q8(333, key, 1000 + 4096, 1000 + (1 << 18) - 50)
+    assert np.array_equal(win, q[4096:4096 + 333])
+    s = synth.host_q8_scales(64, synth.stream_key(3, synth.ROLE_QSCALE, 1, 2), 0, 0.5)
+    assert np.all((s >= 0.5) & (s < 1.0))
+    s2 = synth.host_q8_scales(10, synth.stream_key(3, synth.ROLE_QSCALE, 1, 2), 20, 0.5)
+    assert np.array_equal(s2, s[20:30])
