@@ -58,9 +58,10 @@ def measured_traffic(config: str, launch_key: str):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(w, seconds: float):
+def cpu_baseline(w, seconds: float, variant: str, bytes_per_elem: float):
     """Time the CPU oracle (single thread, as it stands) on a bounded window
-    of the same workload: the first min(n, 2^24) elements of the shard."""
+    of the same workload: the first min(n, 2^24) elements of the shard, with
+    the arithmetic of the entry point being measured."""
     import numpy as np
 
     import oracle
@@ -68,10 +69,14 @@ def cpu_baseline(w, seconds: float):
 
     n = min(w.n, 1 << 24)
     master = synth.host_master(w, 0, n)
-    m = np.zeros(n, np.float32)
-    v = np.zeros(n, np.float32)
+    mv_dtype = np.uint16 if variant == "bf16mv" else np.float32
+    m = np.zeros(n, mv_dtype)
+    v = np.zeros(n, mv_dtype)
     p = np.zeros(n, np.uint16)
-    grads = synth.host_grads(w, w.t0, 0, n)
+    if variant == "q8grad":
+        qgrads, qscales = synth.host_qgrads(w, w.t0, 0, n)
+    else:
+        grads = synth.host_grads(w, w.t0, 0, n)
     segs = synth.clip_segments(w.shard.segments, 0, n)
     hp = oracle.hparams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, 1.0)
     steps = 0
@@ -79,21 +84,28 @@ def cpu_baseline(w, seconds: float):
     t = w.t0
     while elapsed < seconds or steps == 0:
         t0 = time.perf_counter()
-        rc = oracle.shard_step(master, m, v, p, grads, segs, hp, t)
+        if variant == "q8grad":
+            rc = oracle.shard_step_q8grad(master, m, v, p, qgrads, qscales, segs, hp, t)
+        elif variant == "bf16mv":
+            rc = oracle.shard_step_bf16mv(master, m, v, p, grads, segs, hp, t)
+        else:
+            rc = oracle.shard_step(master, m, v, p, grads, segs, hp, t)
+            if variant == "q8ag":
+                oracle.q8_blocks(p, 256)
         elapsed += time.perf_counter() - t0
         assert rc == 0
         steps += 1
         t += 1
-    bpe = 26 + 2 * w.k
     return {
-        "value": round(n * steps * bpe / elapsed / 1e9, 4),
+        "value": round(n * steps * bytes_per_elem / elapsed / 1e9, 4),
         "unit": "GB/s",
         "params_per_s": round(n * steps / elapsed, 1),
         "cores": 1,
         "kind": "oracle",
         "sample": "first %d elements of the %s shard (k=%d, %d segments in the window), "
-                  "%d oracle steps, single-threaded C, %.1f s" % (
-                      n, w.name.split(":")[0].split(" (")[0], w.k, len(segs), steps, elapsed),
+                  "%d oracle steps (%s arithmetic), single-threaded C, %.1f s" % (
+                      n, w.name.split(":")[0].split(" (")[0], w.k, len(segs), steps, variant,
+                      elapsed),
     }
 
 
@@ -124,6 +136,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="70b")
+    ap.add_argument("--variant", default="base", choices=("base", "q8ag", "q8grad", "bf16mv"),
+                    help="entry point: zs_shard_step (base), zs_shard_step_q8ag, "
+                         "zs_shard_step_q8grad or zs_shard_step_bf16mv")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU oracle time budget for the cpu_baseline leg (0 = skip)")
     ap.add_argument("--chunk-tiles", type=int, default=0, help="launch geometry override")
@@ -154,9 +169,10 @@ def main():
 
     w = synth.workload(args.config)
     n, k = w.n, w.k
-    bpe = 26 + 2 * k
-    bytes_per_step = bpe * n
-    assert zs.zs_algorithmic_bytes(k, n) == bytes_per_step
+    bytes_per_step = zs.algorithmic_bytes(args.variant, k, n)
+    bpe = bytes_per_step / n
+    if args.variant == "base":
+        assert zs.zs_algorithmic_bytes(k, n) == bytes_per_step
     log("workload: %s  n=%d k=%d segments=%d bytes/step=%.3f GB" % (
         w.name, n, k, len(w.shard.segments), bytes_per_step / 1e9))
 
@@ -166,11 +182,22 @@ def main():
         log("copy ceiling (torch copy_, %.1f GB): %.1f GB/s" % (args.copy_gb, copy_gbps))
 
     dev = torch.device("cuda:0")
+    var = args.variant
+    nb = -(-n // zs.ZS_Q8_BLOCK)
+    mv_dtype = torch.int16 if var == "bf16mv" else torch.float32
     master = torch.empty(n, dtype=torch.float32, device=dev)
-    m = torch.zeros(n, dtype=torch.float32, device=dev)
-    v = torch.zeros(n, dtype=torch.float32, device=dev)
+    m = torch.zeros(n, dtype=mv_dtype, device=dev)
+    v = torch.zeros(n, dtype=mv_dtype, device=dev)
     param = torch.zeros(n, dtype=torch.int16, device=dev)
-    grads = [torch.empty(n, dtype=torch.int16, device=dev) for _ in range(k)]
+    grads = qgrads = qscales = q8 = q8s = None
+    if var == "q8grad":
+        qgrads = [torch.empty(n, dtype=torch.int8, device=dev) for _ in range(k)]
+        qscales = [torch.empty(nb, dtype=torch.float32, device=dev) for _ in range(k)]
+    else:
+        grads = [torch.empty(n, dtype=torch.int16, device=dev) for _ in range(k)]
+    if var == "q8ag":
+        q8 = torch.zeros(n, dtype=torch.int8, device=dev)
+        q8s = torch.zeros(nb, dtype=torch.float32, device=dev)
     table = torch.tensor([[s, 1 if f else 0] for s, f in w.shard.segments], dtype=torch.int64,
                          device=dev)
     st = zs.seg_table(table)
@@ -179,18 +206,31 @@ def main():
     synth.dev_master(w, master)
 
     def step(t):
-        if args.chunk_tiles or args.nontemporal:
+        if var == "q8ag":
+            zs.zs_shard_step_q8ag(master, m, v, param, q8, q8s, grads, k, n, st, hp, t, stream)
+        elif var == "q8grad":
+            zs.zs_shard_step_q8grad(master, m, v, param, qgrads, qscales, k, n, st, hp, t,
+                                    stream)
+        elif var == "bf16mv":
+            zs.zs_shard_step_bf16mv(master, m, v, param, grads, k, n, st, hp, t, stream)
+        elif args.chunk_tiles or args.nontemporal:
             zs.zs_shard_step_cfg(master, m, v, param, grads, k, n, st, hp, t, stream,
                                  chunk_tiles=args.chunk_tiles, nontemporal=args.nontemporal)
         else:
             zs.zs_shard_step(master, m, v, param, grads, k, n, st, hp, t, stream)
 
+    def fill(t):
+        if var == "q8grad":
+            synth.dev_qgrads(w, t, qgrads, qscales)
+        else:
+            synth.dev_grads(w, t, grads)
+
     # pre-warm of the moments where the workload asks for it (fresh partials per step)
     for t in range(1, w.prewarm_steps + 1):
-        synth.dev_grads(w, t, grads)
+        fill(t)
         step(t)
     # the partials of the first measured step stay resident for every timed step
-    synth.dev_grads(w, w.t0, grads)
+    fill(w.t0)
     torch.cuda.synchronize()
 
     t = w.t0
@@ -218,14 +258,15 @@ def main():
     value = bytes_per_step * args.steps / elapsed / 1e9
     achieved = bytes_per_step / (avg_ms * 1e-3) / 1e9
     launch_key = "chunk_tiles=%d,nontemporal=%d" % (args.chunk_tiles, args.nontemporal)
-    traffic = measured_traffic(args.config, launch_key)
+    traffic_key = args.config if var == "base" else "%s/%s" % (args.config, var)
+    traffic = measured_traffic(traffic_key, launch_key)
 
-    del master, m, v, param, grads
+    del master, m, v, param, grads, qgrads, qscales, q8, q8s
     torch.cuda.empty_cache()
 
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, args.cpu_seconds)
+        cpu = cpu_baseline(w, args.cpu_seconds, var, bpe)
         log("cpu oracle: %.3f GB/s (%s)" % (cpu["value"], cpu["sample"]))
 
     out = {
@@ -239,15 +280,19 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32 state, bf16 partials and param",
+        "dtype": {"base": "f32 state, bf16 partials and param",
+                  "q8ag": "f32 state, bf16 partials and param, int8 param copy",
+                  "q8grad": "f32 state, int8 partials, bf16 param",
+                  "bf16mv": "f32 master, bf16 m/v, partials and param"}[var],
         "data": "synthetic (seeded SplitMix64 / Irwin-Hall draws; partials of the first "
                 "measured step kept resident across timed steps)",
         "config": {
             "workload": w.name,
+            "entry_point": "zs_shard_step" if var == "base" else "zs_shard_step_" + var,
             "shard_params": n,
             "k_partials": k,
             "segments": len(w.shard.segments),
-            "bytes_per_param": bpe,
+            "bytes_per_param": round(bpe, 4),
             "bytes_per_step": bytes_per_step,
             "first_step_t": w.t0 + args.warmup,
         },
@@ -261,7 +306,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": "shard_step_kernel<K=%d>" % k,
+            "kernel": "shard_step_kernel<K=%d,%s>" % (k, var),
             "avg_launch_ms": round(avg_ms, 4),
         },
         "cpu_baseline": cpu,
