@@ -130,15 +130,111 @@ def copy_ceiling(torch, nbytes: int):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+def host_copy_ceiling(nbytes: int, threads: int):
+    """Host memory copy bandwidth (read + write GB/s): `threads` threads each
+    copying a contiguous slice with numpy (which releases the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    n = nbytes // 4
+    src = np.ones(n, np.float32)
+    dst = np.zeros(n, np.float32)
+    step = -(-n // threads)
+    parts = [(dst[a:a + step], src[a:a + step]) for a in range(0, n, step)]
+    best = 0.0
+    with ThreadPoolExecutor(threads) as ex:
+        for _ in range(6):
+            t0 = time.perf_counter()
+            list(ex.map(lambda ds: np.copyto(ds[0], ds[1]), parts))
+            best = max(best, 2 * nbytes / (time.perf_counter() - t0) / 1e9)
+    return best
+
+
+def offload_main(args):
+    """The ZeRO-Offload host step on host memory: one shard step of the
+    workload per timed step, all host threads.  The roofline reference is the
+    host's measured copy bandwidth (no published peak for this host)."""
+    import numpy as np
+
+    import sharded_mixed_precision_shard_amd as zs
+    import synth
+
+    w = synth.workload(args.config)
+    n, k = w.n, w.k
+    threads = zs.zs_host_max_threads()
+    bytes_per_step = zs.algorithmic_bytes("base", k, n)
+    log("offload workload: %s  n=%d k=%d, %d host threads, %s" % (
+        w.name, n, k, threads, zs.zs_host_isa()))
+    ceiling = host_copy_ceiling(min(4 << 30, 4 * n), threads)
+    log("host copy ceiling: %.1f GB/s" % ceiling)
+    master = synth.host_master(w, threads=threads)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    p = np.zeros(n, np.uint16)
+    m.fill(0.0)
+    v.fill(0.0)
+    p.fill(0)
+    grads = synth.host_grads(w, w.t0, threads=threads)
+    segs = zs.host_segments(w.shard.segments)
+    hp = zs.hparams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, 1.0)
+    t = 1
+    for t in range(1, w.prewarm_steps + 1):
+        zs.zs_host_shard_step(master, m, v, p, synth.host_grads(w, t, threads=threads), k, n,
+                              segs, hp, t)
+    t = w.t0
+    for _ in range(args.warmup):
+        zs.zs_host_shard_step(master, m, v, p, grads, k, n, segs, hp, t)
+        t += 1
+    times = []
+    for _ in range(args.steps):
+        t0 = time.perf_counter()
+        zs.zs_host_shard_step(master, m, v, p, grads, k, n, segs, hp, t)
+        times.append(time.perf_counter() - t0)
+        t += 1
+    elapsed = sum(times)
+    value = bytes_per_step * args.steps / elapsed / 1e9
+    cpu = cpu_baseline(w, args.cpu_seconds, "base", 26 + 2 * k) if args.cpu_seconds > 0 \
+        else None
+    out = {
+        "metric": "achieved host DRAM GB/s and params/s for the ZeRO-Offload shard AdamW step",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 0,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 state, bf16 partials and param",
+        "data": "synthetic (seeded SplitMix64 / Irwin-Hall draws)",
+        "config": {"workload": w.name, "entry_point": "zs_host_shard_step", "shard_params": n,
+                   "k_partials": k, "segments": len(w.shard.segments),
+                   "bytes_per_param": 26 + 2 * k, "bytes_per_step": bytes_per_step,
+                   "host_threads": threads, "isa": zs.zs_host_isa()},
+        "params_per_s": round(n * args.steps / elapsed, 1),
+        "roofline": {"bound": "host-dram", "achieved": round(value, 2),
+                     "peak": round(ceiling, 1), "unit": "GB/s",
+                     "frac": round(value / ceiling, 4), "traffic": None,
+                     "peak_kind": "measured host copy bandwidth (threaded numpy copy, "
+                                  "read + write)"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="70b")
-    ap.add_argument("--variant", default="base", choices=("base", "q8ag", "q8grad", "bf16mv"),
+    ap.add_argument("--variant", default="base",
+                    choices=("base", "q8ag", "q8grad", "bf16mv", "offload"),
                     help="entry point: zs_shard_step (base), zs_shard_step_q8ag, "
-                         "zs_shard_step_q8grad or zs_shard_step_bf16mv")
+                         "zs_shard_step_q8grad, zs_shard_step_bf16mv, or the host "
+                         "(ZeRO-Offload) step zs_host_shard_step, which runs on the CPU "
+                         "and needs no GPU")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU oracle time budget for the cpu_baseline leg (0 = skip)")
     ap.add_argument("--chunk-tiles", type=int, default=0, help="launch geometry override")
@@ -153,6 +249,9 @@ def main():
               "cross-GPU work (the reduce-scatter and all-gather around it are not built). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.variant == "offload":
+        offload_main(args)
+        return
 
     import torch
 

@@ -17,6 +17,7 @@ import os
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libzs.so")
+HOST_LIB_PATH = os.path.join(PKG_DIR, "libzs_host.so")
 
 ZS_MAX_K = 16
 ZS_MAX_SEGMENTS = 65536
@@ -109,6 +110,8 @@ def _addr(x) -> int:
         return 0
     if isinstance(x, int):
         return x
+    if hasattr(x, "ctypes") and hasattr(x, "dtype"):  # numpy array (host memory)
+        return int(x.ctypes.data)
     if hasattr(x, "data_ptr"):
         return int(x.data_ptr())
     raise TypeError("expected a tensor with data_ptr() or an integer address, got %r" % type(x))
@@ -262,3 +265,64 @@ def algorithmic_bytes(variant: str, k: int, n: int) -> int:
     if variant == "bf16mv":
         return (18 + 2 * k) * n
     raise ValueError(variant)
+
+
+# ------------------------------------------------ host (ZeRO-Offload) step
+
+HOST_EXPORTS = ("zs_host_shard_step", "zs_host_max_threads", "zs_host_isa")
+_host_lib = None
+
+
+def load_host_library():
+    """Load libzs_host.so (include/zs_host.h); raise if it is missing."""
+    global _host_lib
+    if _host_lib is not None:
+        return _host_lib
+    if not os.path.exists(HOST_LIB_PATH):
+        raise ImportError("libzs_host.so is not built (expected at %s)" % HOST_LIB_PATH)
+    lib = ctypes.CDLL(HOST_LIB_PATH)
+    P = ctypes.c_void_p
+    lib.zs_host_shard_step.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int64, P,
+                                       ctypes.c_int32, P, ctypes.c_int64, ctypes.c_int]
+    lib.zs_host_shard_step.restype = ctypes.c_int
+    lib.zs_host_max_threads.argtypes = []
+    lib.zs_host_max_threads.restype = ctypes.c_int
+    lib.zs_host_isa.argtypes = []
+    lib.zs_host_isa.restype = ctypes.c_char_p
+    _host_lib = lib
+    return lib
+
+
+def host_segments(segs):
+    """[(start, wd_on), ...] -> ctypes array of ZsSegment (host table)."""
+    arr = (ZsSegment * len(segs))()
+    for i, (st, f) in enumerate(segs):
+        arr[i].start = int(st)
+        arr[i].wd_on = 1 if f else 0
+        arr[i].reserved = 0
+    return arr
+
+
+def zs_host_shard_step(master, m, v, param_bf16, grads, k, n, segs, hparams_, step,
+                       nthreads=0, check=True) -> int:
+    """Host shard step on host buffers (numpy arrays, CPU tensors or addresses).
+    ``segs`` is a list of (start, wd_on) or a ZsSegment array."""
+    gp = (ctypes.c_void_p * max(len(grads), 1))(*[_addr(g) for g in grads])
+    arr = segs if isinstance(segs, ctypes.Array) else host_segments(segs)
+    rc = load_host_library().zs_host_shard_step(
+        ctypes.c_void_p(_addr(master)), ctypes.c_void_p(_addr(m)), ctypes.c_void_p(_addr(v)),
+        ctypes.c_void_p(_addr(param_bf16)), ctypes.cast(gp, ctypes.c_void_p),
+        int(len(grads) if k is None else k), int(n), ctypes.cast(arr, ctypes.c_void_p), len(arr),
+        ctypes.byref(hparams_), int(step), int(nthreads))
+    if check and rc != ZS_OK:
+        raise RuntimeError("zs_host_shard_step failed: %s (status %d)" % (
+            zs_status_string(rc) if os.path.exists(LIB_PATH) else "", rc))
+    return rc
+
+
+def zs_host_max_threads() -> int:
+    return load_host_library().zs_host_max_threads()
+
+
+def zs_host_isa() -> str:
+    return load_host_library().zs_host_isa().decode()

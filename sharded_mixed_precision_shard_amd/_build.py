@@ -14,6 +14,13 @@ REPO_DIR = os.path.dirname(PKG_DIR)
 INCLUDE_DIR = os.path.join(REPO_DIR, "include")
 SRC = os.path.join(PKG_DIR, "csrc", "zs_step.hip")
 LIB = os.path.join(PKG_DIR, "libzs.so")
+HOST_SRC = os.path.join(PKG_DIR, "csrc", "zs_host.cpp")
+HOST_LIB = os.path.join(PKG_DIR, "libzs_host.so")
+
+# Host (ZeRO-Offload) step: OpenMP threads, AVX-512 chosen at run time, no
+# contraction and no fast-math so that the results match the device path.
+GXX_FLAGS = ["-O3", "-std=c++17", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+             "-shared", "-Wall"]
 
 ARCH = "gfx950"
 
@@ -40,14 +47,27 @@ def hipcc() -> str:
     return path
 
 
+def build_host(verbose: bool = False) -> str:
+    """Compile libzs_host.so with g++."""
+    tmp = HOST_LIB + ".tmp%d" % os.getpid()
+    cmd = ["g++", *GXX_FLAGS, "-I", INCLUDE_DIR, "-o", tmp, HOST_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, HOST_LIB)
+    return HOST_LIB
+
+
 def build(verbose: bool = False) -> str:
-    """Compile libzs.so (always recompiles).  Returns the library path."""
+    """Compile libzs.so and libzs_host.so (always recompiles).  Returns the
+    device library path."""
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE_DIR, "-o", tmp, SRC]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    build_host(verbose)
     return LIB
 
 

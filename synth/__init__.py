@@ -140,23 +140,47 @@ def host_normal_bf16(n, key, index0, valid_end, sigma, hkey=0, heavy_p=0.0, heav
     return out
 
 
-def host_master(w: Workload, lo: int = 0, hi: int = None):
+def _fill_parallel(out, fn, index0, threads):
+    """Fill out[:] with fn(sub_out, n, index0 + offset) in `threads` slices
+    (the C generators release the GIL, so the slices run concurrently)."""
+    n = out.shape[0]
+    if threads <= 1 or n < (1 << 20):
+        fn(out, n, index0)
+        return out
+    from concurrent.futures import ThreadPoolExecutor
+    step = -(-n // threads)
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(lambda a: fn(out[a:a + step], min(step, n - a), index0 + a),
+                    range(0, n, step)))
+    return out
+
+
+def host_master(w: Workload, lo: int = 0, hi: int = None, threads: int = 1):
     """fp32 master weights of shard elements [lo, hi)."""
     hi = w.n if hi is None else hi
     key = stream_key(w.seed, ROLE_MASTER, 0, 0)
-    return host_normal_f32(hi - lo, key, w.shard.index0 + lo, w.shard.valid_end,
-                           w.master_sigma)
+    sc = scale_of(w.master_sigma)
+    lib = _host_lib()
+    out = np.empty(hi - lo, dtype=np.float32)
+    return _fill_parallel(out, lambda o, n, i0: lib.synth_normal_f32(
+        o.ctypes.data, n, key, 0, i0, w.shard.valid_end, sc, 0, np.float32(0)),
+        w.shard.index0 + lo, threads)
 
 
-def host_grads(w: Workload, t: int, lo: int = 0, hi: int = None):
+def host_grads(w: Workload, t: int, lo: int = 0, hi: int = None, threads: int = 1):
     """The k bf16 partials of step t for shard elements [lo, hi)."""
     hi = w.n if hi is None else hi
+    lib = _host_lib()
     out = []
     for j in range(w.k):
         key = stream_key(w.seed, ROLE_GRAD, j, t)
         hkey = stream_key(w.seed, ROLE_HEAVY, j, t)
-        out.append(host_normal_bf16(hi - lo, key, w.shard.index0 + lo, w.shard.valid_end,
-                                    w.grad_sigma, hkey, w.heavy_p, w.heavy_sigma))
+        sc, hth, hsc = scale_of(w.grad_sigma), heavy_threshold(w.heavy_p), \
+            scale_of(w.heavy_sigma)
+        o = np.empty(hi - lo, dtype=np.uint16)
+        out.append(_fill_parallel(o, lambda oo, n, i0: lib.synth_normal_bf16(
+            oo.ctypes.data, n, key, hkey, i0, w.shard.valid_end, sc, hth, hsc),
+            w.shard.index0 + lo, threads))
     return out
 
 
