@@ -175,12 +175,15 @@ def offload_main(args):
     v.fill(0.0)
     p.fill(0)
     grads = synth.host_grads(w, w.t0, threads=threads)
+    log("host inputs generated")
     segs = zs.host_segments(w.shard.segments)
     hp = zs.hparams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, 1.0)
-    t = 1
+    # pre-warm steps reuse the resident partials (drawing fresh host partials
+    # for each of them would dominate the run; traffic does not depend on values)
     for t in range(1, w.prewarm_steps + 1):
-        zs.zs_host_shard_step(master, m, v, p, synth.host_grads(w, t, threads=threads), k, n,
-                              segs, hp, t)
+        zs.zs_host_shard_step(master, m, v, p, grads, k, n, segs, hp, t)
+        if t % 20 == 0:
+            log("pre-warm step %d" % t)
     t = w.t0
     for _ in range(args.warmup):
         zs.zs_host_shard_step(master, m, v, p, grads, k, n, segs, hp, t)
@@ -191,6 +194,7 @@ def offload_main(args):
         zs.zs_host_shard_step(master, m, v, p, grads, k, n, segs, hp, t)
         times.append(time.perf_counter() - t0)
         t += 1
+    log("host step: %.3f ms average over %d steps" % (1e3 * sum(times) / len(times), len(times)))
     elapsed = sum(times)
     value = bytes_per_step * args.steps / elapsed / 1e9
     cpu = cpu_baseline(w, args.cpu_seconds, "base", 26 + 2 * k) if args.cpu_seconds > 0 \

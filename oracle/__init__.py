@@ -53,33 +53,38 @@ def _load():
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             build(force=False)
-        lib = ctypes.CDLL(_LIB_PATH)
-        P = ctypes.c_void_p
-        lib.zs_oracle_shard_step.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int64,
-                                             P, ctypes.c_int32, P, ctypes.c_int64]
-        lib.zs_oracle_shard_step.restype = ctypes.c_int
-        lib.zs_oracle_adamw_unsharded.argtypes = [P, P, P, P, P, P, ctypes.c_int64, P,
-                                                  ctypes.c_int64]
-        lib.zs_oracle_adamw_unsharded.restype = ctypes.c_int
-        lib.zs_oracle_bf16_rne.argtypes = [ctypes.c_float]
-        lib.zs_oracle_bf16_rne.restype = ctypes.c_uint16
-        lib.zs_oracle_bf16_rne_array.argtypes = [P, P, ctypes.c_int64]
-        lib.zs_oracle_bf16_rne_array.restype = None
-        lib.zs_oracle_scalars.argtypes = [P, ctypes.c_int64, P]
-        lib.zs_oracle_scalars.restype = None
-        lib.zs_oracle_q8_blocks.argtypes = [P, ctypes.c_int64, ctypes.c_int32, P, P]
-        lib.zs_oracle_q8_blocks.restype = ctypes.c_int
-        lib.zs_oracle_q8_dequant.argtypes = [P, P, ctypes.c_int64, ctypes.c_int32, P]
-        lib.zs_oracle_q8_dequant.restype = None
-        lib.zs_oracle_shard_step_q8grad.argtypes = [P, P, P, P, P, P, ctypes.c_int,
-                                                    ctypes.c_int64, ctypes.c_int32, P,
-                                                    ctypes.c_int32, P, ctypes.c_int64]
-        lib.zs_oracle_shard_step_q8grad.restype = ctypes.c_int
-        lib.zs_oracle_shard_step_bf16mv.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int64,
-                                                    P, ctypes.c_int32, P, ctypes.c_int64]
-        lib.zs_oracle_shard_step_bf16mv.restype = ctypes.c_int
-        _lib = lib
+        _lib = load_library(_LIB_PATH)
     return _lib
+
+
+def load_library(path: str):
+    """Load an oracle shared library from `path` with its C signatures."""
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.zs_oracle_shard_step.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int64,
+                                         P, ctypes.c_int32, P, ctypes.c_int64]
+    lib.zs_oracle_shard_step.restype = ctypes.c_int
+    lib.zs_oracle_adamw_unsharded.argtypes = [P, P, P, P, P, P, ctypes.c_int64, P,
+                                              ctypes.c_int64]
+    lib.zs_oracle_adamw_unsharded.restype = ctypes.c_int
+    lib.zs_oracle_bf16_rne.argtypes = [ctypes.c_float]
+    lib.zs_oracle_bf16_rne.restype = ctypes.c_uint16
+    lib.zs_oracle_bf16_rne_array.argtypes = [P, P, ctypes.c_int64]
+    lib.zs_oracle_bf16_rne_array.restype = None
+    lib.zs_oracle_scalars.argtypes = [P, ctypes.c_int64, P]
+    lib.zs_oracle_scalars.restype = None
+    lib.zs_oracle_q8_blocks.argtypes = [P, ctypes.c_int64, ctypes.c_int32, P, P]
+    lib.zs_oracle_q8_blocks.restype = ctypes.c_int
+    lib.zs_oracle_q8_dequant.argtypes = [P, P, ctypes.c_int64, ctypes.c_int32, P]
+    lib.zs_oracle_q8_dequant.restype = None
+    lib.zs_oracle_shard_step_q8grad.argtypes = [P, P, P, P, P, P, ctypes.c_int,
+                                                ctypes.c_int64, ctypes.c_int32, P,
+                                                ctypes.c_int32, P, ctypes.c_int64]
+    lib.zs_oracle_shard_step_q8grad.restype = ctypes.c_int
+    lib.zs_oracle_shard_step_bf16mv.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int64,
+                                                P, ctypes.c_int32, P, ctypes.c_int64]
+    lib.zs_oracle_shard_step_bf16mv.restype = ctypes.c_int
+    return lib
 
 
 def hparams(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, grad_scale=1.0):
