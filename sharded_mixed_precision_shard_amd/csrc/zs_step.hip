@@ -10,12 +10,12 @@
 //
 // The work is purely elementwise and bandwidth bound (about 0.5 flop per HBM
 // byte), so there is no MFMA here.  Design for CDNA4:
-//   * a workgroup tile is 2048 elements; wavefront w of the workgroup owns
-//     the 512-element window [512w, 512w + 512) of it, as two 256-element
-//     halves; lane l owns elements 4l..4l+3 of each half.  Every load and
-//     store instruction of a wavefront is then one dense, contiguous run
-//     (1 KB per fp32 array, 512 B per bf16 array) of 16-byte (fp32) or
-//     8-byte (bf16) accesses, and every byte is read once and written once;
+//   * a wavefront's window is Q sub-windows of 256 elements (Q = 1 for one
+//     or two partials, 4 for more; a workgroup tile is four windows); lane
+//     l owns elements 4l..4l+3 of each sub-window.  Every load and store
+//     instruction of a wavefront is then one dense, contiguous run (1 KB per
+//     fp32 array, 512 B per bf16 array) of 16-byte (fp32) or 8-byte (bf16)
+//     accesses, and every byte is read once and written once;
 //   * a workgroup owns a contiguous chunk of tiles (one tile by default: the
 //     resident workgroups then sweep memory as one compact front);
 //   * the segment holding the chunk's first element is found by one
@@ -44,16 +44,21 @@ namespace {
 
 constexpr int kThreads = 256;                 // 4 wavefronts of 64 lanes
 constexpr int kWave = 64;
-constexpr int kQuad = 4;                      // contiguous elements per lane per half
-constexpr int kHalf = kWave * kQuad;          // 256 elements per half window
-constexpr int kWindow = 2 * kHalf;            // 512 elements per wave per tile
-constexpr int kTile = (kThreads / kWave) * kWindow;  // 2048 elements per tile
+constexpr int kQuad = 4;                      // contiguous elements per lane per sub-window
+constexpr int kSub = kWave * kQuad;           // 256: one dense instruction per array per wave
+
+// Sub-windows (quads per lane) a wave handles per tile.  Measured on MI355X:
+// with one or two partials the fewest bytes in flight per wave streamed best
+// (one quad); with three or more partials each lane already has many loads
+// in flight and four quads per lane streamed best.
+constexpr int quads_for(int k) { return k <= 2 ? 1 : 4; }
+constexpr int tile_for(int k) { return (kThreads / kWave) * quads_for(k) * kSub; }
 constexpr int kLdsSegs = 1024;                // staged segment entries
 constexpr int kMaxChunkTiles = 4096;
 constexpr int64_t kNoStart = INT64_MAX;       // sentinel past the table end
 
 static_assert(kLdsSegs % kThreads == 0, "staging rounds must be whole");
-static_assert(kTile == 2048, "tile size is part of the launch arithmetic");
+static_assert(tile_for(1) == 1024 && tile_for(8) == 4096, "tile sizes");
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -196,7 +201,7 @@ constexpr int kOutQ8 = 1;
 constexpr int kGradQ8 = 2;
 constexpr int kMvBf16 = 4;
 constexpr int kQ8Block = ZS_Q8_BLOCK;
-static_assert(kQ8Block == kHalf, "a quantization block is one half window");
+static_assert(kQ8Block == kSub, "a quantization block is one sub-window of a wave");
 
 __device__ __forceinline__ f32x4 bf16x4_to_f32x4(u32x2 d) {
     f32x4 r;
@@ -346,6 +351,9 @@ __device__ __forceinline__ void quad_update(f32x4 &w, f32x4 &m, f32x4 &v,
 
 template <int K, int V, int NT>
 __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) {
+    constexpr int kQuads = quads_for(K);      // sub-windows per wave per tile
+    constexpr int kWindow = kQuads * kSub;    // elements per wave per tile
+    constexpr int kTile = tile_for(K);        // elements per workgroup tile
     __shared__ int64_t s_start[kLdsSegs];
     __shared__ uint8_t s_flag[kLdsSegs];
     __shared__ int32_t s_info[2];
@@ -373,22 +381,24 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
         const int64_t w0 = t0 + (int64_t)wave * kWindow;
         if (w0 >= tend) continue;  // wave-uniform
         const int64_t w1 = (w0 + kWindow < tend) ? w0 + kWindow : tend;
-        const int64_t ea = w0 + (int64_t)lane * kQuad;  // first half: ea .. ea+3
-        const int64_t eb = ea + kHalf;                  // second half: eb .. eb+3
+        // This lane's quads: elements e[qd] .. e[qd]+3 of sub-window qd.
+        int64_t e[kQuads];
+#pragma unroll
+        for (int qd = 0; qd < kQuads; ++qd) e[qd] = w0 + (int64_t)qd * kSub + (int64_t)lane * kQuad;
 
-        // Decay flags of this lane's 8 elements: bits 0-3 for ea+q, 4-7 for eb+q.
+        // Decay flags of this lane's elements: bit 4*qd + j for element e[qd] + j.
         uint32_t mask;
         if (uniform >= 0) {
-            mask = uniform ? 0xffu : 0u;
+            mask = uniform ? 0xffffu : 0u;
         } else if (!overflow) {
             while (s_start[wc + 1] <= w0) ++wc;
             if (s_start[wc + 1] >= w1) {
-                mask = s_flag[wc] ? 0xffu : 0u;
+                mask = s_flag[wc] ? 0xffffu : 0u;
             } else {
                 mask = 0;
                 int lc = wc;
-                for (int q = 0; q < 2 * kQuad; ++q) {
-                    const int64_t eq = (q < kQuad ? ea : eb - kQuad) + q;
+                for (int q = 0; q < kQuads * kQuad; ++q) {
+                    const int64_t eq = e[q / kQuad] + (q % kQuad);
                     if (eq >= w1) break;
                     while (s_start[lc + 1] <= eq) ++lc;
                     mask |= (uint32_t)s_flag[lc] << q;
@@ -396,8 +406,8 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
             }
         } else {
             mask = 0;
-            for (int q = 0; q < 2 * kQuad; ++q) {
-                const int64_t eq = (q < kQuad ? ea : eb - kQuad) + q;
+            for (int q = 0; q < kQuads * kQuad; ++q) {
+                const int64_t eq = e[q / kQuad] + (q % kQuad);
                 if (eq >= w1) break;
                 const int32_t s = last_le(a.segs, a.nseg, eq);
                 mask |= (uint32_t)(a.segs[s].wd_on != 0) << q;
@@ -405,105 +415,91 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
         }
 
         if (w0 + kWindow <= a.n) {
-            // Whole window in range: dense vector traffic only.
-            const int64_t qa = ea / kQuad, qb = eb / kQuad;  // quad indices
+            // Whole window in range: dense vector traffic only.  All loads of
+            // every quad are issued before any arithmetic.
             f32x4 *pw = reinterpret_cast<f32x4 *>(a.master);
-            f32x4 wa = load<NT>(pw + qa), wb = load<NT>(pw + qb);
-            f32x4 ma, mb, va, vb;
-            if constexpr (V & kMvBf16) {
-                const u32x2 *pm = reinterpret_cast<const u32x2 *>(a.m);
-                const u32x2 *pv = reinterpret_cast<const u32x2 *>(a.v);
-                ma = bf16x4_to_f32x4(load<NT>(pm + qa));
-                mb = bf16x4_to_f32x4(load<NT>(pm + qb));
-                va = bf16x4_to_f32x4(load<NT>(pv + qa));
-                vb = bf16x4_to_f32x4(load<NT>(pv + qb));
-            } else {
-                const f32x4 *pm = reinterpret_cast<const f32x4 *>(a.m);
-                const f32x4 *pv = reinterpret_cast<const f32x4 *>(a.v);
-                ma = load<NT>(pm + qa);
-                mb = load<NT>(pm + qb);
-                va = load<NT>(pv + qa);
-                vb = load<NT>(pv + qb);
+            f32x4 wv[kQuads], mv[kQuads], vv[kQuads];
+            QuadGrads<K, V, NT> gq[kQuads];
+#pragma unroll
+            for (int qd = 0; qd < kQuads; ++qd) {
+                const int64_t qi = e[qd] / kQuad;
+                wv[qd] = load<NT>(pw + qi);
+                if constexpr (V & kMvBf16) {
+                    mv[qd] = bf16x4_to_f32x4(load<NT>(reinterpret_cast<const u32x2 *>(a.m) + qi));
+                    vv[qd] = bf16x4_to_f32x4(load<NT>(reinterpret_cast<const u32x2 *>(a.v) + qi));
+                } else {
+                    mv[qd] = load<NT>(reinterpret_cast<const f32x4 *>(a.m) + qi);
+                    vv[qd] = load<NT>(reinterpret_cast<const f32x4 *>(a.v) + qi);
+                }
+                gq[qd].load_from(a, qi);
             }
-            QuadGrads<K, V, NT> ga, gb;
-            ga.load_from(a, qa);
-            gb.load_from(a, qb);
-            u32x2 pa, pb;
-            quad_update<K, V, NT>(wa, ma, va, ga, mask & 0xfu, a, pa);
-            quad_update<K, V, NT>(wb, mb, vb, gb, mask >> 4, a, pb);
-            store<NT>(pw + qa, wa);
-            store<NT>(pw + qb, wb);
-            if constexpr (V & kMvBf16) {
-                u32x2 *pm = reinterpret_cast<u32x2 *>(a.m);
-                u32x2 *pv = reinterpret_cast<u32x2 *>(a.v);
-                store<NT>(pm + qa, f32x4_to_bf16x4(ma));
-                store<NT>(pm + qb, f32x4_to_bf16x4(mb));
-                store<NT>(pv + qa, f32x4_to_bf16x4(va));
-                store<NT>(pv + qb, f32x4_to_bf16x4(vb));
-            } else {
-                f32x4 *pm = reinterpret_cast<f32x4 *>(a.m);
-                f32x4 *pv = reinterpret_cast<f32x4 *>(a.v);
-                store<NT>(pm + qa, ma);
-                store<NT>(pm + qb, mb);
-                store<NT>(pv + qa, va);
-                store<NT>(pv + qb, vb);
-            }
-            u32x2 *pp = reinterpret_cast<u32x2 *>(a.param);
-            store<NT>(pp + qa, pa);
-            store<NT>(pp + qb, pb);
-            if constexpr (V & kOutQ8) {
-                const uint32_t ba[4] = {pa[0] << 16, pa[0] & 0xffff0000u, pa[1] << 16,
-                                        pa[1] & 0xffff0000u};
-                const uint32_t bb[4] = {pb[0] << 16, pb[0] & 0xffff0000u, pb[1] << 16,
-                                        pb[1] & 0xffff0000u};
-                const int64_t blk = w0 / kQ8Block;
-                const uint32_t qwa = quantize_block(ba, 0xfu, a, blk, true);
-                const uint32_t qwb = quantize_block(bb, 0xfu, a, blk + 1, true);
-                uint32_t *pq = reinterpret_cast<uint32_t *>(a.q8);
-                store<NT>(pq + qa, qwa);
-                store<NT>(pq + qb, qwb);
+#pragma unroll
+            for (int qd = 0; qd < kQuads; ++qd) {
+                const int64_t qi = e[qd] / kQuad;
+                u32x2 pq;
+                quad_update<K, V, NT>(wv[qd], mv[qd], vv[qd], gq[qd], (mask >> (kQuad * qd)) & 0xfu,
+                                      a, pq);
+                store<NT>(pw + qi, wv[qd]);
+                if constexpr (V & kMvBf16) {
+                    store<NT>(reinterpret_cast<u32x2 *>(a.m) + qi, f32x4_to_bf16x4(mv[qd]));
+                    store<NT>(reinterpret_cast<u32x2 *>(a.v) + qi, f32x4_to_bf16x4(vv[qd]));
+                } else {
+                    store<NT>(reinterpret_cast<f32x4 *>(a.m) + qi, mv[qd]);
+                    store<NT>(reinterpret_cast<f32x4 *>(a.v) + qi, vv[qd]);
+                }
+                store<NT>(reinterpret_cast<u32x2 *>(a.param) + qi, pq);
+                if constexpr (V & kOutQ8) {
+                    const uint32_t bits[4] = {pq[0] << 16, pq[0] & 0xffff0000u, pq[1] << 16,
+                                              pq[1] & 0xffff0000u};
+                    const int64_t blk = (w0 + (int64_t)qd * kSub) / kQ8Block;
+                    const uint32_t word = quantize_block(bits, 0xfu, a, blk, true);
+                    store<NT>(reinterpret_cast<uint32_t *>(a.q8) + qi, word);
+                }
             }
         } else {
             // The shard's last, partial window: element by element (the whole
             // wavefront stays here together, for the block maxima).
-            uint32_t pbits[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            uint32_t pbits[kQuads * kQuad];
             uint32_t valid = 0;
-            for (int q = 0; q < 2 * kQuad; ++q) {
-                const int64_t i = (q < kQuad ? ea : eb - kQuad) + q;
+            for (int q = 0; q < kQuads * kQuad; ++q) {
+                pbits[q] = 0;
+                const int64_t i = e[q / kQuad] + (q % kQuad);
                 if (i >= a.n) continue;
                 valid |= 1u << q;
                 const float g = scalar_grad<K, V>(a, i);
-                float wv = a.master[i], mv, vv;
+                float wv = a.master[i], mvv, vvv;
                 if constexpr (V & kMvBf16) {
-                    mv = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(a.m)[i] << 16);
-                    vv = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(a.v)[i] << 16);
+                    mvv = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(a.m)[i] << 16);
+                    vvv = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(a.v)[i] << 16);
                 } else {
-                    mv = reinterpret_cast<const float *>(a.m)[i];
-                    vv = reinterpret_cast<const float *>(a.v)[i];
+                    mvv = reinterpret_cast<const float *>(a.m)[i];
+                    vvv = reinterpret_cast<const float *>(a.v)[i];
                 }
-                adamw(wv, mv, vv, g, (mask >> q) & 1u, a);
+                adamw(wv, mvv, vvv, g, (mask >> q) & 1u, a);
                 a.master[i] = wv;
                 if constexpr (V & kMvBf16) {
-                    reinterpret_cast<uint16_t *>(a.m)[i] = (uint16_t)to_bf16(mv);
-                    reinterpret_cast<uint16_t *>(a.v)[i] = (uint16_t)to_bf16(vv);
+                    reinterpret_cast<uint16_t *>(a.m)[i] = (uint16_t)to_bf16(mvv);
+                    reinterpret_cast<uint16_t *>(a.v)[i] = (uint16_t)to_bf16(vvv);
                 } else {
-                    reinterpret_cast<float *>(a.m)[i] = mv;
-                    reinterpret_cast<float *>(a.v)[i] = vv;
+                    reinterpret_cast<float *>(a.m)[i] = mvv;
+                    reinterpret_cast<float *>(a.v)[i] = vvv;
                 }
                 const uint32_t pbf = to_bf16(wv);
                 a.param[i] = (uint16_t)pbf;
                 pbits[q] = pbf << 16;
             }
             if constexpr (V & kOutQ8) {
-                const int64_t blk = w0 / kQ8Block;
-                const uint32_t qwa = quantize_block(pbits, valid & 0xfu, a, blk, w0 < a.n);
-                const uint32_t qwb = quantize_block(pbits + 4, valid >> 4, a, blk + 1,
-                                                    w0 + kHalf < a.n);
-                for (int q = 0; q < 2 * kQuad; ++q) {
-                    if (!((valid >> q) & 1u)) continue;
-                    const int64_t i = (q < kQuad ? ea : eb - kQuad) + q;
-                    const uint32_t word = q < kQuad ? qwa : qwb;
-                    a.q8[i] = (int8_t)(uint8_t)(word >> (8 * (q % kQuad)));
+#pragma unroll
+                for (int qd = 0; qd < kQuads; ++qd) {
+                    const int64_t sub0 = w0 + (int64_t)qd * kSub;
+                    const uint32_t word = quantize_block(pbits + kQuad * qd,
+                                                         (valid >> (kQuad * qd)) & 0xfu, a,
+                                                         sub0 / kQ8Block, sub0 < a.n);
+                    for (int j = 0; j < kQuad; ++j) {
+                        const int q = kQuad * qd + j;
+                        if ((valid >> q) & 1u)
+                            a.q8[e[qd] + j] = (int8_t)(uint8_t)(word >> (8 * j));
+                    }
                 }
             }
         }
@@ -711,7 +707,7 @@ int validate_and_launch(const Request &r) {
     a.gscale = hp->grad_scale;
 
     if (chunk_tiles == 0) chunk_tiles = pick_chunk_tiles(n, g_dev[dev].cus);
-    int64_t chunk = (int64_t)chunk_tiles * kTile;
+    int64_t chunk = (int64_t)chunk_tiles * tile_for(r.k);
     int64_t blocks = (n + chunk - 1) / chunk;
     while (blocks > 0x7fffffffLL) {  // keep the grid inside the 32-bit limit
         chunk *= 2;

@@ -202,10 +202,13 @@ def test_segment_overflow_and_restaging(gpu):
             segs.append((a, bool(rng.random() < 0.5)))  # duplicate start
         a += int(rng.integers(1, 4))
     segs += [(n, True), (n + 10, False)]
-    for chunk_tiles in (1, 4, 12):
-        got, ref = _run_both(gpu, n, 2, segs, range(1, 3), seed=9,
-                             cfg=dict(chunk_tiles=chunk_tiles))
-        H.assert_parity(got, ref, "chunk_tiles=%d" % chunk_tiles)
+    # k = 2 (1024-element tiles) and k = 4 (4096-element tiles: a tile holds
+    # more entries than the LDS slice, so the per-element global lookup runs)
+    for k in (2, 4):
+        for chunk_tiles in (1, 4, 12):
+            got, ref = _run_both(gpu, n, k, segs, range(1, 3), seed=9,
+                                 cfg=dict(chunk_tiles=chunk_tiles))
+            H.assert_parity(got, ref, "k=%d chunk_tiles=%d" % (k, chunk_tiles))
 
 
 def test_launch_geometry_is_bitwise_invariant(gpu):
