@@ -18,14 +18,13 @@
 //     accesses, and every byte is read once and written once;
 //   * a workgroup owns a contiguous chunk of tiles (one tile by default: the
 //     resident workgroups then sweep memory as one compact front);
-//   * the segment holding the chunk's first element is found by one
-//     wavefront with a 64-way search of the device table (two dependent
-//     loads for up to 4096 entries); a chunk that lies inside one segment
-//     takes a workgroup-uniform decay flag, otherwise the slice of the table
-//     it touches is staged in LDS (restaged if it exceeds kLdsSegs entries);
-//   * segment boundaries inside a staged chunk are resolved per wavefront: a
-//     window inside one segment takes a wave-uniform flag; only windows that
-//     contain a boundary resolve flags per lane;
+//   * every wavefront resolves the weight-decay flags of its own window, with
+//     no workgroup barrier and after issuing its loads (so the lookup
+//     overlaps them): a 64-way search of the device table finds the entry
+//     covering the window (two dependent loads for up to 4096 entries); a
+//     window inside one segment takes that segment's flag, a window with
+//     segment boundaries stages the 64 entries around it in the wave's LDS
+//     slot and each lane walks them for its own elements;
 //   * 64-bit element indices throughout (shards exceed 2^31 elements).
 //
 // Numerics follow the header: binary32, no contraction, correctly rounded
@@ -53,11 +52,9 @@ constexpr int kSub = kWave * kQuad;           // 256: one dense instruction per 
 // in flight and four quads per lane streamed best.
 constexpr int quads_for(int k) { return k <= 2 ? 1 : 4; }
 constexpr int tile_for(int k) { return (kThreads / kWave) * quads_for(k) * kSub; }
-constexpr int kLdsSegs = 1024;                // staged segment entries
 constexpr int kMaxChunkTiles = 4096;
 constexpr int64_t kNoStart = INT64_MAX;       // sentinel past the table end
 
-static_assert(kLdsSegs % kThreads == 0, "staging rounds must be whole");
 static_assert(tile_for(1) == 1024 && tile_for(8) == 4096, "tile sizes");
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -129,63 +126,83 @@ __device__ int32_t last_le(const zs_segment *segs, int32_t nseg, int64_t e) {
     return lo;
 }
 
-// The same search done by a whole wavefront, 64 probes per round: each round
-// narrows [lo, hi) to one of 64 sub-ranges, so a table of up to 4096
-// entries takes two dependent loads.  All 64 lanes must be active; every
-// lane returns the same index.  Reads stay in [0, nseg).
-__device__ int32_t wave_last_le(const zs_segment *segs, int32_t nseg, int64_t e) {
+// Per-wavefront LDS slot: the 64 table entries around a window that holds
+// segment boundaries.
+struct WaveSlot {
+    int64_t start[kWave];
+    uint8_t flag[kWave];
+};
+
+// Decay flags of this lane's elements in the window [w0, w1) (w0 < w1, both
+// wave-uniform): bit q belongs to element q of the lane, whose index is
+// elem(q), increasing in q; elements at or past w1 get no bit.  Done by the
+// wavefront alone, with no workgroup barrier.  A 64-way search finds the
+// entry covering w0: each round probes 64 entries at once and narrows the
+// range 64-fold, and the last round loads 64 consecutive entries (two
+// dependent loads in all for tables of up to 4096 entries).  A window inside
+// one segment takes that segment's flag; a window that holds boundaries stages
+// the 64 loaded entries in the wave's LDS slot and every lane walks them for
+// its own elements; a window with more boundaries than the slot holds looks
+// each element up in the table.  All 64 lanes must call this; every read
+// stays inside segs[0 .. nseg-1] and the slot, sorted table or not.
+template <typename ElemFn>
+__device__ uint32_t window_mask(const StepArgs &a, int64_t w0, int64_t w1, int nelem,
+                                ElemFn elem, WaveSlot &slot) {
     const int lane = (int)(threadIdx.x % kWave);
-    int32_t lo = 0, hi = nseg;  // answer in [lo, hi)
-    while (hi - lo > 1) {
+    int32_t lo = 0, hi = a.nseg;  // the entry covering w0 lies in [lo, hi)
+    while (hi - lo > kWave) {
         const int32_t step = (hi - lo + kWave - 1) / kWave;
         const int64_t idx = (int64_t)lo + (int64_t)lane * step;
-        const bool le = idx < hi && segs[idx].start <= e;
-        const uint64_t mask = __ballot(le);
-        const int top = mask ? 63 - __clzll(mask) : 0;
+        const bool le = idx < hi && a.segs[idx].start <= w0;
+        const uint64_t b = __ballot(le);
+        const int top = b ? 63 - __clzll(b) : 0;
         lo = lo + top * step;
         hi = (lo + step < hi) ? lo + step : hi;
     }
-    return lo;
-}
+    const int64_t idx = (int64_t)lo + lane;
+    int64_t st = kNoStart;
+    uint32_t fl = 0;
+    if (idx < a.nseg) {
+        st = a.segs[idx].start;
+        fl = a.segs[idx].wd_on != 0;
+    }
+    const uint64_t b = __ballot(st <= w0);
+    const int cov = b ? 63 - __clzll(b) : 0;  // lane holding the covering entry
+    const uint32_t cov_flag = (uint32_t)__shfl((int)fl, cov, kWave);
+    int64_t next;
+    if (cov < kWave - 1) {
+        next = __shfl(st, cov + 1, kWave);
+    } else {
+        next = lo + kWave < a.nseg ? a.segs[lo + kWave].start : kNoStart;
+    }
+    const uint32_t all = (nelem >= 32) ? 0xffffffffu : ((1u << nelem) - 1u);
+    if (next >= w1) return cov_flag ? all : 0u;
 
-// Locate the segment of element `from` and either report that [from, until)
-// lies inside it (returns until, *uniform = its decay flag) or stage the
-// table entries from it onward into LDS, in rounds of kThreads, stopping
-// after the round that reaches an entry whose start is >= until; entries
-// past the table end read as kNoStart (*uniform = -1 then).  In the staged
-// case every element e with from <= e < result resolves inside the slice.
-// Block-uniform: all threads must call it.
-__device__ int64_t locate_segments(const StepArgs &a, int64_t from, int64_t until,
-                                   int64_t *s_start, uint8_t *s_flag, int32_t *s_info,
-                                   int *uniform) {
-    if (threadIdx.x < kWave) {
-        const int32_t s = wave_last_le(a.segs, a.nseg, from);
-        if (threadIdx.x == 0) {
-            const int64_t next = s + 1 < a.nseg ? a.segs[s + 1].start : kNoStart;
-            s_info[0] = s;
-            s_info[1] = next >= until ? (a.segs[s].wd_on != 0) : -1;
+    uint32_t mask = 0;
+    if (__shfl(st, kWave - 1, kWave) >= w1) {
+        // every entry the window needs is among the 64 loaded ones
+        slot.start[lane] = st;
+        slot.flag[lane] = (uint8_t)fl;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        int c = cov;
+        for (int q = 0; q < nelem; ++q) {
+            const int64_t eq = elem(q);
+            if (eq >= w1) break;
+            while (c + 1 < kWave && slot.start[c + 1] <= eq) ++c;
+            mask |= (uint32_t)slot.flag[c] << q;
+        }
+        __builtin_amdgcn_wave_barrier();
+    } else {
+        for (int q = 0; q < nelem; ++q) {
+            const int64_t eq = elem(q);
+            if (eq >= w1) break;
+            const int32_t s = last_le(a.segs, a.nseg, eq);
+            mask |= (uint32_t)(a.segs[s].wd_on != 0) << q;
         }
     }
-    __syncthreads();
-    const int64_t base = s_info[0];
-    *uniform = s_info[1];
-    if (*uniform >= 0) return until;
-    int staged = 0;
-    for (int r = 0; r < kLdsSegs; r += kThreads) {
-        const int j = r + (int)threadIdx.x;
-        const int64_t idx = base + j;
-        int64_t st = kNoStart;
-        uint8_t fl = 0;
-        if (idx < a.nseg) {
-            st = a.segs[idx].start;
-            fl = a.segs[idx].wd_on != 0;
-        }
-        s_start[j] = st;
-        s_flag[j] = fl;
-        staged = r + kThreads;
-        if (__syncthreads_or(st >= until)) break;
-    }
-    return s_start[staged - 1];
+    return mask;
 }
 
 // Variants of the step, chosen at compile time (bit mask):
@@ -354,69 +371,28 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
     constexpr int kQuads = quads_for(K);      // sub-windows per wave per tile
     constexpr int kWindow = kQuads * kSub;    // elements per wave per tile
     constexpr int kTile = tile_for(K);        // elements per workgroup tile
-    __shared__ int64_t s_start[kLdsSegs];
-    __shared__ uint8_t s_flag[kLdsSegs];
-    __shared__ int32_t s_info[2];
+    __shared__ WaveSlot s_slot[kThreads / kWave];
 
     const int tid = (int)threadIdx.x;
     const int lane = tid % kWave;
     const int wave = tid / kWave;
     const int64_t c0 = (int64_t)blockIdx.x * a.chunk;
-    if (c0 >= a.n) return;  // block-uniform
     const int64_t c1 = (c0 + a.chunk < a.n) ? c0 + a.chunk : a.n;
 
-    int uniform;  // decay flag of the whole located range, or -1 when staged
-    int64_t lim = locate_segments(a, c0, c1, s_start, s_flag, s_info, &uniform);
-    int wc = 0;   // this wave's cursor into the staged slice
-
+    // Every wavefront works on its own windows; there is no workgroup barrier.
     for (int64_t t0 = c0; t0 < c1; t0 += kTile) {
-        const int64_t tend = (t0 + kTile < c1) ? t0 + kTile : c1;
-        bool overflow = false;
-        if (tend > lim) {  // block-uniform: the located range ends inside this tile
-            __syncthreads();
-            lim = locate_segments(a, t0, c1, s_start, s_flag, s_info, &uniform);
-            wc = 0;
-            overflow = tend > lim;
-        }
         const int64_t w0 = t0 + (int64_t)wave * kWindow;
-        if (w0 >= tend) continue;  // wave-uniform
-        const int64_t w1 = (w0 + kWindow < tend) ? w0 + kWindow : tend;
+        if (w0 >= c1) continue;  // wave-uniform
+        const int64_t w1 = (w0 + kWindow < c1) ? w0 + kWindow : c1;
         // This lane's quads: elements e[qd] .. e[qd]+3 of sub-window qd.
         int64_t e[kQuads];
 #pragma unroll
         for (int qd = 0; qd < kQuads; ++qd) e[qd] = w0 + (int64_t)qd * kSub + (int64_t)lane * kQuad;
-
-        // Decay flags of this lane's elements: bit 4*qd + j for element e[qd] + j.
-        uint32_t mask;
-        if (uniform >= 0) {
-            mask = uniform ? 0xffffu : 0u;
-        } else if (!overflow) {
-            while (s_start[wc + 1] <= w0) ++wc;
-            if (s_start[wc + 1] >= w1) {
-                mask = s_flag[wc] ? 0xffffu : 0u;
-            } else {
-                mask = 0;
-                int lc = wc;
-                for (int q = 0; q < kQuads * kQuad; ++q) {
-                    const int64_t eq = e[q / kQuad] + (q % kQuad);
-                    if (eq >= w1) break;
-                    while (s_start[lc + 1] <= eq) ++lc;
-                    mask |= (uint32_t)s_flag[lc] << q;
-                }
-            }
-        } else {
-            mask = 0;
-            for (int q = 0; q < kQuads * kQuad; ++q) {
-                const int64_t eq = e[q / kQuad] + (q % kQuad);
-                if (eq >= w1) break;
-                const int32_t s = last_le(a.segs, a.nseg, eq);
-                mask |= (uint32_t)(a.segs[s].wd_on != 0) << q;
-            }
-        }
+        auto elem = [&](int q) { return e[q / kQuad] + (q % kQuad); };
 
         if (w0 + kWindow <= a.n) {
-            // Whole window in range: dense vector traffic only.  All loads of
-            // every quad are issued before any arithmetic.
+            // Whole window in range: dense vector traffic only.  The loads are
+            // issued first, so the segment search below overlaps them.
             f32x4 *pw = reinterpret_cast<f32x4 *>(a.master);
             f32x4 wv[kQuads], mv[kQuads], vv[kQuads];
             QuadGrads<K, V, NT> gq[kQuads];
@@ -433,6 +409,8 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
                 }
                 gq[qd].load_from(a, qi);
             }
+            // Decay flags: bit 4*qd + j for element e[qd] + j.
+            const uint32_t mask = window_mask(a, w0, w1, kQuads * kQuad, elem, s_slot[wave]);
 #pragma unroll
             for (int qd = 0; qd < kQuads; ++qd) {
                 const int64_t qi = e[qd] / kQuad;
@@ -458,7 +436,8 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
             }
         } else {
             // The shard's last, partial window: element by element (the whole
-            // wavefront stays here together, for the block maxima).
+            // wavefront stays here together, for the search and block maxima).
+            const uint32_t mask = window_mask(a, w0, w1, kQuads * kQuad, elem, s_slot[wave]);
             uint32_t pbits[kQuads * kQuad];
             uint32_t valid = 0;
             for (int q = 0; q < kQuads * kQuad; ++q) {
