@@ -22,6 +22,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -61,7 +62,8 @@ def measured_traffic(config: str, launch_key: str):
 def cpu_baseline(w, seconds: float, variant: str, bytes_per_elem: float):
     """Time the CPU oracle (single thread, as it stands) on a bounded window
     of the same workload: the first min(n, 2^24) elements of the shard, with
-    the arithmetic of the entry point being measured."""
+    the arithmetic of the entry point being measured.  The "threaded" entry
+    times the same oracle over T contiguous ranges of that window."""
     import numpy as np
 
     import oracle
@@ -82,6 +84,7 @@ def cpu_baseline(w, seconds: float, variant: str, bytes_per_elem: float):
     steps = 0
     elapsed = 0.0
     t = w.t0
+    warm = True  # one untimed step first: the first touch of the fresh arrays
     while elapsed < seconds or steps == 0:
         t0 = time.perf_counter()
         if variant == "q8grad":
@@ -92,21 +95,77 @@ def cpu_baseline(w, seconds: float, variant: str, bytes_per_elem: float):
             rc = oracle.shard_step(master, m, v, p, grads, segs, hp, t)
             if variant == "q8ag":
                 oracle.q8_blocks(p, 256)
-        elapsed += time.perf_counter() - t0
         assert rc == 0
-        steps += 1
         t += 1
+        if warm:
+            warm = False
+            continue
+        elapsed += time.perf_counter() - t0
+        steps += 1
+    threaded = _threaded_oracle(master, m, v, p, grads if variant != "q8grad" else None,
+                                segs, hp, t, variant, bytes_per_elem,
+                                qgrads if variant == "q8grad" else None,
+                                qscales if variant == "q8grad" else None)
     return {
         "value": round(n * steps * bytes_per_elem / elapsed / 1e9, 4),
         "unit": "GB/s",
         "params_per_s": round(n * steps / elapsed, 1),
         "cores": 1,
+        "threaded": threaded,
         "kind": "oracle",
         "sample": "first %d elements of the %s shard (k=%d, %d segments in the window), "
-                  "%d oracle steps (%s arithmetic), single-threaded C, %.1f s" % (
+                  "%d timed oracle steps after one untimed (%s arithmetic), single-threaded C, %.1f s" % (
                       n, w.name.split(":")[0].split(" (")[0], w.k, len(segs), steps, variant,
                       elapsed),
     }
+
+
+def _threaded_oracle(master, m, v, p, grads, segs, hp, t, variant, bytes_per_elem,
+                     qgrads=None, qscales=None, seconds=3.0):
+    """The same oracle driven from T threads over T contiguous ranges of the
+    window (the step is elementwise, so the split does not change a bit);
+    T = the CPUs this process may use, at most 16."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    import synth
+
+    n = master.shape[0]
+    threads = max(1, min(len(os.sched_getaffinity(0)), 16))
+    # ranges on 256-element boundaries so that q8 blocks never straddle two threads
+    per = -(-n // threads)
+    per = -(-per // 256) * 256
+    ranges = [(a, min(a + per, n)) for a in range(0, n, per)]
+    tabs = [synth.clip_segments(segs, a, b) for a, b in ranges]
+
+    def one(i, step):
+        a, b = ranges[i]
+        if variant == "q8grad":
+            return oracle.shard_step_q8grad(master[a:b], m[a:b], v[a:b], p[a:b],
+                                            [q[a:b] for q in qgrads],
+                                            [s[a // 256:-(-b // 256)] for s in qscales],
+                                            tabs[i], hp, step)
+        if variant == "bf16mv":
+            return oracle.shard_step_bf16mv(master[a:b], m[a:b], v[a:b], p[a:b],
+                                            [g[a:b] for g in grads], tabs[i], hp, step)
+        rc = oracle.shard_step(master[a:b], m[a:b], v[a:b], p[a:b], [g[a:b] for g in grads],
+                               tabs[i], hp, step)
+        if variant == "q8ag":
+            oracle.q8_blocks(p[a:b], 256)
+        return rc
+
+    steps, elapsed = 0, 0.0
+    with ThreadPoolExecutor(len(ranges)) as ex:
+        while elapsed < seconds or steps == 0:
+            t0 = time.perf_counter()
+            assert all(rc == 0 for rc in ex.map(one, range(len(ranges)),
+                                                [t] * len(ranges)))
+            elapsed += time.perf_counter() - t0
+            steps += 1
+            t += 1
+    return {"value": round(n * steps * bytes_per_elem / elapsed / 1e9, 4),
+            "params_per_s": round(n * steps / elapsed, 1), "cores": len(ranges),
+            "steps": steps}
 
 
 def copy_ceiling(torch, nbytes: int):
@@ -412,6 +471,8 @@ def main():
             "kernel": "shard_step_kernel<K=%d,%s>" % (k, var),
             "avg_launch_ms": round(avg_ms, 4),
         },
+        "kernel_ms": {"median": round(statistics.median(kernel_ms), 4),
+                      "min": round(min(kernel_ms), 4), "max": round(max(kernel_ms), 4)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
