@@ -31,7 +31,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
-KERNEL_SRC = os.path.join(ROOT, "sharded_mixed_precision_shard_amd", "csrc", "zs_step.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "sharded_mixed_precision_shard_amd", "csrc", f)
+               for f in ("zs_kernels.hip", "zs_kernels.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -40,8 +41,13 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] over the kernel sources (device code and the argument
+    block it reads), in a fixed order; host-side changes leave it alone."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(config: str, launch_key: str):
@@ -302,10 +308,15 @@ def main():
                     help="CPU oracle time budget for the cpu_baseline leg (0 = skip)")
     ap.add_argument("--chunk-tiles", type=int, default=0, help="launch geometry override")
     ap.add_argument("--nontemporal", type=int, default=0, help="0 default, 1 on, 2 off")
+    ap.add_argument("--groups-per-cu", type=int, default=0,
+                    help="cap on resident workgroups per compute unit (0 = default)")
     ap.add_argument("--copy-gb", type=float, default=8.0,
                     help="size of the in-run copy-ceiling measurement (0 = skip)")
     args = ap.parse_args()
 
+    if args.variant != "base" and (args.chunk_tiles or args.nontemporal or args.groups_per_cu):
+        ap.error("--chunk-tiles, --nontemporal and --groups-per-cu apply to the base entry "
+                 "point (zs_shard_step_cfg) only")
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one rank's shard step on ONE GPU; the shard step has no "
@@ -375,9 +386,10 @@ def main():
                                     stream)
         elif var == "bf16mv":
             zs.zs_shard_step_bf16mv(master, m, v, param, grads, k, n, st, hp, t, stream)
-        elif args.chunk_tiles or args.nontemporal:
+        elif args.chunk_tiles or args.nontemporal or args.groups_per_cu:
             zs.zs_shard_step_cfg(master, m, v, param, grads, k, n, st, hp, t, stream,
-                                 chunk_tiles=args.chunk_tiles, nontemporal=args.nontemporal)
+                                 chunk_tiles=args.chunk_tiles, nontemporal=args.nontemporal,
+                                 groups_per_cu=args.groups_per_cu)
         else:
             zs.zs_shard_step(master, m, v, param, grads, k, n, st, hp, t, stream)
 
@@ -420,6 +432,8 @@ def main():
     value = bytes_per_step * args.steps / elapsed / 1e9
     achieved = bytes_per_step / (avg_ms * 1e-3) / 1e9
     launch_key = "chunk_tiles=%d,nontemporal=%d" % (args.chunk_tiles, args.nontemporal)
+    if args.groups_per_cu:
+        launch_key += ",groups_per_cu=%d" % args.groups_per_cu
     traffic_key = args.config if var == "base" else "%s/%s" % (args.config, var)
     traffic = measured_traffic(traffic_key, launch_key)
 

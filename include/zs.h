@@ -49,6 +49,7 @@ extern "C" {
 #define ZS_MAX_K 16           /* most gradient partials one call sums */
 #define ZS_MAX_SEGMENTS 65536 /* most entries in one segment table */
 #define ZS_Q8_BLOCK 256       /* elements per int8 quantization block */
+#define ZS_MAX_GROUPS_PER_CU 32 /* largest zs_launch_cfg.groups_per_cu */
 
 typedef enum {
     ZS_OK = 0,
@@ -95,7 +96,15 @@ typedef struct {
                              when k <= 2 and 4096 elements when k >= 3 */
     int32_t nontemporal;  /* 0 = default (streaming), 1 = streaming (non-temporal)
                              loads/stores, 2 = ordinary cached loads/stores */
-    int32_t reserved[2];
+    int32_t groups_per_cu; /* 0 = as many resident workgroups per compute unit as
+                              fit (default); 1..ZS_MAX_GROUPS_PER_CU caps them by
+                              reserving that share of the unit's LDS per workgroup.
+                              Fewer requests in flight can relieve DRAM congestion
+                              on some physical placements of the arrays; a cap at
+                              or above the kernel's own occupancy has no effect.  A
+                              cap whose LDS share exceeds the per-workgroup limit
+                              returns ZS_ERR_INVALID_ARGUMENT. */
+    int32_t reserved;
 } zs_launch_cfg;
 
 /* Prepare the library for one device: records its compute-unit count and

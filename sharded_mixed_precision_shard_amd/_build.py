@@ -1,4 +1,5 @@
-"""Build the gfx950 shared library ``libzs.so`` from ``csrc/zs_step.hip``.
+"""Build the gfx950 shared library ``libzs.so`` from ``csrc/zs_kernels.hip``
+(the kernels) and ``csrc/zs_api.hip`` (the C ABI), and ``libzs_host.so``.
 
 hipcc cross-compiles for gfx950 without a GPU, so this runs anywhere the
 ROCm toolchain is installed.  The library is built in-tree, next to this file.
@@ -12,7 +13,11 @@ import subprocess
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 REPO_DIR = os.path.dirname(PKG_DIR)
 INCLUDE_DIR = os.path.join(REPO_DIR, "include")
-SRC = os.path.join(PKG_DIR, "csrc", "zs_step.hip")
+SRCS = [os.path.join(PKG_DIR, "csrc", "zs_kernels.hip"),
+        os.path.join(PKG_DIR, "csrc", "zs_api.hip")]
+# The sources the kernels are compiled from (their hash keys measured traffic).
+KERNEL_SRCS = [os.path.join(PKG_DIR, "csrc", "zs_kernels.hip"),
+               os.path.join(PKG_DIR, "csrc", "zs_kernels.h")]
 LIB = os.path.join(PKG_DIR, "libzs.so")
 HOST_SRC = os.path.join(PKG_DIR, "csrc", "zs_host.cpp")
 HOST_LIB = os.path.join(PKG_DIR, "libzs_host.so")
@@ -62,7 +67,7 @@ def build(verbose: bool = False) -> str:
     """Compile libzs.so and libzs_host.so (always recompiles).  Returns the
     device library path."""
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE_DIR, "-o", tmp, SRC]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE_DIR, "-o", tmp, *SRCS]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

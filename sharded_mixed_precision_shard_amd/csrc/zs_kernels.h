@@ -1,0 +1,70 @@
+// zs_kernels.h -- what the C ABI layer (zs_api.hip) and the kernels
+// (zs_kernels.hip) share: the launch geometry, the kernel argument block, the
+// variant bits and the kernel table.  Private to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "zs.h"
+
+namespace zs_detail {
+
+constexpr int kThreads = 256;                 // 4 wavefronts of 64 lanes
+constexpr int kWave = 64;
+constexpr int kQuad = 4;                      // contiguous elements per lane per sub-window
+constexpr int kSub = kWave * kQuad;           // 256: one dense instruction per array per wave
+
+// Sub-windows (quads per lane) a wave handles per tile.  Measured on MI355X:
+// with one or two partials the fewest bytes in flight per wave streamed best
+// (one quad); with three or more partials each lane already has many loads
+// in flight and four quads per lane streamed best.
+constexpr int quads_for(int k) { return k <= 2 ? 1 : 4; }
+constexpr int tile_for(int k) { return (kThreads / kWave) * quads_for(k) * kSub; }
+
+static_assert(tile_for(1) == 1024 && tile_for(8) == 4096, "tile sizes");
+
+struct StepArgs {
+    float *master;
+    void *m;         // fp32 [n], or bf16 [n] in the bf16-moment variant
+    void *v;
+    uint16_t *param;
+    int8_t *q8;      // quantized parameter copy (variant with an int8 payload)
+    float *q8_scale;
+    const uint16_t *grads[ZS_MAX_K];   // bf16 partials
+    const int8_t *qgrads[ZS_MAX_K];    // int8 partials (block-quantized variant)
+    const float *qscales[ZS_MAX_K];
+    const zs_segment *segs;
+    int64_t n;
+    int64_t chunk;  // elements per workgroup, a multiple of tile_for(k)
+    int32_t nseg;
+    float lr, b1, b2, c1, c2, bc1, bc2, eps, df, gscale;
+};
+
+// Variants of the step, chosen at compile time (bit mask):
+//   kOutQ8  - also write the block-quantized int8 copy of the new parameters
+//             with one fp32 scale per kQ8Block elements (the payload of a
+//             quantized all-gather);
+//   kGradQ8 - the k partials arrive as int8 with one fp32 scale per
+//             kQ8Block elements each (a block-quantized reduce-scatter) and
+//             are dequantized inside the reduce;
+//   kMvBf16 - the moments m and v are stored as bf16 (12 bytes per parameter
+//             of optimizer state plus weight instead of 16).
+constexpr int kOutQ8 = 1;
+constexpr int kGradQ8 = 2;
+constexpr int kMvBf16 = 4;
+constexpr int kQ8Block = ZS_Q8_BLOCK;
+static_assert(kQ8Block == kSub, "a quantization block is one sub-window of a wave");
+
+// LDS each workgroup of every kernel declares: one boundary slot per
+// wavefront, 64 eight-byte segment starts and 64 one-byte flags.
+constexpr int64_t kStaticLds = (int64_t)(8 + 1) * kWave * (kThreads / kWave);
+
+typedef void (*kernel_fn)(const StepArgs);
+
+// The kernel for k partials, a variant (0 or one of the bits above) and
+// streaming (nt = 1) or cached (nt = 0) access; nullptr if there is none.
+kernel_fn pick_kernel(int k, int variant, int nt);
+
+}  // namespace zs_detail

@@ -1,5 +1,5 @@
-// zs_step.hip -- fused reduce + AdamW + bf16-cast shard step for gfx950,
-// and the C ABI declared in include/zs.h.
+// zs_kernels.hip -- fused reduce + AdamW + bf16-cast shard step kernels for
+// gfx950 (the C ABI that launches them is in zs_api.hip).
 //
 // One rank's share of the ZeRO-1 optimizer step ("Chapter 9: Distributed
 // Training and Data Parallelism", section 9.4.2; "Lecture 7: Parallelism I",
@@ -31,51 +31,15 @@
 // divide and square root, denormals kept, bf16 round-to-nearest-even with
 // NaN -> 0x7FC0.
 
-#include <hip/hip_runtime.h>
+#include "zs_kernels.h"
 
-#include <cmath>
-#include <cstdint>
-#include <cstring>
-
-#include "zs.h"
-
+namespace zs_detail {
 namespace {
 
-constexpr int kThreads = 256;                 // 4 wavefronts of 64 lanes
-constexpr int kWave = 64;
-constexpr int kQuad = 4;                      // contiguous elements per lane per sub-window
-constexpr int kSub = kWave * kQuad;           // 256: one dense instruction per array per wave
-
-// Sub-windows (quads per lane) a wave handles per tile.  Measured on MI355X:
-// with one or two partials the fewest bytes in flight per wave streamed best
-// (one quad); with three or more partials each lane already has many loads
-// in flight and four quads per lane streamed best.
-constexpr int quads_for(int k) { return k <= 2 ? 1 : 4; }
-constexpr int tile_for(int k) { return (kThreads / kWave) * quads_for(k) * kSub; }
-constexpr int kMaxChunkTiles = 4096;
 constexpr int64_t kNoStart = INT64_MAX;       // sentinel past the table end
-
-static_assert(tile_for(1) == 1024 && tile_for(8) == 4096, "tile sizes");
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-struct StepArgs {
-    float *master;
-    void *m;         // fp32 [n], or bf16 [n] in the bf16-moment variant
-    void *v;
-    uint16_t *param;
-    int8_t *q8;      // quantized parameter copy (variant with an int8 payload)
-    float *q8_scale;
-    const uint16_t *grads[ZS_MAX_K];   // bf16 partials
-    const int8_t *qgrads[ZS_MAX_K];    // int8 partials (block-quantized variant)
-    const float *qscales[ZS_MAX_K];
-    const zs_segment *segs;
-    int64_t n;
-    int64_t chunk;  // elements per workgroup, a multiple of kTile
-    int32_t nseg;
-    float lr, b1, b2, c1, c2, bc1, bc2, eps, df, gscale;
-};
 
 template <int NT, typename T>
 __device__ __forceinline__ T load(const T *p) {
@@ -204,21 +168,6 @@ __device__ uint32_t window_mask(const StepArgs &a, int64_t w0, int64_t w1, int n
     }
     return mask;
 }
-
-// Variants of the step, chosen at compile time (bit mask):
-//   kOutQ8  - also write the block-quantized int8 copy of the new parameters
-//             with one fp32 scale per kQ8Block elements (the payload of a
-//             quantized all-gather);
-//   kGradQ8 - the k partials arrive as int8 with one fp32 scale per
-//             kQ8Block elements each (a block-quantized reduce-scatter) and
-//             are dequantized inside the reduce;
-//   kMvBf16 - the moments m and v are stored as bf16 (12 bytes per parameter
-//             of optimizer state plus weight instead of 16).
-constexpr int kOutQ8 = 1;
-constexpr int kGradQ8 = 2;
-constexpr int kMvBf16 = 4;
-constexpr int kQ8Block = ZS_Q8_BLOCK;
-static_assert(kQ8Block == kSub, "a quantization block is one sub-window of a wave");
 
 __device__ __forceinline__ f32x4 bf16x4_to_f32x4(u32x2 d) {
     f32x4 r;
@@ -485,7 +434,9 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
     }
 }
 
-typedef void (*kernel_fn)(const StepArgs);
+static_assert(sizeof(WaveSlot) * (kThreads / kWave) == kStaticLds, "LDS per workgroup");
+
+}  // namespace
 
 template <int K>
 kernel_fn pick_variant(int variant, int nt) {
@@ -520,303 +471,4 @@ kernel_fn pick_kernel(int k, int variant, int nt) {
     }
 }
 
-// ---------------------------------------------------------------- host side
-
-constexpr int kMaxDevices = 64;
-
-struct DeviceInfo {
-    int ready;
-    int cus;
-};
-
-DeviceInfo g_dev[kMaxDevices];
-int g_initialized = 0;
-thread_local int t_last_hip_error = 0;
-
-int device_error(hipError_t e) {
-    t_last_hip_error = (int)e;
-    return ZS_ERR_DEVICE;
-}
-
-bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
-    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
-    const uintptr_t a1 = a0 + (uintptr_t)abytes, b1 = b0 + (uintptr_t)bbytes;
-    return a0 < b1 && b0 < a1;
-}
-
-int pick_chunk_tiles(int64_t n, int cus) {
-    // One tile per workgroup: the resident workgroups then cover one compact
-    // stretch of every array and sweep through memory together, which
-    // measured best on MI355X for every shard size (longer chunks spread the
-    // active front over more DRAM pages).  The per-workgroup segment search
-    // is two dependent table loads and hides behind the other workgroups.
-    (void)n;
-    (void)cus;
-    return 1;
-}
-
-// One call, whatever the variant: the buffers it reads and writes.
-struct Request {
-    float *master = nullptr;
-    void *m = nullptr;
-    void *v = nullptr;
-    uint16_t *param = nullptr;
-    int8_t *q8 = nullptr;
-    float *q8_scale = nullptr;
-    const uint16_t *const *grads = nullptr;
-    const int8_t *const *qgrads = nullptr;
-    const float *const *qscales = nullptr;
-    int k = 0;
-    int64_t n = 0;
-    const zs_seg_table *st = nullptr;
-    const zs_hparams *hp = nullptr;
-    int64_t step = 0;
-    void *stream = nullptr;
-    const zs_launch_cfg *cfg = nullptr;
-    int variant = 0;
-};
-
-struct Span {
-    const void *p;
-    int64_t bytes;
-    uintptr_t align;
-};
-
-int validate_and_launch(const Request &r) {
-    if (!g_initialized) return ZS_ERR_NOT_INITIALIZED;
-    const bool gq = (r.variant & kGradQ8) != 0;
-    if (r.k < 1 || r.k > ZS_MAX_K || r.n < 0 || r.step < 1 || !r.st || !r.hp)
-        return ZS_ERR_INVALID_ARGUMENT;
-    if (gq ? (!r.qgrads || !r.qscales) : !r.grads) return ZS_ERR_INVALID_ARGUMENT;
-    const zs_hparams *hp = r.hp;
-    if (!std::isfinite(hp->lr) || !std::isfinite(hp->beta1) || !std::isfinite(hp->beta2) ||
-        !std::isfinite(hp->eps) || !std::isfinite(hp->weight_decay) ||
-        !std::isfinite(hp->grad_scale))
-        return ZS_ERR_INVALID_ARGUMENT;
-    if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f) ||
-        hp->eps < 0.0f)
-        return ZS_ERR_INVALID_ARGUMENT;
-    if (r.st->count < 1) return ZS_ERR_INVALID_ARGUMENT;
-    if (r.st->count > ZS_MAX_SEGMENTS) return ZS_ERR_TOO_MANY_SEGMENTS;
-    // Streaming (non-temporal) loads and stores by default: nothing is
-    // reused, and on MI355X they measured 5-10 % faster than cached access.
-    int chunk_tiles = 0, nt = 1;
-    if (r.cfg) {
-        if (r.cfg->chunk_tiles < 0 || r.cfg->chunk_tiles > kMaxChunkTiles)
-            return ZS_ERR_INVALID_ARGUMENT;
-        if (r.cfg->nontemporal < 0 || r.cfg->nontemporal > 2) return ZS_ERR_INVALID_ARGUMENT;
-        chunk_tiles = r.cfg->chunk_tiles;
-        nt = r.cfg->nontemporal == 2 ? 0 : 1;
-    }
-    if (r.n == 0) return ZS_OK;
-    if (r.n > INT64_MAX / 8) return ZS_ERR_INVALID_ARGUMENT;
-    if (!r.st->segs) return ZS_ERR_INVALID_ARGUMENT;
-    if ((uintptr_t)r.st->segs & 7u) return ZS_ERR_MISALIGNED;
-
-    const int64_t n = r.n;
-    const int64_t nblocks = (n + kQ8Block - 1) / kQ8Block;
-    const int64_t mv_bytes = (r.variant & kMvBf16) ? 2 * n : 4 * n;
-    Span outs[6];
-    int nouts = 0;
-    outs[nouts++] = {r.master, 4 * n, 16};
-    outs[nouts++] = {r.m, mv_bytes, 16};
-    outs[nouts++] = {r.v, mv_bytes, 16};
-    outs[nouts++] = {r.param, 2 * n, 16};
-    if (r.variant & kOutQ8) {
-        outs[nouts++] = {r.q8, n, 16};
-        outs[nouts++] = {r.q8_scale, 4 * nblocks, 4};
-    }
-    Span ins[2 * ZS_MAX_K];
-    int nins = 0;
-    for (int j = 0; j < r.k; ++j) {
-        if (gq) {
-            ins[nins++] = {r.qgrads[j], n, 16};
-            ins[nins++] = {r.qscales[j], 4 * nblocks, 4};
-        } else {
-            ins[nins++] = {r.grads[j], 2 * n, 16};
-        }
-    }
-    for (int x = 0; x < nouts; ++x)
-        if (!outs[x].p) return ZS_ERR_INVALID_ARGUMENT;
-    for (int x = 0; x < nins; ++x)
-        if (!ins[x].p) return ZS_ERR_INVALID_ARGUMENT;
-    for (int x = 0; x < nouts; ++x)
-        if ((uintptr_t)outs[x].p & (outs[x].align - 1)) return ZS_ERR_MISALIGNED;
-    for (int x = 0; x < nins; ++x)
-        if ((uintptr_t)ins[x].p & (ins[x].align - 1)) return ZS_ERR_MISALIGNED;
-    for (int x = 0; x < nouts; ++x) {
-        for (int y = x + 1; y < nouts; ++y)
-            if (overlaps(outs[x].p, outs[x].bytes, outs[y].p, outs[y].bytes)) return ZS_ERR_ALIASING;
-        for (int y = 0; y < nins; ++y)
-            if (overlaps(outs[x].p, outs[x].bytes, ins[y].p, ins[y].bytes)) return ZS_ERR_ALIASING;
-    }
-
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return device_error(e);
-    if (dev < 0 || dev >= kMaxDevices || !g_dev[dev].ready) return ZS_ERR_NOT_INITIALIZED;
-
-    StepArgs a;
-    a.master = r.master;
-    a.m = r.m;
-    a.v = r.v;
-    a.param = r.param;
-    a.q8 = r.q8;
-    a.q8_scale = r.q8_scale;
-    for (int j = 0; j < ZS_MAX_K; ++j) {
-        a.grads[j] = (!gq && j < r.k) ? r.grads[j] : nullptr;
-        a.qgrads[j] = (gq && j < r.k) ? r.qgrads[j] : nullptr;
-        a.qscales[j] = (gq && j < r.k) ? r.qscales[j] : nullptr;
-    }
-    a.segs = r.st->segs;
-    a.nseg = r.st->count;
-    a.n = n;
-    a.lr = hp->lr;
-    a.b1 = hp->beta1;
-    a.b2 = hp->beta2;
-    a.c1 = 1.0f - hp->beta1;
-    a.c2 = 1.0f - hp->beta2;
-    a.bc1 = (float)(1.0 - std::pow((double)hp->beta1, (double)r.step));
-    a.bc2 = (float)(1.0 - std::pow((double)hp->beta2, (double)r.step));
-    a.eps = hp->eps;
-    {
-        const float lrwd = hp->lr * hp->weight_decay;
-        a.df = 1.0f - lrwd;
-    }
-    a.gscale = hp->grad_scale;
-
-    if (chunk_tiles == 0) chunk_tiles = pick_chunk_tiles(n, g_dev[dev].cus);
-    int64_t chunk = (int64_t)chunk_tiles * tile_for(r.k);
-    int64_t blocks = (n + chunk - 1) / chunk;
-    while (blocks > 0x7fffffffLL) {  // keep the grid inside the 32-bit limit
-        chunk *= 2;
-        blocks = (n + chunk - 1) / chunk;
-    }
-    a.chunk = chunk;
-
-    kernel_fn fn = pick_kernel(r.k, r.variant, nt);
-    if (!fn) return ZS_ERR_INVALID_ARGUMENT;
-    void *args[] = {&a};
-    e = hipLaunchKernel((const void *)fn, dim3((unsigned)blocks), dim3(kThreads), args, 0,
-                        (hipStream_t)r.stream);
-    if (e != hipSuccess) return device_error(e);
-    return ZS_OK;
-}
-
-Request base_request(float *master, void *m, void *v, uint16_t *param, int k, int64_t n,
-                     const zs_seg_table *st, const zs_hparams *hp, int64_t step, void *stream) {
-    Request r;
-    r.master = master;
-    r.m = m;
-    r.v = v;
-    r.param = param;
-    r.k = k;
-    r.n = n;
-    r.st = st;
-    r.hp = hp;
-    r.step = step;
-    r.stream = stream;
-    return r;
-}
-
-}  // namespace
-
-extern "C" {
-
-int zs_init(int device_ordinal) {
-    int count = 0;
-    hipError_t e = hipGetDeviceCount(&count);
-    if (e != hipSuccess) return device_error(e);
-    if (device_ordinal < 0 || device_ordinal >= count || device_ordinal >= kMaxDevices)
-        return ZS_ERR_INVALID_ARGUMENT;
-    hipDeviceProp_t prop;
-    e = hipGetDeviceProperties(&prop, device_ordinal);
-    if (e != hipSuccess) return device_error(e);
-    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return ZS_ERR_DEVICE;
-    g_dev[device_ordinal].cus = prop.multiProcessorCount;
-    g_dev[device_ordinal].ready = 1;
-    g_initialized = 1;
-    return ZS_OK;
-}
-
-int zs_shard_step(float *master, float *m, float *v, uint16_t *param_bf16,
-                  const uint16_t *const *grads, int k, int64_t n,
-                  const zs_seg_table *seg_table, const zs_hparams *hparams,
-                  int64_t step, void *stream) {
-    Request r = base_request(master, m, v, param_bf16, k, n, seg_table, hparams, step, stream);
-    r.grads = grads;
-    return validate_and_launch(r);
-}
-
-int zs_shard_step_cfg(float *master, float *m, float *v, uint16_t *param_bf16,
-                      const uint16_t *const *grads, int k, int64_t n,
-                      const zs_seg_table *seg_table, const zs_hparams *hparams,
-                      int64_t step, void *stream, const zs_launch_cfg *cfg) {
-    Request r = base_request(master, m, v, param_bf16, k, n, seg_table, hparams, step, stream);
-    r.grads = grads;
-    r.cfg = cfg;
-    return validate_and_launch(r);
-}
-
-int zs_shard_step_q8ag(float *master, float *m, float *v, uint16_t *param_bf16,
-                       int8_t *param_q8, float *param_q8_scale,
-                       const uint16_t *const *grads, int k, int64_t n,
-                       const zs_seg_table *seg_table, const zs_hparams *hparams,
-                       int64_t step, void *stream) {
-    Request r = base_request(master, m, v, param_bf16, k, n, seg_table, hparams, step, stream);
-    r.grads = grads;
-    r.q8 = param_q8;
-    r.q8_scale = param_q8_scale;
-    r.variant = kOutQ8;
-    return validate_and_launch(r);
-}
-
-int zs_shard_step_q8grad(float *master, float *m, float *v, uint16_t *param_bf16,
-                         const int8_t *const *qgrads, const float *const *qscales, int k,
-                         int64_t n, const zs_seg_table *seg_table, const zs_hparams *hparams,
-                         int64_t step, void *stream) {
-    Request r = base_request(master, m, v, param_bf16, k, n, seg_table, hparams, step, stream);
-    r.qgrads = qgrads;
-    r.qscales = qscales;
-    r.variant = kGradQ8;
-    return validate_and_launch(r);
-}
-
-int zs_shard_step_bf16mv(float *master, uint16_t *m_bf16, uint16_t *v_bf16,
-                         uint16_t *param_bf16, const uint16_t *const *grads, int k, int64_t n,
-                         const zs_seg_table *seg_table, const zs_hparams *hparams,
-                         int64_t step, void *stream) {
-    Request r = base_request(master, m_bf16, v_bf16, param_bf16, k, n, seg_table, hparams, step,
-                             stream);
-    r.grads = grads;
-    r.variant = kMvBf16;
-    return validate_and_launch(r);
-}
-
-int zs_fini(void) {
-    for (int d = 0; d < kMaxDevices; ++d) g_dev[d].ready = 0;
-    g_initialized = 0;
-    return ZS_OK;
-}
-
-const char *zs_status_string(int status) {
-    switch (status) {
-        case ZS_OK: return "ok";
-        case ZS_ERR_NOT_INITIALIZED: return "library not initialized for this device";
-        case ZS_ERR_INVALID_ARGUMENT: return "invalid argument";
-        case ZS_ERR_MISALIGNED: return "buffer not aligned";
-        case ZS_ERR_TOO_MANY_SEGMENTS: return "segment table too large";
-        case ZS_ERR_DEVICE: return "HIP runtime error";
-        case ZS_ERR_ALIASING: return "output buffers overlap";
-        default: return "unknown status";
-    }
-}
-
-int zs_last_device_error(void) { return t_last_hip_error; }
-
-int64_t zs_algorithmic_bytes(int k, int64_t n) {
-    if (k < 1 || n < 0) return 0;
-    return n * (int64_t)(12 + 2 * k) + n * 14;
-}
-
-}  // extern "C"
+}  // namespace zs_detail

@@ -47,15 +47,23 @@ def test_step_before_init_is_rejected_without_touching_a_device():
     assert rc == zs.ZS_ERR_NOT_INITIALIZED
 
 
+def test_constants_match_header():
+    text = open(HEADER).read()
+    for name in ("ZS_MAX_K", "ZS_MAX_SEGMENTS", "ZS_Q8_BLOCK", "ZS_MAX_GROUPS_PER_CU"):
+        m = re.search(r"#define %s (\d+)" % name, text)
+        assert m and int(m.group(1)) == getattr(zs, name), name
+
+
 def test_struct_layout_matches_header():
     src = r'''
     #include <stddef.h>
     #include <stdio.h>
     #include "zs.h"
     int main(void) {
-      printf("%zu %zu %zu %zu %zu %zu %zu\n", sizeof(zs_hparams), sizeof(zs_segment),
+      printf("%zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(zs_hparams), sizeof(zs_segment),
              sizeof(zs_seg_table), sizeof(zs_launch_cfg), offsetof(zs_segment, wd_on),
-             offsetof(zs_seg_table, count), offsetof(zs_hparams, grad_scale));
+             offsetof(zs_seg_table, count), offsetof(zs_hparams, grad_scale),
+             offsetof(zs_launch_cfg, groups_per_cu));
       return 0; }
     '''
     with tempfile.TemporaryDirectory() as d:
@@ -69,7 +77,7 @@ def test_struct_layout_matches_header():
     want = [ctypes.sizeof(zs.ZsHparams), ctypes.sizeof(zs.ZsSegment),
             ctypes.sizeof(zs.ZsSegTable), ctypes.sizeof(zs.ZsLaunchCfg),
             zs.ZsSegment.wd_on.offset, zs.ZsSegTable.count.offset,
-            zs.ZsHparams.grad_scale.offset]
+            zs.ZsHparams.grad_scale.offset, zs.ZsLaunchCfg.groups_per_cu.offset]
     assert got == want
     import oracle
     assert ctypes.sizeof(oracle.Segment) == ctypes.sizeof(zs.ZsSegment)

@@ -202,8 +202,8 @@ def test_segment_overflow_and_restaging(gpu):
             segs.append((a, bool(rng.random() < 0.5)))  # duplicate start
         a += int(rng.integers(1, 4))
     segs += [(n, True), (n + 10, False)]
-    # k = 2 (1024-element tiles) and k = 4 (4096-element tiles: a tile holds
-    # more entries than the LDS slice, so the per-element global lookup runs)
+    # k = 2 (256-element windows) and k = 4 (1024-element windows): the windows
+    # hold more than 64 boundaries, so the per-element table lookup runs too
     for k in (2, 4):
         for chunk_tiles in (1, 4, 12):
             got, ref = _run_both(gpu, n, k, segs, range(1, 3), seed=9,
@@ -226,6 +226,46 @@ def test_launch_geometry_is_bitwise_invariant(gpu):
     for o in outs[1:]:
         for a, b in zip(outs[0], o):
             assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_occupancy_cap_is_bitwise_invariant(gpu):
+    """groups_per_cu only reserves LDS: every cap gives the same bits as the
+    default launch, for the one-quad (k = 2) and four-quad (k = 8) kernels."""
+    torch = gpu
+    rng = np.random.default_rng(16)
+    n = 4096 * 30 + 777
+    segs = _random_segments(rng, n, short_frac=0.2)
+    for k in (2, 8):
+        base, ref = _run_both(torch, n, k, segs, range(1, 3), seed=16)
+        H.assert_parity(base, ref, "k=%d default" % k)
+        for g in (2, 3, 6, 32):
+            got, _ = _run_both(torch, n, k, segs, range(1, 3), seed=16,
+                               cfg=dict(groups_per_cu=g))
+            for a, b in zip(base, got):
+                assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), (k, g)
+
+
+def test_launch_cfg_errors(gpu):
+    torch = gpu
+    n = 1024
+    f = [torch.zeros(n, dtype=torch.float32, device="cuda") for _ in range(3)]
+    p = torch.zeros(n, dtype=torch.int16, device="cuda")
+    g = [torch.zeros(n, dtype=torch.int16, device="cuda") for _ in range(2)]
+    table = H.segment_tensor([(0, True)], "cuda")
+
+    def call(**cfg):
+        return zs.zs_shard_step_cfg(f[0], f[1], f[2], p, g, 2, n, zs.seg_table(table),
+                                    zs.hparams(), 1, None, check=False, **cfg)
+
+    assert call() == zs.ZS_OK
+    for bad in (dict(chunk_tiles=-1), dict(chunk_tiles=4097), dict(nontemporal=3),
+                dict(groups_per_cu=-1), dict(groups_per_cu=zs.ZS_MAX_GROUPS_PER_CU + 1)):
+        assert call(**bad) == zs.ZS_ERR_INVALID_ARGUMENT, bad
+    # a one-workgroup-per-unit cap fits only where one workgroup may take the
+    # whole LDS of a unit; either way the call answers synchronously
+    assert call(groups_per_cu=1) in (zs.ZS_OK, zs.ZS_ERR_INVALID_ARGUMENT)
+    assert call(groups_per_cu=zs.ZS_MAX_GROUPS_PER_CU) == zs.ZS_OK
+    torch.cuda.synchronize()
 
 
 def test_hparam_variants(gpu):
