@@ -36,6 +36,12 @@
  * Threading: zs_init/zs_fini must not race with other calls.  After
  * zs_init the library holds no mutable state, so zs_shard_step may be
  * called concurrently from several threads and on several streams.
+ *
+ * Graph capture: a step call enqueues one kernel and nothing else (no
+ * allocation, memset or synchronisation), so it may be recorded into a HIP
+ * graph.  The arguments are checked and the bias corrections formed when the
+ * call is made, i.e. at capture: every replay repeats the captured call with
+ * the same step t and the same buffers.
  */
 #ifndef ZS_H_
 #define ZS_H_

@@ -1,0 +1,91 @@
+"""The shard step captured in a HIP graph (torch.cuda.CUDAGraph) and replayed.
+
+A launch of the library does no allocation, no memset and no synchronisation,
+so it can be captured.  The graph keeps the arguments of the captured call,
+including the step t, so every replay repeats that call.  Each replay is
+compared bitwise with the same call made eagerly on twin buffers, with other
+eager work and synchronisations between replays.
+"""
+import numpy as np
+import pytest
+
+import sharded_mixed_precision_shard_amd as zs
+from tests import _gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gpu():
+    import torch
+    assert torch.cuda.is_available()
+    torch.cuda.set_device(0)
+    rc = zs.zs_init(0)
+    assert rc == zs.ZS_OK, zs.zs_status_string(rc)
+    yield torch
+    torch.cuda.synchronize()
+
+
+def _state(torch, w0, n, k, seed, q8):
+    rng = np.random.default_rng(seed)
+    f = lambda a: torch.from_numpy(a.copy()).cuda()  # noqa: E731
+    st = dict(master=f(w0), m=torch.zeros(n, dtype=torch.float32, device="cuda"),
+              v=torch.zeros(n, dtype=torch.float32, device="cuda"),
+              param=torch.zeros(n, dtype=torch.int16, device="cuda"),
+              grads=[f((rng.normal(0, 1e-2, n).astype(np.float32).view(np.uint32) >> 16)
+                       .astype(np.uint16).view(np.int16)) for _ in range(k)])
+    if q8:
+        st["q8"] = torch.zeros(n, dtype=torch.int8, device="cuda")
+        st["q8s"] = torch.zeros(-(-n // zs.ZS_Q8_BLOCK), dtype=torch.float32, device="cuda")
+    return st
+
+
+def _call(st, k, n, table, hp, t, stream):
+    if "q8" in st:
+        zs.zs_shard_step_q8ag(st["master"], st["m"], st["v"], st["param"], st["q8"], st["q8s"],
+                              st["grads"], k, n, zs.seg_table(table), hp, t, stream)
+    else:
+        zs.zs_shard_step(st["master"], st["m"], st["v"], st["param"], st["grads"], k, n,
+                         zs.seg_table(table), hp, t, stream)
+
+
+def _same(torch, a, b):
+    for key in a:
+        xs = a[key] if isinstance(a[key], list) else [a[key]]
+        ys = b[key] if isinstance(b[key], list) else [b[key]]
+        for x, y in zip(xs, ys):
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), key
+
+
+@pytest.mark.parametrize("q8", [False, True], ids=["zs_shard_step", "zs_shard_step_q8ag"])
+@pytest.mark.parametrize("t", [7, 10000])
+def test_graph_replays_match_eager_calls(gpu, q8, t):
+    torch = gpu
+    n, k = 100_003, 3
+    rng = np.random.default_rng(21)
+    w0 = rng.normal(0, 0.02, n).astype(np.float32)
+    segs, a = [], 0
+    while a < n:
+        segs.append((a, bool(rng.random() < 0.5)))
+        a += int(rng.integers(1, 5000))
+    table = H.segment_tensor(segs, "cuda")
+    hp = zs.hparams(1e-3, 0.9, 0.95, 1e-8, 0.1, 1.0)
+    eager = _state(torch, w0, n, k, 5, q8)
+    graphed = _state(torch, w0, n, k, 5, q8)
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _call(graphed, k, n, table, hp, t, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    _same(torch, graphed, _state(torch, w0, n, k, 5, q8))  # capture ran nothing
+
+    for rep in range(4):
+        g.replay()
+        _call(eager, k, n, table, hp, t, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        x = torch.randn(4096, device="cuda")
+        assert torch.isfinite((x * x).sum())  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        _same(torch, graphed, eager)
+    assert not torch.equal(graphed["master"], torch.from_numpy(w0).cuda())
