@@ -98,8 +98,7 @@ typedef struct {
 /* Launch geometry override, for tuning and for determinism tests.  Zero in a
  * field selects the library default.  Results never depend on it. */
 typedef struct {
-    int32_t chunk_tiles;  /* tiles per workgroup (1..4096); a tile is 1024 elements
-                             when k <= 2 and 4096 elements when k >= 3 */
+    int32_t chunk_tiles;  /* tiles per workgroup (1..4096); a tile is 1024 elements */
     int32_t nontemporal;  /* 0 = default (streaming), 1 = streaming (non-temporal)
                              loads/stores, 2 = ordinary cached loads/stores */
     int32_t groups_per_cu; /* 0 = as many resident workgroups per compute unit as

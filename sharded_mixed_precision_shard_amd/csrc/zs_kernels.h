@@ -16,14 +16,16 @@ constexpr int kWave = 64;
 constexpr int kQuad = 4;                      // contiguous elements per lane per sub-window
 constexpr int kSub = kWave * kQuad;           // 256: one dense instruction per array per wave
 
-// Sub-windows (quads per lane) a wave handles per tile.  Measured on MI355X:
-// with one or two partials the fewest bytes in flight per wave streamed best
-// (one quad); with three or more partials each lane already has many loads
-// in flight and four quads per lane streamed best.
-constexpr int quads_for(int k) { return k <= 2 ? 1 : 4; }
+// Sub-windows (quads per lane) a wave handles per tile.  Measured on MI355X
+// with the per-wavefront segment lookup: one quad per lane, i.e. the fewest
+// bytes in flight per wave and the most waves, streamed as fast as or faster
+// than two or four quads for every partial count (even on the eight-partial
+// 7B shard, 5-12 % faster on small shards, which get four times the
+// workgroups).
+constexpr int quads_for(int k) { return (void)k, 1; }
 constexpr int tile_for(int k) { return (kThreads / kWave) * quads_for(k) * kSub; }
 
-static_assert(tile_for(1) == 1024 && tile_for(8) == 4096, "tile sizes");
+static_assert(tile_for(1) == 1024 && tile_for(16) == 1024, "tile sizes");
 
 struct StepArgs {
     float *master;

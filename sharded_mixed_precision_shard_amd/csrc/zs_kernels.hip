@@ -10,9 +10,9 @@
 //
 // The work is purely elementwise and bandwidth bound (about 0.5 flop per HBM
 // byte), so there is no MFMA here.  Design for CDNA4:
-//   * a wavefront's window is Q sub-windows of 256 elements (Q = 1 for one
-//     or two partials, 4 for more; a workgroup tile is four windows); lane
-//     l owns elements 4l..4l+3 of each sub-window.  Every load and store
+//   * a wavefront's window is Q sub-windows of 256 elements (Q = 1, measured
+//     best; a workgroup tile is four windows); lane l owns elements
+//     4l..4l+3 of each sub-window.  Every load and store
 //     instruction of a wavefront is then one dense, contiguous run (1 KB per
 //     fp32 array, 512 B per bf16 array) of 16-byte (fp32) or 8-byte (bf16)
 //     accesses, and every byte is read once and written once;

@@ -190,9 +190,10 @@ def test_ragged_sizes_and_tiny_segments(gpu, n, k):
 
 
 def test_segment_overflow_and_restaging(gpu):
-    """More segments inside one workgroup chunk than the LDS slice holds, and
-    tiles whose segments do not fit at all: the restaging and global-lookup
-    paths.  Also duplicate starts (empty segments) and entries past n."""
+    """Segments every 1-3 elements: each 256-element window holds more table
+    entries than a wavefront's 64-entry slot, so the per-element table lookup
+    runs; over several chunk lengths.  Also duplicate starts (empty segments)
+    and entries past n."""
     rng = np.random.default_rng(5)
     n = 2048 * 12 + 5
     segs, a = [], 0
@@ -202,8 +203,7 @@ def test_segment_overflow_and_restaging(gpu):
             segs.append((a, bool(rng.random() < 0.5)))  # duplicate start
         a += int(rng.integers(1, 4))
     segs += [(n, True), (n + 10, False)]
-    # k = 2 (256-element windows) and k = 4 (1024-element windows): the windows
-    # hold more than 64 boundaries, so the per-element table lookup runs too
+    # the lookup does not depend on k; two partial counts for good measure
     for k in (2, 4):
         for chunk_tiles in (1, 4, 12):
             got, ref = _run_both(gpu, n, k, segs, range(1, 3), seed=9,
@@ -230,7 +230,7 @@ def test_launch_geometry_is_bitwise_invariant(gpu):
 
 def test_occupancy_cap_is_bitwise_invariant(gpu):
     """groups_per_cu only reserves LDS: every cap gives the same bits as the
-    default launch, for the one-quad (k = 2) and four-quad (k = 8) kernels."""
+    default launch, with two and with eight partials."""
     torch = gpu
     rng = np.random.default_rng(16)
     n = 4096 * 30 + 777
