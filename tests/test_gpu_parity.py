@@ -35,8 +35,10 @@ def _dev(torch, a):
     return torch.from_numpy(a.copy()).cuda()
 
 
-def _run_both(torch, n, k, segs, steps, seed, hp_kw=None, cfg=None, w0=None, grads_fn=None):
-    """Same inputs on GPU and oracle; returns (gpu outputs, oracle outputs)."""
+def _run_both(torch, n, k, segs, steps, seed, hp_kw=None, cfg=None, w0=None, grads_fn=None,
+              ref_segs=None):
+    """Same inputs on GPU and oracle; returns (gpu outputs, oracle outputs).
+    ref_segs: a different (valid) table for the oracle side."""
     hp_kw = hp_kw or {}
     w = synth.host_normal_f32(n, synth.stream_key(seed, 1, 0, 0), 0, n, 0.02) if w0 is None \
         else w0.copy()
@@ -59,7 +61,7 @@ def _run_both(torch, n, k, segs, steps, seed, hp_kw=None, cfg=None, w0=None, gra
         else:
             zs.zs_shard_step_cfg(dw, dm, dv, dp, dgs, k, n, zs.seg_table(table), hpz, t,
                                  torch.cuda.current_stream(), **cfg)
-        assert oracle.shard_step(*ref, gs, segs, hpo, t) == 0
+        assert oracle.shard_step(*ref, gs, segs if ref_segs is None else ref_segs, hpo, t) == 0
     torch.cuda.synchronize()
     got = (dw.cpu().numpy(), dm.cpu().numpy(), dv.cpu().numpy(),
            dp.cpu().numpy().view(np.uint16))
@@ -209,6 +211,44 @@ def test_segment_overflow_and_restaging(gpu):
             got, ref = _run_both(gpu, n, k, segs, range(1, 3), seed=9,
                                  cfg=dict(chunk_tiles=chunk_tiles))
             H.assert_parity(got, ref, "k=%d chunk_tiles=%d" % (k, chunk_tiles))
+
+
+def test_largest_segment_table(gpu):
+    """ZS_MAX_SEGMENTS entries (three rounds of the 64-way search), most of
+    them one or two elements long, the last ones past n."""
+    rng = np.random.default_rng(17)
+    n = 100_000
+    count = zs.ZS_MAX_SEGMENTS
+    starts = np.sort(rng.choice(np.arange(1, n + 5000), count - 1, replace=False))
+    segs = [(0, True)] + [(int(a), bool(rng.random() < 0.5)) for a in starts]
+    assert len(segs) == count
+    got, ref = _run_both(gpu, n, 2, segs, range(1, 4), seed=17)
+    H.assert_parity(got, ref, "%d segments" % count)
+
+
+def test_unsorted_table_stays_in_bounds(gpu):
+    """An unsorted device table (which the library cannot check) gives
+    unspecified decay flags but reads nothing outside the table: the call
+    completes, m and v (which do not depend on the flags) equal the oracle's
+    bitwise, and every weight is the oracle's with decay on or with decay off."""
+    torch = gpu
+    rng = np.random.default_rng(18)
+    n = 50_003
+    segs = [(int(a), bool(rng.random() < 0.5))
+            for a in rng.integers(-1000, n + 1000, 3000)]  # unsorted, duplicates, out of range
+    segs[0] = (0, True)
+    for name, table in (("random order", segs), ("reversed", sorted(segs)[::-1])):
+        got, _ = _run_both(torch, n, 3, table, range(1, 4), seed=18,
+                           ref_segs=[(0, True)])
+        on = _run_both(torch, n, 3, [(0, True)], range(1, 4), seed=18)[1]
+        off = _run_both(torch, n, 3, [(0, False)], range(1, 4), seed=18)[1]
+        for i in (1, 2):  # m, v
+            assert np.array_equal(got[i].view(np.uint32), on[i].view(np.uint32)), name
+        w, p = got[0].view(np.uint32), got[3]
+        either = (w == on[0].view(np.uint32)) | (w == off[0].view(np.uint32))
+        assert either.all(), "%s: %d weights are neither" % (name, int((~either).sum()))
+        pe = np.where(w == on[0].view(np.uint32), on[3], off[3])
+        assert np.array_equal(p, pe), name
 
 
 def test_launch_geometry_is_bitwise_invariant(gpu):

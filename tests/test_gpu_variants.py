@@ -47,7 +47,7 @@ def _bf16_partials(rng, k, n, sigma=1e-2):
 
 
 @pytest.mark.parametrize("n", SIZES)
-@pytest.mark.parametrize("k", [1, 2, 5])
+@pytest.mark.parametrize("k", [1, 2, 5, 16])
 def test_q8ag_matches_oracle(gpu, n, k):
     torch = gpu
     rng = np.random.default_rng(100 + n * 7 + k)
@@ -77,7 +77,7 @@ def test_q8ag_matches_oracle(gpu, n, k):
 
 
 @pytest.mark.parametrize("n", SIZES)
-@pytest.mark.parametrize("k", [1, 3, 8])
+@pytest.mark.parametrize("k", [1, 3, 8, 16])
 def test_q8grad_matches_oracle(gpu, n, k):
     torch = gpu
     rng = np.random.default_rng(200 + n * 7 + k)
@@ -102,7 +102,7 @@ def test_q8grad_matches_oracle(gpu, n, k):
 
 
 @pytest.mark.parametrize("n", SIZES)
-@pytest.mark.parametrize("k", [1, 2, 8])
+@pytest.mark.parametrize("k", [1, 2, 8, 16])
 def test_bf16mv_matches_oracle(gpu, n, k):
     torch = gpu
     rng = np.random.default_rng(300 + n * 7 + k)
