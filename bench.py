@@ -22,6 +22,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -40,13 +41,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and with runs of white space collapsed
+    (the kernel sources hold no string literal with comment markers)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
-    """sha256[:16] over the kernel sources (device code and the argument
-    block it reads), in a fixed order; host-side changes leave it alone."""
+    """sha256[:16] over the code of the kernel sources (device code and the
+    argument block it reads), comments and layout ignored, in a fixed order;
+    host-side changes leave it alone."""
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -47,8 +47,7 @@ int pick_chunk_tiles(int64_t n, int cus) {
     // One tile per workgroup: the resident workgroups then cover one compact
     // stretch of every array and sweep through memory together, which
     // measured best on MI355X for every shard size (longer chunks spread the
-    // active front over more DRAM pages).  The per-workgroup segment search
-    // is two dependent table loads and hides behind the other workgroups.
+    // active front over more DRAM pages).
     (void)n;
     (void)cus;
     return 1;

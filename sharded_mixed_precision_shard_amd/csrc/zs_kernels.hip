@@ -263,7 +263,7 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
     return x;
 }
 
-// Quantize one block (one half window: 64 lanes x 4 bf16 values) to int8.
+// Quantize one block (one sub-window: 64 lanes x 4 bf16 values) to int8.
 // `bits` are the lane's four bf16 values widened to fp32 bit patterns;
 // `valid` marks which of them lie inside the shard.  The block maximum of
 // |x| is taken on the bit patterns (integer order of |x| bits = order of

@@ -77,3 +77,17 @@ def test_threaded_split_is_bitwise_identical():
             assert step(*b, grads, segs, hp, 4) == 0
         for x, y in zip(a, b):
             assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), variant
+
+
+def test_kernel_hash_ignores_comments_not_code():
+    src = "int f(int x) { // add one\n  return x + 1; /* done */ }\n"
+    same = "// header\nint f(int x) {\n\n  return x + 1;   }\n"
+    other = "int f(int x) { return x + 2; }"
+    assert bench._code_only(src) == bench._code_only(same)
+    assert bench._code_only(src) != bench._code_only(other)
+    h = bench.kernel_source_hash()
+    assert len(h) == 16 and int(h, 16) >= 0
+    with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+        entries = json.load(f)
+    # every committed traffic measurement belongs to the kernel code as it stands
+    assert all(e["kernel_sha"] == h for e in entries.values())
