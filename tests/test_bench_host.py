@@ -89,5 +89,8 @@ def test_kernel_hash_ignores_comments_not_code():
     assert len(h) == 16 and int(h, 16) >= 0
     with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
         entries = json.load(f)
-    # every committed traffic measurement belongs to the kernel code as it stands
-    assert all(e["kernel_sha"] == h for e in entries.values())
+    # a measurement is reported only for the kernel code it was taken on
+    for key, e in entries.items():
+        got = bench.measured_traffic(key, e["launch"])
+        assert got == (e["bytes_per_launch"] if e["kernel_sha"] == h else None), key
+        assert bench.measured_traffic(key, e["launch"] + ",other") is None
