@@ -14,7 +14,9 @@ import pytest
 
 import oracle
 from tests import test_oracle_pins as P
+from tests import test_oracle_q8 as Q
 from tests import test_oracle_sharding as S
+from tests import test_oracle_variants as V
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "zs_oracle.c")
 
@@ -70,6 +72,49 @@ MUTATIONS = [
      "        adamw_element(&master[i], &m[i], &v[i], g, decay, hp, &sc);"),
 ]
 
+# Mistakes in the variant routines (quantized payload, quantized partials,
+# bf16 moments): caught by the variant pins.
+VARIANT_MUTATIONS = [
+    ("q8 scale over 128 levels",
+     "float s = a / 127.0f;", "float s = a / 128.0f;"),
+    ("q8 ties rounded away from zero",
+     "float r = rintf(bf16_to_f32(x_bf16[i]) / s);", "float r = roundf(bf16_to_f32(x_bf16[i]) / s);"),
+    ("q8 codes truncated",
+     "float r = rintf(bf16_to_f32(x_bf16[i]) / s);", "float r = truncf(bf16_to_f32(x_bf16[i]) / s);"),
+    ("q8 block maximum of x instead of |x|",
+     "else if (fabsf(x) > a) a = fabsf(x);", "else if (x > a) a = x;"),
+    ("q8 NaN does not poison its block",
+     "if (has_nan) a = NAN;", "if (0) a = NAN;"),
+    ("q8grad every partial scaled by partial 0's scale",
+     "float t = (float)q[j][i] * scale[j][b];", "float t = (float)q[j][i] * scale[0][b];"),
+    ("q8grad last partial dropped",
+     "for (int j = 1; j < k; ++j) {\n            float t = (float)q[j][i]",
+     "for (int j = 1; j < k - 1; ++j) {\n            float t = (float)q[j][i]"),
+    ("q8grad grad_scale ignored",
+     "g = g * hp->grad_scale;\n        adamw_element(&master[i], &m[i], &v[i], g, segs[seg].wd_on",
+     "g = g;\n        adamw_element(&master[i], &m[i], &v[i], g, segs[seg].wd_on"),
+    ("bf16mv first moment not carried across steps",
+     "float mf = bf16_to_f32(m[i]);", "float mf = 0.0f;"),
+    ("bf16mv second moment stored from the first",
+     "v[i] = zs_oracle_bf16_rne(vf);", "v[i] = zs_oracle_bf16_rne(mf);"),
+    ("bf16mv moments truncated",
+     "m[i] = zs_oracle_bf16_rne(mf);\n        v[i] = zs_oracle_bf16_rne(vf);",
+     "{ union { float f; uint32_t u; } cm, cv; cm.f = mf; cv.f = vf;\n"
+     "          m[i] = (uint16_t)(cm.u >> 16); v[i] = (uint16_t)(cv.u >> 16); }"),
+]
+
+VARIANT_BATTERY = [Q.test_hand_worked_block_with_ties, Q.test_zero_block_and_single_element,
+                   Q.test_nonfinite_blocks_only_poison_themselves,
+                   lambda: Q.test_error_bound_and_extremes(7),
+                   lambda: Q.test_error_bound_and_extremes(256),
+                   Q.test_matches_torch_elementwise_formula,
+                   V.test_q8grad_reduce_scatter_exercise,
+                   lambda: V.test_q8grad_equals_bf16_path_on_exact_partials(1.0),
+                   lambda: V.test_q8grad_equals_bf16_path_on_exact_partials(0.125),
+                   V.test_q8grad_products_round_once, V.test_bf16mv_first_step_equals_fp32_path,
+                   V.test_bf16mv_closed_form_with_halving_betas,
+                   V.test_bf16mv_stays_close_to_fp32_path]
+
 BATTERY = [P.test_reduce_scatter_exercise_values, P.test_ring_demo_values,
            P.test_reduce_brute_force_small_integers, P.test_reduce_is_a_left_fold,
            P.test_grad_scale_multiplies_after_the_sum, P.test_bias_correction_scalars,
@@ -88,15 +133,15 @@ def _compile(src_text, d):
     return so
 
 
-def _first_failing_pin(lib):
+def _first_failing_pin(lib, battery=None):
     saved = oracle._lib
     oracle._lib = lib
     try:
-        for pin in BATTERY:
+        for pin in battery or BATTERY:
             try:
                 pin()
             except (AssertionError, ValueError, FloatingPointError):
-                return pin.__name__
+                return getattr(pin, "__name__", "pin")
         return None
     finally:
         oracle._lib = saved
@@ -106,6 +151,7 @@ def test_unmutated_copy_passes_the_battery():
     with tempfile.TemporaryDirectory() as d:
         lib = oracle.load_library(_compile(open(SRC).read(), d))
         assert _first_failing_pin(lib) is None
+        assert _first_failing_pin(lib, VARIANT_BATTERY) is None
 
 
 @pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
@@ -118,3 +164,15 @@ def test_planted_mistake_is_caught(name, old, new):
         caught = _first_failing_pin(lib)
     assert caught is not None, "no pin catches: %s" % name
     print("%-45s caught by %s" % (name, caught))
+
+
+@pytest.mark.parametrize("name,old,new", VARIANT_MUTATIONS, ids=[m[0] for m in VARIANT_MUTATIONS])
+def test_planted_variant_mistake_is_caught(name, old, new):
+    text = open(SRC).read()
+    assert text.count(old) == 1, "mutation site not found once: %s" % name
+    mutated = text.replace(old, new, 1)
+    with tempfile.TemporaryDirectory() as d:
+        lib = oracle.load_library(_compile(mutated, d))
+        caught = _first_failing_pin(lib, VARIANT_BATTERY)
+    assert caught is not None, "no pin catches: %s" % name
+    print("%-50s caught by %s" % (name, caught))

@@ -2,6 +2,7 @@
 moments.  Each variant is tied to the pinned ordinary step where the two must
 agree exactly, plus hand-worked closed forms."""
 import numpy as np
+import pytest
 
 import oracle
 from tests.conftest import read_golden
@@ -34,10 +35,11 @@ def test_q8grad_reduce_scatter_exercise():
     assert m.tolist() == g["all_reduce"]
 
 
-def test_q8grad_equals_bf16_path_on_exact_partials():
+@pytest.mark.parametrize("grad_scale", [1.0, 0.125, 3.0])
+def test_q8grad_equals_bf16_path_on_exact_partials(grad_scale):
     """With power-of-two block scales every q*scale is exact in bf16, so the
     int8 path must equal the ordinary step fed those bf16 partials, bitwise,
-    over 10 steps, ragged n, several segments and varying scales."""
+    over 10 steps, ragged n, several segments, varying scales and grad_scale."""
     rng = np.random.default_rng(21)
     n, k, block = 1000, 3, 256
     nb = -(-n // block)
@@ -45,7 +47,7 @@ def test_q8grad_equals_bf16_path_on_exact_partials():
     segs = [(0, True), (300, False), (301, True), (777, False)]
     a = _state(n, w0)
     b = _state(n, w0)
-    hp = oracle.hparams()
+    hp = oracle.hparams(grad_scale=grad_scale)
     for t in range(1, 11):
         qs = [rng.integers(-127, 128, n).astype(np.int8) for _ in range(k)]
         ss = [(2.0 ** rng.integers(-16, -8, nb)).astype(F32) for _ in range(k)]
