@@ -106,16 +106,54 @@ def load_library():
     return lib
 
 
-def _addr(x) -> int:
+def _host(x, nbytes: int, name: str) -> int:
+    """Address of a buffer for the host step: a contiguous numpy array or CPU
+    tensor holding at least ``nbytes``, or an integer host address."""
     if x is None:
         return 0
     if isinstance(x, int):
         return x
-    if hasattr(x, "ctypes") and hasattr(x, "dtype"):  # numpy array (host memory)
-        return int(x.ctypes.data)
+    if hasattr(x, "ctypes") and hasattr(x, "dtype"):  # numpy array
+        if not x.flags["C_CONTIGUOUS"]:
+            raise ValueError("%s must be contiguous" % name)
+        have = x.nbytes
+        addr = int(x.ctypes.data)
+    elif hasattr(x, "data_ptr"):
+        if getattr(x, "is_cuda", False):
+            raise ValueError("%s: a GPU tensor cannot be passed to the host step" % name)
+        if not x.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+        have = x.numel() * x.element_size()
+        addr = int(x.data_ptr())
+    else:
+        raise TypeError("%s: expected a host array or an integer address, got %r" % (name,
+                                                                                   type(x)))
+    if have < nbytes:
+        raise ValueError("%s holds %d bytes; the call needs %d" % (name, have, nbytes))
+    return addr
+
+
+def _dev(x, nbytes: int, name: str) -> int:
+    """Address of a buffer for a GPU entry point.  A torch tensor must live on
+    a GPU, be contiguous and hold at least ``nbytes``; a host (numpy) array is
+    refused, since its address would reach the kernel.  An integer is taken
+    as a device address on the caller's word; None is the null pointer."""
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "ctypes") and hasattr(x, "dtype"):
+        raise TypeError("%s: a host (numpy) array cannot be passed to a GPU entry point" % name)
     if hasattr(x, "data_ptr"):
+        if not getattr(x, "is_cuda", False):
+            raise ValueError("%s must be a GPU tensor (got device %s)" % (name, x.device))
+        if not x.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+        have = x.numel() * x.element_size()
+        if have < nbytes:
+            raise ValueError("%s holds %d bytes; the call needs %d" % (name, have, nbytes))
         return int(x.data_ptr())
-    raise TypeError("expected a tensor with data_ptr() or an integer address, got %r" % type(x))
+    raise TypeError("%s: expected a GPU tensor or an integer address, got %r" % (name, type(x)))
 
 
 def _stream_handle(stream) -> int:
@@ -134,10 +172,14 @@ def hparams(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, grad_sca
 
 def seg_table(segs, count=None) -> ZsSegTable:
     """Describe a device-resident table.  ``segs`` is a device tensor of int64
-    pairs [count, 2] = (start, wd_on | reserved << 32) or an address."""
+    pairs [count, 2] = (start, wd_on | reserved << 32) or an address.  A count
+    beyond the tensor's rows is refused here unless the library itself would
+    refuse it (more than ZS_MAX_SEGMENTS entries: nothing is read)."""
     if count is None:
         count = int(segs.shape[0])
-    return ZsSegTable(_addr(segs), int(count), 0)
+    count = int(count)
+    need = 16 * count if 0 < count <= ZS_MAX_SEGMENTS else 0
+    return ZsSegTable(_dev(segs, need, "segment table"), count, 0)
 
 
 def zs_init(device_ordinal: int = 0) -> int:
@@ -160,21 +202,30 @@ def zs_algorithmic_bytes(k: int, n: int) -> int:
     return load_library().zs_algorithmic_bytes(int(k), int(n))
 
 
-def _marshal(master, m, v, param_bf16, grads, k, seg_table_, hparams_):
+def _marshal(master, m, v, param_bf16, grads, k, n, seg_table_, hparams_, mv_size=4):
+    """Pointers of one step call; every tensor checked against n elements."""
     if k is None:
         k = len(grads)
-    gp = (ctypes.c_void_p * max(len(grads), 1))(*[_addr(g) for g in grads])
+    nn = max(int(n), 0)
+    gp = _ptr_array(grads, 2 * nn, "grads")
     st = seg_table_ if isinstance(seg_table_, ZsSegTable) else seg_table(seg_table_)
-    return (ctypes.c_void_p(_addr(master)), ctypes.c_void_p(_addr(m)), ctypes.c_void_p(_addr(v)),
-            ctypes.c_void_p(_addr(param_bf16)), ctypes.cast(gp, ctypes.c_void_p), int(k), st,
-            hparams_, gp)
+    return (ctypes.c_void_p(_dev(master, 4 * nn, "master")),
+            ctypes.c_void_p(_dev(m, mv_size * nn, "m")),
+            ctypes.c_void_p(_dev(v, mv_size * nn, "v")),
+            ctypes.c_void_p(_dev(param_bf16, 2 * nn, "param_bf16")),
+            ctypes.cast(gp, ctypes.c_void_p), int(k), st, hparams_, gp)
+
+
+def _ptr_array(xs, nbytes, name):
+    return (ctypes.c_void_p * max(len(xs), 1))(
+        *[_dev(x, nbytes, "%s[%d]" % (name, j)) for j, x in enumerate(xs)])
 
 
 def zs_shard_step(master, m, v, param_bf16, grads, k, n, seg_table_, hparams_, step,
                   stream=None, check=True) -> int:
     """Enqueue one shard step (see include/zs.h).  Raises ZsError on a
     non-zero status when ``check`` is true; returns the status otherwise."""
-    pm, pmm, pv, pp, pg, kk, st, hp, keep = _marshal(master, m, v, param_bf16, grads, k,
+    pm, pmm, pv, pp, pg, kk, st, hp, keep = _marshal(master, m, v, param_bf16, grads, k, n,
                                                      seg_table_, hparams_)
     rc = load_library().zs_shard_step(pm, pmm, pv, pp, pg, kk, int(n), ctypes.byref(st),
                                       ctypes.byref(hp), int(step),
@@ -189,7 +240,7 @@ def zs_shard_step_cfg(master, m, v, param_bf16, grads, k, n, seg_table_, hparams
                       stream=None, chunk_tiles=0, nontemporal=0, groups_per_cu=0,
                       check=True) -> int:
     """zs_shard_step with an explicit launch geometry (results never change)."""
-    pm, pmm, pv, pp, pg, kk, st, hp, keep = _marshal(master, m, v, param_bf16, grads, k,
+    pm, pmm, pv, pp, pg, kk, st, hp, keep = _marshal(master, m, v, param_bf16, grads, k, n,
                                                      seg_table_, hparams_)
     cfg = ZsLaunchCfg(int(chunk_tiles), int(nontemporal), int(groups_per_cu), 0)
     rc = load_library().zs_shard_step_cfg(pm, pmm, pv, pp, pg, kk, int(n), ctypes.byref(st),
@@ -202,22 +253,19 @@ def zs_shard_step_cfg(master, m, v, param_bf16, grads, k, n, seg_table_, hparams
     return rc
 
 
-def _ptr_array(xs):
-    return (ctypes.c_void_p * max(len(xs), 1))(*[_addr(x) for x in xs])
-
-
 def zs_shard_step_q8ag(master, m, v, param_bf16, param_q8, param_q8_scale, grads, k, n,
                        seg_table_, hparams_, step, stream=None, check=True) -> int:
     """zs_shard_step that also writes the int8 block-quantized parameter copy
     (param_q8: int8[n]) and its block scales (float32[ceil(n/256)])."""
-    gp = _ptr_array(grads)
-    st = seg_table_ if isinstance(seg_table_, ZsSegTable) else seg_table(seg_table_)
+    pm, pmm, pv, pp, pg, kk, st, hp, keep = _marshal(master, m, v, param_bf16, grads, k, n,
+                                                     seg_table_, hparams_)
+    nn = max(int(n), 0)
+    nb = -(-nn // ZS_Q8_BLOCK)
     rc = load_library().zs_shard_step_q8ag(
-        ctypes.c_void_p(_addr(master)), ctypes.c_void_p(_addr(m)), ctypes.c_void_p(_addr(v)),
-        ctypes.c_void_p(_addr(param_bf16)), ctypes.c_void_p(_addr(param_q8)),
-        ctypes.c_void_p(_addr(param_q8_scale)), ctypes.cast(gp, ctypes.c_void_p),
-        int(len(grads) if k is None else k), int(n), ctypes.byref(st), ctypes.byref(hparams_),
-        int(step), ctypes.c_void_p(_stream_handle(stream)))
+        pm, pmm, pv, pp, ctypes.c_void_p(_dev(param_q8, nn, "param_q8")),
+        ctypes.c_void_p(_dev(param_q8_scale, 4 * nb, "param_q8_scale")), pg, kk, int(n),
+        ctypes.byref(st), ctypes.byref(hp), int(step), ctypes.c_void_p(_stream_handle(stream)))
+    del keep
     if check and rc != ZS_OK:
         raise ZsError(rc, "zs_shard_step_q8ag")
     return rc
@@ -227,15 +275,16 @@ def zs_shard_step_q8grad(master, m, v, param_bf16, qgrads, qscales, k, n, seg_ta
                          step, stream=None, check=True) -> int:
     """zs_shard_step on int8 partials qgrads[j] (int8[n]) with block scales
     qscales[j] (float32[ceil(n/256)])."""
-    qp = _ptr_array(qgrads)
-    sp = _ptr_array(qscales)
-    st = seg_table_ if isinstance(seg_table_, ZsSegTable) else seg_table(seg_table_)
+    nn = max(int(n), 0)
+    nb = -(-nn // ZS_Q8_BLOCK)
+    pm, pmm, pv, pp, _, _, st, hp, _ = _marshal(master, m, v, param_bf16, [], 0, n, seg_table_,
+                                                hparams_)
+    qp = _ptr_array(qgrads, nn, "qgrads")
+    sp = _ptr_array(qscales, 4 * nb, "qscales")
     rc = load_library().zs_shard_step_q8grad(
-        ctypes.c_void_p(_addr(master)), ctypes.c_void_p(_addr(m)), ctypes.c_void_p(_addr(v)),
-        ctypes.c_void_p(_addr(param_bf16)), ctypes.cast(qp, ctypes.c_void_p),
-        ctypes.cast(sp, ctypes.c_void_p), int(len(qgrads) if k is None else k), int(n),
-        ctypes.byref(st), ctypes.byref(hparams_), int(step),
-        ctypes.c_void_p(_stream_handle(stream)))
+        pm, pmm, pv, pp, ctypes.cast(qp, ctypes.c_void_p), ctypes.cast(sp, ctypes.c_void_p),
+        int(len(qgrads) if k is None else k), int(n), ctypes.byref(st), ctypes.byref(hp),
+        int(step), ctypes.c_void_p(_stream_handle(stream)))
     if check and rc != ZS_OK:
         raise ZsError(rc, "zs_shard_step_q8grad")
     return rc
@@ -245,7 +294,7 @@ def zs_shard_step_bf16mv(master, m_bf16, v_bf16, param_bf16, grads, k, n, seg_ta
                          step, stream=None, check=True) -> int:
     """zs_shard_step with bf16 moments m_bf16, v_bf16 (bf16[n], in place)."""
     pm, pmm, pv, pp, pg, kk, st, hp, keep = _marshal(master, m_bf16, v_bf16, param_bf16, grads,
-                                                     k, seg_table_, hparams_)
+                                                     k, n, seg_table_, hparams_, mv_size=2)
     rc = load_library().zs_shard_step_bf16mv(pm, pmm, pv, pp, pg, kk, int(n), ctypes.byref(st),
                                              ctypes.byref(hp), int(step),
                                              ctypes.c_void_p(_stream_handle(stream)))
@@ -309,11 +358,14 @@ def zs_host_shard_step(master, m, v, param_bf16, grads, k, n, segs, hparams_, st
                        nthreads=0, check=True) -> int:
     """Host shard step on host buffers (numpy arrays, CPU tensors or addresses).
     ``segs`` is a list of (start, wd_on) or a ZsSegment array."""
-    gp = (ctypes.c_void_p * max(len(grads), 1))(*[_addr(g) for g in grads])
+    nn = max(int(n), 0)
+    gp = (ctypes.c_void_p * max(len(grads), 1))(
+        *[_host(g, 2 * nn, "grads[%d]" % j) for j, g in enumerate(grads)])
     arr = segs if isinstance(segs, ctypes.Array) else host_segments(segs)
     rc = load_host_library().zs_host_shard_step(
-        ctypes.c_void_p(_addr(master)), ctypes.c_void_p(_addr(m)), ctypes.c_void_p(_addr(v)),
-        ctypes.c_void_p(_addr(param_bf16)), ctypes.cast(gp, ctypes.c_void_p),
+        ctypes.c_void_p(_host(master, 4 * nn, "master")), ctypes.c_void_p(_host(m, 4 * nn, "m")),
+        ctypes.c_void_p(_host(v, 4 * nn, "v")),
+        ctypes.c_void_p(_host(param_bf16, 2 * nn, "param_bf16")), ctypes.cast(gp, ctypes.c_void_p),
         int(len(grads) if k is None else k), int(n), ctypes.cast(arr, ctypes.c_void_p), len(arr),
         ctypes.byref(hparams_), int(step), int(nthreads))
     if check and rc != ZS_OK:

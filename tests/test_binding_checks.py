@@ -1,0 +1,109 @@
+"""The Python binding refuses buffers that would send a host address to the
+GPU kernel (or a device address to the host step), and buffers too small for
+n, before anything reaches the C library (CPU only: no call gets that far)."""
+import numpy as np
+import pytest
+
+import sharded_mixed_precision_shard_amd as zs
+
+
+class FakeGpuTensor:
+    """Stands in for a device tensor: the binding only asks these questions.
+    Its address is null, so even a check that wrongly let it through would
+    meet the library's null-pointer error, never a kernel launch."""
+
+    def __init__(self, nbytes, contiguous=True, addr=0):
+        self._n, self._c, self._a = nbytes, contiguous, addr
+        self.is_cuda = True
+        self.device = "cuda:0"
+
+    def data_ptr(self):
+        return self._a
+
+    def is_contiguous(self):
+        return self._c
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        return 1
+
+
+N = 1000
+HP = zs.hparams()
+
+
+def _dev_args(**over):
+    a = dict(master=FakeGpuTensor(4 * N), m=FakeGpuTensor(4 * N), v=FakeGpuTensor(4 * N),
+             param=FakeGpuTensor(2 * N), grads=[FakeGpuTensor(2 * N), FakeGpuTensor(2 * N)],
+             table=FakeGpuTensor(16))
+    a.update(over)
+    return a
+
+
+def _call(**over):
+    a = _dev_args(**over)
+    return zs.zs_shard_step(a["master"], a["m"], a["v"], a["param"], a["grads"], 2, N,
+                            zs.seg_table(a["table"], 1), HP, 1)
+
+
+def test_host_arrays_are_refused_by_the_gpu_entry_points():
+    with pytest.raises(TypeError, match="host"):
+        _call(master=np.zeros(N, np.float32))
+    with pytest.raises(TypeError, match="host"):
+        _call(grads=[FakeGpuTensor(2 * N), np.zeros(N, np.uint16)])
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError, match="GPU tensor"):
+        _call(v=torch.zeros(N))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        zs.seg_table(torch.zeros(1, 2, dtype=torch.int64))
+
+
+def test_short_or_strided_device_buffers_are_refused():
+    with pytest.raises(ValueError, match="master holds"):
+        _call(master=FakeGpuTensor(4 * N - 4))
+    with pytest.raises(ValueError, match=r"grads\[1\] holds"):
+        _call(grads=[FakeGpuTensor(2 * N), FakeGpuTensor(2 * N - 2)])
+    with pytest.raises(ValueError, match="contiguous"):
+        _call(m=FakeGpuTensor(4 * N, contiguous=False))
+    with pytest.raises(ValueError, match="segment table"):
+        zs.seg_table(FakeGpuTensor(16), 2)
+    # a count the library refuses by itself is passed through (nothing is read)
+    assert zs.seg_table(FakeGpuTensor(16), zs.ZS_MAX_SEGMENTS + 1).count == \
+        zs.ZS_MAX_SEGMENTS + 1
+
+
+def test_variant_buffers_are_sized_by_their_own_types():
+    a = _dev_args()
+    nb = -(-N // zs.ZS_Q8_BLOCK)
+    with pytest.raises(ValueError, match="param_q8 holds"):
+        zs.zs_shard_step_q8ag(a["master"], a["m"], a["v"], a["param"], FakeGpuTensor(N - 1),
+                              FakeGpuTensor(4 * nb), a["grads"], 2, N,
+                              zs.seg_table(a["table"], 1), HP, 1)
+    with pytest.raises(ValueError, match="param_q8_scale holds"):
+        zs.zs_shard_step_q8ag(a["master"], a["m"], a["v"], a["param"], FakeGpuTensor(N),
+                              FakeGpuTensor(4 * nb - 4), a["grads"], 2, N,
+                              zs.seg_table(a["table"], 1), HP, 1)
+    with pytest.raises(ValueError, match=r"qscales\[0\] holds"):
+        zs.zs_shard_step_q8grad(a["master"], a["m"], a["v"], a["param"], [FakeGpuTensor(N)],
+                                [FakeGpuTensor(4 * nb - 1)], 1, N,
+                                zs.seg_table(a["table"], 1), HP, 1)
+    # bf16 moments need 2 bytes per element, not 4
+    with pytest.raises(ValueError, match="v holds"):
+        zs.zs_shard_step_bf16mv(a["master"], FakeGpuTensor(2 * N), FakeGpuTensor(2 * N - 1),
+                                a["param"], a["grads"], 2, N, zs.seg_table(a["table"], 1), HP, 1)
+
+
+def test_host_step_refuses_device_and_short_buffers():
+    w, m, v = (np.zeros(N, np.float32) for _ in range(3))
+    p = np.zeros(N, np.uint16)
+    g = [np.zeros(N, np.uint16)]
+    with pytest.raises(ValueError, match="GPU tensor"):
+        zs.zs_host_shard_step(FakeGpuTensor(4 * N), m, v, p, g, 1, N, [(0, True)], HP, 1)
+    with pytest.raises(ValueError, match="m holds"):
+        zs.zs_host_shard_step(w, np.zeros(N - 1, np.float32), v, p, g, 1, N, [(0, True)], HP, 1)
+    with pytest.raises(ValueError, match="contiguous"):
+        zs.zs_host_shard_step(w, m, np.zeros(2 * N, np.float32)[::2], p, g, 1, N, [(0, True)],
+                              HP, 1)
+    assert zs.zs_host_shard_step(w, m, v, p, g, 1, N, [(0, True)], HP, 1) == zs.ZS_OK
