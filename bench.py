@@ -298,6 +298,9 @@ def offload_main(args):
                      "peak_kind": "measured host copy bandwidth (threaded numpy copy, "
                                   "read + write)"},
         "cpu_baseline": cpu,
+        "speedup_vs_cpu_oracle": None if not cpu else {
+            "single_thread": round(value / cpu["value"], 1),
+            "threaded": round(value / cpu["threaded"]["value"], 1)},
     }
     print(json.dumps(out), flush=True)
 
@@ -498,6 +501,9 @@ def main():
         "kernel_ms": {"median": round(statistics.median(kernel_ms), 4),
                       "min": round(min(kernel_ms), 4), "max": round(max(kernel_ms), 4)},
         "cpu_baseline": cpu,
+        "speedup_vs_cpu_oracle": None if not cpu else {
+            "single_thread": round(value / cpu["value"], 1),
+            "threaded": round(value / cpu["threaded"]["value"], 1)},
     }
     print(json.dumps(out), flush=True)
 

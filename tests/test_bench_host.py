@@ -43,6 +43,8 @@ def test_offload_run_prints_one_json_line():
     cpu = out["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["cores"] == 1 and cpu["value"] > 0
     assert cpu["threaded"]["cores"] >= 1
+    sp = out["speedup_vs_cpu_oracle"]
+    assert abs(sp["single_thread"] - out["value"] / cpu["value"]) <= 0.05 + 1e-3 * sp["single_thread"]
 
 
 def test_cpu_baseline_fields():
