@@ -323,13 +323,16 @@ def main():
     ap.add_argument("--nontemporal", type=int, default=0, help="0 default, 1 on, 2 off")
     ap.add_argument("--groups-per-cu", type=int, default=0,
                     help="cap on resident workgroups per compute unit (0 = default)")
+    ap.add_argument("--block-order", type=int, default=0,
+                    help="0 default, 1 linear, 2 XCD-contiguous chunk order")
     ap.add_argument("--copy-gb", type=float, default=8.0,
                     help="size of the in-run copy-ceiling measurement (0 = skip)")
     args = ap.parse_args()
 
-    if args.variant != "base" and (args.chunk_tiles or args.nontemporal or args.groups_per_cu):
-        ap.error("--chunk-tiles, --nontemporal and --groups-per-cu apply to the base entry "
-                 "point (zs_shard_step_cfg) only")
+    if args.variant != "base" and (args.chunk_tiles or args.nontemporal or args.groups_per_cu
+                                   or args.block_order):
+        ap.error("--chunk-tiles, --nontemporal, --groups-per-cu and --block-order apply to the "
+                 "base entry point (zs_shard_step_cfg) only")
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one rank's shard step on ONE GPU; the shard step has no "
@@ -399,10 +402,11 @@ def main():
                                     stream)
         elif var == "bf16mv":
             zs.zs_shard_step_bf16mv(master, m, v, param, grads, k, n, st, hp, t, stream)
-        elif args.chunk_tiles or args.nontemporal or args.groups_per_cu:
+        elif args.chunk_tiles or args.nontemporal or args.groups_per_cu or args.block_order:
             zs.zs_shard_step_cfg(master, m, v, param, grads, k, n, st, hp, t, stream,
                                  chunk_tiles=args.chunk_tiles, nontemporal=args.nontemporal,
-                                 groups_per_cu=args.groups_per_cu)
+                                 groups_per_cu=args.groups_per_cu,
+                                 block_order=args.block_order)
         else:
             zs.zs_shard_step(master, m, v, param, grads, k, n, st, hp, t, stream)
 
@@ -447,6 +451,8 @@ def main():
     launch_key = "chunk_tiles=%d,nontemporal=%d" % (args.chunk_tiles, args.nontemporal)
     if args.groups_per_cu:
         launch_key += ",groups_per_cu=%d" % args.groups_per_cu
+    if args.block_order:
+        launch_key += ",block_order=%d" % args.block_order
     traffic_key = args.config if var == "base" else "%s/%s" % (args.config, var)
     traffic = measured_traffic(traffic_key, launch_key)
 

@@ -109,7 +109,11 @@ typedef struct {
                               or above the kernel's own occupancy has no effect.  A
                               cap whose LDS share exceeds the per-workgroup limit
                               returns ZS_ERR_INVALID_ARGUMENT. */
-    int32_t reserved;
+    int32_t block_order;  /* 0 = default, 1 = linear (workgroup b takes chunk b),
+                             2 = XCD-contiguous (the workgroups the dispatcher deals to
+                             one XCD take one contiguous run of chunks).  The default
+                             is XCD-contiguous for grids of at least 65536 workgroups
+                             on a part with several XCDs, linear otherwise. */
 } zs_launch_cfg;
 
 /* Prepare the library for one device: records its compute-unit count and

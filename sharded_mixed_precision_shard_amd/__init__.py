@@ -56,7 +56,7 @@ class ZsSegTable(ctypes.Structure):
 
 class ZsLaunchCfg(ctypes.Structure):
     _fields_ = [("chunk_tiles", ctypes.c_int32), ("nontemporal", ctypes.c_int32),
-                ("groups_per_cu", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("groups_per_cu", ctypes.c_int32), ("block_order", ctypes.c_int32)]
 
 
 class ZsError(RuntimeError):
@@ -238,11 +238,11 @@ def zs_shard_step(master, m, v, param_bf16, grads, k, n, seg_table_, hparams_, s
 
 def zs_shard_step_cfg(master, m, v, param_bf16, grads, k, n, seg_table_, hparams_, step,
                       stream=None, chunk_tiles=0, nontemporal=0, groups_per_cu=0,
-                      check=True) -> int:
+                      block_order=0, check=True) -> int:
     """zs_shard_step with an explicit launch geometry (results never change)."""
     pm, pmm, pv, pp, pg, kk, st, hp, keep = _marshal(master, m, v, param_bf16, grads, k, n,
                                                      seg_table_, hparams_)
-    cfg = ZsLaunchCfg(int(chunk_tiles), int(nontemporal), int(groups_per_cu), 0)
+    cfg = ZsLaunchCfg(int(chunk_tiles), int(nontemporal), int(groups_per_cu), int(block_order))
     rc = load_library().zs_shard_step_cfg(pm, pmm, pv, pp, pg, kk, int(n), ctypes.byref(st),
                                           ctypes.byref(hp), int(step),
                                           ctypes.c_void_p(_stream_handle(stream)),

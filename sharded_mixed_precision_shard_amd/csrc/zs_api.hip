@@ -26,7 +26,14 @@ struct DeviceInfo {
     int cus;
     int64_t lds_per_cu;     // bytes of LDS one compute unit holds
     int64_t lds_per_group;  // most LDS bytes one workgroup may take
+    int xcds;               // accelerator complex dies the device's CUs sit on
 };
+
+// Grids at least this large default to the XCD-contiguous chunk order (on
+// MI355X it measured 0-3 % faster on shards of 10^8-10^10 elements and slower
+// on shards that fit the 256 MB last-level cache).
+constexpr int64_t kXcdOrderMinBlocks = 65536;
+constexpr int kCusPerXcd = 32;  // gfx950
 
 DeviceInfo g_dev[kMaxDevices];
 int g_initialized = 0;
@@ -98,16 +105,18 @@ int validate_and_launch(const Request &r) {
     if (r.st->count > ZS_MAX_SEGMENTS) return ZS_ERR_TOO_MANY_SEGMENTS;
     // Streaming (non-temporal) loads and stores by default: nothing is
     // reused, and on MI355X they measured 5-10 % faster than cached access.
-    int chunk_tiles = 0, nt = 1, groups_per_cu = 0;
+    int chunk_tiles = 0, nt = 1, groups_per_cu = 0, block_order = 0;
     if (r.cfg) {
         if (r.cfg->chunk_tiles < 0 || r.cfg->chunk_tiles > kMaxChunkTiles)
             return ZS_ERR_INVALID_ARGUMENT;
         if (r.cfg->nontemporal < 0 || r.cfg->nontemporal > 2) return ZS_ERR_INVALID_ARGUMENT;
         if (r.cfg->groups_per_cu < 0 || r.cfg->groups_per_cu > ZS_MAX_GROUPS_PER_CU)
             return ZS_ERR_INVALID_ARGUMENT;
+        if (r.cfg->block_order < 0 || r.cfg->block_order > 2) return ZS_ERR_INVALID_ARGUMENT;
         chunk_tiles = r.cfg->chunk_tiles;
         nt = r.cfg->nontemporal == 2 ? 0 : 1;
         groups_per_cu = r.cfg->groups_per_cu;
+        block_order = r.cfg->block_order;
     }
     if (r.n == 0) return ZS_OK;
     if (r.n > INT64_MAX / 8) return ZS_ERR_INVALID_ARGUMENT;
@@ -194,6 +203,9 @@ int validate_and_launch(const Request &r) {
         blocks = (n + chunk - 1) / chunk;
     }
     a.chunk = chunk;
+    const bool xcd_order =
+        block_order == 2 || (block_order == 0 && blocks >= kXcdOrderMinBlocks);
+    a.xcds = xcd_order ? g_dev[dev].xcds : 1;
 
     // Occupancy cap: each workgroup reserves 1/groups_per_cu of the unit's
     // LDS (rounded down to 1 KB), so at most groups_per_cu of them fit.  The
@@ -248,6 +260,11 @@ int zs_init(int device_ordinal) {
     g_dev[device_ordinal].cus = prop.multiProcessorCount;
     g_dev[device_ordinal].lds_per_cu = (int64_t)prop.maxSharedMemoryPerMultiProcessor;
     g_dev[device_ordinal].lds_per_group = (int64_t)prop.sharedMemPerBlock;
+    // A whole MI355X has 8 XCDs of 32 CUs; a partition holds fewer.
+    g_dev[device_ordinal].xcds =
+        prop.multiProcessorCount % kCusPerXcd == 0 && prop.multiProcessorCount >= kCusPerXcd
+            ? prop.multiProcessorCount / kCusPerXcd
+            : 1;
     g_dev[device_ordinal].ready = 1;
     g_initialized = 1;
     return ZS_OK;

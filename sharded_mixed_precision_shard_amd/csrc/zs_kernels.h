@@ -41,6 +41,7 @@ struct StepArgs {
     int64_t n;
     int64_t chunk;  // elements per workgroup, a multiple of tile_for(k)
     int32_t nseg;
+    int32_t xcds;   // XCDs the dispatcher deals workgroups to in turn; 1 = linear order
     float lr, b1, b2, c1, c2, bc1, bc2, eps, df, gscale;
 };
 

@@ -325,7 +325,17 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
     const int tid = (int)threadIdx.x;
     const int lane = tid % kWave;
     const int wave = tid / kWave;
-    const int64_t c0 = (int64_t)blockIdx.x * a.chunk;
+    // Chunk order.  The dispatcher deals workgroup b to XCD b % xcds; with
+    // xcds > 1 each XCD is given one contiguous run of the nb = xcds*q + r
+    // chunks (XCD x: q or q + 1 chunks from x*q + min(x, r)), so its L2 sees
+    // a sequential stream; the map is a bijection onto [0, nb).
+    int64_t b = blockIdx.x;
+    if (a.xcds > 1) {
+        const int64_t nb = gridDim.x, q = nb / a.xcds, r = nb % a.xcds;
+        const int64_t x = b % a.xcds, y = b / a.xcds;
+        b = x * q + (x < r ? x : r) + y;
+    }
+    const int64_t c0 = b * a.chunk;
     const int64_t c1 = (c0 + a.chunk < a.n) ? c0 + a.chunk : a.n;
 
     // Every wavefront works on its own windows; there is no workgroup barrier.

@@ -36,9 +36,10 @@ def _dev(torch, a):
 
 
 def _run_both(torch, n, k, segs, steps, seed, hp_kw=None, cfg=None, w0=None, grads_fn=None,
-              ref_segs=None):
+              ref_segs=None, with_oracle=True):
     """Same inputs on GPU and oracle; returns (gpu outputs, oracle outputs).
-    ref_segs: a different (valid) table for the oracle side."""
+    ref_segs: a different (valid) table for the oracle side; with_oracle=False
+    skips the oracle (the second result is then None)."""
     hp_kw = hp_kw or {}
     w = synth.host_normal_f32(n, synth.stream_key(seed, 1, 0, 0), 0, n, 0.02) if w0 is None \
         else w0.copy()
@@ -61,11 +62,13 @@ def _run_both(torch, n, k, segs, steps, seed, hp_kw=None, cfg=None, w0=None, gra
         else:
             zs.zs_shard_step_cfg(dw, dm, dv, dp, dgs, k, n, zs.seg_table(table), hpz, t,
                                  torch.cuda.current_stream(), **cfg)
-        assert oracle.shard_step(*ref, gs, segs if ref_segs is None else ref_segs, hpo, t) == 0
+        if with_oracle:
+            assert oracle.shard_step(*ref, gs, segs if ref_segs is None else ref_segs, hpo,
+                                     t) == 0
     torch.cuda.synchronize()
     got = (dw.cpu().numpy(), dm.cpu().numpy(), dv.cpu().numpy(),
            dp.cpu().numpy().view(np.uint16))
-    return got, ref
+    return got, (ref if with_oracle else None)
 
 
 def _random_segments(rng, n, short_frac=0.5):
@@ -213,6 +216,27 @@ def test_segment_overflow_and_restaging(gpu):
             H.assert_parity(got, ref, "k=%d chunk_tiles=%d" % (k, chunk_tiles))
 
 
+@pytest.mark.parametrize("n", [1, 1023, 1024 * 8 - 5, 1024 * 8 * 9 + 3 * 1024 + 17, 70_000 * 1024 + 333])
+def test_xcd_chunk_order_covers_every_element(gpu, n):
+    """XCD-contiguous order is a bijection of the chunks for any grid size
+    (grids that are and are not multiples of the XCD count, and one above the
+    default threshold): bitwise the same as the linear order."""
+    torch = gpu
+    rng = np.random.default_rng(n % 1000)
+    segs = _random_segments(rng, n, short_frac=0.05)
+    small = n < 2_000_000
+    lin, ref = _run_both(torch, n, 2, segs, range(1, 3), seed=19, cfg=dict(block_order=1),
+                         with_oracle=small)
+    xcd, _ = _run_both(torch, n, 2, segs, range(1, 3), seed=19, cfg=dict(block_order=2),
+                       with_oracle=False)
+    dflt, _ = _run_both(torch, n, 2, segs, range(1, 3), seed=19, with_oracle=False)
+    if small:
+        H.assert_parity(lin, ref, "n=%d linear" % n)
+    for a, b, c in zip(lin, xcd, dflt):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+        assert np.array_equal(a.view(np.uint8), c.view(np.uint8))
+
+
 def test_largest_segment_table(gpu):
     """ZS_MAX_SEGMENTS entries (three rounds of the 64-way search), most of
     them one or two elements long, the last ones past n."""
@@ -259,7 +283,8 @@ def test_launch_geometry_is_bitwise_invariant(gpu):
     outs = []
     for cfg in (dict(), dict(chunk_tiles=1), dict(chunk_tiles=3), dict(chunk_tiles=7),
                 dict(chunk_tiles=64), dict(chunk_tiles=2, nontemporal=1),
-                dict(chunk_tiles=5, nontemporal=2)):
+                dict(chunk_tiles=5, nontemporal=2), dict(block_order=1), dict(block_order=2),
+                dict(block_order=2, chunk_tiles=3), dict(block_order=2, groups_per_cu=4)):
         got, ref = _run_both(torch, n, 5, segs, range(1, 4), seed=3, cfg=cfg or None)
         H.assert_parity(got, ref, str(cfg))
         outs.append(got)
@@ -299,7 +324,8 @@ def test_launch_cfg_errors(gpu):
 
     assert call() == zs.ZS_OK
     for bad in (dict(chunk_tiles=-1), dict(chunk_tiles=4097), dict(nontemporal=3),
-                dict(groups_per_cu=-1), dict(groups_per_cu=zs.ZS_MAX_GROUPS_PER_CU + 1)):
+                dict(groups_per_cu=-1), dict(groups_per_cu=zs.ZS_MAX_GROUPS_PER_CU + 1),
+                dict(block_order=-1), dict(block_order=3)):
         assert call(**bad) == zs.ZS_ERR_INVALID_ARGUMENT, bad
     # a one-workgroup-per-unit cap fits only where one workgroup may take the
     # whole LDS of a unit; either way the call answers synchronously
