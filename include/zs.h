@@ -116,8 +116,9 @@ typedef struct {
                              on a part with several XCDs, linear otherwise. */
 } zs_launch_cfg;
 
-/* Prepare the library for one device: records its compute-unit count and
- * checks that it is a gfx950 part.  Idempotent for the same ordinal.
+/* Prepare the library for one device: records its compute-unit count, its
+ * LDS sizes and its XCD count (compute units / 32), and checks that it is a
+ * gfx950 part.  Idempotent for the same ordinal.
  * Returns ZS_OK, ZS_ERR_INVALID_ARGUMENT (no such device) or
  * ZS_ERR_DEVICE (HIP error, or the device is not gfx950). */
 int zs_init(int device_ordinal);
