@@ -237,6 +237,17 @@ const char *zs_status_string(int status);
 /* The last hipError_t seen by the library on the calling thread (0 = none). */
 int zs_last_device_error(void);
 
+/* The grid a step over n elements with k partials would launch (cfg may be
+ * NULL; only its chunk_tiles matters): *workgroups of 256 threads, each
+ * owning *chunk_elements consecutive elements (the last one fewer).  The
+ * chunk is chunk_tiles tiles of 1024 elements (default 1), doubled as often
+ * as needed to keep workgroups * 256 below 2^32, the largest grid a dispatch
+ * can describe.  Host-only; needs no device and no zs_init.  n == 0 gives 0
+ * and 0.  Returns ZS_OK or ZS_ERR_INVALID_ARGUMENT (k or n out of range,
+ * null output, chunk_tiles out of range). */
+int zs_launch_geometry(int k, int64_t n, const zs_launch_cfg *cfg, int64_t *workgroups,
+                       int64_t *chunk_elements);
+
 /* Bytes one zs_shard_step call moves through HBM, by the algorithm:
  * n * (12 + 2k) read + n * 14 written.  For reporting only. */
 int64_t zs_algorithmic_bytes(int k, int64_t n);

@@ -35,7 +35,7 @@ ZS_ERR_ALIASING = 6
 # Symbols declared in include/zs.h.
 EXPORTS = ("zs_init", "zs_shard_step", "zs_shard_step_cfg", "zs_shard_step_q8ag",
            "zs_shard_step_q8grad", "zs_shard_step_bf16mv", "zs_fini", "zs_status_string",
-           "zs_last_device_error", "zs_algorithmic_bytes")
+           "zs_last_device_error", "zs_algorithmic_bytes", "zs_launch_geometry")
 
 
 class ZsHparams(ctypes.Structure):
@@ -102,6 +102,8 @@ def load_library():
     lib.zs_last_device_error.restype = ctypes.c_int
     lib.zs_algorithmic_bytes.argtypes = [ctypes.c_int, ctypes.c_int64]
     lib.zs_algorithmic_bytes.restype = ctypes.c_int64
+    lib.zs_launch_geometry.argtypes = [ctypes.c_int, ctypes.c_int64, P, P, P]
+    lib.zs_launch_geometry.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -200,6 +202,17 @@ def zs_last_device_error() -> int:
 
 def zs_algorithmic_bytes(k: int, n: int) -> int:
     return load_library().zs_algorithmic_bytes(int(k), int(n))
+
+
+def zs_launch_geometry(k: int, n: int, chunk_tiles: int = 0):
+    """(workgroups, elements per workgroup) of the grid a step would launch."""
+    cfg = ZsLaunchCfg(int(chunk_tiles), 0, 0, 0)
+    wg, ch = ctypes.c_int64(0), ctypes.c_int64(0)
+    rc = load_library().zs_launch_geometry(int(k), int(n), ctypes.byref(cfg), ctypes.byref(wg),
+                                           ctypes.byref(ch))
+    if rc != ZS_OK:
+        raise ZsError(rc, "zs_launch_geometry")
+    return wg.value, ch.value
 
 
 def _marshal(master, m, v, param_bf16, grads, k, n, seg_table_, hparams_, mv_size=4):

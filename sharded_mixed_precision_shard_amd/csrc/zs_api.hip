@@ -50,14 +50,28 @@ bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
     return a0 < b1 && b0 < a1;
 }
 
-int pick_chunk_tiles(int64_t n, int cus) {
-    // One tile per workgroup: the resident workgroups then cover one compact
-    // stretch of every array and sweep through memory together, which
-    // measured best on MI355X for every shard size (longer chunks spread the
-    // active front over more DRAM pages).
-    (void)n;
-    (void)cus;
-    return 1;
+// One tile per workgroup by default: the resident workgroups then cover one
+// compact stretch of every array and sweep through memory together, which
+// measured best on MI355X for every shard size (longer chunks spread the
+// active front over more DRAM pages).
+constexpr int kDefaultChunkTiles = 1;
+
+// A dispatch packet holds the grid size in work-items as a 32-bit number.
+constexpr int64_t kMaxBlocks = 0xffffffffLL / kThreads;
+
+// Elements per workgroup and workgroup count for n elements: chunk_tiles
+// tiles per workgroup (0 = default), doubled until the grid fits.
+void launch_geometry(int k, int64_t n, int chunk_tiles, int64_t *chunk_out,
+                     int64_t *blocks_out) {
+    if (chunk_tiles == 0) chunk_tiles = kDefaultChunkTiles;
+    int64_t chunk = (int64_t)chunk_tiles * tile_for(k);
+    int64_t blocks = (n + chunk - 1) / chunk;
+    while (blocks > kMaxBlocks) {
+        chunk *= 2;
+        blocks = (n + chunk - 1) / chunk;
+    }
+    *chunk_out = chunk;
+    *blocks_out = blocks;
 }
 
 // One call, whatever the variant: the buffers it reads and writes.
@@ -195,13 +209,8 @@ int validate_and_launch(const Request &r) {
     }
     a.gscale = hp->grad_scale;
 
-    if (chunk_tiles == 0) chunk_tiles = pick_chunk_tiles(n, g_dev[dev].cus);
-    int64_t chunk = (int64_t)chunk_tiles * tile_for(r.k);
-    int64_t blocks = (n + chunk - 1) / chunk;
-    while (blocks > 0x7fffffffLL) {  // keep the grid inside the 32-bit limit
-        chunk *= 2;
-        blocks = (n + chunk - 1) / chunk;
-    }
+    int64_t chunk = 0, blocks = 0;
+    launch_geometry(r.k, n, chunk_tiles, &chunk, &blocks);
     a.chunk = chunk;
     const bool xcd_order =
         block_order == 2 || (block_order == 0 && blocks >= kXcdOrderMinBlocks);
@@ -344,6 +353,25 @@ const char *zs_status_string(int status) {
 }
 
 int zs_last_device_error(void) { return t_last_hip_error; }
+
+int zs_launch_geometry(int k, int64_t n, const zs_launch_cfg *cfg, int64_t *workgroups,
+                       int64_t *chunk_elements) {
+    if (k < 1 || k > ZS_MAX_K || n < 0 || n > INT64_MAX / 8 || !workgroups || !chunk_elements)
+        return ZS_ERR_INVALID_ARGUMENT;
+    int chunk_tiles = 0;
+    if (cfg) {
+        if (cfg->chunk_tiles < 0 || cfg->chunk_tiles > kMaxChunkTiles)
+            return ZS_ERR_INVALID_ARGUMENT;
+        chunk_tiles = cfg->chunk_tiles;
+    }
+    if (n == 0) {
+        *workgroups = 0;
+        *chunk_elements = 0;
+        return ZS_OK;
+    }
+    launch_geometry(k, n, chunk_tiles, chunk_elements, workgroups);
+    return ZS_OK;
+}
 
 int64_t zs_algorithmic_bytes(int k, int64_t n) {
     if (k < 1 || n < 0) return 0;

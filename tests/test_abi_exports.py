@@ -102,3 +102,32 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(zs, "LIB_PATH", "/nonexistent/libzs.so")
     with pytest.raises(ImportError):
         zs.load_library()
+
+
+def test_launch_geometry_keeps_the_grid_describable():
+    """The grid a step launches (host-only query, no device): one 1024-element
+    tile per workgroup by default, chunks doubled once workgroups * 256 would
+    reach 2^32, every element covered exactly once."""
+    tile = 1024
+    assert zs.zs_launch_geometry(2, 0) == (0, 0)
+    assert zs.zs_launch_geometry(2, 1) == (1, tile)
+    assert zs.zs_launch_geometry(8, 8_053_473_280) == (7_864_720, tile)
+    assert zs.zs_launch_geometry(2, 5 * tile + 1, chunk_tiles=3) == (2, 3 * tile)
+    limit = (2 ** 32 - 1) // 256
+    for n in (limit * tile, limit * tile + 1, 17_500_000_000, 18 * 10 ** 9, 2 ** 40 + 3):
+        wg, chunk = zs.zs_launch_geometry(1, n)
+        assert wg * 256 < 2 ** 32, n
+        assert chunk % tile == 0 and (chunk // tile) & (chunk // tile - 1) == 0, n
+        assert (wg - 1) * chunk < n <= wg * chunk, n
+    assert zs.zs_launch_geometry(1, limit * tile)[1] == tile
+    assert zs.zs_launch_geometry(1, limit * tile + 1)[1] == 2 * tile
+    lib = zs.load_library()
+    out = ctypes.c_int64(0)
+    assert lib.zs_launch_geometry(0, 10, None, ctypes.byref(out), ctypes.byref(out)) == \
+        zs.ZS_ERR_INVALID_ARGUMENT
+    assert lib.zs_launch_geometry(1, -1, None, ctypes.byref(out), ctypes.byref(out)) == \
+        zs.ZS_ERR_INVALID_ARGUMENT
+    assert lib.zs_launch_geometry(1, 10, None, None, ctypes.byref(out)) == \
+        zs.ZS_ERR_INVALID_ARGUMENT
+    with pytest.raises(zs.ZsError):
+        zs.zs_launch_geometry(1, 10, chunk_tiles=4097)
