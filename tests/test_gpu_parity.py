@@ -421,6 +421,60 @@ def test_side_stream(gpu):
     H.assert_parity(got, ref, "side stream")
 
 
+def test_concurrent_calls_from_threads_and_streams(gpu):
+    """Four host threads, each with its own stream and buffers, call the step
+    at the same time (the library keeps no mutable state after zs_init);
+    every thread's result equals the oracle's."""
+    import threading
+    torch = gpu
+    jobs = []
+    for j in range(4):
+        n = 40_000 + 777 * j
+        rng = np.random.default_rng(100 + j)
+        segs = _random_segments(rng, n, short_frac=0.2)
+        w0 = rng.normal(0, 0.02, n).astype(F32)
+        gs = [[(rng.normal(0, 1e-2, n).astype(F32).view(np.uint32) >> 16).astype(np.uint16)
+               for _ in range(j + 1)] for _ in range(3)]
+        jobs.append(dict(n=n, k=j + 1, segs=segs, w0=w0, gs=gs))
+    dev = []
+    for jb in jobs:
+        n = jb["n"]
+        dev.append(dict(w=_dev(torch, jb["w0"]), m=torch.zeros(n, device="cuda"),
+                        v=torch.zeros(n, device="cuda"),
+                        p=torch.zeros(n, dtype=torch.int16, device="cuda"),
+                        g=[[_dev(torch, g) for g in step] for step in jb["gs"]],
+                        table=H.segment_tensor(jb["segs"], "cuda"), stream=torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    errors = []
+    start = threading.Barrier(len(jobs))
+
+    def run(jb, d):
+        try:
+            start.wait()
+            for t in range(1, 4):
+                zs.zs_shard_step(d["w"], d["m"], d["v"], d["p"], d["g"][t - 1], jb["k"], jb["n"],
+                                 zs.seg_table(d["table"]), zs.hparams(), t, d["stream"])
+            d["stream"].synchronize()
+        except Exception as e:  # noqa: BLE001 - reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(jb, d)) for jb, d in zip(jobs, dev)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=60)
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for jb, d in zip(jobs, dev):
+        n = jb["n"]
+        ref = [jb["w0"].copy(), np.zeros(n, F32), np.zeros(n, F32), np.zeros(n, np.uint16)]
+        for t in range(1, 4):
+            assert oracle.shard_step(*ref, jb["gs"][t - 1], jb["segs"], oracle.hparams(), t) == 0
+        got = (d["w"].cpu().numpy(), d["m"].cpu().numpy(), d["v"].cpu().numpy(),
+               d["p"].cpu().numpy().view(np.uint16))
+        H.assert_parity(got, ref, "thread k=%d" % jb["k"])
+
+
 # ------------------------------------------------------- model-shaped shards
 
 def test_gpt2_small_rank0_full_shard(gpu):
