@@ -246,9 +246,8 @@ def offload_main(args):
     m = np.zeros(n, np.float32)
     v = np.zeros(n, np.float32)
     p = np.zeros(n, np.uint16)
-    m.fill(0.0)
-    v.fill(0.0)
-    p.fill(0)
+    for a in (m, v, p):  # np.zeros maps pages lazily: touch them before anything is timed
+        a.fill(0)
     grads = synth.host_grads(w, w.t0, threads=threads)
     log("host inputs generated")
     segs = zs.host_segments(w.shard.segments)
