@@ -346,6 +346,21 @@ def test_hparam_variants(gpu):
         H.assert_parity(got, ref, str(hp))
 
 
+@pytest.mark.parametrize("hp,ts", [
+    (dict(lr=1.0, weight_decay=1.0), (1, 2, 3)),                 # df = 0: decayed weights -> 0
+    (dict(beta1=0.999999, beta2=0.999999), (1, 2)),              # corrections near 1e-6
+    (dict(eps=1e-45), (1, 2, 3)),                                # subnormal epsilon
+    (dict(grad_scale=0.0), (1, 2)),                              # every gradient scaled to 0
+    (dict(lr=3e-4, beta1=0.5, beta2=0.25), (10 ** 9, 10 ** 9 + 1)),  # huge t
+])
+def test_extreme_hyperparameters(gpu, hp, ts):
+    rng = np.random.default_rng(20)
+    n = 20_011
+    segs = _random_segments(rng, n, short_frac=0.2)
+    got, ref = _run_both(gpu, n, 3, segs, ts, seed=20, hp_kw=hp)
+    H.assert_parity(got, ref, str(hp))
+
+
 def test_bias_correction_limit_steps(gpu):
     """t = 10000, 10001, 10002: bias corrections are exactly 1."""
     rng = np.random.default_rng(10)
