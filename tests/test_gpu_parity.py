@@ -361,6 +361,19 @@ def test_extreme_hyperparameters(gpu, hp, ts):
     H.assert_parity(got, ref, str(hp))
 
 
+def test_zero_epsilon_with_zero_gradient_is_nan_on_both_sides(gpu):
+    """The degenerate case of the update: eps = 0, m = v = 0 and a zero
+    gradient give 0/0; both sides produce NaN weights and the canonical bf16
+    NaN, and zero moments."""
+    n = 3000
+    zeros = lambda t: [np.zeros(n, np.uint16) for _ in range(2)]  # noqa: E731
+    got, ref = _run_both(gpu, n, 2, [(0, True), (1000, False)], (1, 2), seed=21,
+                         hp_kw=dict(eps=0.0), grads_fn=zeros)
+    H.assert_parity(got, ref, "eps=0, g=0")
+    assert np.isnan(got[0]).all() and (got[3] == 0x7FC0).all()
+    assert not got[1].any() and not got[2].any()
+
+
 def test_bias_correction_limit_steps(gpu):
     """t = 10000, 10001, 10002: bias corrections are exactly 1."""
     rng = np.random.default_rng(10)
