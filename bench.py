@@ -324,6 +324,9 @@ def main():
                     help="cap on resident workgroups per compute unit (0 = default)")
     ap.add_argument("--block-order", type=int, default=0,
                     help="0 default, 1 linear, 2 XCD-contiguous chunk order")
+    ap.add_argument("--graph", action="store_true",
+                    help="record the timed steps into one HIP graph and launch it once "
+                         "(per-launch times are then the graph's average per step)")
     ap.add_argument("--copy-gb", type=float, default=8.0,
                     help="size of the in-run copy-ceiling measurement (0 = skip)")
     args = ap.parse_args()
@@ -393,21 +396,21 @@ def main():
     stream = torch.cuda.current_stream()
     synth.dev_master(w, master)
 
-    def step(t):
+    def step(t, on=None):
+        on = stream if on is None else on
         if var == "q8ag":
-            zs.zs_shard_step_q8ag(master, m, v, param, q8, q8s, grads, k, n, st, hp, t, stream)
+            zs.zs_shard_step_q8ag(master, m, v, param, q8, q8s, grads, k, n, st, hp, t, on)
         elif var == "q8grad":
-            zs.zs_shard_step_q8grad(master, m, v, param, qgrads, qscales, k, n, st, hp, t,
-                                    stream)
+            zs.zs_shard_step_q8grad(master, m, v, param, qgrads, qscales, k, n, st, hp, t, on)
         elif var == "bf16mv":
-            zs.zs_shard_step_bf16mv(master, m, v, param, grads, k, n, st, hp, t, stream)
+            zs.zs_shard_step_bf16mv(master, m, v, param, grads, k, n, st, hp, t, on)
         elif args.chunk_tiles or args.nontemporal or args.groups_per_cu or args.block_order:
-            zs.zs_shard_step_cfg(master, m, v, param, grads, k, n, st, hp, t, stream,
+            zs.zs_shard_step_cfg(master, m, v, param, grads, k, n, st, hp, t, on,
                                  chunk_tiles=args.chunk_tiles, nontemporal=args.nontemporal,
                                  groups_per_cu=args.groups_per_cu,
                                  block_order=args.block_order)
         else:
-            zs.zs_shard_step(master, m, v, param, grads, k, n, st, hp, t, stream)
+            zs.zs_shard_step(master, m, v, param, grads, k, n, st, hp, t, on)
 
     def fill(t):
         if var == "q8grad":
@@ -429,18 +432,38 @@ def main():
         t += 1
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_begin = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step(t)
-        ends[i].record(stream)
-        t += 1
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_begin
-    kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    if args.graph:
+        # the K timed steps (each with its own t) recorded once into a HIP graph,
+        # then launched as one: no host launch cost between the kernels
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream()
+            for i in range(args.steps):
+                step(t + i, cap)
+        t += args.steps
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_begin = time.perf_counter()
+        g0.record(stream)
+        graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t_begin
+        kernel_ms = [g0.elapsed_time(g1) / args.steps] * args.steps
+        del graph
+    else:
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t_begin = time.perf_counter()
+        for i in range(args.steps):
+            starts[i].record(stream)
+            step(t)
+            ends[i].record(stream)
+            t += 1
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t_begin
+        kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_ms = sum(kernel_ms) / len(kernel_ms)
     log("kernel ms per launch: avg %.4f min %.4f max %.4f" % (avg_ms, min(kernel_ms),
                                                               max(kernel_ms)))
@@ -502,6 +525,8 @@ def main():
             "traffic": traffic,
             "kernel": "shard_step_kernel<K=%d,%s>" % (k, var),
             "avg_launch_ms": round(avg_ms, 4),
+            "timing": "one HIP graph of the timed steps, average per step" if args.graph
+                      else "HIP events around each launch on the launch stream",
         },
         "kernel_ms": {"median": round(statistics.median(kernel_ms), 4),
                       "min": round(min(kernel_ms), 4), "max": round(max(kernel_ms), 4)},
