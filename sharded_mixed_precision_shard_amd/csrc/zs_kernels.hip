@@ -12,12 +12,15 @@
 // byte), so there is no MFMA here.  Design for CDNA4:
 //   * a wavefront's window is Q sub-windows of 256 elements (Q = 1, measured
 //     best; a workgroup tile is four windows); lane l owns elements
-//     4l..4l+3 of each sub-window.  Every load and store
-//     instruction of a wavefront is then one dense, contiguous run (1 KB per
-//     fp32 array, 512 B per bf16 array) of 16-byte (fp32) or 8-byte (bf16)
-//     accesses, and every byte is read once and written once;
-//   * a workgroup owns a contiguous chunk of tiles (one tile by default: the
-//     resident workgroups then sweep memory as one compact front);
+//     4l..4l+3 of each sub-window.  Every load and store instruction of a
+//     wavefront is then one dense, contiguous run (1 KB per fp32 array, 512 B
+//     per bf16 array) of 16-byte (fp32) or 8-byte (bf16) accesses, and every
+//     byte is read once and written once;
+//   * a workgroup owns a contiguous chunk of tiles (one tile by default); on
+//     large grids the chunks are ordered so that the workgroups the
+//     dispatcher deals to one XCD take one contiguous run, giving each XCD's
+//     L2 a sequential stream (eight fronts sweep the arrays), on small grids
+//     linearly (one front);
 //   * every wavefront resolves the weight-decay flags of its own window, with
 //     no workgroup barrier and after issuing its loads (so the lookup
 //     overlaps them): a 64-way search of the device table finds the entry
