@@ -125,8 +125,10 @@ int zs_init(int device_ordinal);
 
 /*
  * Enqueue one shard step on `stream` (a hipStream_t; NULL = the null
- * stream).  Asynchronous: returns once the kernel is enqueued; faults during
- * execution surface at the caller's next synchronisation of the stream.
+ * stream).  The step runs on the calling thread's current device, which
+ * zs_init must have prepared; the stream and every buffer must belong to it.
+ * Asynchronous: returns once the kernel is enqueued; faults during execution
+ * surface at the caller's next synchronisation of the stream.
  *
  *   master, m, v : DEVICE fp32 [n], read and updated in place
  *   param_bf16   : DEVICE bf16 [n] (raw 16-bit patterns), written only
