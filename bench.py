@@ -284,7 +284,8 @@ def offload_main(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32 state, bf16 partials and param",
+        "dtype": "f32",
+        "storage": "f32 master/m/v, bf16 partials and param",
         "data": "synthetic (seeded SplitMix64 / Irwin-Hall draws)",
         "config": {"workload": w.name, "entry_point": "zs_host_shard_step", "shard_params": n,
                    "k_partials": k, "segments": len(w.shard.segments),
@@ -497,10 +498,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"base": "f32 state, bf16 partials and param",
-                  "q8ag": "f32 state, bf16 partials and param, int8 param copy",
-                  "q8grad": "f32 state, int8 partials, bf16 param",
-                  "bf16mv": "f32 master, bf16 m/v, partials and param"}[var],
+        "dtype": "f32",
+        "storage": {"base": "f32 master/m/v, bf16 partials and param",
+                    "q8ag": "f32 master/m/v, bf16 partials and param, int8 param copy",
+                    "q8grad": "f32 master/m/v, int8 partials, bf16 param",
+                    "bf16mv": "f32 master, bf16 m/v, partials and param"}[var],
         "data": "synthetic (seeded SplitMix64 / Irwin-Hall draws; partials of the first "
                 "measured step kept resident across timed steps)",
         "config": {

@@ -38,6 +38,7 @@ def test_offload_run_prints_one_json_line():
                 "roofline", "cpu_baseline"):
         assert key in out, key
     assert out["steps"] == 3 and out["warmup"] == 1 and out["value"] > 0
+    assert out["dtype"] == "f32"
     assert out["config"]["workload"].startswith("tiny")
     assert 0 < out["roofline"]["frac"] and out["roofline"]["unit"] == "GB/s"
     cpu = out["cpu_baseline"]

@@ -32,6 +32,7 @@ def test_bench_line(extra):
     assert out["n_gpus"] == 1 and out["steps"] == 5 and out["warmup"] == 1
     assert out["value"] > 0 and out["ms_per_step"] > 0 and out["higher_is_better"] is True
     assert out["config"]["workload"].startswith("tiny")
+    assert out["dtype"] == "f32" and "bf16" in out["storage"]
     r = out["roofline"]
     assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["unit"] == "GB/s"
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
