@@ -1,0 +1,66 @@
+"""The kernel's fp32 -> bf16 cast over all 2^32 fp32 bit patterns, pinned to
+torch's CPU conversion (a library routine, not the oracle).
+
+With lr = 0, weight_decay = 0, zero gradients, zero moments and eps = 1 the
+update is the identity (u = 0 / (0 + 1) = 0, w' = w * 1 - 0), so after one
+step master must hold its input bit for bit (denormals, signed zeros and
+infinities included; NaNs stay NaN), m and v must stay 0, and param must be
+round-to-nearest-even of the input, every NaN giving 0x7FC0."""
+import numpy as np
+import pytest
+
+import sharded_mixed_precision_shard_amd as zs
+from tests import _gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+CHUNK = 1 << 28
+
+
+@pytest.fixture(scope="module")
+def gpu():
+    import torch
+    assert torch.cuda.is_available()
+    torch.cuda.set_device(0)
+    assert zs.zs_init(0) == zs.ZS_OK
+    yield torch
+    torch.cuda.synchronize()
+
+
+def test_every_fp32_pattern(gpu):
+    torch = gpu
+    n = CHUNK
+    dw = torch.empty(n, dtype=torch.int32, device="cuda")
+    dm = torch.zeros(n, dtype=torch.float32, device="cuda")
+    dv = torch.zeros(n, dtype=torch.float32, device="cuda")
+    dp = torch.empty(n, dtype=torch.int16, device="cuda")
+    dg = [torch.zeros(n, dtype=torch.int16, device="cuda") for _ in range(2)]
+    # both decay branches (df = 1 - 0 * 0 = 1 either way)
+    table = H.segment_tensor([(0, True), (n // 3, False), (n // 2, True), (n // 2 + 1, False)],
+                             "cuda")
+    hp = zs.hparams(lr=0.0, beta1=0.9, beta2=0.95, eps=1.0, weight_decay=0.0)
+    base = torch.arange(n, dtype=torch.int64, device="cuda")
+    for c in range(1 << 32 >> 28):
+        lo = c * n
+        vals = base + lo  # the uint32 patterns lo .. lo + n - 1, as int32 bit patterns
+        dw.copy_(torch.where(vals >= 1 << 31, vals - (1 << 32), vals).to(torch.int32))
+        del vals
+        dm.zero_()
+        dv.zero_()
+        zs.zs_shard_step(dw.view(torch.float32), dm, dv, dp, dg, 2, n, zs.seg_table(table), hp,
+                         1, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        w_in = np.arange(lo, lo + n, dtype=np.uint32)
+        w_out = dw.cpu().numpy().view(np.uint32)
+        p_out = dp.cpu().numpy().view(np.uint16)
+        f_in = w_in.view(np.float32)
+        nan = np.isnan(f_in)
+        assert np.array_equal(w_out[~nan], w_in[~nan]), "chunk %d: master changed" % c
+        assert np.isnan(w_out.view(np.float32)[nan]).all(), "chunk %d: NaN lost" % c
+        assert not dm.any().item() and not dv.any().item(), "chunk %d: moments moved" % c
+        want = torch.from_numpy(f_in.copy()).to(torch.bfloat16).view(torch.int16).numpy()
+        want = want.view(np.uint16).copy()
+        want[nan] = 0x7FC0
+        bad = p_out != want
+        assert not bad.any(), "chunk %d: %d patterns cast differently, first %#010x" % (
+            c, int(bad.sum()), int(w_in[np.argmax(bad)]))
