@@ -64,3 +64,42 @@ def test_every_fp32_pattern(gpu):
         bad = p_out != want
         assert not bad.any(), "chunk %d: %d patterns cast differently, first %#010x" % (
             c, int(bad.sum()), int(w_in[np.argmax(bad)]))
+
+
+def test_every_pair_of_bf16_partials(gpu):
+    """The reduce over all 2^32 pairs (G0, G1) of bf16 partials, pinned to
+    numpy's binary32 addition: with beta1 = 0 and zero moments the new first
+    moment is 0 + 1 * g, so m exposes fp32(G0) + fp32(G1) (NaNs compared as
+    NaN).  lr = 0 keeps the weights finite."""
+    torch = gpu
+    n = CHUNK
+    dw = torch.zeros(n, dtype=torch.float32, device="cuda")
+    dm = torch.empty(n, dtype=torch.float32, device="cuda")
+    dv = torch.empty(n, dtype=torch.float32, device="cuda")
+    dp = torch.empty(n, dtype=torch.int16, device="cuda")
+    g0 = torch.empty(n, dtype=torch.int16, device="cuda")
+    g1 = torch.empty(n, dtype=torch.int16, device="cuda")
+    table = H.segment_tensor([(0, False)], "cuda")
+    hp = zs.hparams(lr=0.0, beta1=0.0, beta2=0.5, eps=1.0, weight_decay=0.0)
+    low = torch.arange(1 << 16, dtype=torch.int32, device="cuda")
+    low16 = torch.where(low >= 1 << 15, low - (1 << 16), low).to(torch.int16)
+    for c in range(1 << 32 >> 28):
+        hi0 = c << 12  # G0 takes the values hi0 .. hi0 + 4095, each against every G1
+        h = torch.arange(hi0, hi0 + (n >> 16), dtype=torch.int32, device="cuda")
+        h16 = torch.where(h >= 1 << 15, h - (1 << 16), h).to(torch.int16)
+        g0.copy_(h16.repeat_interleave(1 << 16))
+        g1.copy_(low16.repeat(n >> 16))
+        dm.zero_()
+        dv.zero_()
+        zs.zs_shard_step(dw, dm, dv, dp, [g0, g1], 2, n, zs.seg_table(table), hp, 1,
+                         torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        a = np.repeat(np.arange(hi0, hi0 + (n >> 16), dtype=np.uint32) << 16, 1 << 16)
+        b = np.tile(np.arange(1 << 16, dtype=np.uint32) << 16, n >> 16)
+        with np.errstate(invalid="ignore", over="ignore"):
+            want = np.float32(0.0) + (a.view(np.float32) + b.view(np.float32))
+        got = dm.cpu().numpy()
+        nan = np.isnan(want)
+        assert np.array_equal(np.isnan(got), nan), "chunk %d: NaN pattern differs" % c
+        same = got.view(np.uint32)[~nan] == want.view(np.uint32)[~nan]
+        assert same.all(), "chunk %d: %d sums differ" % (c, int((~same).sum()))
