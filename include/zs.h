@@ -101,14 +101,15 @@ typedef struct {
     int32_t chunk_tiles;  /* tiles per workgroup (1..4096); a tile is 1024 elements */
     int32_t nontemporal;  /* 0 = default (streaming), 1 = streaming (non-temporal)
                              loads/stores, 2 = ordinary cached loads/stores */
-    int32_t groups_per_cu; /* 0 = as many resident workgroups per compute unit as
-                              fit (default); 1..ZS_MAX_GROUPS_PER_CU caps them by
-                              reserving that share of the unit's LDS per workgroup.
-                              Fewer requests in flight can relieve DRAM congestion
-                              on some physical placements of the arrays; a cap at
-                              or above the kernel's own occupancy has no effect.  A
-                              cap whose LDS share exceeds the per-workgroup limit
-                              returns ZS_ERR_INVALID_ARGUMENT. */
+    int32_t groups_per_cu; /* 1..ZS_MAX_GROUPS_PER_CU caps resident workgroups per
+                              compute unit by reserving that share of the unit's LDS
+                              per workgroup; ZS_MAX_GROUPS_PER_CU never binds (no
+                              cap).  Fewer requests in flight relieve DRAM
+                              congestion on many physical placements of the arrays.
+                              0 = default: a cap of 5 for grids of 65536 to 4194303
+                              workgroups (shards of about 6.7e7 to 4.3e9 elements),
+                              none otherwise.  A cap whose LDS share exceeds the
+                              per-workgroup limit returns ZS_ERR_INVALID_ARGUMENT. */
     int32_t block_order;  /* 0 = default, 1 = linear (workgroup b takes chunk b),
                              2 = XCD-contiguous (the workgroups the dispatcher deals to
                              one XCD take one contiguous run of chunks).  The default

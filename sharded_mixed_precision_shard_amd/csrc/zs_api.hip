@@ -33,6 +33,14 @@ struct DeviceInfo {
 // MI355X it measured 0-3 % faster on shards of 10^8-10^10 elements and slower
 // on shards that fit the 256 MB last-level cache).
 constexpr int64_t kXcdOrderMinBlocks = 65536;
+
+// Default occupancy cap for grids in [kXcdOrderMinBlocks, kCapMaxBlocks):
+// 5 resident workgroups per CU measured 0-8 % faster on shards of 1-6 x 10^9
+// elements on MI355X (most on placements where DRAM queues congest), but
+// 3-6 % slower on the 8 x 10^9-element 70B shard, which needs the full depth
+// of requests in flight.
+constexpr int64_t kCapMaxBlocks = int64_t(1) << 22;
+constexpr int kDefaultCap = 5;
 constexpr int kCusPerXcd = 32;  // gfx950
 
 DeviceInfo g_dev[kMaxDevices];
@@ -215,6 +223,8 @@ int validate_and_launch(const Request &r) {
     const bool xcd_order =
         block_order == 2 || (block_order == 0 && blocks >= kXcdOrderMinBlocks);
     a.xcds = xcd_order ? g_dev[dev].xcds : 1;
+    if (groups_per_cu == 0 && blocks >= kXcdOrderMinBlocks && blocks < kCapMaxBlocks)
+        groups_per_cu = kDefaultCap;
 
     // Occupancy cap: each workgroup reserves 1/groups_per_cu of the unit's
     // LDS (rounded down to 1 KB), so at most groups_per_cu of them fit.  The
