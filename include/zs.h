@@ -108,7 +108,8 @@ typedef struct {
                               congestion on many physical placements of the arrays.
                               0 = default: a cap of 5 for grids of 65536 to 4194303
                               workgroups (shards of about 6.7e7 to 4.3e9 elements),
-                              none otherwise.  A cap whose LDS share exceeds the
+                              none otherwise; zs_shard_step_bf16mv never caps by
+                              default.  A cap whose LDS share exceeds the
                               per-workgroup limit returns ZS_ERR_INVALID_ARGUMENT. */
     int32_t block_order;  /* 0 = default, 1 = linear (workgroup b takes chunk b),
                              2 = XCD-contiguous (the workgroups the dispatcher deals to

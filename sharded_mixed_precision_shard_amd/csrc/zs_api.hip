@@ -38,7 +38,8 @@ constexpr int64_t kXcdOrderMinBlocks = 65536;
 // 5 resident workgroups per CU measured 0-8 % faster on shards of 1-6 x 10^9
 // elements on MI355X (most on placements where DRAM queues congest), but
 // 3-6 % slower on the 8 x 10^9-element 70B shard, which needs the full depth
-// of requests in flight.
+// of requests in flight, and 0-1 % slower for the bf16-moment variant (fewer
+// bytes per element), which therefore keeps no default cap.
 constexpr int64_t kCapMaxBlocks = int64_t(1) << 22;
 constexpr int kDefaultCap = 5;
 constexpr int kCusPerXcd = 32;  // gfx950
@@ -223,7 +224,8 @@ int validate_and_launch(const Request &r) {
     const bool xcd_order =
         block_order == 2 || (block_order == 0 && blocks >= kXcdOrderMinBlocks);
     a.xcds = xcd_order ? g_dev[dev].xcds : 1;
-    if (groups_per_cu == 0 && blocks >= kXcdOrderMinBlocks && blocks < kCapMaxBlocks)
+    if (groups_per_cu == 0 && blocks >= kXcdOrderMinBlocks && blocks < kCapMaxBlocks &&
+        !(r.variant & kMvBf16))
         groups_per_cu = kDefaultCap;
 
     // Occupancy cap: each workgroup reserves 1/groups_per_cu of the unit's
