@@ -397,21 +397,23 @@ def main():
     stream = torch.cuda.current_stream()
     synth.dev_master(w, master)
 
+    # the call is checked and marshalled once; each step passes t and the stream
+    if var == "q8grad":
+        call = zs.ShardStep(master, m, v, param, qgrads, n, st, hp, variant="q8grad",
+                            qscales=qscales)
+    elif var == "q8ag":
+        call = zs.ShardStep(master, m, v, param, grads, n, st, hp, variant="q8ag",
+                            param_q8=q8, param_q8_scale=q8s)
+    elif var == "bf16mv":
+        call = zs.ShardStep(master, m, v, param, grads, n, st, hp, variant="bf16mv")
+    else:
+        cfg = dict(chunk_tiles=args.chunk_tiles, nontemporal=args.nontemporal,
+                   groups_per_cu=args.groups_per_cu, block_order=args.block_order)
+        call = zs.ShardStep(master, m, v, param, grads, n, st, hp,
+                            cfg=cfg if any(cfg.values()) else None)
+
     def step(t, on=None):
-        on = stream if on is None else on
-        if var == "q8ag":
-            zs.zs_shard_step_q8ag(master, m, v, param, q8, q8s, grads, k, n, st, hp, t, on)
-        elif var == "q8grad":
-            zs.zs_shard_step_q8grad(master, m, v, param, qgrads, qscales, k, n, st, hp, t, on)
-        elif var == "bf16mv":
-            zs.zs_shard_step_bf16mv(master, m, v, param, grads, k, n, st, hp, t, on)
-        elif args.chunk_tiles or args.nontemporal or args.groups_per_cu or args.block_order:
-            zs.zs_shard_step_cfg(master, m, v, param, grads, k, n, st, hp, t, on,
-                                 chunk_tiles=args.chunk_tiles, nontemporal=args.nontemporal,
-                                 groups_per_cu=args.groups_per_cu,
-                                 block_order=args.block_order)
-        else:
-            zs.zs_shard_step(master, m, v, param, grads, k, n, st, hp, t, on)
+        call(t, stream if on is None else on)
 
     def fill(t):
         if var == "q8grad":

@@ -317,6 +317,71 @@ def zs_shard_step_bf16mv(master, m_bf16, v_bf16, param_bf16, grads, k, n, seg_ta
     return rc
 
 
+class ShardStep:
+    """One rank's step with its buffers fixed: the arguments are checked and
+    marshalled once, and each call passes only the step t and the stream to
+    the C ABI (include/zs.h) -- for loops that call the step many times on
+    the same state.  ``variant`` is "base" (zs_shard_step, or
+    zs_shard_step_cfg when ``cfg`` is given as a dict of ZsLaunchCfg fields),
+    "q8ag" (needs ``param_q8`` and ``param_q8_scale``), "q8grad" (``grads``
+    are the int8 partials, ``qscales`` their block scales) or "bf16mv" (m and
+    v are bf16).  The tensors are referenced for the object's lifetime."""
+
+    def __init__(self, master, m, v, param_bf16, grads, n, seg_table_, hparams_,
+                 variant="base", param_q8=None, param_q8_scale=None, qscales=None, cfg=None):
+        lib = load_library()
+        self._keep = [master, m, v, param_bf16, list(grads), seg_table_, param_q8,
+                      param_q8_scale, qscales]
+        self.n = int(n)
+        nn = max(self.n, 0)
+        nb = -(-nn // ZS_Q8_BLOCK)
+        k = len(grads)
+        if variant == "q8grad":
+            pm, pmm, pv, pp, _, _, st, hp, _ = _marshal(master, m, v, param_bf16, [], 0, n,
+                                                        seg_table_, hparams_)
+            qp = _ptr_array(grads, nn, "qgrads")
+            sp = _ptr_array(qscales or [], 4 * nb, "qscales")
+            if len(qscales or []) != k:
+                raise ValueError("q8grad needs one scale array per int8 partial")
+            self._c = (qp, sp)
+            head = [pm, pmm, pv, pp, ctypes.cast(qp, ctypes.c_void_p),
+                    ctypes.cast(sp, ctypes.c_void_p)]
+            fn = lib.zs_shard_step_q8grad
+        else:
+            mv = 2 if variant == "bf16mv" else 4
+            pm, pmm, pv, pp, pg, _, st, hp, gp = _marshal(master, m, v, param_bf16, grads, k, n,
+                                                          seg_table_, hparams_, mv_size=mv)
+            self._c = (gp,)
+            if variant == "q8ag":
+                head = [pm, pmm, pv, pp, ctypes.c_void_p(_dev(param_q8, nn, "param_q8")),
+                        ctypes.c_void_p(_dev(param_q8_scale, 4 * nb, "param_q8_scale")), pg]
+                fn = lib.zs_shard_step_q8ag
+            elif variant == "bf16mv":
+                head, fn = [pm, pmm, pv, pp, pg], lib.zs_shard_step_bf16mv
+            elif variant == "base":
+                head = [pm, pmm, pv, pp, pg]
+                fn = lib.zs_shard_step_cfg if cfg else lib.zs_shard_step
+            else:
+                raise ValueError("unknown variant %r" % (variant,))
+        self._st, self._hp = st, hp
+        self._head = head + [int(k), self.n, ctypes.byref(st), ctypes.byref(hp)]
+        self._tail = []
+        if cfg and variant == "base":
+            self._cfg = ZsLaunchCfg(**{f: int(cfg.get(f, 0)) for f, _ in ZsLaunchCfg._fields_})
+            self._tail = [ctypes.byref(self._cfg)]
+        elif cfg:
+            raise ValueError("a launch cfg applies to the base entry point only")
+        self._fn = fn
+        self.variant = variant
+
+    def __call__(self, step, stream=None, check=True) -> int:
+        rc = self._fn(*self._head, int(step), ctypes.c_void_p(_stream_handle(stream)),
+                      *self._tail)
+        if check and rc != ZS_OK:
+            raise ZsError(rc, "ShardStep(%s)" % self.variant)
+        return rc
+
+
 def algorithmic_bytes(variant: str, k: int, n: int) -> int:
     """HBM bytes one call moves by the algorithm, per entry point."""
     nb = -(-n // ZS_Q8_BLOCK)

@@ -107,3 +107,27 @@ def test_host_step_refuses_device_and_short_buffers():
         zs.zs_host_shard_step(w, m, np.zeros(2 * N, np.float32)[::2], p, g, 1, N, [(0, True)],
                               HP, 1)
     assert zs.zs_host_shard_step(w, m, v, p, g, 1, N, [(0, True)], HP, 1) == zs.ZS_OK
+
+
+def test_prepared_call_checks_once_at_construction():
+    a = _dev_args()
+    with pytest.raises(TypeError, match="host"):
+        zs.ShardStep(np.zeros(N, np.float32), a["m"], a["v"], a["param"], a["grads"], N,
+                     zs.seg_table(a["table"], 1), HP)
+    with pytest.raises(ValueError, match="m holds"):
+        zs.ShardStep(a["master"], FakeGpuTensor(2 * N), a["v"], a["param"], a["grads"], N,
+                     zs.seg_table(a["table"], 1), HP)
+    # bf16 moments take 2 bytes per element
+    zs.ShardStep(a["master"], FakeGpuTensor(2 * N), FakeGpuTensor(2 * N), a["param"],
+                 a["grads"], N, zs.seg_table(a["table"], 1), HP, variant="bf16mv")
+    with pytest.raises(ValueError, match="one scale array"):
+        zs.ShardStep(a["master"], a["m"], a["v"], a["param"], [FakeGpuTensor(N)] * 2, N,
+                     zs.seg_table(a["table"], 1), HP, variant="q8grad",
+                     qscales=[FakeGpuTensor(16)])
+    with pytest.raises(ValueError, match="unknown variant"):
+        zs.ShardStep(a["master"], a["m"], a["v"], a["param"], a["grads"], N,
+                     zs.seg_table(a["table"], 1), HP, variant="fp8")
+    with pytest.raises(ValueError, match="base entry point only"):
+        zs.ShardStep(a["master"], FakeGpuTensor(2 * N), FakeGpuTensor(2 * N), a["param"],
+                     a["grads"], N, zs.seg_table(a["table"], 1), HP, variant="bf16mv",
+                     cfg=dict(chunk_tiles=2))

@@ -212,3 +212,60 @@ def test_variants_on_70b_shard_windows(gpu, variant):
 @pytest.mark.parametrize("variant", ["q8ag", "q8grad", "bf16mv"])
 def test_variants_on_gpt2_shard_windows(gpu, variant):
     _large_variant(gpu, "gpt2-small", variant, 1 << 14, 30)
+
+
+@pytest.mark.parametrize("variant", ["base", "cfg", "q8ag", "q8grad", "bf16mv"])
+def test_prepared_call_matches_the_plain_call(gpu, variant):
+    """zs.ShardStep (arguments checked and marshalled once) gives the same bits
+    as the plain entry-point call on twin buffers, over three steps."""
+    torch = gpu
+    n, k = 70_001, 3
+    rng = np.random.default_rng(7)
+    segs = _segments(rng, n)
+    nb = -(-n // BLOCK)
+    w0 = rng.normal(0, 0.02, n).astype(F32)
+    mvt = torch.int16 if variant == "bf16mv" else torch.float32
+
+    def twin():
+        d = dict(w=_dev(torch, w0), m=torch.zeros(n, dtype=mvt, device="cuda"),
+                 v=torch.zeros(n, dtype=mvt, device="cuda"),
+                 p=torch.zeros(n, dtype=torch.int16, device="cuda"),
+                 q8=torch.zeros(n, dtype=torch.int8, device="cuda"),
+                 q8s=torch.zeros(nb, dtype=torch.float32, device="cuda"))
+        return d
+
+    a, b = twin(), twin()
+    table = H.segment_tensor(segs, "cuda")
+    st, hp = zs.seg_table(table), zs.hparams()
+    qs = [_dev(torch, rng.integers(-127, 128, n).astype(np.int8)) for _ in range(k)]
+    ss = [_dev(torch, (rng.random(nb) * 1e-4).astype(F32)) for _ in range(k)]
+    gs = [_dev(torch, g) for g in _bf16_partials(rng, k, n)]
+    cfg = dict(chunk_tiles=3, block_order=2, groups_per_cu=4)
+    if variant == "q8grad":
+        call = zs.ShardStep(b["w"], b["m"], b["v"], b["p"], qs, n, st, hp, variant="q8grad",
+                            qscales=ss)
+    elif variant == "q8ag":
+        call = zs.ShardStep(b["w"], b["m"], b["v"], b["p"], gs, n, st, hp, variant="q8ag",
+                            param_q8=b["q8"], param_q8_scale=b["q8s"])
+    elif variant == "bf16mv":
+        call = zs.ShardStep(b["w"], b["m"], b["v"], b["p"], gs, n, st, hp, variant="bf16mv")
+    else:
+        call = zs.ShardStep(b["w"], b["m"], b["v"], b["p"], gs, n, st, hp,
+                            cfg=cfg if variant == "cfg" else None)
+    s = torch.cuda.current_stream()
+    for t in (1, 2, 3):
+        if variant == "q8grad":
+            zs.zs_shard_step_q8grad(a["w"], a["m"], a["v"], a["p"], qs, ss, k, n, st, hp, t, s)
+        elif variant == "q8ag":
+            zs.zs_shard_step_q8ag(a["w"], a["m"], a["v"], a["p"], a["q8"], a["q8s"], gs, k, n,
+                                  st, hp, t, s)
+        elif variant == "bf16mv":
+            zs.zs_shard_step_bf16mv(a["w"], a["m"], a["v"], a["p"], gs, k, n, st, hp, t, s)
+        elif variant == "cfg":
+            zs.zs_shard_step_cfg(a["w"], a["m"], a["v"], a["p"], gs, k, n, st, hp, t, s, **cfg)
+        else:
+            zs.zs_shard_step(a["w"], a["m"], a["v"], a["p"], gs, k, n, st, hp, t, s)
+        call(t, s)
+    torch.cuda.synchronize()
+    for key in ("w", "m", "v", "p", "q8", "q8s"):
+        assert torch.equal(a[key].view(torch.uint8), b[key].view(torch.uint8)), key
