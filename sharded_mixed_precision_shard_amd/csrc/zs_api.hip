@@ -224,19 +224,22 @@ int validate_and_launch(const Request &r) {
     const bool xcd_order =
         block_order == 2 || (block_order == 0 && blocks >= kXcdOrderMinBlocks);
     a.xcds = xcd_order ? g_dev[dev].xcds : 1;
-    if (groups_per_cu == 0 && blocks >= kXcdOrderMinBlocks && blocks < kCapMaxBlocks &&
-        !(r.variant & kMvBf16))
-        groups_per_cu = kDefaultCap;
+    const bool default_cap = groups_per_cu == 0 && blocks >= kXcdOrderMinBlocks &&
+                             blocks < kCapMaxBlocks && !(r.variant & kMvBf16);
+    if (default_cap) groups_per_cu = kDefaultCap;
 
     // Occupancy cap: each workgroup reserves 1/groups_per_cu of the unit's
     // LDS (rounded down to 1 KB), so at most groups_per_cu of them fit.  The
     // kernels never touch the reserved bytes.
+    // A cap the caller asked for and cannot be met is an error; the default
+    // cap is simply dropped on a device where it does not fit.
     size_t dyn_lds = 0;
     if (groups_per_cu > 0) {
         const int64_t share = g_dev[dev].lds_per_cu / groups_per_cu / 1024 * 1024;
-        if (share > g_dev[dev].lds_per_group || share < kStaticLds)
+        if (share <= g_dev[dev].lds_per_group && share >= kStaticLds)
+            dyn_lds = (size_t)(share - kStaticLds);
+        else if (!default_cap)
             return ZS_ERR_INVALID_ARGUMENT;
-        dyn_lds = (size_t)(share - kStaticLds);
     }
 
     kernel_fn fn = pick_kernel(r.k, r.variant, nt);
