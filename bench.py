@@ -520,6 +520,8 @@ def main():
         "params_per_s": round(n * args.steps / elapsed, 1),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "copy_ceiling_gbps": round(copy_gbps, 1) if copy_gbps else None,
+        "copy_ceiling_kind": "torch copy_ (the runtime's blit kernel) of --copy-gb bytes, "
+                             "read + write, in the same run",
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
