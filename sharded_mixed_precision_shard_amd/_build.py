@@ -19,6 +19,8 @@ SRCS = [os.path.join(PKG_DIR, "csrc", "zs_kernels.hip"),
 KERNEL_SRCS = [os.path.join(PKG_DIR, "csrc", "zs_kernels.hip"),
                os.path.join(PKG_DIR, "csrc", "zs_kernels.h")]
 LIB = os.path.join(PKG_DIR, "libzs.so")
+CEILING_SRC = os.path.join(PKG_DIR, "csrc", "zs_ceiling.hip")
+CEILING_LIB = os.path.join(PKG_DIR, "libzs_ceiling.so")
 HOST_SRC = os.path.join(PKG_DIR, "csrc", "zs_host.cpp")
 HOST_LIB = os.path.join(PKG_DIR, "libzs_host.so")
 
@@ -63,9 +65,21 @@ def build_host(verbose: bool = False) -> str:
     return HOST_LIB
 
 
+def build_ceiling(verbose: bool = False) -> str:
+    """Compile libzs_ceiling.so, the streaming copy bench.py measures beside the
+    step (measurement only)."""
+    tmp = CEILING_LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, CEILING_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, CEILING_LIB)
+    return CEILING_LIB
+
+
 def build(verbose: bool = False) -> str:
-    """Compile libzs.so and libzs_host.so (always recompiles).  Returns the
-    device library path."""
+    """Compile libzs.so, libzs_host.so and libzs_ceiling.so (always
+    recompiles).  Returns the device library path."""
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE_DIR, "-o", tmp, *SRCS]
     if verbose:
@@ -73,6 +87,7 @@ def build(verbose: bool = False) -> str:
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     build_host(verbose)
+    build_ceiling(verbose)
     return LIB
 
 

@@ -97,3 +97,13 @@ def test_kernel_hash_ignores_comments_not_code():
         got = bench.measured_traffic(key, e["launch"])
         assert got == (e["bytes_per_launch"] if e["kernel_sha"] == h else None), key
         assert bench.measured_traffic(key, e["launch"] + ",other") is None
+
+
+def test_ceiling_library_loads_and_rejects_bad_arguments():
+    """Loads on the CPU; the argument checks return before any device call."""
+    lib = bench._ceiling_lib()
+    assert lib.zs_ceiling_copy(16, 4096, 100, None) == -1   # not a multiple of 16
+    assert lib.zs_ceiling_copy(8, 4096, 64, None) == -1     # misaligned
+    assert lib.zs_ceiling_copy(0, 4096, 64, None) == -1     # null source
+    assert lib.zs_ceiling_copy(4096, 4112, 64, None) == -1  # overlap
+    assert lib.zs_ceiling_copy(0, 0, 0, None) == 0          # nothing to do

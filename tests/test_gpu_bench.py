@@ -40,6 +40,29 @@ def test_bench_line(extra):
     cpu = out["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["cores"] == 1 and cpu["value"] > 0
     assert out["speedup_vs_cpu_oracle"]["single_thread"] > 1
+    assert out["copy_ceiling_gbps"] > 0 and out["torch_copy_gbps"] > 0
+    assert out["pct_of_copy_ceiling"] > 0
     variant = extra[1] if extra[:1] == ["--variant"] else "base"
     want = "zs_shard_step" if variant == "base" else "zs_shard_step_" + variant
     assert out["config"]["entry_point"] == want
+
+
+def test_streaming_copy_of_the_ceiling_library():
+    """The copy bench.py measures as its in-run ceiling copies exactly and
+    refuses bad arguments without launching."""
+    import torch
+    sys.path.insert(0, ROOT)
+    import bench
+    lib = bench._ceiling_lib()
+    torch.cuda.set_device(0)
+    n = (1 << 22) + 4
+    src = torch.randn(n, device="cuda")
+    dst = torch.zeros(n, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    assert lib.zs_ceiling_copy(src.data_ptr(), dst.data_ptr(), 4 * n, s) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+    assert lib.zs_ceiling_copy(src.data_ptr(), dst.data_ptr(), 4 * n - 4, s) == -1
+    assert lib.zs_ceiling_copy(src.data_ptr() + 4, dst.data_ptr(), 16, s) == -1
+    assert lib.zs_ceiling_copy(src.data_ptr(), src.data_ptr() + 16, 64, s) == -1
+    assert lib.zs_ceiling_copy(src.data_ptr(), dst.data_ptr(), 0, s) == 0
