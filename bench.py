@@ -332,7 +332,9 @@ def offload_main(args):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 10; 200 for the tiny and GPT-2 shards, whose "
+                         "steps take microseconds)")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="70b")
     ap.add_argument("--variant", default="base",
@@ -355,6 +357,8 @@ def main():
     ap.add_argument("--copy-gb", type=float, default=8.0,
                     help="size of the in-run copy-ceiling measurement (0 = skip)")
     args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 200 if args.config in ("tiny", "gpt2-small") else 10
 
     if args.variant != "base" and (args.chunk_tiles or args.nontemporal or args.groups_per_cu
                                    or args.block_order):
