@@ -103,3 +103,51 @@ def test_every_pair_of_bf16_partials(gpu):
         assert np.array_equal(np.isnan(got), nan), "chunk %d: NaN pattern differs" % c
         same = got.view(np.uint32)[~nan] == want.view(np.uint32)[~nan]
         assert same.all(), "chunk %d: %d sums differ" % (c, int((~same).sum()))
+
+
+def test_int8_payload_of_every_bf16_pattern(gpu):
+    """zs_shard_step_q8ag's int8 payload for parameters taking every bf16 bit
+    pattern (in order, shuffled and sign-flipped, so blocks mix magnitudes,
+    NaNs and infinities), pinned to torch's formula on the CPU: per block of
+    256, scale = max |x| / 127 in binary32 (NaN if any x is NaN), q =
+    clamp(round-half-even(x / scale), -127, 127), q = 0 where the scale is 0
+    or not finite.  The identity update makes param equal the patterns."""
+    torch = gpu
+    rng = np.random.default_rng(33)
+    pats = np.arange(1 << 16, dtype=np.uint32)
+    order = np.concatenate([pats, rng.permutation(pats), rng.permutation(pats) ^ 0x8000,
+                            rng.permutation(pats)[: 40_000]]).astype(np.uint32)
+    n = order.shape[0]
+    w0 = (order << 16).view(np.float32)
+    nb = -(-n // zs.ZS_Q8_BLOCK)
+    dw = torch.from_numpy(w0.copy()).cuda()
+    dm = torch.zeros(n, device="cuda")
+    dv = torch.zeros(n, device="cuda")
+    dp = torch.zeros(n, dtype=torch.int16, device="cuda")
+    dq = torch.zeros(n, dtype=torch.int8, device="cuda")
+    ds = torch.zeros(nb, dtype=torch.float32, device="cuda")
+    dg = [torch.zeros(n, dtype=torch.int16, device="cuda")]
+    table = H.segment_tensor([(0, True)], "cuda")
+    hp = zs.hparams(lr=0.0, beta1=0.9, beta2=0.95, eps=1.0, weight_decay=0.0)
+    zs.zs_shard_step_q8ag(dw, dm, dv, dp, dq, ds, dg, 1, n, zs.seg_table(table), hp, 1,
+                          torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    p = dp.cpu().numpy().view(np.uint16)
+    want_p = (order & 0xFFFF).astype(np.uint16)
+    nan_in = np.isnan(w0)
+    assert np.array_equal(p[~nan_in], want_p[~nan_in]) and (p[nan_in] == 0x7FC0).all()
+    x = torch.from_numpy((p.astype(np.uint32) << 16).view(np.float32).copy())
+    pad = torch.zeros(nb * zs.ZS_Q8_BLOCK - n)
+    blocks = torch.cat([x, pad]).view(nb, zs.ZS_Q8_BLOCK)
+    amax = blocks.abs().amax(dim=1)
+    scale = amax / 127.0
+    usable = torch.isfinite(scale) & (scale > 0)
+    safe = torch.where(usable, scale, torch.ones_like(scale))
+    q = torch.clamp(torch.round(blocks / safe[:, None]), -127, 127)
+    q = torch.where(usable[:, None], q, torch.zeros_like(q)).to(torch.int8).view(-1)[:n]
+    got_s = ds.cpu().numpy()
+    want_s = scale.numpy()
+    assert np.array_equal(got_s, want_s, equal_nan=True), "block scales differ"
+    got_q = dq.cpu().numpy()
+    bad = got_q != q.numpy()
+    assert not bad.any(), "%d codes differ, first at %d" % (int(bad.sum()), int(np.argmax(bad)))
