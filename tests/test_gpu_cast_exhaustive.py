@@ -151,3 +151,77 @@ def test_int8_payload_of_every_bf16_pattern(gpu):
     got_q = dq.cpu().numpy()
     bad = got_q != q.numpy()
     assert not bad.any(), "%d codes differ, first at %d" % (int(bad.sum()), int(np.argmax(bad)))
+
+
+def test_int8_partials_every_pair(gpu):
+    """zs_shard_step_q8grad's dequantize-and-reduce for every pair (q0, q1) of
+    int8 codes under 64 random (not power-of-two) block scales each, pinned to
+    numpy's binary32 arithmetic: with beta1 = 0 the new m is
+    0 + (fl(q0 * s0) + fl(q1 * s1))."""
+    torch = gpu
+    rng = np.random.default_rng(34)
+    reps = 64
+    q = np.arange(-128, 128, dtype=np.int32)
+    q0 = np.tile(np.repeat(q, 256), reps).astype(np.int8)
+    q1 = np.tile(np.tile(q, 256), reps).astype(np.int8)
+    n = q0.shape[0]
+    nb = -(-n // zs.ZS_Q8_BLOCK)
+    s0 = (rng.random(nb) * 1e-2 + 1e-6).astype(np.float32)
+    s1 = (rng.random(nb) * 1e-3 + 1e-7).astype(np.float32)
+    dm = torch.zeros(n, device="cuda")
+    dv = torch.zeros(n, device="cuda")
+    dw = torch.zeros(n, device="cuda")
+    dp = torch.zeros(n, dtype=torch.int16, device="cuda")
+    table = H.segment_tensor([(0, False)], "cuda")
+    hp = zs.hparams(lr=0.0, beta1=0.0, beta2=0.5, eps=1.0, weight_decay=0.0)
+    dq = [torch.from_numpy(q0.copy()).cuda(), torch.from_numpy(q1.copy()).cuda()]
+    dsc = [torch.from_numpy(s0.copy()).cuda(), torch.from_numpy(s1.copy()).cuda()]
+    zs.zs_shard_step_q8grad(dw, dm, dv, dp, dq, dsc, 2, n, zs.seg_table(table), hp, 1,
+                            torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    b = np.arange(n) // zs.ZS_Q8_BLOCK
+    want = np.float32(0.0) + (q0.astype(np.float32) * s0[b] + q1.astype(np.float32) * s1[b])
+    got = dm.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), want.astype(np.float32).view(np.uint32))
+
+
+def test_bf16_moments_of_every_pair(gpu):
+    """zs_shard_step_bf16mv's moment rounding over all 2^32 pairs of bf16
+    partials, pinned to torch's bf16 conversion: with beta1 = beta2 = 0 the
+    stored moments are bf16(0 + g) and bf16(0 + g * g), g = fp32(G0) + fp32(G1)."""
+    torch = gpu
+    n = CHUNK
+    dw = torch.zeros(n, dtype=torch.float32, device="cuda")
+    dm = torch.empty(n, dtype=torch.int16, device="cuda")
+    dv = torch.empty(n, dtype=torch.int16, device="cuda")
+    dp = torch.empty(n, dtype=torch.int16, device="cuda")
+    g0 = torch.empty(n, dtype=torch.int16, device="cuda")
+    g1 = torch.empty(n, dtype=torch.int16, device="cuda")
+    table = H.segment_tensor([(0, False)], "cuda")
+    hp = zs.hparams(lr=0.0, beta1=0.0, beta2=0.0, eps=1.0, weight_decay=0.0)
+    low = torch.arange(1 << 16, dtype=torch.int32, device="cuda")
+    low16 = torch.where(low >= 1 << 15, low - (1 << 16), low).to(torch.int16)
+    for c in range(1 << 32 >> 28):
+        hi0 = c << 12
+        h = torch.arange(hi0, hi0 + (n >> 16), dtype=torch.int32, device="cuda")
+        g0.copy_(torch.where(h >= 1 << 15, h - (1 << 16), h).to(torch.int16)
+                 .repeat_interleave(1 << 16))
+        g1.copy_(low16.repeat(n >> 16))
+        dm.zero_()
+        dv.zero_()
+        zs.zs_shard_step_bf16mv(dw, dm, dv, dp, [g0, g1], 2, n, zs.seg_table(table), hp, 1,
+                                torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        a = np.repeat(np.arange(hi0, hi0 + (n >> 16), dtype=np.uint32) << 16, 1 << 16)
+        b = np.tile(np.arange(1 << 16, dtype=np.uint32) << 16, n >> 16)
+        with np.errstate(invalid="ignore", over="ignore"):
+            g = a.view(np.float32) + b.view(np.float32)
+            m_ref = np.float32(0.0) + g
+            v_ref = np.float32(0.0) + g * g
+        for name, dev, ref in (("m", dm, m_ref), ("v", dv, v_ref)):
+            want = torch.from_numpy(ref).to(torch.bfloat16).view(torch.int16).numpy()
+            want = want.view(np.uint16).copy()
+            want[np.isnan(ref)] = 0x7FC0
+            got = dev.cpu().numpy().view(np.uint16)
+            bad = got != want
+            assert not bad.any(), "chunk %d %s: %d values differ" % (c, name, int(bad.sum()))
