@@ -8,7 +8,8 @@ or as plain integer device addresses.  There is no CPU fallback: if
 Entry points keep the C names: :func:`zs_init`, :func:`zs_shard_step`,
 :func:`zs_shard_step_cfg`, :func:`zs_shard_step_q8ag`, :func:`zs_shard_step_q8grad`,
 :func:`zs_shard_step_bf16mv`, :func:`zs_fini`, :func:`zs_status_string`,
-:func:`zs_last_device_error`, :func:`zs_algorithmic_bytes`.
+:func:`zs_last_device_error`, :func:`zs_algorithmic_bytes`,
+:func:`zs_launch_geometry`, :func:`zs_launch_plan`.
 """
 from __future__ import annotations
 
@@ -32,10 +33,13 @@ ZS_ERR_TOO_MANY_SEGMENTS = 4
 ZS_ERR_DEVICE = 5
 ZS_ERR_ALIASING = 6
 
+ZS_VARIANT = {"base": 0, "q8ag": 1, "q8grad": 2, "bf16mv": 4}
+
 # Symbols declared in include/zs.h.
 EXPORTS = ("zs_init", "zs_shard_step", "zs_shard_step_cfg", "zs_shard_step_q8ag",
            "zs_shard_step_q8grad", "zs_shard_step_bf16mv", "zs_fini", "zs_status_string",
-           "zs_last_device_error", "zs_algorithmic_bytes", "zs_launch_geometry")
+           "zs_last_device_error", "zs_algorithmic_bytes", "zs_launch_geometry",
+           "zs_launch_plan")
 
 
 class ZsHparams(ctypes.Structure):
@@ -57,6 +61,12 @@ class ZsSegTable(ctypes.Structure):
 class ZsLaunchCfg(ctypes.Structure):
     _fields_ = [("chunk_tiles", ctypes.c_int32), ("nontemporal", ctypes.c_int32),
                 ("groups_per_cu", ctypes.c_int32), ("block_order", ctypes.c_int32)]
+
+
+class ZsLaunchInfo(ctypes.Structure):
+    _fields_ = [("workgroups", ctypes.c_int64), ("chunk_elements", ctypes.c_int64),
+                ("block_order", ctypes.c_int32), ("groups_per_cu", ctypes.c_int32),
+                ("nontemporal", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class ZsError(RuntimeError):
@@ -104,6 +114,8 @@ def load_library():
     lib.zs_algorithmic_bytes.restype = ctypes.c_int64
     lib.zs_launch_geometry.argtypes = [ctypes.c_int, ctypes.c_int64, P, P, P]
     lib.zs_launch_geometry.restype = ctypes.c_int
+    lib.zs_launch_plan.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, P, P]
+    lib.zs_launch_plan.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -215,10 +227,37 @@ def zs_launch_geometry(k: int, n: int, chunk_tiles: int = 0):
     return wg.value, ch.value
 
 
+def _check_k(k, arrays, name):
+    """The partial count the C call receives: len(arrays), or an explicit k
+    that must equal it (the library reads k pointers from the array, so a
+    larger k would read past its end)."""
+    if k is None:
+        return len(arrays)
+    if int(k) != len(arrays):
+        raise ValueError("k=%d but %d %s were given" % (int(k), len(arrays), name))
+    return int(k)
+
+
+def zs_launch_plan(k: int, n: int, variant: str = "base", cfg=None) -> dict:
+    """The launch a call of entry point ``variant`` ("base", "q8ag", "q8grad",
+    "bf16mv") would make: grid, chunk, chunk order, occupancy cap and cache
+    policy, as a dict of the zs_launch_info fields.  ``cfg`` (base only) is a
+    dict of ZsLaunchCfg fields or None."""
+    c = None
+    if cfg:
+        c = ZsLaunchCfg(**{f: int(cfg.get(f, 0)) for f, _ in ZsLaunchCfg._fields_})
+    out = ZsLaunchInfo()
+    rc = load_library().zs_launch_plan(int(k), int(n), ZS_VARIANT[variant],
+                                       ctypes.byref(c) if c is not None else None,
+                                       ctypes.byref(out))
+    if rc != ZS_OK:
+        raise ZsError(rc, "zs_launch_plan")
+    return {f: getattr(out, f) for f, _ in ZsLaunchInfo._fields_ if f != "reserved"}
+
+
 def _marshal(master, m, v, param_bf16, grads, k, n, seg_table_, hparams_, mv_size=4):
     """Pointers of one step call; every tensor checked against n elements."""
-    if k is None:
-        k = len(grads)
+    k = _check_k(k, grads, "grads")
     nn = max(int(n), 0)
     gp = _ptr_array(grads, 2 * nn, "grads")
     st = seg_table_ if isinstance(seg_table_, ZsSegTable) else seg_table(seg_table_)
@@ -290,13 +329,17 @@ def zs_shard_step_q8grad(master, m, v, param_bf16, qgrads, qscales, k, n, seg_ta
     qscales[j] (float32[ceil(n/256)])."""
     nn = max(int(n), 0)
     nb = -(-nn // ZS_Q8_BLOCK)
+    k = _check_k(k, qgrads, "qgrads")
+    if len(qscales) != len(qgrads):
+        raise ValueError("%d qscales for %d qgrads: one scale array per int8 partial"
+                         % (len(qscales), len(qgrads)))
     pm, pmm, pv, pp, _, _, st, hp, _ = _marshal(master, m, v, param_bf16, [], 0, n, seg_table_,
                                                 hparams_)
     qp = _ptr_array(qgrads, nn, "qgrads")
     sp = _ptr_array(qscales, 4 * nb, "qscales")
     rc = load_library().zs_shard_step_q8grad(
         pm, pmm, pv, pp, ctypes.cast(qp, ctypes.c_void_p), ctypes.cast(sp, ctypes.c_void_p),
-        int(len(qgrads) if k is None else k), int(n), ctypes.byref(st), ctypes.byref(hp),
+        k, int(n), ctypes.byref(st), ctypes.byref(hp),
         int(step), ctypes.c_void_p(_stream_handle(stream)))
     if check and rc != ZS_OK:
         raise ZsError(rc, "zs_shard_step_q8grad")
@@ -437,6 +480,7 @@ def zs_host_shard_step(master, m, v, param_bf16, grads, k, n, segs, hparams_, st
     """Host shard step on host buffers (numpy arrays, CPU tensors or addresses).
     ``segs`` is a list of (start, wd_on) or a ZsSegment array."""
     nn = max(int(n), 0)
+    k = _check_k(k, grads, "grads")
     gp = (ctypes.c_void_p * max(len(grads), 1))(
         *[_host(g, 2 * nn, "grads[%d]" % j) for j, g in enumerate(grads)])
     arr = segs if isinstance(segs, ctypes.Array) else host_segments(segs)
@@ -444,7 +488,7 @@ def zs_host_shard_step(master, m, v, param_bf16, grads, k, n, segs, hparams_, st
         ctypes.c_void_p(_host(master, 4 * nn, "master")), ctypes.c_void_p(_host(m, 4 * nn, "m")),
         ctypes.c_void_p(_host(v, 4 * nn, "v")),
         ctypes.c_void_p(_host(param_bf16, 2 * nn, "param_bf16")), ctypes.cast(gp, ctypes.c_void_p),
-        int(len(grads) if k is None else k), int(n), ctypes.cast(arr, ctypes.c_void_p), len(arr),
+        k, int(n), ctypes.cast(arr, ctypes.c_void_p), len(arr),
         ctypes.byref(hparams_), int(step), int(nthreads))
     if check and rc != ZS_OK:
         raise RuntimeError("zs_host_shard_step failed: %s (status %d)" % (

@@ -131,3 +131,41 @@ def test_prepared_call_checks_once_at_construction():
         zs.ShardStep(a["master"], FakeGpuTensor(2 * N), FakeGpuTensor(2 * N), a["param"],
                      a["grads"], N, zs.seg_table(a["table"], 1), HP, variant="bf16mv",
                      cfg=dict(chunk_tiles=2))
+
+
+def test_k_must_match_the_number_of_partials():
+    """An explicit k that differs from the number of partial pointers is
+    refused in Python: the library would read k pointers from the array."""
+    a = _dev_args()
+    st = zs.seg_table(a["table"], 1)
+    f = (a["master"], a["m"], a["v"], a["param"])
+    for k in (1, 3, 16):
+        with pytest.raises(ValueError, match="k=%d but 2 grads" % k):
+            zs.zs_shard_step(*f, a["grads"], k, N, st, HP, 1)
+        with pytest.raises(ValueError, match="k=%d but 2 grads" % k):
+            zs.zs_shard_step_cfg(*f, a["grads"], k, N, st, HP, 1, chunk_tiles=2)
+        with pytest.raises(ValueError, match="k=%d but 2 grads" % k):
+            zs.zs_shard_step_q8ag(*f, FakeGpuTensor(N), FakeGpuTensor(16), a["grads"], k, N,
+                                  st, HP, 1)
+        with pytest.raises(ValueError, match="k=%d but 2 grads" % k):
+            zs.zs_shard_step_bf16mv(a["master"], FakeGpuTensor(2 * N), FakeGpuTensor(2 * N),
+                                    a["param"], a["grads"], k, N, st, HP, 1)
+    q = [FakeGpuTensor(N), FakeGpuTensor(N)]
+    s = [FakeGpuTensor(16), FakeGpuTensor(16)]
+    with pytest.raises(ValueError, match="k=3 but 2 qgrads"):
+        zs.zs_shard_step_q8grad(*f, q, s, 3, N, st, HP, 1)
+    with pytest.raises(ValueError, match="1 qscales for 2 qgrads"):
+        zs.zs_shard_step_q8grad(*f, q, s[:1], 2, N, st, HP, 1)
+    with pytest.raises(ValueError, match="3 qscales for 2 qgrads"):
+        zs.zs_shard_step_q8grad(*f, q, s + s[:1], None, N, st, HP, 1)
+    # the host step: plain integer host addresses, never dereferenced here
+    with pytest.raises(ValueError, match="k=2 but 1 grads"):
+        zs.zs_host_shard_step(4096, 4096, 4096, 4096, [4096], 2, 16, [(0, True)], HP, 1)
+    # k=None takes the list's length; k=0 with no partials reaches the
+    # library, which refuses k=0 itself
+    w, m, v = (np.zeros(N, np.float32) for _ in range(3))
+    p = np.zeros(N, np.uint16)
+    assert zs.zs_host_shard_step(w, m, v, p, [], 0, N, [(0, True)], HP, 1, check=False) == \
+        zs.ZS_ERR_INVALID_ARGUMENT
+    assert zs.zs_host_shard_step(w, m, v, p, [np.zeros(N, np.uint16)], None, N, [(0, True)],
+                                 HP, 1) == zs.ZS_OK

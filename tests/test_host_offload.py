@@ -101,7 +101,7 @@ def test_argument_errors():
     hp = zs.hparams()
     call = lambda *x, **kw: zs.zs_host_shard_step(*x, check=False, **kw)  # noqa: E731
     assert call(w, m, v, p, g, 1, n, [(0, True)], hp, 1) == zs.ZS_OK
-    assert call(w, m, v, p, g, 0, n, [(0, True)], hp, 1) == zs.ZS_ERR_INVALID_ARGUMENT
+    assert call(w, m, v, p, [], 0, n, [(0, True)], hp, 1) == zs.ZS_ERR_INVALID_ARGUMENT
     assert call(w, m, v, p, g, 1, n, [(0, True)], hp, 0) == zs.ZS_ERR_INVALID_ARGUMENT
     assert call(w, m, v, p, g, 1, n, [(1, True)], hp, 1) == zs.ZS_ERR_INVALID_ARGUMENT
     assert call(w, m, v, p, g, 1, n, [(0, True), (9, True), (3, False)], hp, 1) == \

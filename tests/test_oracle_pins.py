@@ -366,6 +366,29 @@ def test_accounting_pins():
     assert [accounting.shard_step_hbm_bytes_per_param(k) for k in (1, 2, 8)] == [28, 30, 42]
 
 
+def test_shard_resident_bytes_pins():
+    """Resident bytes per shard parameter: the fp32 state, the bf16 output
+    and the k bf16 partials."""
+    g = {k: v[0] for k, v in read_golden("zero_memory.txt").items()}
+    # one partial is the one bf16 gradient of the page's five copies: 16 bytes
+    assert accounting.shard_resident_bytes_per_param(1) == g["bytes_per_param"] == 16
+    # hand-derived: k = 2 is 4 + 4 + 4 + 2 + 2 + 2 = 18 bytes; the 70B-shaped
+    # rank-0 shard of 8,053,473,280 parameters then holds 144,962,519,040 bytes
+    assert accounting.shard_resident_bytes_per_param(2) == 18
+    assert accounting.shard_resident_bytes_per_param(2) * 8_053_473_280 == 144_962_519_040
+    assert accounting.shard_resident_bytes_per_param(8) == 30
+    # the buffers a shard step actually holds, counted from their dtypes
+    n = 1000
+    for k in (1, 2, 3, 16):
+        bufs = [np.zeros(n, np.float32) for _ in range(3)] + [np.zeros(n, np.uint16)] + \
+               [np.zeros(n, np.uint16) for _ in range(k)]
+        assert sum(b.nbytes for b in bufs) == accounting.shard_resident_bytes_per_param(k) * n
+    # what a step moves = what it holds + the fp32 state written back (12 B)
+    for k in (1, 2, 8):
+        assert accounting.shard_step_hbm_bytes_per_param(k) == \
+            accounting.shard_resident_bytes_per_param(k) + 12
+
+
 # ---------------------------------------------------- argument validation
 
 def test_oracle_rejects_invalid_arguments():
