@@ -252,6 +252,36 @@ int zs_last_device_error(void);
 int zs_launch_geometry(int k, int64_t n, const zs_launch_cfg *cfg, int64_t *workgroups,
                        int64_t *chunk_elements);
 
+/* Entry points, as zs_launch_plan names them. */
+#define ZS_VARIANT_BASE 0   /* zs_shard_step, zs_shard_step_cfg */
+#define ZS_VARIANT_Q8AG 1   /* zs_shard_step_q8ag */
+#define ZS_VARIANT_Q8GRAD 2 /* zs_shard_step_q8grad */
+#define ZS_VARIANT_BF16MV 4 /* zs_shard_step_bf16mv */
+
+/* The launch a step call resolves its defaults to. */
+typedef struct {
+    int64_t workgroups;     /* workgroups of 256 threads (0 when n == 0) */
+    int64_t chunk_elements; /* consecutive elements each workgroup owns (the last fewer) */
+    int32_t block_order;    /* 1 = linear, 2 = XCD-contiguous (a part with a single XCD
+                               runs the linear order either way) */
+    int32_t groups_per_cu;  /* resident-workgroup cap per compute unit the launch asks
+                               for, 0 = none (a default cap the device cannot hold is
+                               dropped at launch) */
+    int32_t nontemporal;    /* 1 = streaming loads and stores, 0 = cached */
+    int32_t reserved;       /* 0 */
+} zs_launch_info;
+
+/* The launch a call of entry point `variant` (ZS_VARIANT_*) over n elements
+ * with k partials and the override cfg (NULL = defaults, the only choice for
+ * the variants other than ZS_VARIANT_BASE) would make: grid, chunk, chunk
+ * order, occupancy cap and cache policy.  These decide the kernel's memory
+ * traffic pattern; its arithmetic does not depend on them.  Host-only; needs
+ * no device and no zs_init.  Returns ZS_OK or ZS_ERR_INVALID_ARGUMENT (k, n,
+ * variant or a cfg field out of range, a cfg with a variant other than
+ * ZS_VARIANT_BASE, or a null out). */
+int zs_launch_plan(int k, int64_t n, int variant, const zs_launch_cfg *cfg,
+                   zs_launch_info *out);
+
 /* Bytes one zs_shard_step call moves through HBM, by the algorithm:
  * n * (12 + 2k) read + n * 14 written.  For reporting only. */
 int64_t zs_algorithmic_bytes(int k, int64_t n);

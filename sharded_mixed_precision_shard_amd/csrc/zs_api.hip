@@ -83,6 +83,45 @@ void launch_geometry(int k, int64_t n, int chunk_tiles, int64_t *chunk_out,
     *blocks_out = blocks;
 }
 
+// The launch of one call: the geometry, chunk order, occupancy cap and cache
+// policy its cfg and the defaults resolve to (device-independent; the XCD
+// count and the LDS sizes are applied at launch).
+int resolve_launch(int k, int64_t n, int variant, const zs_launch_cfg *cfg,
+                   zs_launch_info *out) {
+    if (k < 1 || k > ZS_MAX_K || n < 0 || n > INT64_MAX / 8) return ZS_ERR_INVALID_ARGUMENT;
+    if (variant != 0 && variant != kOutQ8 && variant != kGradQ8 && variant != kMvBf16)
+        return ZS_ERR_INVALID_ARGUMENT;
+    // Streaming (non-temporal) loads and stores by default: nothing is
+    // reused, and on MI355X they measured 5-10 % faster than cached access.
+    int chunk_tiles = 0, nt = 1, groups_per_cu = 0, block_order = 0;
+    if (cfg) {
+        if (cfg->chunk_tiles < 0 || cfg->chunk_tiles > kMaxChunkTiles)
+            return ZS_ERR_INVALID_ARGUMENT;
+        if (cfg->nontemporal < 0 || cfg->nontemporal > 2) return ZS_ERR_INVALID_ARGUMENT;
+        if (cfg->groups_per_cu < 0 || cfg->groups_per_cu > ZS_MAX_GROUPS_PER_CU)
+            return ZS_ERR_INVALID_ARGUMENT;
+        if (cfg->block_order < 0 || cfg->block_order > 2) return ZS_ERR_INVALID_ARGUMENT;
+        chunk_tiles = cfg->chunk_tiles;
+        nt = cfg->nontemporal == 2 ? 0 : 1;
+        groups_per_cu = cfg->groups_per_cu;
+        block_order = cfg->block_order;
+    }
+    int64_t chunk = 0, blocks = 0;
+    if (n > 0) launch_geometry(k, n, chunk_tiles, &chunk, &blocks);
+    const bool xcd_order =
+        block_order == 2 || (block_order == 0 && blocks >= kXcdOrderMinBlocks);
+    if (groups_per_cu == 0 && blocks >= kXcdOrderMinBlocks && blocks < kCapMaxBlocks &&
+        !(variant & kMvBf16))
+        groups_per_cu = -kDefaultCap;  // a default cap: dropped where it does not fit
+    out->workgroups = blocks;
+    out->chunk_elements = chunk;
+    out->block_order = xcd_order ? 2 : 1;
+    out->groups_per_cu = groups_per_cu;
+    out->nontemporal = nt;
+    out->reserved = 0;
+    return ZS_OK;
+}
+
 // One call, whatever the variant: the buffers it reads and writes.
 struct Request {
     float *master = nullptr;
@@ -115,6 +154,9 @@ int validate_and_launch(const Request &r) {
     const bool gq = (r.variant & kGradQ8) != 0;
     if (r.k < 1 || r.k > ZS_MAX_K || r.n < 0 || r.step < 1 || !r.st || !r.hp)
         return ZS_ERR_INVALID_ARGUMENT;
+    zs_launch_info plan;
+    const int pst = resolve_launch(r.k, r.n, r.variant, r.cfg, &plan);
+    if (pst != ZS_OK) return pst;
     if (gq ? (!r.qgrads || !r.qscales) : !r.grads) return ZS_ERR_INVALID_ARGUMENT;
     const zs_hparams *hp = r.hp;
     if (!std::isfinite(hp->lr) || !std::isfinite(hp->beta1) || !std::isfinite(hp->beta2) ||
@@ -126,21 +168,6 @@ int validate_and_launch(const Request &r) {
         return ZS_ERR_INVALID_ARGUMENT;
     if (r.st->count < 1) return ZS_ERR_INVALID_ARGUMENT;
     if (r.st->count > ZS_MAX_SEGMENTS) return ZS_ERR_TOO_MANY_SEGMENTS;
-    // Streaming (non-temporal) loads and stores by default: nothing is
-    // reused, and on MI355X they measured 5-10 % faster than cached access.
-    int chunk_tiles = 0, nt = 1, groups_per_cu = 0, block_order = 0;
-    if (r.cfg) {
-        if (r.cfg->chunk_tiles < 0 || r.cfg->chunk_tiles > kMaxChunkTiles)
-            return ZS_ERR_INVALID_ARGUMENT;
-        if (r.cfg->nontemporal < 0 || r.cfg->nontemporal > 2) return ZS_ERR_INVALID_ARGUMENT;
-        if (r.cfg->groups_per_cu < 0 || r.cfg->groups_per_cu > ZS_MAX_GROUPS_PER_CU)
-            return ZS_ERR_INVALID_ARGUMENT;
-        if (r.cfg->block_order < 0 || r.cfg->block_order > 2) return ZS_ERR_INVALID_ARGUMENT;
-        chunk_tiles = r.cfg->chunk_tiles;
-        nt = r.cfg->nontemporal == 2 ? 0 : 1;
-        groups_per_cu = r.cfg->groups_per_cu;
-        block_order = r.cfg->block_order;
-    }
     if (r.n == 0) return ZS_OK;
     if (r.n > INT64_MAX / 8) return ZS_ERR_INVALID_ARGUMENT;
     if (!r.st->segs) return ZS_ERR_INVALID_ARGUMENT;
@@ -218,15 +245,11 @@ int validate_and_launch(const Request &r) {
     }
     a.gscale = hp->grad_scale;
 
-    int64_t chunk = 0, blocks = 0;
-    launch_geometry(r.k, n, chunk_tiles, &chunk, &blocks);
-    a.chunk = chunk;
-    const bool xcd_order =
-        block_order == 2 || (block_order == 0 && blocks >= kXcdOrderMinBlocks);
-    a.xcds = xcd_order ? g_dev[dev].xcds : 1;
-    const bool default_cap = groups_per_cu == 0 && blocks >= kXcdOrderMinBlocks &&
-                             blocks < kCapMaxBlocks && !(r.variant & kMvBf16);
-    if (default_cap) groups_per_cu = kDefaultCap;
+    const int64_t blocks = plan.workgroups;
+    a.chunk = plan.chunk_elements;
+    a.xcds = plan.block_order == 2 ? g_dev[dev].xcds : 1;
+    const bool default_cap = plan.groups_per_cu < 0;
+    const int groups_per_cu = default_cap ? -plan.groups_per_cu : plan.groups_per_cu;
 
     // Occupancy cap: each workgroup reserves 1/groups_per_cu of the unit's
     // LDS (rounded down to 1 KB), so at most groups_per_cu of them fit.  The
@@ -242,7 +265,8 @@ int validate_and_launch(const Request &r) {
             return ZS_ERR_INVALID_ARGUMENT;
     }
 
-    kernel_fn fn = pick_kernel(r.k, r.variant, nt);
+    const int unit_bc = (a.bc1 == 1.0f ? 1 : 0) | (a.bc2 == 1.0f ? 2 : 0);
+    kernel_fn fn = pick_kernel(r.k, r.variant, plan.nontemporal, unit_bc);
     if (!fn) return ZS_ERR_INVALID_ARGUMENT;
     void *args[] = {&a};
     e = hipLaunchKernel((const void *)fn, dim3((unsigned)blocks), dim3(kThreads), args, dyn_lds,
@@ -385,6 +409,15 @@ int zs_launch_geometry(int k, int64_t n, const zs_launch_cfg *cfg, int64_t *work
         return ZS_OK;
     }
     launch_geometry(k, n, chunk_tiles, chunk_elements, workgroups);
+    return ZS_OK;
+}
+
+int zs_launch_plan(int k, int64_t n, int variant, const zs_launch_cfg *cfg,
+                   zs_launch_info *out) {
+    if (!out || (cfg && variant != 0)) return ZS_ERR_INVALID_ARGUMENT;
+    const int st = resolve_launch(k, n, variant, cfg, out);
+    if (st != ZS_OK) return st;
+    if (out->groups_per_cu < 0) out->groups_per_cu = -out->groups_per_cu;
     return ZS_OK;
 }
 

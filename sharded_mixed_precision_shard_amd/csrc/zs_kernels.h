@@ -66,8 +66,10 @@ constexpr int64_t kStaticLds = (int64_t)(8 + 1) * kWave * (kThreads / kWave);
 
 typedef void (*kernel_fn)(const StepArgs);
 
-// The kernel for k partials, a variant (0 or one of the bits above) and
-// streaming (nt = 1) or cached (nt = 0) access; nullptr if there is none.
-kernel_fn pick_kernel(int k, int variant, int nt);
+// The kernel for k partials, a variant (0 or one of the bits above),
+// streaming (nt = 1) or cached (nt = 0) access and the bias corrections that
+// are exactly 1.0f (unit_bc bit 0: bc1, bit 1: bc2; a streaming kernel then
+// leaves out that division); nullptr if there is none.
+kernel_fn pick_kernel(int k, int variant, int nt, int unit_bc);
 
 }  // namespace zs_detail

@@ -67,14 +67,18 @@ __device__ __forceinline__ uint32_t to_bf16(float x) {
     return ((u & 0x7fffffffu) > 0x7f800000u) ? 0x7fc0u : r;
 }
 
-// One element of the update: g is the reduced, scaled gradient.
+// One element of the update: g is the reduced, scaled gradient.  U1 (U2)
+// says that bc1 (bc2) is exactly 1.0f, which it is once beta^t has fallen
+// below 2^-25: x / 1.0f == x for every x, so the division is left out and
+// the result is bit for bit the same.
+template <bool U1 = false, bool U2 = false>
 __device__ __forceinline__ void adamw(float &w, float &m, float &v, float g, bool decay,
                                       const StepArgs &a) {
 #pragma clang fp contract(off)
     const float m1 = a.b1 * m + a.c1 * g;
     const float v1 = a.b2 * v + a.c2 * (g * g);
-    const float mh = m1 / a.bc1;
-    const float vh = v1 / a.bc2;
+    const float mh = U1 ? m1 : m1 / a.bc1;
+    const float vh = U2 ? v1 : v1 / a.bc2;
     const float u = mh / (sqrtf(vh) + a.eps);
     const float wd = decay ? w * a.df : w;
     w = wd - a.lr * u;
@@ -302,7 +306,7 @@ __device__ __forceinline__ uint32_t quantize_block(const uint32_t bits[4], uint3
 }
 
 // Reduce, update and pack one lane's quad.  mask bit e = decay of element e.
-template <int K, int V, int NT>
+template <int K, int V, int NT, bool U1, bool U2>
 __device__ __forceinline__ void quad_update(f32x4 &w, f32x4 &m, f32x4 &v,
                                             const QuadGrads<K, V, NT> &gr, uint32_t mask,
                                             const StepArgs &a, u32x2 &pout) {
@@ -310,7 +314,7 @@ __device__ __forceinline__ void quad_update(f32x4 &w, f32x4 &m, f32x4 &v,
     for (int e = 0; e < 4; ++e) {
         const float g = gr.reduced(e, a);
         float we = w[e], me = m[e], ve = v[e];
-        adamw(we, me, ve, g, (mask >> e) & 1u, a);
+        adamw<U1, U2>(we, me, ve, g, (mask >> e) & 1u, a);
         w[e] = we;
         m[e] = me;
         v[e] = ve;
@@ -318,7 +322,9 @@ __device__ __forceinline__ void quad_update(f32x4 &w, f32x4 &m, f32x4 &v,
     pout = f32x4_to_bf16x4(w);
 }
 
-template <int K, int V, int NT>
+// U: bit 0 leaves out the division by bc1, bit 1 the division by bc2 (the
+// host picks these kernels only when that correction is exactly 1.0f).
+template <int K, int V, int NT, int U>
 __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) {
     constexpr int kQuads = quads_for(K);      // sub-windows per wave per tile
     constexpr int kWindow = kQuads * kSub;    // elements per wave per tile
@@ -377,8 +383,8 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
             for (int qd = 0; qd < kQuads; ++qd) {
                 const int64_t qi = e[qd] / kQuad;
                 u32x2 pq;
-                quad_update<K, V, NT>(wv[qd], mv[qd], vv[qd], gq[qd], (mask >> (kQuad * qd)) & 0xfu,
-                                      a, pq);
+                quad_update<K, V, NT, (U & 1) != 0, (U & 2) != 0>(
+                    wv[qd], mv[qd], vv[qd], gq[qd], (mask >> (kQuad * qd)) & 0xfu, a, pq);
                 store<NT>(pw + qi, wv[qd]);
                 if constexpr (V & kMvBf16) {
                     store<NT>(reinterpret_cast<u32x2 *>(a.m) + qi, f32x4_to_bf16x4(mv[qd]));
@@ -416,7 +422,7 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
                     mvv = reinterpret_cast<const float *>(a.m)[i];
                     vvv = reinterpret_cast<const float *>(a.v)[i];
                 }
-                adamw(wv, mvv, vvv, g, (mask >> q) & 1u, a);
+                adamw<(U & 1) != 0, (U & 2) != 0>(wv, mvv, vvv, g, (mask >> q) & 1u, a);
                 a.master[i] = wv;
                 if constexpr (V & kMvBf16) {
                     reinterpret_cast<uint16_t *>(a.m)[i] = (uint16_t)to_bf16(mvv);
@@ -451,35 +457,47 @@ static_assert(sizeof(WaveSlot) * (kThreads / kWave) == kStaticLds, "LDS per work
 
 }  // namespace
 
+template <int K, int V>
+kernel_fn pick_unit(int unit) {
+    switch (unit) {
+        case 3: return shard_step_kernel<K, V, 1, 3>;
+        case 1: return shard_step_kernel<K, V, 1, 1>;
+        default: return shard_step_kernel<K, V, 1, 0>;
+    }
+}
+
 template <int K>
-kernel_fn pick_variant(int variant, int nt) {
+kernel_fn pick_variant(int variant, int nt, int unit) {
     switch (variant) {
-        case 0: return nt ? shard_step_kernel<K, 0, 1> : shard_step_kernel<K, 0, 0>;
-        case kOutQ8: return shard_step_kernel<K, kOutQ8, 1>;
-        case kGradQ8: return shard_step_kernel<K, kGradQ8, 1>;
-        case kMvBf16: return shard_step_kernel<K, kMvBf16, 1>;
+        case 0: return nt ? pick_unit<K, 0>(unit) : shard_step_kernel<K, 0, 0, 0>;
+        case kOutQ8: return pick_unit<K, kOutQ8>(unit);
+        case kGradQ8: return pick_unit<K, kGradQ8>(unit);
+        case kMvBf16: return pick_unit<K, kMvBf16>(unit);
         default: return nullptr;
     }
 }
 
-kernel_fn pick_kernel(int k, int variant, int nt) {
+kernel_fn pick_kernel(int k, int variant, int nt, int unit_bc) {
+    // kernels without the bc1 division, or without both; otherwise the
+    // general one (bc2 reaching 1.0f before bc1 needs beta2 < beta1)
+    const int unit = unit_bc == 3 ? 3 : (unit_bc & 1);
     switch (k) {
-        case 1: return pick_variant<1>(variant, nt);
-        case 2: return pick_variant<2>(variant, nt);
-        case 3: return pick_variant<3>(variant, nt);
-        case 4: return pick_variant<4>(variant, nt);
-        case 5: return pick_variant<5>(variant, nt);
-        case 6: return pick_variant<6>(variant, nt);
-        case 7: return pick_variant<7>(variant, nt);
-        case 8: return pick_variant<8>(variant, nt);
-        case 9: return pick_variant<9>(variant, nt);
-        case 10: return pick_variant<10>(variant, nt);
-        case 11: return pick_variant<11>(variant, nt);
-        case 12: return pick_variant<12>(variant, nt);
-        case 13: return pick_variant<13>(variant, nt);
-        case 14: return pick_variant<14>(variant, nt);
-        case 15: return pick_variant<15>(variant, nt);
-        case 16: return pick_variant<16>(variant, nt);
+        case 1: return pick_variant<1>(variant, nt, unit);
+        case 2: return pick_variant<2>(variant, nt, unit);
+        case 3: return pick_variant<3>(variant, nt, unit);
+        case 4: return pick_variant<4>(variant, nt, unit);
+        case 5: return pick_variant<5>(variant, nt, unit);
+        case 6: return pick_variant<6>(variant, nt, unit);
+        case 7: return pick_variant<7>(variant, nt, unit);
+        case 8: return pick_variant<8>(variant, nt, unit);
+        case 9: return pick_variant<9>(variant, nt, unit);
+        case 10: return pick_variant<10>(variant, nt, unit);
+        case 11: return pick_variant<11>(variant, nt, unit);
+        case 12: return pick_variant<12>(variant, nt, unit);
+        case 13: return pick_variant<13>(variant, nt, unit);
+        case 14: return pick_variant<14>(variant, nt, unit);
+        case 15: return pick_variant<15>(variant, nt, unit);
+        case 16: return pick_variant<16>(variant, nt, unit);
         default: return nullptr;
     }
 }
