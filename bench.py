@@ -75,18 +75,199 @@ def measured_traffic(config: str, launch_key: str):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(w, seconds: float, variant: str, bytes_per_elem: float):
-    """Time the CPU oracle (single thread, as it stands) on a bounded window
-    of the same workload: the first min(n, 2^24) elements of the shard, with
-    the arithmetic of the entry point being measured.  The "threaded" entry
-    times the same oracle over T contiguous ranges of that window."""
+def launch_key(plan: dict) -> str:
+    """The launch a step resolves to (zs_launch_plan), as the key under which
+    measured traffic is stored: any change of the library's defaults that
+    changes grid, chunk, chunk order, occupancy cap or cache policy changes it."""
+    return "wg=%d,chunk=%d,order=%d,cap=%d,nt=%d" % (
+        plan["workgroups"], plan["chunk_elements"], plan["block_order"],
+        plan["groups_per_cu"], plan["nontemporal"])
+
+
+def host_info():
+    """CPU model, online CPUs and the CPUs this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "online_cpus": os.cpu_count(),
+            "usable_cpus": len(os.sched_getaffinity(0))}
+
+
+# A one-GPU share of the GPU hosts is 16 CPUs: the threaded oracle uses at most
+# that many threads, whatever the host has online.
+HOST_THREAD_CAP = 16
+
+
+def oracle_threads() -> int:
+    return max(1, min(len(os.sched_getaffinity(0)), HOST_THREAD_CAP))
+
+
+# ---------------------------------------------------------------- parity windows
+
+PARITY_WINDOW = 1 << 16
+
+
+def parity_windows(w, n: int, count: int = 10):
+    """Windows [a, b) of the shard that the cpu_baseline leg replays with the
+    oracle: the first, the last (the tail), up to six around segment
+    boundaries and random ones; starts on 256-element block boundaries."""
+    import random
+    L = min(PARITY_WINDOW, n)
+
+    def at(a):
+        a = max(0, min(a, n - L)) // 256 * 256
+        return (a, min(a + L, n))
+
+    wins = [at(0), at(n - L)]
+    starts = [s for s, _ in w.shard.segments[1:] if 0 < s < n]
+    if starts:
+        pick = sorted(set(starts[i * len(starts) // 6] for i in range(min(6, len(starts)))))
+        wins += [at(s - L // 2) for s in pick]
+    rng = random.Random(w.seed)
+    while len(wins) < count:
+        wins.append(at(rng.randrange(0, max(1, n - L))))
+    out = []
+    for x in sorted(set(wins)):
+        if not out or x[0] >= out[-1][1]:
+            out.append(x)
+    return out
+
+
+def snapshot(tensors, wins):
+    """D2H copies of the windows of each tensor: {name: [np.ndarray per window]}."""
+    out = {}
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        out[name] = [t[a:b].cpu().numpy().copy() for a, b in wins]
+    return out
+
+
+def block_slice(t, a, b):
+    return t[a // 256:-(-b // 256)]
+
+
+def _rel_err(got, ref):
+    import numpy as np
+    g = got.astype(np.float64)
+    r = ref.astype(np.float64)
+    both_nan = np.isnan(g) & np.isnan(r)
+    d = np.where(both_nan, 0.0, np.abs(g - r) / np.maximum(1.0, np.abs(r)))
+    d = np.where(np.isnan(d), np.inf, d)
+    return float(d.max()) if d.size else 0.0
+
+
+def _bf16_ulp(got, ref):
+    import numpy as np
+    g = got.view(np.uint16).astype(np.int64)
+    r = ref.view(np.uint16).astype(np.int64)
+    nan = lambda x: ((x & 0x7fff) > 0x7f80)  # noqa: E731
+    same = (g == r) | (nan(g) & nan(r))
+    # signed-magnitude order of the bit patterns
+    key = lambda x: np.where(x & 0x8000, -(x & 0x7fff), x)  # noqa: E731
+    d = np.where(same, 0, np.abs(key(g) - key(r)))
+    return int(d.max()) if d.size else 0
+
+
+def cpu_baseline(w, seconds: float, variant: str, bytes_per_elem: float, parity=None):
+    """The CPU oracle, as it stands, on bounded samples of the same workload.
+
+    1. Parity (when `parity` holds the GPU run's windows): the oracle replays
+       the timed run's step sequence on the windows' initial state and the
+       resident partials, and its results are compared with the GPU's state
+       after the timed steps (the step is elementwise, so a window's result
+       depends only on that window's inputs).
+    2. Throughput: the oracle, single-threaded, on the first min(n, 2^27)
+       elements of the shard for about `seconds`, and the same oracle driven
+       from T threads over T contiguous ranges of that window."""
+    par = _parity_replay(w, variant, parity) if parity else None
+    res = _throughput_sample(w, seconds, variant, bytes_per_elem)
+    res["parity"] = par
+    return res
+
+
+def _parity_replay(w, variant, par):
     import numpy as np
 
     import oracle
     import synth
 
-    n = min(w.n, 1 << 24)
-    master = synth.host_master(w, 0, n)
+    wins, before, after, ts = par["windows"], par["before"], par["after"], par["ts"]
+    hp = oracle.hparams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, 1.0)
+    errs = {"master": 0.0, "m": 0.0, "v": 0.0}
+    ulp_p = ulp_mv = dq = 0
+    exact = True
+    elems = 0
+    t_start = time.perf_counter()
+    for i, (a, b) in enumerate(wins):
+        n = b - a
+        elems += n
+        master = before["master"][i].copy()
+        m = before["m"][i].copy()
+        v = before["v"][i].copy()
+        p = np.zeros(n, np.uint16)
+        segs = synth.clip_segments(w.shard.segments, a, b)
+        for t in ts:
+            if variant == "q8grad":
+                rc = oracle.shard_step_q8grad(master, m, v, p, [q[i] for q in par["qgrads"]],
+                                              [s[i] for s in par["qscales"]], segs, hp, t)
+            elif variant == "bf16mv":
+                rc = oracle.shard_step_bf16mv(master, m.view(np.uint16), v.view(np.uint16), p,
+                                              [g[i].view(np.uint16) for g in par["grads"]],
+                                              segs, hp, t)
+            else:
+                rc = oracle.shard_step(master, m, v, p,
+                                       [g[i].view(np.uint16) for g in par["grads"]], segs, hp, t)
+            assert rc == 0, rc
+        gm, gmm, gv = after["master"][i], after["m"][i], after["v"][i]
+        gp = after["param"][i].view(np.uint16)
+        exact &= gm.tobytes() == master.tobytes() and gmm.tobytes() == m.tobytes() and \
+            gv.tobytes() == v.tobytes() and gp.tobytes() == p.tobytes()
+        errs["master"] = max(errs["master"], _rel_err(gm, master))
+        if variant == "bf16mv":
+            ulp_mv = max(ulp_mv, _bf16_ulp(gmm, m), _bf16_ulp(gv, v))
+        else:
+            errs["m"] = max(errs["m"], _rel_err(gmm, m))
+            errs["v"] = max(errs["v"], _rel_err(gv, v))
+        ulp_p = max(ulp_p, _bf16_ulp(gp, p))
+        if variant == "q8ag":
+            q, sc = oracle.q8_blocks(p, 256)
+            gq = after["q8"][i]
+            gs = after["q8s"][i]
+            exact &= gq.tobytes() == q.tobytes() and gs.tobytes() == sc.tobytes()
+            dq = max(dq, int(np.abs(gq.astype(np.int32) - q.astype(np.int32)).max()))
+    elapsed = time.perf_counter() - t_start
+    out = {"windows": len(wins), "window_elements": elems, "steps_replayed": len(ts),
+           "first_t": ts[0], "last_t": ts[-1],
+           "max_rel_err": {k: float("%.3g" % e) for k, e in errs.items()
+                           if not (variant == "bf16mv" and k != "master")},
+           "max_param_bf16_ulp": ulp_p, "bitwise_equal": bool(exact),
+           "oracle_seconds": round(elapsed, 3)}
+    if variant == "bf16mv":
+        out["max_moment_bf16_ulp"] = ulp_mv
+    if variant == "q8ag":
+        out["max_q8_code_diff"] = dq
+    tol_ok = all(e <= 1e-6 for e in errs.values()) and ulp_p <= 1 and ulp_mv <= 1 and dq <= 1
+    out["within_tolerance"] = bool(tol_ok)
+    out["tolerance"] = "|d| <= 1e-6*max(1,|x|) on fp32 master/m/v, <= 1 bf16 ulp on bf16 outputs"
+    return out
+
+
+def _throughput_sample(w, seconds, variant, bytes_per_elem):
+    import numpy as np
+
+    import oracle
+    import synth
+
+    n = min(w.n, 1 << 27)
+    threads = oracle_threads()
+    master = synth.host_master(w, 0, n, threads=threads)
     mv_dtype = np.uint16 if variant == "bf16mv" else np.float32
     m = np.zeros(n, mv_dtype)
     v = np.zeros(n, mv_dtype)
@@ -94,7 +275,7 @@ def cpu_baseline(w, seconds: float, variant: str, bytes_per_elem: float):
     if variant == "q8grad":
         qgrads, qscales = synth.host_qgrads(w, w.t0, 0, n)
     else:
-        grads = synth.host_grads(w, w.t0, 0, n)
+        grads = synth.host_grads(w, w.t0, 0, n, threads=threads)
     segs = synth.clip_segments(w.shard.segments, 0, n)
     hp = oracle.hparams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, 1.0)
     steps = 0
@@ -119,7 +300,7 @@ def cpu_baseline(w, seconds: float, variant: str, bytes_per_elem: float):
         elapsed += time.perf_counter() - t0
         steps += 1
     threaded = _threaded_oracle(master, m, v, p, grads if variant != "q8grad" else None,
-                                segs, hp, t, variant, bytes_per_elem,
+                                segs, hp, t, variant, bytes_per_elem, threads,
                                 qgrads if variant == "q8grad" else None,
                                 qscales if variant == "q8grad" else None)
     return {
@@ -129,6 +310,7 @@ def cpu_baseline(w, seconds: float, variant: str, bytes_per_elem: float):
         "cores": 1,
         "threaded": threaded,
         "kind": "oracle",
+        "host": host_info(),
         "sample": "first %d elements of the %s shard (k=%d, %d segments in the window), "
                   "%d timed oracle steps after one untimed (%s arithmetic), single-threaded C, %.1f s" % (
                       n, w.name.split(":")[0].split(" (")[0], w.k, len(segs), steps, variant,
@@ -136,18 +318,17 @@ def cpu_baseline(w, seconds: float, variant: str, bytes_per_elem: float):
     }
 
 
-def _threaded_oracle(master, m, v, p, grads, segs, hp, t, variant, bytes_per_elem,
+def _threaded_oracle(master, m, v, p, grads, segs, hp, t, variant, bytes_per_elem, threads,
                      qgrads=None, qscales=None, seconds=3.0):
     """The same oracle driven from T threads over T contiguous ranges of the
     window (the step is elementwise, so the split does not change a bit);
-    T = the CPUs this process may use, at most 16."""
+    T = the CPUs this process may use, at most HOST_THREAD_CAP."""
     from concurrent.futures import ThreadPoolExecutor
 
     import oracle
     import synth
 
     n = master.shape[0]
-    threads = max(1, min(len(os.sched_getaffinity(0)), 16))
     # ranges on 256-element boundaries so that q8 blocks never straddle two threads
     per = -(-n // threads)
     per = -(-per // 256) * 256
@@ -181,7 +362,9 @@ def _threaded_oracle(master, m, v, p, grads, segs, hp, t, variant, bytes_per_ele
             t += 1
     return {"value": round(n * steps * bytes_per_elem / elapsed / 1e9, 4),
             "params_per_s": round(n * steps / elapsed, 1), "cores": len(ranges),
-            "steps": steps}
+            "steps": steps,
+            "thread_rule": "the CPUs this process may use, at most %d (one GPU's share of "
+                           "the host)" % HOST_THREAD_CAP}
 
 
 def _ceiling_lib():
@@ -190,10 +373,72 @@ def _ceiling_lib():
     if not os.path.exists(path):
         raise ImportError("libzs_ceiling.so is not built; run __graft_entry__.build()")
     lib = ctypes.CDLL(path)
-    lib.zs_ceiling_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-                                    ctypes.c_void_p]
+    P = ctypes.c_void_p
+    lib.zs_ceiling_copy.argtypes = [P, P, ctypes.c_int64, P]
     lib.zs_ceiling_copy.restype = ctypes.c_int
+    lib.zs_ceiling_twin.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P, P, P, P, P, P,
+                                    ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                    ctypes.c_int, P]
+    lib.zs_ceiling_twin.restype = ctypes.c_int
     return lib
+
+
+def twin_bytes(variant: str, k: int, n: int):
+    """(read, written) bytes of the step's streams over n elements."""
+    nb = -(-n // 256)
+    return {"base": ((12 + 2 * k) * n, 14 * n),
+            "q8ag": ((12 + 2 * k) * n, 15 * n + 4 * nb),
+            "q8grad": (12 * n + k * (n + 4 * nb), 14 * n),
+            "bf16mv": ((8 + 2 * k) * n, 10 * n)}[variant]
+
+
+class Twin:
+    """The step's traffic without its arithmetic (libzs_ceiling.so), on the
+    step's own buffers and in the step's own launch."""
+    MODES = {"step": 0, "read": 1, "write": 2}
+    LAYOUT = {"base": 0, "q8ag": 1, "q8grad": 2, "bf16mv": 4}
+
+    def __init__(self, torch, variant, bufs, k, n, plan):
+        import ctypes
+        self.torch, self.variant, self.k = torch, variant, k
+        self.lib = _ceiling_lib()
+        self.chunk = plan["chunk_elements"]
+        self.n = n // self.chunk * self.chunk if self.chunk else 0
+        self.ok = plan["nontemporal"] == 1 and self.n > 0 and self.chunk % 1024 == 0
+        self.plan = plan
+        ptr = lambda t: ctypes.c_void_p(t.data_ptr() if t is not None else 0)  # noqa: E731
+        self.head = [ptr(bufs["master"]), ptr(bufs["m"]), ptr(bufs["v"]), ptr(bufs["param"]),
+                     ptr(bufs.get("q8")), ptr(bufs.get("q8s"))]
+        gl = bufs.get("qgrads") if variant == "q8grad" else bufs["grads"]
+        self.gp = (ctypes.c_void_p * k)(*[g.data_ptr() for g in gl])
+        sl = bufs.get("qscales") if variant == "q8grad" else None
+        self.sp = (ctypes.c_void_p * k)(*[s.data_ptr() for s in sl]) if sl else None
+
+    def launch(self, mode, stream):
+        import ctypes
+        rc = self.lib.zs_ceiling_twin(
+            self.MODES[mode], self.LAYOUT[self.variant], *self.head,
+            ctypes.cast(self.gp, ctypes.c_void_p),
+            ctypes.cast(self.sp, ctypes.c_void_p) if self.sp is not None else None,
+            self.k, self.n, self.chunk, self.plan["block_order"], self.plan["groups_per_cu"],
+            ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError("zs_ceiling_twin(%s) failed: %d" % (mode, rc))
+
+    def rate(self, mode, stream, reps=4):
+        """GB/s of one mode: the bytes it moves over its mean HIP-event time."""
+        torch = self.torch
+        rb, wb = twin_bytes(self.variant, self.k, self.n)
+        nbytes = {"step": rb + wb, "read": rb, "write": wb}[mode]
+        self.launch(mode, stream)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for _ in range(reps):
+            self.launch(mode, stream)
+        e.record(stream)
+        torch.cuda.synchronize()
+        return nbytes / (s.elapsed_time(e) / reps * 1e-3) / 1e9
 
 
 def copy_ceiling(torch, nbytes: int):
@@ -357,6 +602,8 @@ def main():
                          "(per-launch times are then the graph's average per step)")
     ap.add_argument("--copy-gb", type=float, default=8.0,
                     help="size of the in-run copy-ceiling measurement (0 = skip)")
+    ap.add_argument("--no-twin", action="store_true",
+                    help="skip the twin ceilings (the step's traffic without arithmetic)")
     args = ap.parse_args()
     if args.steps is None:
         args.steps = 200 if args.config in ("tiny", "gpt2-small") else 10
@@ -390,12 +637,19 @@ def main():
 
     w = synth.workload(args.config)
     n, k = w.n, w.k
-    bytes_per_step = zs.algorithmic_bytes(args.variant, k, n)
+    var = args.variant
+    bytes_per_step = zs.algorithmic_bytes(var, k, n)
     bpe = bytes_per_step / n
-    if args.variant == "base":
+    if var == "base":
         assert zs.zs_algorithmic_bytes(k, n) == bytes_per_step
     log("workload: %s  n=%d k=%d segments=%d bytes/step=%.3f GB" % (
         w.name, n, k, len(w.shard.segments), bytes_per_step / 1e9))
+    cfg = dict(chunk_tiles=args.chunk_tiles, nontemporal=args.nontemporal,
+               groups_per_cu=args.groups_per_cu, block_order=args.block_order)
+    cfg = cfg if any(cfg.values()) else None
+    plan = zs.zs_launch_plan(k, n, var, cfg)
+    key = launch_key(plan)
+    log("launch: %s" % key)
 
     copies = {}
     if args.copy_gb > 0:
@@ -404,7 +658,6 @@ def main():
             args.copy_gb, copies["stream"], copies["torch"]))
 
     dev = torch.device("cuda:0")
-    var = args.variant
     nb = -(-n // zs.ZS_Q8_BLOCK)
     mv_dtype = torch.int16 if var == "bf16mv" else torch.float32
     master = torch.empty(n, dtype=torch.float32, device=dev)
@@ -425,7 +678,21 @@ def main():
     st = zs.seg_table(table)
     hp = zs.hparams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, 1.0)
     stream = torch.cuda.current_stream()
+
+    # Twin ceilings: the step's traffic without its arithmetic, on these very
+    # buffers and in the step's launch.  Writes only first (it overwrites the
+    # state, which is initialised afterwards), reads only and the whole
+    # traffic (which leaves the state as it was) once the inputs are in place.
+    twin = None
+    ceil = {}
+    if not args.no_twin:
+        twin = Twin(torch, var, dict(master=master, m=m, v=v, param=param, q8=q8, q8s=q8s,
+                                     grads=grads, qgrads=qgrads, qscales=qscales), k, n, plan)
+        if twin.ok:
+            ceil["write"] = twin.rate("write", stream)
     synth.dev_master(w, master)
+    m.zero_()
+    v.zero_()
 
     # the call is checked and marshalled once; each step passes t and the stream
     if var == "q8grad":
@@ -437,10 +704,7 @@ def main():
     elif var == "bf16mv":
         call = zs.ShardStep(master, m, v, param, grads, n, st, hp, variant="bf16mv")
     else:
-        cfg = dict(chunk_tiles=args.chunk_tiles, nontemporal=args.nontemporal,
-                   groups_per_cu=args.groups_per_cu, block_order=args.block_order)
-        call = zs.ShardStep(master, m, v, param, grads, n, st, hp,
-                            cfg=cfg if any(cfg.values()) else None)
+        call = zs.ShardStep(master, m, v, param, grads, n, st, hp, cfg=cfg)
 
     def step(t, on=None):
         call(t, stream if on is None else on)
@@ -458,6 +722,24 @@ def main():
     # the partials of the first measured step stay resident for every timed step
     fill(w.t0)
     torch.cuda.synchronize()
+    if twin is not None and twin.ok:
+        ceil["read"] = twin.rate("read", stream)
+        ceil["step"] = twin.rate("step", stream)
+        log("twin of the step's traffic: whole %.1f GB/s, reads %.1f GB/s, writes %.1f GB/s"
+            % (ceil["step"], ceil["read"], ceil["write"]))
+
+    # the windows the cpu_baseline leg replays with the oracle: their inputs now
+    par = None
+    if args.cpu_seconds > 0:
+        wins = parity_windows(w, n)
+        before = snapshot({"master": master, "m": m, "v": v}, wins)
+        if var == "q8grad":
+            qg = [[q[a:b].cpu().numpy().copy() for a, b in wins] for q in qgrads]
+            qs = [[block_slice(s, a, b).cpu().numpy().copy() for a, b in wins] for s in qscales]
+            par = dict(qgrads=qg, qscales=qs)
+        else:
+            par = dict(grads=[[g[a:b].cpu().numpy().copy() for a, b in wins] for g in grads])
+        par.update(windows=wins, before=before)
 
     t = w.t0
     for _ in range(args.warmup):
@@ -500,25 +782,41 @@ def main():
     avg_ms = sum(kernel_ms) / len(kernel_ms)
     log("kernel ms per launch: avg %.4f min %.4f max %.4f" % (avg_ms, min(kernel_ms),
                                                               max(kernel_ms)))
+    if par is not None:
+        after = snapshot({"master": master, "m": m, "v": v, "param": param, "q8": q8}, wins)
+        if var == "q8ag":
+            after["q8s"] = [block_slice(q8s, a, b).cpu().numpy().copy() for a, b in wins]
+        par.update(after=after, ts=list(range(w.t0, t)))
 
     value = bytes_per_step * args.steps / elapsed / 1e9
     achieved = bytes_per_step / (avg_ms * 1e-3) / 1e9
-    launch_key = "chunk_tiles=%d,nontemporal=%d" % (args.chunk_tiles, args.nontemporal)
-    if args.groups_per_cu:
-        launch_key += ",groups_per_cu=%d" % args.groups_per_cu
-    if args.block_order:
-        launch_key += ",block_order=%d" % args.block_order
     traffic_key = args.config if var == "base" else "%s/%s" % (args.config, var)
-    traffic = measured_traffic(traffic_key, launch_key)
+    traffic = measured_traffic(traffic_key, key)
 
-    del master, m, v, param, grads, qgrads, qscales, q8, q8s
+    del master, m, v, param, grads, qgrads, qscales, q8, q8s, twin
     torch.cuda.empty_cache()
 
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, args.cpu_seconds, var, bpe)
+        cpu = cpu_baseline(w, args.cpu_seconds, var, bpe, par)
         log("cpu oracle: %.3f GB/s (%s)" % (cpu["value"], cpu["sample"]))
+        log("parity of the timed run: %s" % json.dumps(cpu["parity"]))
 
+    ceilings = None
+    if ceil:
+        rb, wb = twin_bytes(var, k, n)
+        ceilings = {
+            "twin_step_gbps": round(ceil["step"], 1),
+            "twin_read_gbps": round(ceil["read"], 1),
+            "twin_write_gbps": round(ceil["write"], 1),
+            # reads and writes each at their own ceiling, one after the other
+            "serial_read_write_gbps": round((rb + wb) / (rb / ceil["read"] +
+                                                         wb / ceil["write"]), 1),
+            "pct_of_twin": round(100.0 * achieved / ceil["step"], 2),
+            "kind": "the step's own streams, buffers and launch with no arithmetic "
+                    "(libzs_ceiling.so zs_ceiling_twin): whole traffic (state written back "
+                    "unchanged), reads only, writes only; HIP events, same run",
+        }
     out = {
         "metric": "achieved HBM GB/s (% of peak) and params/s for fused ZeRO-shard AdamW step",
         "value": round(value, 2),
@@ -546,6 +844,7 @@ def main():
             "bytes_per_param": round(bpe, 4),
             "bytes_per_step": bytes_per_step,
             "first_step_t": w.t0 + args.warmup,
+            "launch": key,
         },
         "params_per_s": round(n * args.steps / elapsed, 1),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
@@ -554,6 +853,7 @@ def main():
                              "(libzs_ceiling.so) of --copy-gb bytes, read + write, same run",
         "pct_of_copy_ceiling": round(100.0 * achieved / copies["stream"], 2) if copies else None,
         "torch_copy_gbps": round(copies["torch"], 1) if copies else None,
+        "ceilings": ceilings,
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
@@ -568,6 +868,7 @@ def main():
         },
         "kernel_ms": {"median": round(statistics.median(kernel_ms), 4),
                       "min": round(min(kernel_ms), 4), "max": round(max(kernel_ms), 4)},
+        "parity": cpu["parity"] if cpu else None,
         "cpu_baseline": cpu,
         "speedup_vs_cpu_oracle": None if not cpu else {
             "single_thread": round(value / cpu["value"], 1),

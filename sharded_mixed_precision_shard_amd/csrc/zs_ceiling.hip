@@ -1,13 +1,19 @@
-// zs_ceiling.hip -- a plain streaming copy for gfx950, the in-run bandwidth
-// ceiling that bench.py measures beside the shard step (measurement only;
-// the step never calls it).
+// zs_ceiling.hip -- bandwidth ceilings for gfx950 that bench.py measures
+// beside the shard step (measurement only; the step never calls them).
 //
-// Same access pattern as the step: 256-thread workgroups, each lane moving
-// one 16-byte quad per sub-window, every instruction of a wavefront one
-// dense 1 KB run, non-temporal loads and stores, one 4 KB tile per
-// workgroup.  It reads each byte once and writes each byte once, so its
-// rate is the best a one-read-one-write stream reaches on the same box and
-// allocation pattern.
+//  * zs_ceiling_copy: a plain streaming copy (one read stream, one write
+//    stream), 16-byte non-temporal accesses, every wavefront instruction one
+//    dense 1 KB run.
+//  * zs_ceiling_twin: the step's own memory traffic with no arithmetic, on
+//    the step's own buffers and in the step's own launch (grid, chunk, chunk
+//    order, occupancy cap): every stream the step reads is read with the
+//    same instruction shape and every stream it writes is written, in the
+//    same order per wavefront.  Three modes: the whole step's traffic (each
+//    state array is written back with the bits just read, so the state is
+//    left as it was; the output arrays get arbitrary bytes), the read streams
+//    alone, or the write streams alone (which overwrites the state).  Its
+//    rate is what the memory system delivers for exactly this traffic on
+//    this box and this physical placement of the arrays.
 
 #include <hip/hip_runtime.h>
 
@@ -16,8 +22,15 @@
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
+constexpr int kWave = 64;
+constexpr int kQuad = 4;                  // elements per lane per sub-window
+constexpr int kSub = kWave * kQuad;       // 256 elements per wavefront window
+constexpr int kTile = kSub * (kThreads / kWave);
+constexpr int kMaxK = 16;
+constexpr int kBlock = 256;               // int8 quantization block
 // A dispatch packet holds the grid size in work-items as a 32-bit number.
 constexpr int64_t kMaxBlocks = 0xffffffffLL / kThreads;
 
@@ -29,6 +42,207 @@ __global__ __launch_bounds__(kThreads) void stream_copy(const f32x4 *__restrict_
     for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nq; i += stride)
         __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
+
+// Stream layouts of the step's entry points.
+constexpr int kLayoutBase = 0;    // f32 master/m/v, bf16 partials, bf16 param
+constexpr int kLayoutQ8Out = 1;   // + int8 parameter copy and one f32 scale per block
+constexpr int kLayoutQ8Grad = 2;  // int8 partials with one f32 scale per block each
+constexpr int kLayoutBf16Mv = 4;  // bf16 m and v
+
+// Modes: 0 = the step's reads and writes, then
+constexpr int kModeRead = 1;   // its reads only
+constexpr int kModeWrite = 2;  // its writes only
+
+struct TwinArgs {
+    float *master;
+    void *m;
+    void *v;
+    uint16_t *param;
+    int8_t *q8;
+    float *q8_scale;
+    const void *grads[kMaxK];
+    const float *qscales[kMaxK];
+    uint32_t *sink;   // one word, written only if a read-only pass meets a sentinel
+    int64_t n;
+    int64_t chunk;    // elements per workgroup, a multiple of kTile
+    int32_t xcds;     // > 1: XCD-contiguous chunk order
+    int32_t mode;
+};
+
+template <typename T>
+__device__ __forceinline__ T ld(const void *p, int64_t i) {
+    return __builtin_nontemporal_load(reinterpret_cast<const T *>(p) + i);
+}
+template <typename T>
+__device__ __forceinline__ void st(void *p, int64_t i, T x) {
+    __builtin_nontemporal_store(x, reinterpret_cast<T *>(p) + i);
+}
+// Hide a value from the optimizer so that a store of it is kept as it is.
+template <typename T>
+__device__ __forceinline__ void opaque(T &x) {
+    asm volatile("" : "+v"(x));
+}
+
+template <int K, int L>
+__global__ __launch_bounds__(kThreads) void twin_kernel(const TwinArgs a) {
+    constexpr bool kMv16 = (L & kLayoutBf16Mv) != 0;
+    constexpr bool kG8 = (L & kLayoutQ8Grad) != 0;
+    constexpr bool kOut8 = (L & kLayoutQ8Out) != 0;
+    const int lane = (int)(threadIdx.x % kWave);
+    const int wave = (int)(threadIdx.x / kWave);
+    int64_t b = blockIdx.x;
+    if (a.xcds > 1) {
+        const int64_t nb = gridDim.x, q = nb / a.xcds, r = nb % a.xcds;
+        const int64_t x = b % a.xcds, y = b / a.xcds;
+        b = x * q + (x < r ? x : r) + y;
+    }
+    const int64_t c0 = b * a.chunk;
+    const int64_t c1 = (c0 + a.chunk < a.n) ? c0 + a.chunk : a.n;
+    for (int64_t t0 = c0; t0 < c1; t0 += kTile) {
+        const int64_t w0 = t0 + (int64_t)wave * kSub;
+        if (w0 + kSub > c1) continue;  // whole windows only; the host sizes n to match
+        const int64_t qi = w0 / kQuad + lane;  // this lane's quad
+        if (a.mode == kModeWrite) {
+            const f32x4 z = {1.0f, 2.0f, 3.0f, 4.0f};
+            const u32x2 h = {0x3f803f80u, 0x3f803f80u};
+            st<f32x4>(a.master, qi, z);
+            if constexpr (kMv16) {
+                st<u32x2>(a.m, qi, h);
+                st<u32x2>(a.v, qi, h);
+            } else {
+                st<f32x4>(a.m, qi, z);
+                st<f32x4>(a.v, qi, z);
+            }
+            st<u32x2>(a.param, qi, h);
+            if constexpr (kOut8) {
+                st<uint32_t>(a.q8, qi, 0x01010101u);
+                if (lane == 0) a.q8_scale[w0 / kBlock] = 1.0f;
+            }
+            continue;
+        }
+        f32x4 w = ld<f32x4>(a.master, qi);
+        f32x4 m, v;
+        u32x2 mh, vh;
+        if constexpr (kMv16) {
+            mh = ld<u32x2>(a.m, qi);
+            vh = ld<u32x2>(a.v, qi);
+        } else {
+            m = ld<f32x4>(a.m, qi);
+            v = ld<f32x4>(a.v, qi);
+        }
+        u32x2 g[K];
+        uint32_t g8[K];
+        float s[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            if constexpr (kG8) {
+                g8[j] = ld<uint32_t>(a.grads[j], qi);
+                s[j] = a.qscales[j][w0 / kBlock];
+            } else {
+                g[j] = ld<u32x2>(a.grads[j], qi);
+            }
+        }
+        if (a.mode == kModeRead) {
+            uint32_t acc = __float_as_uint(w[0]) ^ __float_as_uint(w[1]) ^
+                           __float_as_uint(w[2]) ^ __float_as_uint(w[3]);
+            if constexpr (kMv16) {
+                acc ^= mh[0] ^ mh[1] ^ vh[0] ^ vh[1];
+            } else {
+                acc ^= __float_as_uint(m[0]) ^ __float_as_uint(m[1]) ^ __float_as_uint(m[2]) ^
+                       __float_as_uint(m[3]) ^ __float_as_uint(v[0]) ^ __float_as_uint(v[1]) ^
+                       __float_as_uint(v[2]) ^ __float_as_uint(v[3]);
+            }
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                if constexpr (kG8) acc ^= g8[j] ^ __float_as_uint(s[j]);
+                else acc ^= g[j][0] ^ g[j][1];
+            }
+            if (acc == 0x9e3779b9u) a.sink[0] = acc;
+            continue;
+        }
+        // The whole step's traffic: state written back bit for bit.  Every
+        // value loaded is pinned, so that no load can be dropped as unused.
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            if constexpr (kG8) {
+                opaque(g8[j]);
+                opaque(s[j]);
+            } else {
+                opaque(g[j]);
+            }
+        }
+        opaque(w);
+        st<f32x4>(a.master, qi, w);
+        if constexpr (kMv16) {
+            opaque(mh);
+            opaque(vh);
+            st<u32x2>(a.m, qi, mh);
+            st<u32x2>(a.v, qi, vh);
+        } else {
+            opaque(m);
+            opaque(v);
+            st<f32x4>(a.m, qi, m);
+            st<f32x4>(a.v, qi, v);
+        }
+        u32x2 p;
+        if constexpr (kG8) {
+            p[0] = g8[0];
+            p[1] = __float_as_uint(s[0]);
+        } else {
+            p = g[0];
+        }
+        opaque(p);
+        st<u32x2>(a.param, qi, p);
+        if constexpr (kOut8) {
+            st<uint32_t>(a.q8, qi, p[0]);
+            if (lane == 0) a.q8_scale[w0 / kBlock] = __uint_as_float(p[1]);
+        }
+    }
+}
+
+typedef void (*twin_fn)(const TwinArgs);
+
+template <int K>
+twin_fn pick_layout(int layout) {
+    switch (layout) {
+        case kLayoutBase: return twin_kernel<K, kLayoutBase>;
+        case kLayoutQ8Out: return twin_kernel<K, kLayoutQ8Out>;
+        case kLayoutQ8Grad: return twin_kernel<K, kLayoutQ8Grad>;
+        case kLayoutBf16Mv: return twin_kernel<K, kLayoutBf16Mv>;
+        default: return nullptr;
+    }
+}
+
+twin_fn pick_twin(int k, int layout) {
+    switch (k) {
+        case 1: return pick_layout<1>(layout);
+        case 2: return pick_layout<2>(layout);
+        case 3: return pick_layout<3>(layout);
+        case 4: return pick_layout<4>(layout);
+        case 5: return pick_layout<5>(layout);
+        case 6: return pick_layout<6>(layout);
+        case 7: return pick_layout<7>(layout);
+        case 8: return pick_layout<8>(layout);
+        case 9: return pick_layout<9>(layout);
+        case 10: return pick_layout<10>(layout);
+        case 11: return pick_layout<11>(layout);
+        case 12: return pick_layout<12>(layout);
+        case 13: return pick_layout<13>(layout);
+        case 14: return pick_layout<14>(layout);
+        case 15: return pick_layout<15>(layout);
+        case 16: return pick_layout<16>(layout);
+        default: return nullptr;
+    }
+}
+
+// Per device: one word the read-only mode may write, and the properties the
+// launch needs (queried once; measurement code, not thread-safe).
+struct DevState {
+    uint32_t *sink;
+    int cus;
+    int64_t lds_per_cu, lds_per_group;
+};
+DevState g_dev[64];
 
 }  // namespace
 
@@ -49,6 +263,89 @@ int zs_ceiling_copy(const void *src, void *dst, int64_t bytes, void *stream) {
     hipLaunchKernelGGL(stream_copy, dim3((unsigned)blocks), dim3(kThreads), 0,
                        (hipStream_t)stream, (const f32x4 *)src, (f32x4 *)dst, nq);
     return (int)hipGetLastError();
+}
+
+// The step's traffic without its arithmetic (see the top of this file), on
+// the calling thread's current device and `stream`.
+//   mode: 0 = the step's reads and writes (state left bit for bit as it
+//         was; param and the int8 copy receive arbitrary bytes), 1 = its
+//         reads only, 2 = its writes only (state overwritten).
+//   layout: 0 = zs_shard_step, 1 = zs_shard_step_q8ag, 2 = zs_shard_step_q8grad,
+//         4 = zs_shard_step_bf16mv (the streams and element sizes that entry
+//         point moves).  grads holds k device pointers (int8 for layout 2,
+//         bf16 otherwise); qscales (layout 2) k device pointers to one f32
+//         per 256 elements; q8 and q8_scale (layout 1) the int8 copy and its
+//         scales.
+//   n: elements; a multiple of 1024 and of chunk (the twin covers whole
+//         windows only, so the host rounds a shard down to that).
+//   chunk, block_order (1 linear, 2 XCD-contiguous), groups_per_cu (0 =
+//         none): the launch zs_launch_plan reports for the step.
+// Every pointer is DEVICE memory sized for n elements, 16-byte aligned (the
+// scale arrays 4-byte).  Returns 0, -1 on a bad argument (nothing enqueued),
+// or a hipError_t.
+int zs_ceiling_twin(int mode, int layout, float *master, void *m, void *v, uint16_t *param,
+                    int8_t *q8, float *q8_scale, const void *const *grads,
+                    const float *const *qscales, int k, int64_t n, int64_t chunk,
+                    int block_order, int groups_per_cu, void *stream) {
+    if (mode < 0 || mode > 2 || k < 1 || k > kMaxK || n < 0 || !grads) return -1;
+    if (n % kTile || chunk < kTile || chunk % kTile || (n && n % chunk)) return -1;
+    if (block_order != 1 && block_order != 2) return -1;
+    if (groups_per_cu < 0 || groups_per_cu > 32) return -1;
+    const twin_fn fn = pick_twin(k, layout);
+    if (!fn) return -1;
+    if (!master || !m || !v || !param) return -1;
+    if ((layout & kLayoutQ8Out) && (!q8 || !q8_scale)) return -1;
+    if ((layout & kLayoutQ8Grad) && !qscales) return -1;
+    for (int j = 0; j < k; ++j)
+        if (!grads[j] || ((layout & kLayoutQ8Grad) && !qscales[j])) return -1;
+    if (n == 0) return 0;
+    const int64_t blocks = n / chunk;
+    if (blocks > kMaxBlocks) return -1;
+
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev < 0 || dev >= 64) return -1;
+    DevState &ds = g_dev[dev];
+    if (!ds.sink) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return (int)e;
+        ds.cus = prop.multiProcessorCount;
+        ds.lds_per_cu = (int64_t)prop.maxSharedMemoryPerMultiProcessor;
+        ds.lds_per_group = (int64_t)prop.sharedMemPerBlock;
+        e = hipMalloc((void **)&ds.sink, sizeof(uint32_t));
+        if (e != hipSuccess) return (int)e;
+    }
+    TwinArgs a = {};
+    a.master = master;
+    a.m = m;
+    a.v = v;
+    a.param = param;
+    a.q8 = q8;
+    a.q8_scale = q8_scale;
+    for (int j = 0; j < k; ++j) {
+        a.grads[j] = grads[j];
+        a.qscales[j] = (layout & kLayoutQ8Grad) ? qscales[j] : nullptr;
+    }
+    a.sink = ds.sink;
+    a.n = n;
+    a.chunk = chunk;
+    // as the step: the XCD count is the CU count over 32 on a whole part
+    const int cus = ds.cus;
+    a.xcds = (block_order == 2 && cus % 32 == 0 && cus >= 32) ? cus / 32 : 1;
+    a.mode = mode;
+    // as the step: a cap reserves 1/groups_per_cu of the CU's LDS per workgroup
+    size_t dyn_lds = 0;
+    if (groups_per_cu > 0) {
+        const int64_t share = ds.lds_per_cu / groups_per_cu / 1024 * 1024;
+        if (share > ds.lds_per_group) return -1;
+        dyn_lds = (size_t)share;
+    }
+    void *args[] = {&a};
+    e = hipLaunchKernel((const void *)fn, dim3((unsigned)blocks), dim3(kThreads), args, dyn_lds,
+                        (hipStream_t)stream);
+    return (int)e;
 }
 
 }  // extern "C"

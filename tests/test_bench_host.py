@@ -53,8 +53,11 @@ def test_cpu_baseline_fields():
     r = bench.cpu_baseline(w, 0.2, "base", 26 + 2 * w.k)
     assert r["kind"] == "oracle" and r["unit"] == "GB/s" and r["cores"] == 1
     assert r["value"] > 0 and r["params_per_s"] > 0
-    assert "first %d elements" % min(w.n, 1 << 24) in r["sample"]
+    assert "first %d elements" % min(w.n, 1 << 27) in r["sample"]
     assert r["threaded"]["cores"] >= 1 and r["threaded"]["value"] > 0
+    assert r["threaded"]["cores"] <= bench.HOST_THREAD_CAP
+    assert r["host"]["online_cpus"] >= r["host"]["usable_cpus"] >= 1
+    assert r["parity"] is None
 
 
 def test_threaded_split_is_bitwise_identical():
@@ -72,10 +75,10 @@ def test_threaded_split_is_bitwise_identical():
         if variant == "q8grad":
             qg = [rng.integers(-127, 128, n).astype(np.int8) for _ in range(3)]
             qs = [rng.uniform(1e-5, 1e-4, -(-n // 256)).astype(np.float32) for _ in range(3)]
-            bench._threaded_oracle(*a, None, segs, hp, 4, variant, 1.0, qg, qs, seconds=0.0)
+            bench._threaded_oracle(*a, None, segs, hp, 4, variant, 1.0, 4, qg, qs, seconds=0.0)
             assert oracle.shard_step_q8grad(*b, qg, qs, segs, hp, 4) == 0
         else:
-            bench._threaded_oracle(*a, grads, segs, hp, 4, variant, 1.0, seconds=0.0)
+            bench._threaded_oracle(*a, grads, segs, hp, 4, variant, 1.0, 4, seconds=0.0)
             step = oracle.shard_step_bf16mv if variant == "bf16mv" else oracle.shard_step
             assert step(*b, grads, segs, hp, 4) == 0
         for x, y in zip(a, b):
@@ -107,3 +110,121 @@ def test_ceiling_library_loads_and_rejects_bad_arguments():
     assert lib.zs_ceiling_copy(0, 4096, 64, None) == -1     # null source
     assert lib.zs_ceiling_copy(4096, 4112, 64, None) == -1  # overlap
     assert lib.zs_ceiling_copy(0, 0, 0, None) == 0          # nothing to do
+
+
+def test_launch_key_follows_the_resolved_launch():
+    """The launch key comes from zs_launch_plan, so the library's defaults
+    (chunk order threshold, occupancy cap and its range) are part of it: a
+    measurement keyed to one plan is not reported for another."""
+    import sharded_mixed_precision_shard_amd as zs
+    p70 = zs.zs_launch_plan(2, synth.workload("70b").n)
+    p175 = zs.zs_launch_plan(2, synth.workload("175b").n)
+    pg2 = zs.zs_launch_plan(8, synth.workload("gpt2-small").n)
+    assert (p70["block_order"], p70["groups_per_cu"]) == (2, 0)    # above the cap's range
+    assert (p175["block_order"], p175["groups_per_cu"]) == (2, 5)  # inside it
+    assert (pg2["block_order"], pg2["groups_per_cu"]) == (1, 0)    # below the XCD threshold
+    assert zs.zs_launch_plan(2, synth.workload("175b").n, "bf16mv")["groups_per_cu"] == 0
+    assert zs.zs_launch_plan(2, 10 ** 8, cfg=dict(nontemporal=2))["nontemporal"] == 0
+    assert zs.zs_launch_plan(2, 0)["workgroups"] == 0
+    # a default that moved (here: the cap of the 175B launch) changes the key
+    moved = dict(p175, groups_per_cu=6)
+    assert bench.launch_key(moved) != bench.launch_key(p175)
+    with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+        entries = json.load(f)
+    for key, e in entries.items():
+        if e["launch"] == bench.launch_key(p175):
+            assert bench.measured_traffic(key, bench.launch_key(moved)) is None
+    with __import__("pytest").raises(zs.ZsError):
+        zs.zs_launch_plan(2, 100, "q8ag", cfg=dict(chunk_tiles=2))  # cfg is base-only
+    with __import__("pytest").raises(zs.ZsError):
+        zs.zs_launch_plan(17, 100)
+
+
+def test_twin_rejects_bad_arguments_before_any_device_call():
+    import ctypes
+    lib = bench._ceiling_lib()
+    g = (ctypes.c_void_p * 2)(4096, 8192)
+    P = ctypes.c_void_p
+
+    def call(mode=0, layout=0, k=2, n=4096, chunk=1024, order=2, cap=0, grads=g):
+        return lib.zs_ceiling_twin(mode, layout, P(4096), P(4096), P(4096), P(4096), None,
+                                   None, ctypes.cast(grads, P), None, k, n, chunk, order, cap,
+                                   None)
+    assert call(mode=3) == -1
+    assert call(layout=3) == -1
+    assert call(k=0) == -1 and call(k=17) == -1
+    assert call(n=4097) == -1 and call(n=3072, chunk=2048) == -1
+    assert call(chunk=512) == -1
+    assert call(order=0) == -1 and call(cap=33) == -1
+    assert call(layout=1) == -1                 # no int8 copy given
+    assert call(layout=2) == -1                 # no scales given
+    assert call(grads=(ctypes.c_void_p * 2)(4096, 0)) == -1
+    assert call(n=0) == 0                       # nothing to do
+
+
+def test_parity_windows_cover_ends_and_boundaries():
+    w = synth.workload("70b")
+    wins = bench.parity_windows(w, w.n)
+    assert wins[0][0] == 0 and wins[-1][1] == w.n
+    assert len(wins) >= 8
+    for a, b in wins:
+        assert a % 256 == 0 and 0 < b - a <= bench.PARITY_WINDOW
+    assert all(x[1] <= y[0] for x, y in zip(wins, wins[1:]))
+    starts = [s for s, _ in w.shard.segments[1:]]
+    assert sum(any(a < s < b for s in starts) for a, b in wins) >= 4
+    t = synth.workload("tiny")
+    assert bench.parity_windows(t, 1000) == [(0, 1000)]
+
+
+def _fake_run(variant, steps, plant=None):
+    """A run's windows whose 'GPU' results are the oracle's own, with an
+    optional planted change; exercises the comparison, not the kernel."""
+    w = synth.workload("tiny")
+    wins = [(0, 4096), (8192, 8192 + 1000)]
+    before, grads = {"master": [], "m": [], "v": []}, [[] for _ in range(w.k)]
+    after = {"master": [], "m": [], "v": [], "param": []}
+    hp = oracle.hparams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, 1.0)
+    mvt = np.uint16 if variant == "bf16mv" else np.float32
+    for a, b in wins:
+        mst = synth.host_master(w, a, b)
+        gs = synth.host_grads(w, w.t0, a, b)
+        before["master"].append(mst.copy())
+        before["m"].append(np.zeros(b - a, mvt))
+        before["v"].append(np.zeros(b - a, mvt))
+        for j in range(w.k):
+            grads[j].append(gs[j].view(np.int16))
+        m, v, p = np.zeros(b - a, mvt), np.zeros(b - a, mvt), np.zeros(b - a, np.uint16)
+        segs = synth.clip_segments(w.shard.segments, a, b)
+        for t in range(w.t0, w.t0 + steps):
+            fn = oracle.shard_step_bf16mv if variant == "bf16mv" else oracle.shard_step
+            assert fn(mst, m, v, p, gs, segs, hp, t) == 0
+        after["master"].append(mst)
+        after["m"].append(m)
+        after["v"].append(v)
+        after["param"].append(p.view(np.int16))
+    if plant:
+        plant(after)
+    return w, dict(windows=wins, before=before, after=after, grads=grads,
+                   ts=list(range(w.t0, w.t0 + steps)))
+
+
+def test_parity_replay_reports_equality_and_planted_differences():
+    for variant in ("base", "bf16mv"):
+        w, par = _fake_run(variant, 3)
+        r = bench._parity_replay(w, variant, par)
+        assert r["bitwise_equal"] and r["within_tolerance"], r
+        assert r["max_param_bf16_ulp"] == 0 and r["steps_replayed"] == 3
+    # one master element (|x| < 1, so the bound is 1e-6 absolute) off by 2e-6
+    def bump(after):
+        after["master"][1][7] += np.float32(2e-6)
+    w, par = _fake_run("base", 2, bump)
+    r = bench._parity_replay(w, "base", par)
+    assert not r["bitwise_equal"] and not r["within_tolerance"]
+    assert 1e-6 < r["max_rel_err"]["master"] < 1e-5
+    # a parameter one bf16 ulp away: not bitwise, still within tolerance
+    def ulp(after):
+        after["param"][0][3] += 1
+    w, par = _fake_run("base", 2, ulp)
+    r = bench._parity_replay(w, "base", par)
+    assert not r["bitwise_equal"] and r["within_tolerance"]
+    assert r["max_param_bf16_ulp"] == 1

@@ -45,6 +45,13 @@ def test_bench_line(extra):
     variant = extra[1] if extra[:1] == ["--variant"] else "base"
     want = "zs_shard_step" if variant == "base" else "zs_shard_step_" + variant
     assert out["config"]["entry_point"] == want
+    c = out["ceilings"]
+    assert c["twin_step_gbps"] > 0 and c["twin_read_gbps"] > 0 and c["twin_write_gbps"] > 0
+    assert c["pct_of_twin"] > 0
+    par = out["parity"]
+    assert par == cpu["parity"] and par["windows"] >= 1
+    assert par["steps_replayed"] == 6  # one warm-up step and five timed ones
+    assert par["within_tolerance"] and par["bitwise_equal"], par
 
 
 def test_streaming_copy_of_the_ceiling_library():
@@ -66,3 +73,46 @@ def test_streaming_copy_of_the_ceiling_library():
     assert lib.zs_ceiling_copy(src.data_ptr() + 4, dst.data_ptr(), 16, s) == -1
     assert lib.zs_ceiling_copy(src.data_ptr(), src.data_ptr() + 16, 64, s) == -1
     assert lib.zs_ceiling_copy(src.data_ptr(), dst.data_ptr(), 0, s) == 0
+
+
+@pytest.mark.parametrize("variant", ["base", "q8ag", "q8grad", "bf16mv"])
+def test_twin_moves_the_step_traffic_without_changing_the_state(variant):
+    """The twin ceiling on a step's buffers: the whole-traffic mode writes the
+    state back bit for bit, the read-only mode changes nothing, the
+    write-only mode overwrites the covered elements with its pattern."""
+    import torch
+    sys.path.insert(0, ROOT)
+    import bench
+    import sharded_mixed_precision_shard_amd as zs
+    torch.cuda.set_device(0)
+    k, n = 3, 1 << 16
+    nb = n // 256
+    g = torch.Generator(device="cuda").manual_seed(5)
+    rnd = lambda dt: torch.randint(-30000, 30000, (n,), generator=g, device="cuda",  # noqa
+                                   dtype=torch.int32).to(dt)
+    mvt = torch.int16 if variant == "bf16mv" else torch.float32
+    bufs = dict(master=torch.randn(n, device="cuda", generator=g), m=rnd(mvt), v=rnd(mvt),
+                param=torch.zeros(n, dtype=torch.int16, device="cuda"),
+                q8=torch.zeros(n, dtype=torch.int8, device="cuda") if variant == "q8ag" else None,
+                q8s=torch.zeros(nb, device="cuda") if variant == "q8ag" else None)
+    if variant == "q8grad":
+        bufs["qgrads"] = [rnd(torch.int8) for _ in range(k)]
+        bufs["qscales"] = [torch.rand(nb, device="cuda", generator=g) for _ in range(k)]
+        bufs["grads"] = None
+    else:
+        bufs["grads"] = [rnd(torch.int16) for _ in range(k)]
+    plan = zs.zs_launch_plan(k, n, variant)
+    twin = bench.Twin(torch, variant, bufs, k, n, plan)
+    assert twin.ok and twin.n == n
+    keep = {x: bufs[x].clone() for x in ("master", "m", "v")}
+    s = torch.cuda.current_stream()
+    for mode in ("step", "read"):
+        twin.launch(mode, s)
+        torch.cuda.synchronize()
+        for x in keep:
+            assert torch.equal(bufs[x].view(torch.int16), keep[x].view(torch.int16)), (mode, x)
+    assert twin.rate("step", s, reps=2) > 0
+    twin.launch("write", s)
+    torch.cuda.synchronize()
+    pattern = torch.tensor([1.0, 2.0, 3.0, 4.0], device="cuda").repeat(n // 4)
+    assert torch.equal(bufs["master"], pattern)
