@@ -42,6 +42,8 @@ namespace {
 constexpr int64_t kNoStart = INT64_MAX;       // sentinel past the table end
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int NT, typename T>
@@ -185,10 +187,21 @@ __device__ __forceinline__ f32x4 bf16x4_to_f32x4(u32x2 d) {
     return r;
 }
 
+// Two values to packed bf16 with gfx950's v_cvt_pk_bf16_f32, which rounds to
+// nearest even and keeps denormals exactly as to_bf16 does but carries a NaN's
+// payload into the result; every NaN is therefore replaced by the canonical
+// quiet NaN first, which converts to 0x7FC0.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const uint32_t qnan = 0x7fc00000u;
+    const f32x2 x = {__uint_as_float(__builtin_isnan(a) ? qnan : __float_as_uint(a)),
+                     __uint_as_float(__builtin_isnan(b) ? qnan : __float_as_uint(b))};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+
 __device__ __forceinline__ u32x2 f32x4_to_bf16x4(f32x4 x) {
     u32x2 r;
-    r[0] = to_bf16(x[0]) | (to_bf16(x[1]) << 16);
-    r[1] = to_bf16(x[2]) | (to_bf16(x[3]) << 16);
+    r[0] = pack_bf16x2(x[0], x[1]);
+    r[1] = pack_bf16x2(x[2], x[3]);
     return r;
 }
 
@@ -290,16 +303,33 @@ __device__ __forceinline__ uint32_t quantize_block(const uint32_t bits[4], uint3
     const float scale = __uint_as_float(amax) / 127.0f;
     const bool usable = scale > 0.0f && scale <= 3.40282347e+38f;
     uint32_t word = 0;
+    if (usable) {
+        // q = rint(x / scale) with the quotient correctly rounded.  x * rcp(scale)
+        // (hardware reciprocal, within 1 ulp) is within 2^-15.4 of the rounded
+        // quotient for |x / scale| < 128, so wherever it lies more than 2^-14 from
+        // a half-integer both round to the same integer; the rare other elements
+        // (and any non-finite product) take the correctly rounded division.
+        const float rs = __builtin_amdgcn_rcpf(scale);
+        float r[4];
+        uint32_t slow = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        int32_t q = 0;
-        if (usable) {
-            float r = __builtin_rintf(__uint_as_float(bits[e]) / scale);
-            r = r > 127.0f ? 127.0f : r;
-            r = r < -127.0f ? -127.0f : r;
-            q = (int32_t)r;
+        for (int e = 0; e < 4; ++e) {
+            const float y = __uint_as_float(bits[e]) * rs;
+            r[e] = __builtin_rintf(y);
+            const bool near_half = !(__builtin_fabsf(y - r[e]) < 0.5f - 0x1p-14f);
+            const bool big = !(__builtin_fabsf(y) < 256.0f);
+            slow |= (uint32_t)(near_half | big) << e;
         }
-        word |= ((uint32_t)q & 0xffu) << (8 * e);
+        if (slow) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if ((slow >> e) & 1u) r[e] = __builtin_rintf(__uint_as_float(bits[e]) / scale);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float c = __builtin_fminf(__builtin_fmaxf(r[e], -127.0f), 127.0f);
+            word |= ((uint32_t)(int32_t)c & 0xffu) << (8 * e);
+        }
     }
     if (block_exists && (threadIdx.x % kWave) == 0) a.q8_scale[block] = scale;
     return word;
