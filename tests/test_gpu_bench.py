@@ -48,6 +48,7 @@ def test_bench_line(extra):
     c = out["ceilings"]
     assert c["twin_step_gbps"] > 0 and c["twin_read_gbps"] > 0 and c["twin_write_gbps"] > 0
     assert c["pct_of_twin"] > 0
+    assert c["twin_best_gbps"] >= c["twin_step_gbps"] and c["pct_of_twin_best"] > 0
     par = out["parity"]
     assert par == cpu["parity"] and par["windows"] >= 1
     assert par["steps_replayed"] == 6  # one warm-up step and five timed ones
@@ -116,3 +117,21 @@ def test_twin_moves_the_step_traffic_without_changing_the_state(variant):
     torch.cuda.synchronize()
     pattern = torch.tensor([1.0, 2.0, 3.0, 4.0], device="cuda").repeat(n // 4)
     assert torch.equal(bufs["master"], pattern)
+
+
+def test_launch_sweep_prints_every_configuration():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--config", "tiny",
+                        "--sweep", "--rounds", "2", "--steps", "3"],
+                       capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-3000:]
+    lines = [ln for ln in r.stdout.splitlines() if ln.strip()]
+    assert len(lines) == 1
+    out = json.loads(lines[0])
+    sys.path.insert(0, ROOT)
+    import bench
+    assert list(out["sweep"]) == [name for name, _ in bench.SWEEP_CFGS]
+    for name, e in out["sweep"].items():
+        assert len(e["kernel_gbps"]) == 2 and len(e["twin_gbps"]) == 2, name
+        assert e["kernel_median"] > 0 and e["twin_median"] > 0
+    assert out["sweep"]["xcd,cap5"]["launch"].endswith("order=2,cap=5,nt=1")
+    assert out["sweep"]["linear"]["launch"].endswith("order=1,cap=32,nt=1")

@@ -1,0 +1,95 @@
+"""The ZeRO-Offload host step (include/zs_host.h) on the GPU host's own CPUs,
+bit for bit against the oracle and against the GPU step (zs_shard_step) on
+the same seeded inputs: GPT-2-small rank 0 over its 10 steps on the whole
+shard, and windows of the 70B-shaped shard at t = 10000..10002.
+
+The host side regenerates every input with the host twin of the generator;
+the GPU side fills HBM with the device twin (the two are tested
+bit-identical elsewhere)."""
+import numpy as np
+import pytest
+
+import sharded_mixed_precision_shard_amd as zs
+import synth
+from tests import _gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+F32 = np.float32
+
+
+@pytest.fixture(scope="module")
+def gpu():
+    import torch
+    assert torch.cuda.is_available()
+    torch.cuda.set_device(0)
+    assert zs.zs_init(0) == zs.ZS_OK
+    yield torch
+    torch.cuda.synchronize()
+
+
+def host_window(w, lo, hi, steps, threads=0):
+    """The host step over shard elements [lo, hi) for the given steps."""
+    n = hi - lo
+    master = synth.host_master(w, lo, hi)
+    m = np.zeros(n, F32)
+    v = np.zeros(n, F32)
+    p = np.zeros(n, np.uint16)
+    segs = synth.clip_segments(w.shard.segments, lo, hi)
+    hp = zs.hparams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, 1.0)
+    for t in steps:
+        gs = synth.host_grads(w, t, lo, hi)
+        zs.zs_host_shard_step(master, m, v, p, gs, w.k, n, segs, hp, t, nthreads=threads)
+    return master, m, v, p
+
+
+def _bitwise(a, b, where):
+    for name, x, y in zip(("master", "m", "v", "param"), a, b):
+        assert np.array_equal(np.ascontiguousarray(x).view(np.uint8),
+                              np.ascontiguousarray(y).view(np.uint8)), "%s %s" % (where, name)
+
+
+def test_host_step_runs_on_this_host():
+    assert zs.zs_host_max_threads() >= 1
+    assert zs.zs_host_isa() in ("avx512", "scalar")
+    print("host step: %d threads, %s" % (zs.zs_host_max_threads(), zs.zs_host_isa()), flush=True)
+
+
+def test_gpt2_rank0_host_equals_oracle_and_gpu(gpu):
+    torch = gpu
+    w = synth.workload("gpt2-small")
+    ts = w.step_ts()
+    host = host_window(w, 0, w.n, ts)
+    ref = H.oracle_window(w, 0, w.n, ts)
+    _bitwise(host, ref, "gpt2 host vs oracle")
+    ds = H.DeviceShard(w)
+    for t in ts:
+        ds.fill_grads(t)
+        ds.step(t)
+    torch.cuda.synchronize()
+    got = ds.window(0, w.n)
+    ds.free()
+    _bitwise(host, got, "gpt2 host vs gpu")
+
+
+def test_70b_windows_host_equals_oracle_and_gpu(gpu):
+    torch = gpu
+    w = synth.workload("70b")
+    free, _ = torch.cuda.mem_get_info()
+    need = w.n * (14 + 2 * w.k) + (1 << 30)
+    if free < need:
+        pytest.skip("needs %.1f GB of free device memory" % (need / 1e9))
+    ts = w.step_ts()
+    ds = H.DeviceShard(w)
+    for t in ts:
+        ds.fill_grads(t)
+        ds.step(t)
+    torch.cuda.synchronize()
+    wins = H.boundary_windows(w, 1 << 15, max_boundaries=32, n_random=4, seed=3)
+    got = [ds.window(lo, hi) for lo, hi in wins]
+    ds.free()
+    for (lo, hi), g in zip(wins, got):
+        host = host_window(w, lo, hi, ts)
+        _bitwise(host, H.oracle_window(w, lo, hi, ts), "70b [%d,%d) host vs oracle" % (lo, hi))
+        _bitwise(host, g, "70b [%d,%d) host vs gpu" % (lo, hi))
+    print("70b: %d windows, host == oracle == gpu" % len(wins), flush=True)
