@@ -106,15 +106,14 @@ typedef struct {
                               per workgroup; ZS_MAX_GROUPS_PER_CU never binds (no
                               cap).  Fewer requests in flight relieve DRAM
                               congestion on many physical placements of the arrays.
-                              0 = default: a cap of 5 for grids of 65536 to 4194303
-                              workgroups (shards of about 6.7e7 to 4.3e9 elements),
-                              none otherwise; zs_shard_step_bf16mv never caps by
-                              default.  A cap whose LDS share exceeds the
+                              0 = default: a cap of 5 for shards of 2^26 to
+                              2^32 - 1 elements, none otherwise;
+                              zs_shard_step_bf16mv never caps by default.  A cap whose LDS share exceeds the
                               per-workgroup limit returns ZS_ERR_INVALID_ARGUMENT. */
     int32_t block_order;  /* 0 = default, 1 = linear (workgroup b takes chunk b),
                              2 = XCD-contiguous (the workgroups the dispatcher deals to
                              one XCD take one contiguous run of chunks).  The default
-                             is XCD-contiguous for grids of at least 65536 workgroups
+                             is XCD-contiguous for shards of at least 2^26 elements
                              on a part with several XCDs, linear otherwise. */
 } zs_launch_cfg;
 

@@ -29,18 +29,18 @@ struct DeviceInfo {
     int xcds;               // accelerator complex dies the device's CUs sit on
 };
 
-// Grids at least this large default to the XCD-contiguous chunk order (on
-// MI355X it measured 0-3 % faster on shards of 10^8-10^10 elements and slower
-// on shards that fit the 256 MB last-level cache).
-constexpr int64_t kXcdOrderMinBlocks = 65536;
+// Shards of at least this many elements default to the XCD-contiguous chunk
+// order (on MI355X it measured 0-3 % faster on shards of 10^8-10^10 elements
+// and slower on shards that fit the 256 MB last-level cache).
+constexpr int64_t kXcdOrderMinElems = int64_t(1) << 26;
 
-// Default occupancy cap for grids in [kXcdOrderMinBlocks, kCapMaxBlocks):
-// 5 resident workgroups per CU measured 0-8 % faster on shards of 1-6 x 10^9
-// elements on MI355X (most on placements where DRAM queues congest), but
-// 3-6 % slower on the 8 x 10^9-element 70B shard, which needs the full depth
-// of requests in flight, and 0-1 % slower for the bf16-moment variant (fewer
-// bytes per element), which therefore keeps no default cap.
-constexpr int64_t kCapMaxBlocks = int64_t(1) << 22;
+// Default occupancy cap for shards of [kXcdOrderMinElems, kCapMaxElems)
+// elements: 5 resident workgroups per CU measured 0-8 % faster on shards of
+// 0.8-6 x 10^9 elements on MI355X (most on placements where DRAM queues
+// congest), but 2-6 % slower on the 8 x 10^9-element 70B shard, which needs
+// the full depth of requests in flight, and 0-1 % slower for the bf16-moment
+// variant (fewer bytes per element), which therefore keeps no default cap.
+constexpr int64_t kCapMaxElems = int64_t(1) << 32;
 constexpr int kDefaultCap = 5;
 constexpr int kCusPerXcd = 32;  // gfx950
 
@@ -69,11 +69,12 @@ constexpr int kDefaultChunkTiles = 1;
 constexpr int64_t kMaxBlocks = 0xffffffffLL / kThreads;
 
 // Elements per workgroup and workgroup count for n elements: chunk_tiles
-// tiles per workgroup (0 = default), doubled until the grid fits.
-void launch_geometry(int k, int64_t n, int chunk_tiles, int64_t *chunk_out,
+// tiles of the variant's kernel per workgroup (0 = default), doubled until
+// the grid fits.
+void launch_geometry(int variant, int64_t n, int chunk_tiles, int64_t *chunk_out,
                      int64_t *blocks_out) {
     if (chunk_tiles == 0) chunk_tiles = kDefaultChunkTiles;
-    int64_t chunk = (int64_t)chunk_tiles * tile_for(k);
+    int64_t chunk = (int64_t)chunk_tiles * tile_for(variant);
     int64_t blocks = (n + chunk - 1) / chunk;
     while (blocks > kMaxBlocks) {
         chunk *= 2;
@@ -107,10 +108,9 @@ int resolve_launch(int k, int64_t n, int variant, const zs_launch_cfg *cfg,
         block_order = cfg->block_order;
     }
     int64_t chunk = 0, blocks = 0;
-    if (n > 0) launch_geometry(k, n, chunk_tiles, &chunk, &blocks);
-    const bool xcd_order =
-        block_order == 2 || (block_order == 0 && blocks >= kXcdOrderMinBlocks);
-    if (groups_per_cu == 0 && blocks >= kXcdOrderMinBlocks && blocks < kCapMaxBlocks &&
+    if (n > 0) launch_geometry(variant, n, chunk_tiles, &chunk, &blocks);
+    const bool xcd_order = block_order == 2 || (block_order == 0 && n >= kXcdOrderMinElems);
+    if (groups_per_cu == 0 && n >= kXcdOrderMinElems && n < kCapMaxElems &&
         !(variant & kMvBf16))
         groups_per_cu = -kDefaultCap;  // a default cap: dropped where it does not fit
     out->workgroups = blocks;
@@ -408,7 +408,7 @@ int zs_launch_geometry(int k, int64_t n, const zs_launch_cfg *cfg, int64_t *work
         *chunk_elements = 0;
         return ZS_OK;
     }
-    launch_geometry(k, n, chunk_tiles, chunk_elements, workgroups);
+    launch_geometry(0, n, chunk_tiles, chunk_elements, workgroups);
     return ZS_OK;
 }
 

@@ -83,11 +83,17 @@ __device__ __forceinline__ void opaque(T &x) {
     asm volatile("" : "+v"(x));
 }
 
+// Sub-windows per wave per tile, as in the step's kernel of that layout (one
+// for every entry point).
+constexpr int quads_of(int layout) { return (void)layout, 1; }
+constexpr int tile_of(int layout) { return kTile * quads_of(layout); }
+
 template <int K, int L>
 __global__ __launch_bounds__(kThreads) void twin_kernel(const TwinArgs a) {
     constexpr bool kMv16 = (L & kLayoutBf16Mv) != 0;
     constexpr bool kG8 = (L & kLayoutQ8Grad) != 0;
     constexpr bool kOut8 = (L & kLayoutQ8Out) != 0;
+    constexpr int kQ = quads_of(L);
     const int lane = (int)(threadIdx.x % kWave);
     const int wave = (int)(threadIdx.x / kWave);
     int64_t b = blockIdx.x;
@@ -98,64 +104,78 @@ __global__ __launch_bounds__(kThreads) void twin_kernel(const TwinArgs a) {
     }
     const int64_t c0 = b * a.chunk;
     const int64_t c1 = (c0 + a.chunk < a.n) ? c0 + a.chunk : a.n;
-    for (int64_t t0 = c0; t0 < c1; t0 += kTile) {
-        const int64_t w0 = t0 + (int64_t)wave * kSub;
-        if (w0 + kSub > c1) continue;  // whole windows only; the host sizes n to match
-        const int64_t qi = w0 / kQuad + lane;  // this lane's quad
+    for (int64_t t0 = c0; t0 < c1; t0 += tile_of(L)) {
+        const int64_t wv0 = t0 + (int64_t)wave * kSub * kQ;
+        if (wv0 + kSub * kQ > c1) continue;  // whole windows only; the host sizes n to match
+        int64_t qi[kQ];  // this lane's quad of each sub-window
+#pragma unroll
+        for (int qd = 0; qd < kQ; ++qd) qi[qd] = (wv0 + (int64_t)qd * kSub) / kQuad + lane;
         if (a.mode == kModeWrite) {
             const f32x4 z = {1.0f, 2.0f, 3.0f, 4.0f};
             const u32x2 h = {0x3f803f80u, 0x3f803f80u};
-            st<f32x4>(a.master, qi, z);
-            if constexpr (kMv16) {
-                st<u32x2>(a.m, qi, h);
-                st<u32x2>(a.v, qi, h);
-            } else {
-                st<f32x4>(a.m, qi, z);
-                st<f32x4>(a.v, qi, z);
-            }
-            st<u32x2>(a.param, qi, h);
-            if constexpr (kOut8) {
-                st<uint32_t>(a.q8, qi, 0x01010101u);
-                if (lane == 0) a.q8_scale[w0 / kBlock] = 1.0f;
+#pragma unroll
+            for (int qd = 0; qd < kQ; ++qd) {
+                st<f32x4>(a.master, qi[qd], z);
+                if constexpr (kMv16) {
+                    st<u32x2>(a.m, qi[qd], h);
+                    st<u32x2>(a.v, qi[qd], h);
+                } else {
+                    st<f32x4>(a.m, qi[qd], z);
+                    st<f32x4>(a.v, qi[qd], z);
+                }
+                st<u32x2>(a.param, qi[qd], h);
+                if constexpr (kOut8) {
+                    st<uint32_t>(a.q8, qi[qd], 0x01010101u);
+                    if (lane == 0) a.q8_scale[(wv0 + (int64_t)qd * kSub) / kBlock] = 1.0f;
+                }
             }
             continue;
         }
-        f32x4 w = ld<f32x4>(a.master, qi);
-        f32x4 m, v;
-        u32x2 mh, vh;
-        if constexpr (kMv16) {
-            mh = ld<u32x2>(a.m, qi);
-            vh = ld<u32x2>(a.v, qi);
-        } else {
-            m = ld<f32x4>(a.m, qi);
-            v = ld<f32x4>(a.v, qi);
-        }
-        u32x2 g[K];
-        uint32_t g8[K];
-        float s[K];
+        // every sub-window's loads first, as the step issues them
+        f32x4 w[kQ], m[kQ], v[kQ];
+        u32x2 mh[kQ], vh[kQ];
+        u32x2 g[kQ][K];
+        uint32_t g8[kQ][K];
+        float s[kQ][K];
 #pragma unroll
-        for (int j = 0; j < K; ++j) {
-            if constexpr (kG8) {
-                g8[j] = ld<uint32_t>(a.grads[j], qi);
-                s[j] = a.qscales[j][w0 / kBlock];
-            } else {
-                g[j] = ld<u32x2>(a.grads[j], qi);
-            }
-        }
-        if (a.mode == kModeRead) {
-            uint32_t acc = __float_as_uint(w[0]) ^ __float_as_uint(w[1]) ^
-                           __float_as_uint(w[2]) ^ __float_as_uint(w[3]);
+        for (int qd = 0; qd < kQ; ++qd) {
+            w[qd] = ld<f32x4>(a.master, qi[qd]);
             if constexpr (kMv16) {
-                acc ^= mh[0] ^ mh[1] ^ vh[0] ^ vh[1];
+                mh[qd] = ld<u32x2>(a.m, qi[qd]);
+                vh[qd] = ld<u32x2>(a.v, qi[qd]);
             } else {
-                acc ^= __float_as_uint(m[0]) ^ __float_as_uint(m[1]) ^ __float_as_uint(m[2]) ^
-                       __float_as_uint(m[3]) ^ __float_as_uint(v[0]) ^ __float_as_uint(v[1]) ^
-                       __float_as_uint(v[2]) ^ __float_as_uint(v[3]);
+                m[qd] = ld<f32x4>(a.m, qi[qd]);
+                v[qd] = ld<f32x4>(a.v, qi[qd]);
             }
 #pragma unroll
             for (int j = 0; j < K; ++j) {
-                if constexpr (kG8) acc ^= g8[j] ^ __float_as_uint(s[j]);
-                else acc ^= g[j][0] ^ g[j][1];
+                if constexpr (kG8) {
+                    g8[qd][j] = ld<uint32_t>(a.grads[j], qi[qd]);
+                    s[qd][j] = a.qscales[j][(wv0 + (int64_t)qd * kSub) / kBlock];
+                } else {
+                    g[qd][j] = ld<u32x2>(a.grads[j], qi[qd]);
+                }
+            }
+        }
+        if (a.mode == kModeRead) {
+            uint32_t acc = 0;
+#pragma unroll
+            for (int qd = 0; qd < kQ; ++qd) {
+                acc ^= __float_as_uint(w[qd][0]) ^ __float_as_uint(w[qd][1]) ^
+                       __float_as_uint(w[qd][2]) ^ __float_as_uint(w[qd][3]);
+                if constexpr (kMv16) {
+                    acc ^= mh[qd][0] ^ mh[qd][1] ^ vh[qd][0] ^ vh[qd][1];
+                } else {
+                    acc ^= __float_as_uint(m[qd][0]) ^ __float_as_uint(m[qd][1]) ^
+                           __float_as_uint(m[qd][2]) ^ __float_as_uint(m[qd][3]) ^
+                           __float_as_uint(v[qd][0]) ^ __float_as_uint(v[qd][1]) ^
+                           __float_as_uint(v[qd][2]) ^ __float_as_uint(v[qd][3]);
+                }
+#pragma unroll
+                for (int j = 0; j < K; ++j) {
+                    if constexpr (kG8) acc ^= g8[qd][j] ^ __float_as_uint(s[qd][j]);
+                    else acc ^= g[qd][j][0] ^ g[qd][j][1];
+                }
             }
             if (acc == 0x9e3779b9u) a.sink[0] = acc;
             continue;
@@ -163,39 +183,42 @@ __global__ __launch_bounds__(kThreads) void twin_kernel(const TwinArgs a) {
         // The whole step's traffic: state written back bit for bit.  Every
         // value loaded is pinned, so that no load can be dropped as unused.
 #pragma unroll
-        for (int j = 0; j < K; ++j) {
-            if constexpr (kG8) {
-                opaque(g8[j]);
-                opaque(s[j]);
-            } else {
-                opaque(g[j]);
+        for (int qd = 0; qd < kQ; ++qd) {
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                if constexpr (kG8) {
+                    opaque(g8[qd][j]);
+                    opaque(s[qd][j]);
+                } else {
+                    opaque(g[qd][j]);
+                }
             }
-        }
-        opaque(w);
-        st<f32x4>(a.master, qi, w);
-        if constexpr (kMv16) {
-            opaque(mh);
-            opaque(vh);
-            st<u32x2>(a.m, qi, mh);
-            st<u32x2>(a.v, qi, vh);
-        } else {
-            opaque(m);
-            opaque(v);
-            st<f32x4>(a.m, qi, m);
-            st<f32x4>(a.v, qi, v);
-        }
-        u32x2 p;
-        if constexpr (kG8) {
-            p[0] = g8[0];
-            p[1] = __float_as_uint(s[0]);
-        } else {
-            p = g[0];
-        }
-        opaque(p);
-        st<u32x2>(a.param, qi, p);
-        if constexpr (kOut8) {
-            st<uint32_t>(a.q8, qi, p[0]);
-            if (lane == 0) a.q8_scale[w0 / kBlock] = __uint_as_float(p[1]);
+            opaque(w[qd]);
+            st<f32x4>(a.master, qi[qd], w[qd]);
+            if constexpr (kMv16) {
+                opaque(mh[qd]);
+                opaque(vh[qd]);
+                st<u32x2>(a.m, qi[qd], mh[qd]);
+                st<u32x2>(a.v, qi[qd], vh[qd]);
+            } else {
+                opaque(m[qd]);
+                opaque(v[qd]);
+                st<f32x4>(a.m, qi[qd], m[qd]);
+                st<f32x4>(a.v, qi[qd], v[qd]);
+            }
+            u32x2 p;
+            if constexpr (kG8) {
+                p[0] = g8[qd][0];
+                p[1] = __float_as_uint(s[qd][0]);
+            } else {
+                p = g[qd][0];
+            }
+            opaque(p);
+            st<u32x2>(a.param, qi[qd], p);
+            if constexpr (kOut8) {
+                st<uint32_t>(a.q8, qi[qd], p[0]);
+                if (lane == 0) a.q8_scale[(wv0 + (int64_t)qd * kSub) / kBlock] = __uint_as_float(p[1]);
+            }
         }
     }
 }
@@ -276,8 +299,9 @@ int zs_ceiling_copy(const void *src, void *dst, int64_t bytes, void *stream) {
 //         bf16 otherwise); qscales (layout 2) k device pointers to one f32
 //         per 256 elements; q8 and q8_scale (layout 1) the int8 copy and its
 //         scales.
-//   n: elements; a multiple of 1024 and of chunk (the twin covers whole
-//         windows only, so the host rounds a shard down to that).
+//   n: elements; a multiple of chunk and of the 1024-element tile (the
+//         twin covers whole windows only, so the host rounds a shard down to
+//         that).
 //   chunk, block_order (1 linear, 2 XCD-contiguous), groups_per_cu (0 =
 //         none): the launch zs_launch_plan reports for the step.
 // Every pointer is DEVICE memory sized for n elements, 16-byte aligned (the
@@ -288,7 +312,11 @@ int zs_ceiling_twin(int mode, int layout, float *master, void *m, void *v, uint1
                     const float *const *qscales, int k, int64_t n, int64_t chunk,
                     int block_order, int groups_per_cu, void *stream) {
     if (mode < 0 || mode > 2 || k < 1 || k > kMaxK || n < 0 || !grads) return -1;
-    if (n % kTile || chunk < kTile || chunk % kTile || (n && n % chunk)) return -1;
+    if (layout != kLayoutBase && layout != kLayoutQ8Out && layout != kLayoutQ8Grad &&
+        layout != kLayoutBf16Mv)
+        return -1;
+    const int64_t tile = tile_of(layout);
+    if (n % tile || chunk < tile || chunk % tile || (n && n % chunk)) return -1;
     if (block_order != 1 && block_order != 2) return -1;
     if (groups_per_cu < 0 || groups_per_cu > 32) return -1;
     const twin_fn fn = pick_twin(k, layout);

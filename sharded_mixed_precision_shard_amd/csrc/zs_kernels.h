@@ -16,16 +16,31 @@ constexpr int kWave = 64;
 constexpr int kQuad = 4;                      // contiguous elements per lane per sub-window
 constexpr int kSub = kWave * kQuad;           // 256: one dense instruction per array per wave
 
+// Variants of the step, chosen at compile time (bit mask):
+//   kOutQ8  - also write the block-quantized int8 copy of the new parameters
+//             with one fp32 scale per kQ8Block elements (the payload of a
+//             quantized all-gather);
+//   kGradQ8 - the k partials arrive as int8 with one fp32 scale per
+//             kQ8Block elements each (a block-quantized reduce-scatter) and
+//             are dequantized inside the reduce;
+//   kMvBf16 - the moments m and v are stored as bf16 (12 bytes per parameter
+//             of optimizer state plus weight instead of 16).
+constexpr int kOutQ8 = 1;
+constexpr int kGradQ8 = 2;
+constexpr int kMvBf16 = 4;
+
 // Sub-windows (quads per lane) a wave handles per tile.  Measured on MI355X
 // with the per-wavefront segment lookup: one quad per lane, i.e. the fewest
-// bytes in flight per wave and the most waves, streamed as fast as or faster
-// than two or four quads for every partial count (even on the eight-partial
-// 7B shard, 5-12 % faster on small shards, which get four times the
-// workgroups).
-constexpr int quads_for(int k) { return (void)k, 1; }
-constexpr int tile_for(int k) { return (kThreads / kWave) * quads_for(k) * kSub; }
+// bytes in flight per wave and the most waves, streams as fast as or faster
+// than two or four quads for every partial count and entry point (even on the
+// eight-partial 7B shard; 5-12 % faster on small shards, which get four times
+// the workgroups; two quads lost 0.2-0.6 % on the 70B- and 175B-shaped shards
+// for the base and bf16-moment steps and 0-2.9 % for the int8-payload step,
+// same process).
+constexpr int quads_for(int variant) { return (void)variant, 1; }
+constexpr int tile_for(int variant) { return (kThreads / kWave) * quads_for(variant) * kSub; }
 
-static_assert(tile_for(1) == 1024 && tile_for(16) == 1024, "tile sizes");
+static_assert(tile_for(0) == 1024 && tile_for(kOutQ8) == 1024, "tile sizes");
 
 struct StepArgs {
     float *master;
@@ -39,24 +54,12 @@ struct StepArgs {
     const float *qscales[ZS_MAX_K];
     const zs_segment *segs;
     int64_t n;
-    int64_t chunk;  // elements per workgroup, a multiple of tile_for(k)
+    int64_t chunk;  // elements per workgroup, a multiple of tile_for(variant)
     int32_t nseg;
     int32_t xcds;   // XCDs the dispatcher deals workgroups to in turn; 1 = linear order
     float lr, b1, b2, c1, c2, bc1, bc2, eps, df, gscale;
 };
 
-// Variants of the step, chosen at compile time (bit mask):
-//   kOutQ8  - also write the block-quantized int8 copy of the new parameters
-//             with one fp32 scale per kQ8Block elements (the payload of a
-//             quantized all-gather);
-//   kGradQ8 - the k partials arrive as int8 with one fp32 scale per
-//             kQ8Block elements each (a block-quantized reduce-scatter) and
-//             are dequantized inside the reduce;
-//   kMvBf16 - the moments m and v are stored as bf16 (12 bytes per parameter
-//             of optimizer state plus weight instead of 16).
-constexpr int kOutQ8 = 1;
-constexpr int kGradQ8 = 2;
-constexpr int kMvBf16 = 4;
 constexpr int kQ8Block = ZS_Q8_BLOCK;
 static_assert(kQ8Block == kSub, "a quantization block is one sub-window of a wave");
 

@@ -356,9 +356,9 @@ __device__ __forceinline__ void quad_update(f32x4 &w, f32x4 &m, f32x4 &v,
 // host picks these kernels only when that correction is exactly 1.0f).
 template <int K, int V, int NT, int U>
 __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) {
-    constexpr int kQuads = quads_for(K);      // sub-windows per wave per tile
+    constexpr int kQuads = quads_for(V);      // sub-windows per wave per tile
     constexpr int kWindow = kQuads * kSub;    // elements per wave per tile
-    constexpr int kTile = tile_for(K);        // elements per workgroup tile
+    constexpr int kTile = tile_for(V);        // elements per workgroup tile
     __shared__ WaveSlot s_slot[kThreads / kWave];
 
     const int tid = (int)threadIdx.x;
