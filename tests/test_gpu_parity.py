@@ -220,18 +220,17 @@ def test_segment_overflow_and_restaging(gpu):
 def test_xcd_chunk_order_covers_every_element(gpu, n):
     """XCD-contiguous order is a bijection of the chunks for any grid size
     (grids that are and are not multiples of the XCD count, and one above the
-    default threshold): bitwise the same as the linear order."""
+    default threshold): the default launch matches the oracle over the whole
+    shard, and the linear and XCD orders match it bitwise."""
     torch = gpu
     rng = np.random.default_rng(n % 1000)
     segs = _random_segments(rng, n, short_frac=0.05)
-    small = n < 2_000_000
-    lin, ref = _run_both(torch, n, 2, segs, range(1, 3), seed=19, cfg=dict(block_order=1),
-                         with_oracle=small)
+    dflt, ref = _run_both(torch, n, 2, segs, range(1, 3), seed=19)
+    assert H.assert_parity(dflt, ref, "n=%d default launch" % n)
+    lin, _ = _run_both(torch, n, 2, segs, range(1, 3), seed=19, cfg=dict(block_order=1),
+                       with_oracle=False)
     xcd, _ = _run_both(torch, n, 2, segs, range(1, 3), seed=19, cfg=dict(block_order=2),
                        with_oracle=False)
-    dflt, _ = _run_both(torch, n, 2, segs, range(1, 3), seed=19, with_oracle=False)
-    if small:
-        H.assert_parity(lin, ref, "n=%d linear" % n)
     for a, b, c in zip(lin, xcd, dflt):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
         assert np.array_equal(a.view(np.uint8), c.view(np.uint8))
