@@ -304,11 +304,13 @@ __device__ __forceinline__ uint32_t quantize_block(const uint32_t bits[4], uint3
     const bool usable = scale > 0.0f && scale <= 3.40282347e+38f;
     uint32_t word = 0;
     if (usable) {
-        // q = rint(x / scale) with the quotient correctly rounded.  x * rcp(scale)
-        // (hardware reciprocal, within 1 ulp) is within 2^-15.4 of the rounded
-        // quotient for |x / scale| < 128, so wherever it lies more than 2^-14 from
-        // a half-integer both round to the same integer; the rare other elements
-        // (and any non-finite product) take the correctly rounded division.
+        // q = rint(x / scale) with the quotient correctly rounded.  y = x * rcp(scale)
+        // (hardware reciprocal within 1 ulp, product rounded) is within
+        // 1.5 * 2^-23 * |y| of x / scale, and the rounded quotient within half an
+        // ulp of it: 1.75 * 2^-16 apart for |y| < 128 (1.75 * 2^-15 below 256), so
+        // wherever y lies more than 2^-14 from a half-integer both round to the
+        // same integer; the rare other elements (and any non-finite or larger y)
+        // take the correctly rounded division.
         const float rs = __builtin_amdgcn_rcpf(scale);
         float r[4];
         uint32_t slow = 0;
