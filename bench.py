@@ -79,9 +79,12 @@ def launch_key(plan: dict) -> str:
     """The launch a step resolves to (zs_launch_plan), as the key under which
     measured traffic is stored: any change of the library's defaults that
     changes grid, chunk, chunk order, occupancy cap or cache policy changes it."""
-    return "wg=%d,chunk=%d,order=%d,cap=%d,nt=%d" % (
+    key = "wg=%d,chunk=%d,order=%d,cap=%d,nt=%d" % (
         plan["workgroups"], plan["chunk_elements"], plan["block_order"],
         plan["groups_per_cu"], plan["nontemporal"])
+    if plan.get("window_quads", 1) != 1:
+        key += ",quads=%d" % plan["window_quads"]
+    return key
 
 
 def host_info():
@@ -378,7 +381,7 @@ def _ceiling_lib():
     lib.zs_ceiling_copy.restype = ctypes.c_int
     lib.zs_ceiling_twin.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P, P, P, P, P, P,
                                     ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
-                                    ctypes.c_int, P]
+                                    ctypes.c_int, ctypes.c_int, P]
     lib.zs_ceiling_twin.restype = ctypes.c_int
     return lib
 
@@ -409,8 +412,10 @@ class Twin:
         self.bufs = bufs
         self.lib = _ceiling_lib()
         self.chunk = plan["chunk_elements"]
+        self.quads = plan.get("window_quads", 1)
         self.n = n // self.chunk * self.chunk if self.chunk else 0
-        self.ok = plan["nontemporal"] == 1 and self.n > 0 and self.chunk % 1024 == 0
+        self.ok = plan["nontemporal"] == 1 and self.n > 0 and \
+            self.chunk % (1024 * self.quads) == 0
         self.plan = plan
         ptr = lambda t: ctypes.c_void_p(t.data_ptr() if t is not None else 0)  # noqa: E731
         self.head = [ptr(bufs["master"]), ptr(bufs["m"]), ptr(bufs["v"]), ptr(bufs["param"]),
@@ -427,7 +432,7 @@ class Twin:
             ctypes.cast(self.gp, ctypes.c_void_p),
             ctypes.cast(self.sp, ctypes.c_void_p) if self.sp is not None else None,
             self.k, self.n, self.chunk, self.plan["block_order"], self.plan["groups_per_cu"],
-            ctypes.c_void_p(stream.cuda_stream))
+            self.quads, ctypes.c_void_p(stream.cuda_stream))
         if rc != 0:
             raise RuntimeError("zs_ceiling_twin(%s) failed: %d" % (mode, rc))
 

@@ -107,8 +107,11 @@ typedef struct {
                               cap).  Fewer requests in flight relieve DRAM
                               congestion on many physical placements of the arrays.
                               0 = default: a cap of 5 for shards of 2^26 to
-                              2^32 - 1 elements, none otherwise;
-                              zs_shard_step_bf16mv never caps by default.  A cap whose LDS share exceeds the
+                              2^32 - 1 elements and none for smaller or larger
+                              ones, except that zs_shard_step_q8ag keeps the cap
+                              above 2^32 elements and zs_shard_step_bf16mv caps
+                              only there (with two 256-element sub-windows per
+                              wavefront, for k <= 4).  A cap whose LDS share exceeds the
                               per-workgroup limit returns ZS_ERR_INVALID_ARGUMENT. */
     int32_t block_order;  /* 0 = default, 1 = linear (workgroup b takes chunk b),
                              2 = XCD-contiguous (the workgroups the dispatcher deals to
@@ -267,7 +270,9 @@ typedef struct {
                                for, 0 = none (a default cap the device cannot hold is
                                dropped at launch) */
     int32_t nontemporal;    /* 1 = streaming loads and stores, 0 = cached */
-    int32_t reserved;       /* 0 */
+    int32_t window_quads;   /* 256-element sub-windows each wavefront takes per tile
+                               (1, or 2 for zs_shard_step_bf16mv on shards of at least
+                               2^32 elements with k <= 4) */
 } zs_launch_info;
 
 /* The launch a call of entry point `variant` (ZS_VARIANT_*) over n elements

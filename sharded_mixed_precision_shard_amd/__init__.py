@@ -66,7 +66,7 @@ class ZsLaunchCfg(ctypes.Structure):
 class ZsLaunchInfo(ctypes.Structure):
     _fields_ = [("workgroups", ctypes.c_int64), ("chunk_elements", ctypes.c_int64),
                 ("block_order", ctypes.c_int32), ("groups_per_cu", ctypes.c_int32),
-                ("nontemporal", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("nontemporal", ctypes.c_int32), ("window_quads", ctypes.c_int32)]
 
 
 class ZsError(RuntimeError):
@@ -240,9 +240,9 @@ def _check_k(k, arrays, name):
 
 def zs_launch_plan(k: int, n: int, variant: str = "base", cfg=None) -> dict:
     """The launch a call of entry point ``variant`` ("base", "q8ag", "q8grad",
-    "bf16mv") would make: grid, chunk, chunk order, occupancy cap and cache
-    policy, as a dict of the zs_launch_info fields.  ``cfg`` (base only) is a
-    dict of ZsLaunchCfg fields or None."""
+    "bf16mv") would make: grid, chunk, chunk order, occupancy cap, cache
+    policy and sub-windows per wavefront, as a dict of the zs_launch_info
+    fields.  ``cfg`` (base only) is a dict of ZsLaunchCfg fields or None."""
     c = None
     if cfg:
         c = ZsLaunchCfg(**{f: int(cfg.get(f, 0)) for f, _ in ZsLaunchCfg._fields_})
@@ -252,7 +252,7 @@ def zs_launch_plan(k: int, n: int, variant: str = "base", cfg=None) -> dict:
                                        ctypes.byref(out))
     if rc != ZS_OK:
         raise ZsError(rc, "zs_launch_plan")
-    return {f: getattr(out, f) for f, _ in ZsLaunchInfo._fields_ if f != "reserved"}
+    return {f: getattr(out, f) for f, _ in ZsLaunchInfo._fields_}
 
 
 def _marshal(master, m, v, param_bf16, grads, k, n, seg_table_, hparams_, mv_size=4):

@@ -39,7 +39,10 @@ constexpr int64_t kXcdOrderMinElems = int64_t(1) << 26;
 // 0.8-6 x 10^9 elements on MI355X (most on placements where DRAM queues
 // congest), but 2-6 % slower on the 8 x 10^9-element 70B shard, which needs
 // the full depth of requests in flight, and 0-1 % slower for the bf16-moment
-// variant (fewer bytes per element), which therefore keeps no default cap.
+// variant (fewer bytes per element), which therefore keeps no default cap
+// there.  Above kCapMaxElems the int8-payload step keeps the cap (+1.9-2.0 %
+// on the 70B shard, same process, three boxes) and the bf16-moment step runs
+// its wide kernel under it (kWide, k <= kWideMaxK).
 constexpr int64_t kCapMaxElems = int64_t(1) << 32;
 constexpr int kDefaultCap = 5;
 constexpr int kCusPerXcd = 32;  // gfx950
@@ -88,7 +91,7 @@ void launch_geometry(int variant, int64_t n, int chunk_tiles, int64_t *chunk_out
 // policy its cfg and the defaults resolve to (device-independent; the XCD
 // count and the LDS sizes are applied at launch).
 int resolve_launch(int k, int64_t n, int variant, const zs_launch_cfg *cfg,
-                   zs_launch_info *out) {
+                   zs_launch_info *out, int *kernel_variant = nullptr) {
     if (k < 1 || k > ZS_MAX_K || n < 0 || n > INT64_MAX / 8) return ZS_ERR_INVALID_ARGUMENT;
     if (variant != 0 && variant != kOutQ8 && variant != kGradQ8 && variant != kMvBf16)
         return ZS_ERR_INVALID_ARGUMENT;
@@ -107,18 +110,22 @@ int resolve_launch(int k, int64_t n, int variant, const zs_launch_cfg *cfg,
         groups_per_cu = cfg->groups_per_cu;
         block_order = cfg->block_order;
     }
+    const bool large = n >= kCapMaxElems;
+    const bool wide = variant == kMvBf16 && large && k <= kWideMaxK;
+    const int kv = wide ? (variant | kWide) : variant;
     int64_t chunk = 0, blocks = 0;
-    if (n > 0) launch_geometry(variant, n, chunk_tiles, &chunk, &blocks);
+    if (n > 0) launch_geometry(kv, n, chunk_tiles, &chunk, &blocks);
     const bool xcd_order = block_order == 2 || (block_order == 0 && n >= kXcdOrderMinElems);
-    if (groups_per_cu == 0 && n >= kXcdOrderMinElems && n < kCapMaxElems &&
-        !(variant & kMvBf16))
+    const bool capped = variant == kMvBf16 ? wide : (!large || variant == kOutQ8);
+    if (groups_per_cu == 0 && n >= kXcdOrderMinElems && capped)
         groups_per_cu = -kDefaultCap;  // a default cap: dropped where it does not fit
     out->workgroups = blocks;
     out->chunk_elements = chunk;
     out->block_order = xcd_order ? 2 : 1;
     out->groups_per_cu = groups_per_cu;
     out->nontemporal = nt;
-    out->reserved = 0;
+    out->window_quads = quads_for(kv);
+    if (kernel_variant) *kernel_variant = kv;
     return ZS_OK;
 }
 
@@ -155,7 +162,8 @@ int validate_and_launch(const Request &r) {
     if (r.k < 1 || r.k > ZS_MAX_K || r.n < 0 || r.step < 1 || !r.st || !r.hp)
         return ZS_ERR_INVALID_ARGUMENT;
     zs_launch_info plan;
-    const int pst = resolve_launch(r.k, r.n, r.variant, r.cfg, &plan);
+    int kernel_variant = r.variant;
+    const int pst = resolve_launch(r.k, r.n, r.variant, r.cfg, &plan, &kernel_variant);
     if (pst != ZS_OK) return pst;
     if (gq ? (!r.qgrads || !r.qscales) : !r.grads) return ZS_ERR_INVALID_ARGUMENT;
     const zs_hparams *hp = r.hp;
@@ -266,7 +274,7 @@ int validate_and_launch(const Request &r) {
     }
 
     const int unit_bc = (a.bc1 == 1.0f ? 1 : 0) | (a.bc2 == 1.0f ? 2 : 0);
-    kernel_fn fn = pick_kernel(r.k, r.variant, plan.nontemporal, unit_bc);
+    kernel_fn fn = pick_kernel(r.k, kernel_variant, plan.nontemporal, unit_bc);
     if (!fn) return ZS_ERR_INVALID_ARGUMENT;
     void *args[] = {&a};
     e = hipLaunchKernel((const void *)fn, dim3((unsigned)blocks), dim3(kThreads), args, dyn_lds,

@@ -83,17 +83,14 @@ __device__ __forceinline__ void opaque(T &x) {
     asm volatile("" : "+v"(x));
 }
 
-// Sub-windows per wave per tile, as in the step's kernel of that layout (one
-// for every entry point).
-constexpr int quads_of(int layout) { return (void)layout, 1; }
-constexpr int tile_of(int layout) { return kTile * quads_of(layout); }
-
-template <int K, int L>
+// kQ: 256-element sub-windows each wave takes per tile, as the step's kernel
+// in that launch (zs_launch_info.window_quads).
+template <int K, int L, int kQ>
 __global__ __launch_bounds__(kThreads) void twin_kernel(const TwinArgs a) {
     constexpr bool kMv16 = (L & kLayoutBf16Mv) != 0;
     constexpr bool kG8 = (L & kLayoutQ8Grad) != 0;
     constexpr bool kOut8 = (L & kLayoutQ8Out) != 0;
-    constexpr int kQ = quads_of(L);
+    constexpr int64_t kTileQ = (int64_t)kTile * kQ;
     const int lane = (int)(threadIdx.x % kWave);
     const int wave = (int)(threadIdx.x / kWave);
     int64_t b = blockIdx.x;
@@ -104,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void twin_kernel(const TwinArgs a) {
     }
     const int64_t c0 = b * a.chunk;
     const int64_t c1 = (c0 + a.chunk < a.n) ? c0 + a.chunk : a.n;
-    for (int64_t t0 = c0; t0 < c1; t0 += tile_of(L)) {
+    for (int64_t t0 = c0; t0 < c1; t0 += kTileQ) {
         const int64_t wv0 = t0 + (int64_t)wave * kSub * kQ;
         if (wv0 + kSub * kQ > c1) continue;  // whole windows only; the host sizes n to match
         int64_t qi[kQ];  // this lane's quad of each sub-window
@@ -225,35 +222,42 @@ __global__ __launch_bounds__(kThreads) void twin_kernel(const TwinArgs a) {
 
 typedef void (*twin_fn)(const TwinArgs);
 
-template <int K>
+template <int K, int Q>
 twin_fn pick_layout(int layout) {
     switch (layout) {
-        case kLayoutBase: return twin_kernel<K, kLayoutBase>;
-        case kLayoutQ8Out: return twin_kernel<K, kLayoutQ8Out>;
-        case kLayoutQ8Grad: return twin_kernel<K, kLayoutQ8Grad>;
-        case kLayoutBf16Mv: return twin_kernel<K, kLayoutBf16Mv>;
+        case kLayoutBase: return twin_kernel<K, kLayoutBase, Q>;
+        case kLayoutQ8Out: return twin_kernel<K, kLayoutQ8Out, Q>;
+        case kLayoutQ8Grad: return twin_kernel<K, kLayoutQ8Grad, Q>;
+        case kLayoutBf16Mv: return twin_kernel<K, kLayoutBf16Mv, Q>;
         default: return nullptr;
     }
 }
 
-twin_fn pick_twin(int k, int layout) {
+template <int K>
+twin_fn pick_quads(int layout, int quads) {
+    // two sub-windows per wave only where the step has such a kernel
+    if (quads == 2) return layout == kLayoutBf16Mv ? pick_layout<K, 2>(layout) : nullptr;
+    return quads == 1 ? pick_layout<K, 1>(layout) : nullptr;
+}
+
+twin_fn pick_twin(int k, int layout, int quads) {
     switch (k) {
-        case 1: return pick_layout<1>(layout);
-        case 2: return pick_layout<2>(layout);
-        case 3: return pick_layout<3>(layout);
-        case 4: return pick_layout<4>(layout);
-        case 5: return pick_layout<5>(layout);
-        case 6: return pick_layout<6>(layout);
-        case 7: return pick_layout<7>(layout);
-        case 8: return pick_layout<8>(layout);
-        case 9: return pick_layout<9>(layout);
-        case 10: return pick_layout<10>(layout);
-        case 11: return pick_layout<11>(layout);
-        case 12: return pick_layout<12>(layout);
-        case 13: return pick_layout<13>(layout);
-        case 14: return pick_layout<14>(layout);
-        case 15: return pick_layout<15>(layout);
-        case 16: return pick_layout<16>(layout);
+        case 1: return pick_quads<1>(layout, quads);
+        case 2: return pick_quads<2>(layout, quads);
+        case 3: return pick_quads<3>(layout, quads);
+        case 4: return pick_quads<4>(layout, quads);
+        case 5: return pick_quads<5>(layout, quads);
+        case 6: return pick_quads<6>(layout, quads);
+        case 7: return pick_quads<7>(layout, quads);
+        case 8: return pick_quads<8>(layout, quads);
+        case 9: return pick_quads<9>(layout, quads);
+        case 10: return pick_quads<10>(layout, quads);
+        case 11: return pick_quads<11>(layout, quads);
+        case 12: return pick_quads<12>(layout, quads);
+        case 13: return pick_quads<13>(layout, quads);
+        case 14: return pick_quads<14>(layout, quads);
+        case 15: return pick_quads<15>(layout, quads);
+        case 16: return pick_quads<16>(layout, quads);
         default: return nullptr;
     }
 }
@@ -299,27 +303,29 @@ int zs_ceiling_copy(const void *src, void *dst, int64_t bytes, void *stream) {
 //         bf16 otherwise); qscales (layout 2) k device pointers to one f32
 //         per 256 elements; q8 and q8_scale (layout 1) the int8 copy and its
 //         scales.
-//   n: elements; a multiple of chunk and of the 1024-element tile (the
-//         twin covers whole windows only, so the host rounds a shard down to
-//         that).
+//   n: elements; a multiple of chunk and of the tile (1024 elements per
+//         sub-window of a wave: the twin covers whole windows only, so the host
+//         rounds a shard down to that).
 //   chunk, block_order (1 linear, 2 XCD-contiguous), groups_per_cu (0 =
-//         none): the launch zs_launch_plan reports for the step.
+//         none), quads (sub-windows per wave: 1, or 2 with layout 4): the
+//         launch zs_launch_plan reports for the step.
 // Every pointer is DEVICE memory sized for n elements, 16-byte aligned (the
 // scale arrays 4-byte).  Returns 0, -1 on a bad argument (nothing enqueued),
 // or a hipError_t.
 int zs_ceiling_twin(int mode, int layout, float *master, void *m, void *v, uint16_t *param,
                     int8_t *q8, float *q8_scale, const void *const *grads,
                     const float *const *qscales, int k, int64_t n, int64_t chunk,
-                    int block_order, int groups_per_cu, void *stream) {
+                    int block_order, int groups_per_cu, int quads, void *stream) {
     if (mode < 0 || mode > 2 || k < 1 || k > kMaxK || n < 0 || !grads) return -1;
     if (layout != kLayoutBase && layout != kLayoutQ8Out && layout != kLayoutQ8Grad &&
         layout != kLayoutBf16Mv)
         return -1;
-    const int64_t tile = tile_of(layout);
+    if (quads != 1 && quads != 2) return -1;
+    const int64_t tile = (int64_t)kTile * quads;
     if (n % tile || chunk < tile || chunk % tile || (n && n % chunk)) return -1;
     if (block_order != 1 && block_order != 2) return -1;
     if (groups_per_cu < 0 || groups_per_cu > 32) return -1;
-    const twin_fn fn = pick_twin(k, layout);
+    const twin_fn fn = pick_twin(k, layout, quads);
     if (!fn) return -1;
     if (!master || !m || !v || !param) return -1;
     if ((layout & kLayoutQ8Out) && (!q8 || !q8_scale)) return -1;

@@ -25,22 +25,29 @@ constexpr int kSub = kWave * kQuad;           // 256: one dense instruction per 
 //             are dequantized inside the reduce;
 //   kMvBf16 - the moments m and v are stored as bf16 (12 bytes per parameter
 //             of optimizer state plus weight instead of 16).
+//   kWide   - two sub-windows per wave instead of one (launch-time choice for
+//             the bf16-moment step on the largest shards, see quads_for).
 constexpr int kOutQ8 = 1;
 constexpr int kGradQ8 = 2;
 constexpr int kMvBf16 = 4;
+constexpr int kWide = 8;
 
 // Sub-windows (quads per lane) a wave handles per tile.  Measured on MI355X
 // with the per-wavefront segment lookup: one quad per lane, i.e. the fewest
 // bytes in flight per wave and the most waves, streams as fast as or faster
-// than two or four quads for every partial count and entry point (even on the
-// eight-partial 7B shard; 5-12 % faster on small shards, which get four times
-// the workgroups; two quads lost 0.2-0.6 % on the 70B- and 175B-shaped shards
-// for the base and bf16-moment steps and 0-2.9 % for the int8-payload step,
-// same process).
-constexpr int quads_for(int variant) { return (void)variant, 1; }
+// than two or four quads for every partial count and entry point in the
+// default launches (even on the eight-partial 7B shard; 5-12 % faster on small
+// shards, which get four times the workgroups; two quads lost 0.2-0.6 % on the
+// 70B- and 175B-shaped shards for the base and bf16-moment steps, same
+// process).  The exception is kWide: on shards of 2^32 elements and more the
+// bf16-moment step with two quads per lane under an occupancy cap of 5 moved
+// 1.3-1.9 % more than with one quad uncapped (same process, three boxes),
+// while one quad under that cap lost 9-11 %: fewer waves, each with twice
+// the loads in flight across its arithmetic.
+constexpr int quads_for(int variant) { return (variant & kWide) ? 2 : 1; }
 constexpr int tile_for(int variant) { return (kThreads / kWave) * quads_for(variant) * kSub; }
 
-static_assert(tile_for(0) == 1024 && tile_for(kOutQ8) == 1024, "tile sizes");
+static_assert(tile_for(0) == 1024 && tile_for(kMvBf16 | kWide) == 2048, "tile sizes");
 
 struct StepArgs {
     float *master;
@@ -69,7 +76,11 @@ constexpr int64_t kStaticLds = (int64_t)(8 + 1) * kWave * (kThreads / kWave);
 
 typedef void (*kernel_fn)(const StepArgs);
 
-// The kernel for k partials, a variant (0 or one of the bits above),
+// Most partials the wide (kWide) kernels are built for.
+constexpr int kWideMaxK = 4;
+
+// The kernel for k partials, a variant (0 or one of the bits above; kWide
+// only with kMvBf16 and k <= kWideMaxK),
 // streaming (nt = 1) or cached (nt = 0) access and the bias corrections that
 // are exactly 1.0f (unit_bc bit 0: bc1, bit 1: bc2; a streaming kernel then
 // leaves out that division); nullptr if there is none.

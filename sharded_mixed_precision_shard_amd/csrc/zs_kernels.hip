@@ -505,6 +505,9 @@ kernel_fn pick_variant(int variant, int nt, int unit) {
         case kOutQ8: return pick_unit<K, kOutQ8>(unit);
         case kGradQ8: return pick_unit<K, kGradQ8>(unit);
         case kMvBf16: return pick_unit<K, kMvBf16>(unit);
+        case kMvBf16 | kWide:
+            if constexpr (K <= kWideMaxK) return pick_unit<K, kMvBf16 | kWide>(unit);
+            return nullptr;
         default: return nullptr;
     }
 }

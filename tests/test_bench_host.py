@@ -124,6 +124,21 @@ def test_launch_key_follows_the_resolved_launch():
     assert (p175["block_order"], p175["groups_per_cu"]) == (2, 5)  # inside it
     assert (pg2["block_order"], pg2["groups_per_cu"]) == (1, 0)    # below the XCD threshold
     assert zs.zs_launch_plan(2, synth.workload("175b").n, "bf16mv")["groups_per_cu"] == 0
+    assert p70["window_quads"] == 1 and p175["window_quads"] == 1
+    # above 2^32 elements: the int8 payload keeps the cap, bf16 moments take the
+    # wide kernel (two sub-windows per wave, 2048-element tiles) under it, for k <= 4
+    n70 = synth.workload("70b").n
+    q8 = zs.zs_launch_plan(2, n70, "q8ag")
+    assert (q8["groups_per_cu"], q8["window_quads"], q8["chunk_elements"]) == (5, 1, 1024)
+    mv = zs.zs_launch_plan(2, n70, "bf16mv")
+    assert (mv["groups_per_cu"], mv["window_quads"], mv["chunk_elements"]) == (5, 2, 2048)
+    assert mv["workgroups"] == -(-n70 // 2048)
+    mv8 = zs.zs_launch_plan(8, n70, "bf16mv")
+    assert (mv8["groups_per_cu"], mv8["window_quads"]) == (0, 1)
+    assert zs.zs_launch_plan(2, (1 << 32) - 1, "bf16mv")["window_quads"] == 1
+    assert zs.zs_launch_plan(2, 1 << 32, "bf16mv")["window_quads"] == 2
+    assert zs.zs_launch_plan(2, n70, "q8grad")["groups_per_cu"] == 0
+    assert bench.launch_key(mv).endswith(",quads=2") and "quads" not in bench.launch_key(p70)
     assert zs.zs_launch_plan(2, 10 ** 8, cfg=dict(nontemporal=2))["nontemporal"] == 0
     assert zs.zs_launch_plan(2, 0)["workgroups"] == 0
     # a default that moved (here: the cap of the 175B launch) changes the key
@@ -146,10 +161,10 @@ def test_twin_rejects_bad_arguments_before_any_device_call():
     g = (ctypes.c_void_p * 2)(4096, 8192)
     P = ctypes.c_void_p
 
-    def call(mode=0, layout=0, k=2, n=4096, chunk=1024, order=2, cap=0, grads=g):
+    def call(mode=0, layout=0, k=2, n=4096, chunk=1024, order=2, cap=0, grads=g, quads=1):
         return lib.zs_ceiling_twin(mode, layout, P(4096), P(4096), P(4096), P(4096), None,
                                    None, ctypes.cast(grads, P), None, k, n, chunk, order, cap,
-                                   None)
+                                   quads, None)
     assert call(mode=3) == -1
     assert call(layout=3) == -1
     assert call(k=0) == -1 and call(k=17) == -1
@@ -159,7 +174,11 @@ def test_twin_rejects_bad_arguments_before_any_device_call():
     assert call(layout=1) == -1                 # no int8 copy given
     assert call(layout=2) == -1                 # no scales given
     assert call(grads=(ctypes.c_void_p * 2)(4096, 0)) == -1
+    assert call(quads=3) == -1 and call(quads=0) == -1
+    assert call(quads=2) == -1                  # two sub-windows only with layout 4
+    assert call(layout=4, quads=2, chunk=1024) == -1  # chunk below the wide tile
     assert call(n=0) == 0                       # nothing to do
+    assert call(n=0, layout=4, quads=2, chunk=2048) == 0
 
 
 def test_parity_windows_cover_ends_and_boundaries():

@@ -76,7 +76,7 @@ def test_streaming_copy_of_the_ceiling_library():
     assert lib.zs_ceiling_copy(src.data_ptr(), dst.data_ptr(), 0, s) == 0
 
 
-@pytest.mark.parametrize("variant", ["base", "q8ag", "q8grad", "bf16mv"])
+@pytest.mark.parametrize("variant", ["base", "q8ag", "q8grad", "bf16mv", "bf16mv-wide"])
 def test_twin_moves_the_step_traffic_without_changing_the_state(variant):
     """The twin ceiling on a step's buffers: the whole-traffic mode writes the
     state back bit for bit, the read-only mode changes nothing, the
@@ -86,6 +86,8 @@ def test_twin_moves_the_step_traffic_without_changing_the_state(variant):
     import bench
     import sharded_mixed_precision_shard_amd as zs
     torch.cuda.set_device(0)
+    wide = variant == "bf16mv-wide"
+    variant = "bf16mv" if wide else variant
     k, n = 3, 1 << 16
     nb = n // 256
     g = torch.Generator(device="cuda").manual_seed(5)
@@ -103,6 +105,9 @@ def test_twin_moves_the_step_traffic_without_changing_the_state(variant):
     else:
         bufs["grads"] = [rnd(torch.int16) for _ in range(k)]
     plan = zs.zs_launch_plan(k, n, variant)
+    if wide:  # the launch shape of the largest shards, on a small buffer
+        plan = dict(plan, chunk_elements=2048, workgroups=n // 2048, window_quads=2,
+                    groups_per_cu=5)
     twin = bench.Twin(torch, variant, bufs, k, n, plan)
     assert twin.ok and twin.n == n
     keep = {x: bufs[x].clone() for x in ("master", "m", "v")}

@@ -178,7 +178,7 @@ def test_device_int8_generator_matches_host(gpu):
                           synth.host_q8_scales(nb, skey, 3, synth.q8_base_scale(1e-3)))
 
 
-def _large_variant(torch, name, variant, window, max_boundaries):
+def _large_variant(torch, name, variant, window, max_boundaries, step_ts=None):
     w = synth.workload(name)
     free, _ = torch.cuda.mem_get_info()
     per = {"base": 14 + 2 * w.k, "q8ag": 15 + 2 * w.k, "q8grad": 14 + w.k,
@@ -187,7 +187,7 @@ def _large_variant(torch, name, variant, window, max_boundaries):
         pytest.skip("needs %.1f GB of free device memory" % (w.n * per / 1e9))
     print("%s %s: n=%d k=%d" % (name, variant, w.n, w.k), flush=True)
     ds = H.DeviceShard(w, variant)
-    ts = list(range(1, w.prewarm_steps + 1)) + w.step_ts()
+    ts = list(range(1, w.prewarm_steps + 1)) + w.step_ts() if step_ts is None else list(step_ts)
     for t in ts:
         ds.fill_grads(t)
         ds.step(t)
@@ -207,6 +207,16 @@ def test_variants_on_70b_shard_windows(gpu, variant):
     t = 10000..10002) in each variant's default launch, compared on windows
     around segment boundaries and at the ragged ends."""
     _large_variant(gpu, "70b", variant, 1 << 14, 48)
+
+
+@pytest.mark.parametrize("ts", [(1, 2, 3), (200, 201, 202)], ids=["t1", "t200"])
+def test_bf16mv_wide_kernel_other_corrections(gpu, ts):
+    """The 70B-shaped shard takes the bf16-moment step's wide launch (two
+    sub-windows per wave, occupancy cap 5); at t = 10000 both bias corrections
+    are 1.0f, here neither (t = 1..3) and only the first (t = 200..202)."""
+    plan = zs.zs_launch_plan(2, synth.workload("70b").n, "bf16mv")
+    assert plan["window_quads"] == 2
+    _large_variant(gpu, "70b", "bf16mv", 1 << 14, 24, step_ts=ts)
 
 
 @pytest.mark.parametrize("variant", ["q8ag", "q8grad", "bf16mv"])
