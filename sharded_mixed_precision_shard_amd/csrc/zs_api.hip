@@ -40,11 +40,14 @@ constexpr int64_t kXcdOrderMinElems = int64_t(1) << 26;
 // congest), but 2-6 % slower on the 8 x 10^9-element 70B shard, which needs
 // the full depth of requests in flight, and 0-1 % slower for the bf16-moment
 // variant (fewer bytes per element), which therefore keeps no default cap
-// there.  Above kCapMaxElems the int8-payload step keeps the cap (+1.9-2.0 %
-// on the 70B shard, same process, three boxes) and the bf16-moment step runs
-// its wide kernel under it (kWide, k <= kWideMaxK).
+// there.  Above kCapMaxElems the int8-payload step keeps the cap (+1.3-2.0 %
+// on the 70B shard, same process, four boxes), the bf16-moment step runs its
+// wide kernel under it (kWide, k <= kWideMaxK), and the base step takes a
+// looser cap of 6 (+0.8 % on three boxes of four, -0.2 % on the fourth;
+// 5 and below cost it 1.8-4.4 %).
 constexpr int64_t kCapMaxElems = int64_t(1) << 32;
 constexpr int kDefaultCap = 5;
+constexpr int kLargeBaseCap = 6;
 constexpr int kCusPerXcd = 32;  // gfx950
 
 DeviceInfo g_dev[kMaxDevices];
@@ -116,9 +119,12 @@ int resolve_launch(int k, int64_t n, int variant, const zs_launch_cfg *cfg,
     int64_t chunk = 0, blocks = 0;
     if (n > 0) launch_geometry(kv, n, chunk_tiles, &chunk, &blocks);
     const bool xcd_order = block_order == 2 || (block_order == 0 && n >= kXcdOrderMinElems);
-    const bool capped = variant == kMvBf16 ? wide : (!large || variant == kOutQ8);
-    if (groups_per_cu == 0 && n >= kXcdOrderMinElems && capped)
-        groups_per_cu = -kDefaultCap;  // a default cap: dropped where it does not fit
+    // the default cap (negative: dropped where the device cannot hold it)
+    int cap = 0;
+    if (!large) cap = variant == kMvBf16 ? 0 : kDefaultCap;
+    else if (variant == 0) cap = kLargeBaseCap;
+    else if (variant == kOutQ8 || wide) cap = kDefaultCap;
+    if (groups_per_cu == 0 && n >= kXcdOrderMinElems && cap) groups_per_cu = -cap;
     out->workgroups = blocks;
     out->chunk_elements = chunk;
     out->block_order = xcd_order ? 2 : 1;

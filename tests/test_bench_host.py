@@ -120,7 +120,7 @@ def test_launch_key_follows_the_resolved_launch():
     p70 = zs.zs_launch_plan(2, synth.workload("70b").n)
     p175 = zs.zs_launch_plan(2, synth.workload("175b").n)
     pg2 = zs.zs_launch_plan(8, synth.workload("gpt2-small").n)
-    assert (p70["block_order"], p70["groups_per_cu"]) == (2, 0)    # above the cap's range
+    assert (p70["block_order"], p70["groups_per_cu"]) == (2, 6)    # above 2^32: a looser cap
     assert (p175["block_order"], p175["groups_per_cu"]) == (2, 5)  # inside it
     assert (pg2["block_order"], pg2["groups_per_cu"]) == (1, 0)    # below the XCD threshold
     assert zs.zs_launch_plan(2, synth.workload("175b").n, "bf16mv")["groups_per_cu"] == 0
@@ -141,6 +141,8 @@ def test_launch_key_follows_the_resolved_launch():
     assert bench.launch_key(mv).endswith(",quads=2") and "quads" not in bench.launch_key(p70)
     assert zs.zs_launch_plan(2, 10 ** 8, cfg=dict(nontemporal=2))["nontemporal"] == 0
     assert zs.zs_launch_plan(2, 0)["workgroups"] == 0
+    assert zs.zs_launch_plan(2, (1 << 32) - 1)["groups_per_cu"] == 5
+    assert zs.zs_launch_plan(2, (1 << 26) - 1)["groups_per_cu"] == 0
     # a default that moved (here: the cap of the 175B launch) changes the key
     moved = dict(p175, groups_per_cu=6)
     assert bench.launch_key(moved) != bench.launch_key(p175)
