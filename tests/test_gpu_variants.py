@@ -279,3 +279,51 @@ def test_prepared_call_matches_the_plain_call(gpu, variant):
     torch.cuda.synchronize()
     for key in ("w", "m", "v", "p", "q8", "q8s"):
         assert torch.equal(a[key].view(torch.uint8), b[key].view(torch.uint8)), key
+
+
+def test_bf16mv_wide_kernel_ragged_tail(gpu):
+    """A bf16-moment shard above 2^32 elements whose length is not a multiple
+    of the wide kernel's 2048-element tile (nor of 256): the last window runs
+    the element-by-element tail.  The buffers are zero except three windows
+    (the first, one across a segment boundary, the last) that get seeded
+    values; those are compared with the oracle after three steps."""
+    torch = gpu
+    n, k = (1 << 32) + 2777, 2
+    plan = zs.zs_launch_plan(k, n, "bf16mv")
+    assert plan["window_quads"] == 2 and n % plan["chunk_elements"]
+    need = n * (4 + 2 + 2 + 2 + 2 * k) + (2 << 30)
+    free, _ = torch.cuda.mem_get_info()
+    if free < need:
+        pytest.skip("needs %.1f GB of free device memory" % (need / 1e9))
+    L = 20_000
+    bnd = 3_000_000_017
+    segs = [(0, True), (bnd, False), (bnd + 5, True), (n - 1500, False)]
+    wins = [(0, L), (bnd - L // 2, bnd + L // 2), (n - L, n)]
+    rng = np.random.default_rng(41)
+    w = torch.zeros(n, dtype=torch.float32, device="cuda")
+    m = torch.zeros(n, dtype=torch.int16, device="cuda")
+    v = torch.zeros(n, dtype=torch.int16, device="cuda")
+    p = torch.zeros(n, dtype=torch.int16, device="cuda")
+    grads = [torch.zeros(n, dtype=torch.int16, device="cuda") for _ in range(k)]
+    ref = []
+    for lo, hi in wins:
+        w0 = rng.normal(0, 0.02, hi - lo).astype(F32)
+        w[lo:hi] = torch.from_numpy(w0).cuda()
+        ref.append([w0, np.zeros(hi - lo, np.uint16), np.zeros(hi - lo, np.uint16),
+                    np.zeros(hi - lo, np.uint16)])
+    table = H.segment_tensor(segs, "cuda")
+    st, hpz, hpo = zs.seg_table(table), zs.hparams(), oracle.hparams()
+    for t in (1, 2, 3):
+        gs = [[_bf16_partials(rng, 1, hi - lo, 1e-3)[0] for _ in range(k)] for lo, hi in wins]
+        for (lo, hi), gw in zip(wins, gs):
+            for j in range(k):
+                grads[j][lo:hi] = _dev(torch, gw[j])
+        zs.zs_shard_step_bf16mv(w, m, v, p, grads, k, n, st, hpz, t, torch.cuda.current_stream())
+        for (lo, hi), gw, r in zip(wins, gs, ref):
+            assert oracle.shard_step_bf16mv(*r, gw, synth.clip_segments(segs, lo, hi), hpo,
+                                            t) == 0
+    torch.cuda.synchronize()
+    for (lo, hi), r in zip(wins, ref):
+        got = (w[lo:hi].cpu().numpy(), m[lo:hi].cpu().numpy().view(np.uint16),
+               v[lo:hi].cpu().numpy().view(np.uint16), p[lo:hi].cpu().numpy().view(np.uint16))
+        assert H.assert_parity(got, r, "wide tail [%d,%d)" % (lo, hi))
