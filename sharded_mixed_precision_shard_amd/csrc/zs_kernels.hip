@@ -70,9 +70,9 @@ __device__ __forceinline__ uint32_t to_bf16(float x) {
 }
 
 // One element of the update: g is the reduced, scaled gradient.  U1 (U2)
-// says that bc1 (bc2) is exactly 1.0f, which it is once beta^t has fallen
-// below 2^-25: x / 1.0f == x for every x, so the division is left out and
-// the result is bit for bit the same.
+// says that bc1 (bc2) is exactly 1.0f, which it is once beta^t is at most
+// 2^-25 (1 - 2^-25 is a tie that rounds to the even 1.0f): x / 1.0f == x for
+// every x, so the division is left out and the result is bit for bit the same.
 template <bool U1 = false, bool U2 = false>
 __device__ __forceinline__ void adamw(float &w, float &m, float &v, float g, bool decay,
                                       const StepArgs &a) {

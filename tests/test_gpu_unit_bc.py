@@ -21,6 +21,7 @@ F32 = np.float32
 HP = dict(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
 
 # step ranges: no unit correction, across bc1 -> 1, bc1 only, across bc2 -> 1, both
+# (tests/test_unit_correction_thresholds.py checks where the thresholds fall)
 RANGES = {"none": range(1, 6), "bc1_switch": range(162, 168), "bc1": range(200, 205),
           "bc2_switch": range(335, 341), "both": range(10000, 10005)}
 
@@ -43,16 +44,6 @@ def _dev(torch, a):
 
 def _bf16(x):
     return (x.astype(F32).view(np.uint32) >> 16).astype(np.uint16)
-
-
-def test_thresholds_are_where_the_ranges_put_them():
-    hp = oracle.hparams(**HP)
-    unit = lambda t: tuple(x == np.float32(1.0) for x in oracle.scalars(hp, t)[2:4])  # noqa: E731
-    assert unit(164) == (False, False) and unit(165) == (True, False)
-    assert unit(337) == (True, False) and unit(338) == (True, True)
-    assert all(unit(t) == (False, False) for t in RANGES["none"])
-    assert all(unit(t) == (True, False) for t in RANGES["bc1"])
-    assert all(unit(t) == (True, True) for t in RANGES["both"])
 
 
 @pytest.mark.parametrize("variant", H.VARIANTS)

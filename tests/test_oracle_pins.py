@@ -389,6 +389,25 @@ def test_shard_resident_bytes_pins():
             accounting.shard_resident_bytes_per_param(k) + 12
 
 
+def test_resident_bytes_pins_catch_planted_mistakes(monkeypatch):
+    """Each plausible slip in the resident-bytes formula fails the pins above."""
+    good = accounting.shard_resident_bytes_per_param
+    mistakes = [lambda k: 3 * 4 + 2 * k,          # the bf16 parameter copy dropped
+                lambda k: 3 * 4 + 2 + 2,          # one partial whatever k is
+                lambda k: 2 * 4 + 2 + 2 * k,      # one fp32 state array dropped
+                lambda k: 3 * 4 + 4 + 2 * k,      # the parameter copy counted as fp32
+                lambda k: 3 * 4 + 2 + 4 * k]      # partials counted as fp32
+    for bad in mistakes:
+        monkeypatch.setattr(accounting, "shard_resident_bytes_per_param", bad)
+        try:
+            test_shard_resident_bytes_pins()
+        except AssertionError:
+            continue
+        finally:
+            monkeypatch.setattr(accounting, "shard_resident_bytes_per_param", good)
+        raise AssertionError("a planted mistake passed the pins")
+
+
 # ---------------------------------------------------- argument validation
 
 def test_oracle_rejects_invalid_arguments():
