@@ -418,21 +418,25 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
             // Decay flags: bit 4*qd + j for element e[qd] + j.
             const uint32_t mask = window_mask(a, w0, w1, kQuads * kQuad, elem, s_slot[wave]);
             u32x2 pq[kQuads];
-#pragma unroll
-            for (int qd = 0; qd < kQuads; ++qd)
-                quad_update<K, V, NT, (U & 1) != 0, (U & 2) != 0>(
-                    wv[qd], mv[qd], vv[qd], gq[qd], (mask >> (kQuad * qd)) & 0xfu, a, pq[qd]);
             // In a full tile every wavefront of the workgroup is on this branch
-            // (the test is workgroup-uniform), and they issue their stores
-            // together: the writes reach memory in denser bursts.  The int8
-            // payload's block maxima sit between the updates and its stores, and
-            // there the wait costs more than the grouping gains.
+            // (the test is workgroup-uniform): all updates first, then the
+            // wavefronts meet and issue their stores together, so the writes
+            // reach memory in denser bursts.  The int8-payload kernel keeps each
+            // quad's update next to its stores: its block maxima sit between
+            // the two, and there the wait costs more than the grouping gains.
             if constexpr (!(V & kOutQ8)) {
+#pragma unroll
+                for (int qd = 0; qd < kQuads; ++qd)
+                    quad_update<K, V, NT, (U & 1) != 0, (U & 2) != 0>(
+                        wv[qd], mv[qd], vv[qd], gq[qd], (mask >> (kQuad * qd)) & 0xfu, a, pq[qd]);
                 if (t0 + kTile <= c1) __syncthreads();
             }
 #pragma unroll
             for (int qd = 0; qd < kQuads; ++qd) {
                 const int64_t qi = e[qd] / kQuad;
+                if constexpr (V & kOutQ8)
+                    quad_update<K, V, NT, (U & 1) != 0, (U & 2) != 0>(
+                        wv[qd], mv[qd], vv[qd], gq[qd], (mask >> (kQuad * qd)) & 0xfu, a, pq[qd]);
                 store<NT>(pw + qi, wv[qd]);
                 if constexpr (V & kMvBf16) {
                     store<NT>(reinterpret_cast<u32x2 *>(a.m) + qi, f32x4_to_bf16x4(mv[qd]));
