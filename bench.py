@@ -594,6 +594,7 @@ SWEEP_CFGS = [
     ("xcd,cap4", dict(block_order=2, groups_per_cu=4)),
     ("xcd,cap5", dict(block_order=2, groups_per_cu=5)),
     ("xcd,cap6", dict(block_order=2, groups_per_cu=6)),
+    ("xcd,cap8", dict(block_order=2, groups_per_cu=8)),
 ]
 
 
