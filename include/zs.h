@@ -106,14 +106,13 @@ typedef struct {
                               per workgroup; ZS_MAX_GROUPS_PER_CU never binds (no
                               cap).  Fewer requests in flight relieve DRAM
                               congestion on many physical placements of the arrays.
-                              0 = default: none below 2^26 elements; a cap of 5
-                              for shards of 2^26 to 2^32 - 1 elements (none for
-                              zs_shard_step_bf16mv); above 2^32 elements a cap of
-                              6 for zs_shard_step(_cfg), 5 for zs_shard_step_q8ag
-                              and for zs_shard_step_bf16mv with k <= 4 (which
-                              then takes two 256-element sub-windows per
-                              wavefront), none for zs_shard_step_q8grad.  A cap whose LDS share exceeds the
-                              per-workgroup limit returns ZS_ERR_INVALID_ARGUMENT. */
+                              0 = default: none below 2^26 elements, a cap of 5
+                              from 2^26 elements on, except for
+                              zs_shard_step_bf16mv below 2^32 elements or with
+                              k > 4 (no cap); from 2^32 elements with k <= 4 it
+                              takes two 256-element sub-windows per wavefront.
+                              A cap whose LDS share exceeds the per-workgroup
+                              limit returns ZS_ERR_INVALID_ARGUMENT. */
     int32_t block_order;  /* 0 = default, 1 = linear (workgroup b takes chunk b),
                              2 = XCD-contiguous (the workgroups the dispatcher deals to
                              one XCD take one contiguous run of chunks).  The default

@@ -34,20 +34,18 @@ struct DeviceInfo {
 // and slower on shards that fit the 256 MB last-level cache).
 constexpr int64_t kXcdOrderMinElems = int64_t(1) << 26;
 
-// Default occupancy cap for shards of [kXcdOrderMinElems, kCapMaxElems)
-// elements: 5 resident workgroups per CU measured 0-8 % faster on shards of
-// 0.8-6 x 10^9 elements on MI355X (most on placements where DRAM queues
-// congest), but 2-6 % slower on the 8 x 10^9-element 70B shard, which needs
-// the full depth of requests in flight, and 0-1 % slower for the bf16-moment
-// variant (fewer bytes per element), which therefore keeps no default cap
-// there.  Above kCapMaxElems the int8-payload step keeps the cap (+1.3-2.0 %
-// on the 70B shard, same process, four boxes), the bf16-moment step runs its
-// wide kernel under it (kWide, k <= kWideMaxK), and the base step takes a
-// looser cap of 6 (+0.8 % on three boxes of four, -0.2 % on the fourth;
-// 5 and below cost it 1.8-4.4 %).
-constexpr int64_t kCapMaxElems = int64_t(1) << 32;
+// Default occupancy cap for shards of at least kXcdOrderMinElems elements:
+// 5 resident workgroups per CU.  On MI355X it measured 0-8 % faster on shards
+// of 0.8-3 x 10^9 elements (most on placements where DRAM queues congest) and
+// 1.3-1.6 % faster for every entry point on the 8 x 10^9-element 70B shard
+// (same process, two boxes; 4 is as good, 6 and more or none slower).  The
+// bf16-moment step with one sub-window per wavefront keeps no default cap
+// (0-1 % slower under it below 2^32 elements, 9-11 % above).
 constexpr int kDefaultCap = 5;
-constexpr int kLargeBaseCap = 6;
+// From this many elements the bf16-moment step with k <= kWideMaxK takes two
+// 256-element sub-windows per wavefront (kWide), which gains 0.5-1.9 % under
+// the cap there.
+constexpr int64_t kWideMinElems = int64_t(1) << 32;
 constexpr int kCusPerXcd = 32;  // gfx950
 
 DeviceInfo g_dev[kMaxDevices];
@@ -113,17 +111,13 @@ int resolve_launch(int k, int64_t n, int variant, const zs_launch_cfg *cfg,
         groups_per_cu = cfg->groups_per_cu;
         block_order = cfg->block_order;
     }
-    const bool large = n >= kCapMaxElems;
-    const bool wide = variant == kMvBf16 && large && k <= kWideMaxK;
+    const bool wide = variant == kMvBf16 && n >= kWideMinElems && k <= kWideMaxK;
     const int kv = wide ? (variant | kWide) : variant;
     int64_t chunk = 0, blocks = 0;
     if (n > 0) launch_geometry(kv, n, chunk_tiles, &chunk, &blocks);
     const bool xcd_order = block_order == 2 || (block_order == 0 && n >= kXcdOrderMinElems);
     // the default cap (negative: dropped where the device cannot hold it)
-    int cap = 0;
-    if (!large) cap = variant == kMvBf16 ? 0 : kDefaultCap;
-    else if (variant == 0) cap = kLargeBaseCap;
-    else if (variant == kOutQ8 || wide) cap = kDefaultCap;
+    const int cap = (variant == kMvBf16 && !wide) ? 0 : kDefaultCap;
     if (groups_per_cu == 0 && n >= kXcdOrderMinElems && cap) groups_per_cu = -cap;
     out->workgroups = blocks;
     out->chunk_elements = chunk;

@@ -123,11 +123,38 @@ struct WaveSlot {
 // its own elements; a window with more boundaries than the slot holds looks
 // each element up in the table.  All 64 lanes must call this; every read
 // stays inside segs[0 .. nseg-1] and the slot, sorted table or not.
+//
+// The search's first round probes the same 64 entries for every window, so
+// its load is issued apart (first_probe), before the window's data loads:
+// waiting for it does not wait for them, and the rest of the search then
+// overlaps them.
+struct FirstProbe {
+    int32_t step;   // entries between probes; 0 = the table needs no search round
+    int64_t start;  // this lane's probe, entry lane * step (kNoStart past the end)
+};
+
+__device__ __forceinline__ FirstProbe first_probe(const StepArgs &a) {
+    FirstProbe p{0, kNoStart};
+    if (a.nseg > kWave) {
+        const int lane = (int)(threadIdx.x % kWave);
+        p.step = (a.nseg + kWave - 1) / kWave;
+        const int64_t idx = (int64_t)lane * p.step;
+        if (idx < a.nseg) p.start = a.segs[idx].start;
+    }
+    return p;
+}
+
 template <typename ElemFn>
-__device__ uint32_t window_mask(const StepArgs &a, int64_t w0, int64_t w1, int nelem,
-                                ElemFn elem, WaveSlot &slot) {
+__device__ uint32_t window_mask(const StepArgs &a, const FirstProbe &probe, int64_t w0,
+                                int64_t w1, int nelem, ElemFn elem, WaveSlot &slot) {
     const int lane = (int)(threadIdx.x % kWave);
     int32_t lo = 0, hi = a.nseg;  // the entry covering w0 lies in [lo, hi)
+    if (probe.step) {
+        const uint64_t b = __ballot(probe.start <= w0);
+        const int top = b ? 63 - __clzll(b) : 0;
+        lo = top * probe.step;
+        hi = (lo + probe.step < hi) ? lo + probe.step : hi;
+    }
     while (hi - lo > kWave) {
         const int32_t step = (hi - lo + kWave - 1) / kWave;
         const int64_t idx = (int64_t)lo + (int64_t)lane * step;
@@ -397,8 +424,10 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
         auto elem = [&](int q) { return e[q / kQuad] + (q % kQuad); };
 
         if (w0 + kWindow <= a.n) {
-            // Whole window in range: dense vector traffic only.  The loads are
-            // issued first, so the segment search below overlaps them.
+            // Whole window in range: dense vector traffic only.  The search's
+            // first probe, then the data loads, so that the rest of the
+            // segment search overlaps them.
+            const FirstProbe probe = first_probe(a);
             f32x4 *pw = reinterpret_cast<f32x4 *>(a.master);
             f32x4 wv[kQuads], mv[kQuads], vv[kQuads];
             QuadGrads<K, V, NT> gq[kQuads];
@@ -416,7 +445,8 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
                 gq[qd].load_from(a, qi);
             }
             // Decay flags: bit 4*qd + j for element e[qd] + j.
-            const uint32_t mask = window_mask(a, w0, w1, kQuads * kQuad, elem, s_slot[wave]);
+            const uint32_t mask =
+                window_mask(a, probe, w0, w1, kQuads * kQuad, elem, s_slot[wave]);
             u32x2 pq[kQuads];
             // In a full tile every wavefront of the workgroup is on this branch
             // (the test is workgroup-uniform): all updates first, then the
@@ -457,7 +487,8 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
         } else {
             // The shard's last, partial window: element by element (the whole
             // wavefront stays here together, for the search and block maxima).
-            const uint32_t mask = window_mask(a, w0, w1, kQuads * kQuad, elem, s_slot[wave]);
+            const uint32_t mask =
+                window_mask(a, first_probe(a), w0, w1, kQuads * kQuad, elem, s_slot[wave]);
             uint32_t pbits[kQuads * kQuad];
             uint32_t valid = 0;
             for (int q = 0; q < kQuads * kQuad; ++q) {

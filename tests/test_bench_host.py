@@ -120,13 +120,14 @@ def test_launch_key_follows_the_resolved_launch():
     p70 = zs.zs_launch_plan(2, synth.workload("70b").n)
     p175 = zs.zs_launch_plan(2, synth.workload("175b").n)
     pg2 = zs.zs_launch_plan(8, synth.workload("gpt2-small").n)
-    assert (p70["block_order"], p70["groups_per_cu"]) == (2, 6)    # above 2^32: a looser cap
-    assert (p175["block_order"], p175["groups_per_cu"]) == (2, 5)  # inside it
+    assert (p70["block_order"], p70["groups_per_cu"]) == (2, 5)    # from 2^26 on: cap 5
+    assert (p175["block_order"], p175["groups_per_cu"]) == (2, 5)
     assert (pg2["block_order"], pg2["groups_per_cu"]) == (1, 0)    # below the XCD threshold
     assert zs.zs_launch_plan(2, synth.workload("175b").n, "bf16mv")["groups_per_cu"] == 0
     assert p70["window_quads"] == 1 and p175["window_quads"] == 1
-    # above 2^32 elements: the int8 payload keeps the cap, bf16 moments take the
-    # wide kernel (two sub-windows per wave, 2048-element tiles) under it, for k <= 4
+    # above 2^32 elements every entry point keeps the cap; bf16 moments take the
+    # wide kernel (two sub-windows per wave, 2048-element tiles) under it, for k <= 4,
+    # and otherwise run uncapped as below 2^32
     n70 = synth.workload("70b").n
     q8 = zs.zs_launch_plan(2, n70, "q8ag")
     assert (q8["groups_per_cu"], q8["window_quads"], q8["chunk_elements"]) == (5, 1, 1024)
@@ -137,7 +138,9 @@ def test_launch_key_follows_the_resolved_launch():
     assert (mv8["groups_per_cu"], mv8["window_quads"]) == (0, 1)
     assert zs.zs_launch_plan(2, (1 << 32) - 1, "bf16mv")["window_quads"] == 1
     assert zs.zs_launch_plan(2, 1 << 32, "bf16mv")["window_quads"] == 2
-    assert zs.zs_launch_plan(2, n70, "q8grad")["groups_per_cu"] == 0
+    assert zs.zs_launch_plan(2, n70, "q8grad")["groups_per_cu"] == 5
+    assert zs.zs_launch_plan(2, (1 << 32) - 1, "bf16mv")["groups_per_cu"] == 0
+    assert zs.zs_launch_plan(2, 1 << 32, "bf16mv")["groups_per_cu"] == 5
     assert bench.launch_key(mv).endswith(",quads=2") and "quads" not in bench.launch_key(p70)
     assert zs.zs_launch_plan(2, 10 ** 8, cfg=dict(nontemporal=2))["nontemporal"] == 0
     assert zs.zs_launch_plan(2, 0)["workgroups"] == 0
