@@ -29,7 +29,8 @@
 //   * every wavefront resolves the weight-decay flags of its own window, with
 //     no workgroup barrier and after issuing its loads (so the lookup
 //     overlaps them): a 64-way search of the device table finds the entry
-//     covering the window (two dependent loads for up to 4096 entries); a
+//     covering the window (up to 4096 entries: a six-step scalar search,
+//     then one vector load of 64 consecutive entries); a
 //     window inside one segment takes that segment's flag, a window with
 //     segment boundaries stages the 64 entries around it in the wave's LDS
 //     slot and each lane walks them for its own elements;
@@ -115,45 +116,41 @@ struct WaveSlot {
 // wave-uniform): bit q belongs to element q of the lane, whose index is
 // elem(q), increasing in q; elements at or past w1 get no bit.  Done by the
 // wavefront alone, with no workgroup barrier.  A 64-way search finds the
-// entry covering w0: each round probes 64 entries at once and narrows the
-// range 64-fold, and the last round loads 64 consecutive entries (two
-// dependent loads in all for tables of up to 4096 entries).  A window inside
+// entry covering w0: each round probes 64 entries and narrows the range
+// 64-fold, and the last round loads 64 consecutive entries.  A window inside
 // one segment takes that segment's flag; a window that holds boundaries stages
 // the 64 loaded entries in the wave's LDS slot and every lane walks them for
 // its own elements; a window with more boundaries than the slot holds looks
 // each element up in the table.  All 64 lanes must call this; every read
 // stays inside segs[0 .. nseg-1] and the slot, sorted table or not.
 //
-// The search's first round probes the same 64 entries for every window, so
-// its load is issued apart (first_probe), before the window's data loads:
-// waiting for it does not wait for them, and the rest of the search then
-// overlaps them.
-struct FirstProbe {
-    int32_t step;   // entries between probes; 0 = the table needs no search round
-    int64_t start;  // this lane's probe, entry lane * step (kNoStart past the end)
-};
-
-__device__ __forceinline__ FirstProbe first_probe(const StepArgs &a) {
-    FirstProbe p{0, kNoStart};
-    if (a.nseg > kWave) {
-        const int lane = (int)(threadIdx.x % kWave);
-        p.step = (a.nseg + kWave - 1) / kWave;
-        const int64_t idx = (int64_t)lane * p.step;
-        if (idx < a.nseg) p.start = a.segs[idx].start;
-    }
-    return p;
-}
-
+// The first round (tables of more than 64 entries) is a binary search over
+// its 64 probe entries j * step with wave-uniform indices, so that it runs on
+// scalar loads: the scalar cache holds the few probe entries every window
+// visits, and the scalar loads' counter is apart from the vector loads', so
+// waiting for them does not wait for the window's data (a vector probe here
+// made each wave wait for its data and then for two table loads in turn).  On
+// a sorted table it finds the probe a 64-lane compare would, the highest whose
+// start is <= w0 (0 if none).  Further rounds (tables of more than 4096
+// entries) probe 64 entries at once with vector loads.
 template <typename ElemFn>
-__device__ uint32_t window_mask(const StepArgs &a, const FirstProbe &probe, int64_t w0,
-                                int64_t w1, int nelem, ElemFn elem, WaveSlot &slot) {
+__device__ uint32_t window_mask(const StepArgs &a, int64_t w0, int64_t w1, int nelem,
+                                ElemFn elem, WaveSlot &slot) {
     const int lane = (int)(threadIdx.x % kWave);
     int32_t lo = 0, hi = a.nseg;  // the entry covering w0 lies in [lo, hi)
-    if (probe.step) {
-        const uint64_t b = __ballot(probe.start <= w0);
-        const int top = b ? 63 - __clzll(b) : 0;
-        lo = top * probe.step;
-        hi = (lo + probe.step < hi) ? lo + probe.step : hi;
+    if (hi > kWave) {
+        const int32_t step = (hi + kWave - 1) / kWave;
+        int32_t jlo = 0, jhi = (hi - 1) / step;  // probes j * step < nseg, j < 64
+        // the table is read-only for the kernel: read it as constant memory
+        typedef const __attribute__((address_space(4))) zs_segment ConstSegment;
+        ConstSegment *cs = (ConstSegment *)a.segs;
+        while (jlo < jhi) {
+            const int32_t mid = jlo + (jhi - jlo + 1) / 2;
+            if (cs[(int64_t)mid * step].start <= w0) jlo = mid;
+            else jhi = mid - 1;
+        }
+        lo = jlo * step;
+        hi = (lo + step < hi) ? lo + step : hi;
     }
     while (hi - lo > kWave) {
         const int32_t step = (hi - lo + kWave - 1) / kWave;
@@ -397,7 +394,8 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
 
     const int tid = (int)threadIdx.x;
     const int lane = tid % kWave;
-    const int wave = tid / kWave;
+    // wave-uniform, so that window starts (and the segment search) are scalar
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     // Chunk order.  The dispatcher deals workgroup b to XCD b % xcds; with
     // xcds > 1 each XCD is given one contiguous run of the nb = xcds*q + r
     // chunks (XCD x: q or q + 1 chunks from x*q + min(x, r)), so its L2 sees
@@ -424,10 +422,8 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
         auto elem = [&](int q) { return e[q / kQuad] + (q % kQuad); };
 
         if (w0 + kWindow <= a.n) {
-            // Whole window in range: dense vector traffic only.  The search's
-            // first probe, then the data loads, so that the rest of the
-            // segment search overlaps them.
-            const FirstProbe probe = first_probe(a);
+            // Whole window in range: dense vector traffic only.  The loads are
+            // issued first, so the segment search below overlaps them.
             f32x4 *pw = reinterpret_cast<f32x4 *>(a.master);
             f32x4 wv[kQuads], mv[kQuads], vv[kQuads];
             QuadGrads<K, V, NT> gq[kQuads];
@@ -445,8 +441,7 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
                 gq[qd].load_from(a, qi);
             }
             // Decay flags: bit 4*qd + j for element e[qd] + j.
-            const uint32_t mask =
-                window_mask(a, probe, w0, w1, kQuads * kQuad, elem, s_slot[wave]);
+            const uint32_t mask = window_mask(a, w0, w1, kQuads * kQuad, elem, s_slot[wave]);
             u32x2 pq[kQuads];
             // In a full tile every wavefront of the workgroup is on this branch
             // (the test is workgroup-uniform): all updates first, then the
@@ -487,8 +482,7 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
         } else {
             // The shard's last, partial window: element by element (the whole
             // wavefront stays here together, for the search and block maxima).
-            const uint32_t mask =
-                window_mask(a, first_probe(a), w0, w1, kQuads * kQuad, elem, s_slot[wave]);
+            const uint32_t mask = window_mask(a, w0, w1, kQuads * kQuad, elem, s_slot[wave]);
             uint32_t pbits[kQuads * kQuad];
             uint32_t valid = 0;
             for (int q = 0; q < kQuads * kQuad; ++q) {
