@@ -179,11 +179,6 @@ __global__ __launch_bounds__(kThreads) void twin_kernel(const TwinArgs a) {
         }
         // The whole step's traffic: state written back bit for bit.  Every
         // value loaded is pinned, so that no load can be dropped as unused.
-        // The step's store grouping: in a full tile the workgroup's wavefronts
-        // meet before their stores (not with the int8 parameter copy).
-        if constexpr (!kOut8) {
-            if (t0 + kTileQ <= c1) __syncthreads();
-        }
 #pragma unroll
         for (int qd = 0; qd < kQ; ++qd) {
 #pragma unroll

@@ -22,10 +22,6 @@
 //     dispatcher deals to one XCD take one contiguous run, giving each XCD's
 //     L2 a sequential stream (eight fronts sweep the arrays), on small grids
 //     linearly (one front);
-//   * in a full tile the four wavefronts meet at one workgroup barrier
-//     between their updates and their stores, so that a workgroup's writes
-//     leave together (not in the int8-payload kernel, where it costs more
-//     than it gains);
 //   * every wavefront resolves the weight-decay flags of its own window, with
 //     no workgroup barrier and after issuing its loads (so the lookup
 //     overlaps them): a 64-way search of the device table finds the entry
@@ -409,8 +405,7 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
     const int64_t c0 = b * a.chunk;
     const int64_t c1 = (c0 + a.chunk < a.n) ? c0 + a.chunk : a.n;
 
-    // Every wavefront works on its own windows; the one workgroup barrier
-    // (below) only groups the stores of a full tile.
+    // Every wavefront works on its own windows; there is no workgroup barrier.
     for (int64_t t0 = c0; t0 < c1; t0 += kTile) {
         const int64_t w0 = t0 + (int64_t)wave * kWindow;
         if (w0 >= c1) continue;  // wave-uniform
@@ -442,26 +437,12 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
             }
             // Decay flags: bit 4*qd + j for element e[qd] + j.
             const uint32_t mask = window_mask(a, w0, w1, kQuads * kQuad, elem, s_slot[wave]);
-            u32x2 pq[kQuads];
-            // In a full tile every wavefront of the workgroup is on this branch
-            // (the test is workgroup-uniform): all updates first, then the
-            // wavefronts meet and issue their stores together, so the writes
-            // reach memory in denser bursts.  The int8-payload kernel keeps each
-            // quad's update next to its stores: its block maxima sit between
-            // the two, and there the wait costs more than the grouping gains.
-            if constexpr (!(V & kOutQ8)) {
-#pragma unroll
-                for (int qd = 0; qd < kQuads; ++qd)
-                    quad_update<K, V, NT, (U & 1) != 0, (U & 2) != 0>(
-                        wv[qd], mv[qd], vv[qd], gq[qd], (mask >> (kQuad * qd)) & 0xfu, a, pq[qd]);
-                if (t0 + kTile <= c1) __syncthreads();
-            }
 #pragma unroll
             for (int qd = 0; qd < kQuads; ++qd) {
                 const int64_t qi = e[qd] / kQuad;
-                if constexpr (V & kOutQ8)
-                    quad_update<K, V, NT, (U & 1) != 0, (U & 2) != 0>(
-                        wv[qd], mv[qd], vv[qd], gq[qd], (mask >> (kQuad * qd)) & 0xfu, a, pq[qd]);
+                u32x2 pq;
+                quad_update<K, V, NT, (U & 1) != 0, (U & 2) != 0>(
+                    wv[qd], mv[qd], vv[qd], gq[qd], (mask >> (kQuad * qd)) & 0xfu, a, pq);
                 store<NT>(pw + qi, wv[qd]);
                 if constexpr (V & kMvBf16) {
                     store<NT>(reinterpret_cast<u32x2 *>(a.m) + qi, f32x4_to_bf16x4(mv[qd]));
@@ -470,10 +451,10 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
                     store<NT>(reinterpret_cast<f32x4 *>(a.m) + qi, mv[qd]);
                     store<NT>(reinterpret_cast<f32x4 *>(a.v) + qi, vv[qd]);
                 }
-                store<NT>(reinterpret_cast<u32x2 *>(a.param) + qi, pq[qd]);
+                store<NT>(reinterpret_cast<u32x2 *>(a.param) + qi, pq);
                 if constexpr (V & kOutQ8) {
-                    const uint32_t bits[4] = {pq[qd][0] << 16, pq[qd][0] & 0xffff0000u,
-                                              pq[qd][1] << 16, pq[qd][1] & 0xffff0000u};
+                    const uint32_t bits[4] = {pq[0] << 16, pq[0] & 0xffff0000u, pq[1] << 16,
+                                              pq[1] & 0xffff0000u};
                     const int64_t blk = (w0 + (int64_t)qd * kSub) / kQ8Block;
                     const uint32_t word = quantize_block(bits, 0xfu, a, blk, true);
                     store<NT>(reinterpret_cast<uint32_t *>(a.q8) + qi, word);
