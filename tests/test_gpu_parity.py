@@ -249,6 +249,30 @@ def test_largest_segment_table(gpu):
     H.assert_parity(got, ref, "%d segments" % count)
 
 
+@pytest.mark.parametrize("nseg", [65, 127, 128, 129, 1970, 4095, 4096, 4097])
+def test_segment_search_probe_edges(gpu, nseg):
+    """Tables of more than 64 entries, just above one search round and around
+    the point where further rounds start, whose entries at the search's probe
+    positions (every ceil(nseg/64)-th) start exactly on a 256-element window
+    start, one element past one, or on the same element as the entry before
+    (a duplicate start, so the later entry wins).  Every flag must equal the
+    oracle's, bit for bit."""
+    rng = np.random.default_rng(nseg)
+    step = -(-nseg // 64)
+    starts = [0]
+    for i in range(1, nseg):
+        if i % step == 0:
+            kind = int(rng.integers(3))
+            nxt = (starts[-1] // 256 + 1) * 256
+            starts.append((starts[-1], nxt, nxt + 1)[kind])
+        else:
+            starts.append(starts[-1] + int(rng.integers(1, 300)))
+    n = starts[-1] + int(rng.integers(1, 2000))
+    segs = [(st, bool(rng.random() < 0.5)) for st in starts]
+    got, ref = _run_both(gpu, n, 2, segs, range(1, 3), seed=nseg)
+    assert H.assert_parity(got, ref, "nseg=%d" % nseg), "nseg=%d: not bitwise equal" % nseg
+
+
 def test_unsorted_table_stays_in_bounds(gpu):
     """An unsorted device table (which the library cannot check) gives
     unspecified decay flags but reads nothing outside the table: the call
