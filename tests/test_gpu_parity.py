@@ -273,6 +273,47 @@ def test_segment_search_probe_edges(gpu, nseg):
     assert H.assert_parity(got, ref, "nseg=%d" % nseg), "nseg=%d: not bitwise equal" % nseg
 
 
+def test_table_rewritten_in_place_between_steps(gpu):
+    """The step reads the segment table through the scalar cache; a table
+    the caller overwrites in place on the same stream between two steps
+    (other starts and flags, more than 64 entries so that the scalar search
+    runs) must be seen whole by the next step: GPU and oracle, table A for
+    step 1 and table B for step 2, bit for bit."""
+    torch = gpu
+    rng = np.random.default_rng(77)
+    n, k, nseg = 150_001, 3, 300
+    def table(seed):
+        r = np.random.default_rng(seed)
+        starts = np.concatenate([[0], np.sort(r.choice(np.arange(1, n), nseg - 1, replace=False))])
+        return [(int(st), bool(r.random() < 0.5)) for st in starts]
+    ta, tb = table(1), table(2)
+    w = synth.host_normal_f32(n, synth.stream_key(77, 1, 0, 0), 0, n, 0.02)
+    ref = [w.copy(), np.zeros(n, F32), np.zeros(n, F32), np.zeros(n, np.uint16)]
+    dw, dm, dv = _dev(torch, w), _dev(torch, ref[1]), _dev(torch, ref[2])
+    dp = torch.zeros(n, dtype=torch.int16, device="cuda")
+    dtab = H.segment_tensor(ta, "cuda")
+    st = zs.seg_table(dtab)
+    hpo, hpz = oracle.hparams(), zs.hparams()
+    s = torch.cuda.current_stream()
+    for t, segs in ((1, ta), (2, tb)):
+        if t == 2:
+            dtab.copy_(H.segment_tensor(tb, "cuda"))  # same buffer, same stream
+        gs = [synth.host_normal_bf16(n, synth.stream_key(77, 2, j, t), 0, n, 0.01)
+              for j in range(k)]
+        zs.zs_shard_step(dw, dm, dv, dp, [_dev(torch, g) for g in gs], k, n, st, hpz, t, s)
+        assert oracle.shard_step(*ref, gs, segs, hpo, t) == 0
+    torch.cuda.synchronize()
+    got = [dw.cpu().numpy(), dm.cpu().numpy(), dv.cpu().numpy(), dp.cpu().numpy().view(np.uint16)]
+    assert H.assert_parity(got, ref, "table A then B"), "not bitwise equal"
+    # a step 2 that still saw table A would differ: the test can tell them apart
+    stale = [w.copy(), np.zeros(n, F32), np.zeros(n, F32), np.zeros(n, np.uint16)]
+    for t in (1, 2):
+        gs = [synth.host_normal_bf16(n, synth.stream_key(77, 2, j, t), 0, n, 0.01)
+              for j in range(k)]
+        assert oracle.shard_step(*stale, gs, ta, hpo, t) == 0
+    assert not np.array_equal(stale[0].view(np.uint32), ref[0].view(np.uint32))
+
+
 def test_unsorted_table_stays_in_bounds(gpu):
     """An unsorted device table (which the library cannot check) gives
     unspecified decay flags but reads nothing outside the table: the call
