@@ -7,7 +7,8 @@ or as plain integer device addresses.  There is no CPU fallback: if
 
 Entry points keep the C names: :func:`zs_init`, :func:`zs_shard_step`,
 :func:`zs_shard_step_cfg`, :func:`zs_shard_step_q8ag`, :func:`zs_shard_step_q8grad`,
-:func:`zs_shard_step_bf16mv`, :func:`zs_fini`, :func:`zs_status_string`,
+:func:`zs_shard_step_bf16mv`, :func:`zs_shard_step_packed`, :func:`zs_pack_state`,
+:func:`zs_unpack_state`, :func:`zs_fini`, :func:`zs_status_string`,
 :func:`zs_last_device_error`, :func:`zs_algorithmic_bytes`,
 :func:`zs_launch_geometry`, :func:`zs_launch_plan`.
 """
@@ -33,13 +34,19 @@ ZS_ERR_TOO_MANY_SEGMENTS = 4
 ZS_ERR_DEVICE = 5
 ZS_ERR_ALIASING = 6
 
-ZS_VARIANT = {"base": 0, "q8ag": 1, "q8grad": 2, "bf16mv": 4}
+ZS_VARIANT = {"base": 0, "q8ag": 1, "q8grad": 2, "bf16mv": 4, "packed": 16}
 
 # Symbols declared in include/zs.h.
 EXPORTS = ("zs_init", "zs_shard_step", "zs_shard_step_cfg", "zs_shard_step_q8ag",
-           "zs_shard_step_q8grad", "zs_shard_step_bf16mv", "zs_fini", "zs_status_string",
+           "zs_shard_step_q8grad", "zs_shard_step_bf16mv", "zs_shard_step_packed",
+           "zs_pack_state", "zs_unpack_state", "zs_fini", "zs_status_string",
            "zs_last_device_error", "zs_algorithmic_bytes", "zs_launch_geometry",
            "zs_launch_plan")
+
+
+def packed_floats(n: int) -> int:
+    """Floats of the packed optimizer state for n elements (ZS_PACKED_FLOATS)."""
+    return 768 * ((int(n) + 255) // 256)
 
 
 class ZsHparams(ctypes.Structure):
@@ -104,6 +111,13 @@ def load_library():
     lib.zs_shard_step_q8grad.restype = ctypes.c_int
     lib.zs_shard_step_bf16mv.argtypes = step_args
     lib.zs_shard_step_bf16mv.restype = ctypes.c_int
+    lib.zs_shard_step_packed.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int64, P, P,
+                                         ctypes.c_int64, P]
+    lib.zs_shard_step_packed.restype = ctypes.c_int
+    lib.zs_pack_state.argtypes = [P, P, P, P, ctypes.c_int64, P]
+    lib.zs_pack_state.restype = ctypes.c_int
+    lib.zs_unpack_state.argtypes = [P, P, P, P, ctypes.c_int64, P]
+    lib.zs_unpack_state.restype = ctypes.c_int
     lib.zs_fini.argtypes = []
     lib.zs_fini.restype = ctypes.c_int
     lib.zs_status_string.argtypes = [ctypes.c_int]
@@ -360,6 +374,49 @@ def zs_shard_step_bf16mv(master, m_bf16, v_bf16, param_bf16, grads, k, n, seg_ta
     return rc
 
 
+def zs_shard_step_packed(state, param_bf16, grads, k, n, seg_table_, hparams_, step,
+                         stream=None, check=True) -> int:
+    """zs_shard_step on the packed optimizer state (fp32 [packed_floats(n)]:
+    per 256-element block its master values, then m, then v)."""
+    k = _check_k(k, grads, "grads")
+    nn = max(int(n), 0)
+    gp = _ptr_array(grads, 2 * nn, "grads")
+    st = seg_table_ if isinstance(seg_table_, ZsSegTable) else seg_table(seg_table_)
+    rc = load_library().zs_shard_step_packed(
+        ctypes.c_void_p(_dev(state, 4 * packed_floats(nn), "state")),
+        ctypes.c_void_p(_dev(param_bf16, 2 * nn, "param_bf16")), ctypes.cast(gp, ctypes.c_void_p),
+        int(k), int(n), ctypes.byref(st), ctypes.byref(hparams_), int(step),
+        ctypes.c_void_p(_stream_handle(stream)))
+    if check and rc != ZS_OK:
+        raise ZsError(rc, "zs_shard_step_packed")
+    return rc
+
+
+def zs_pack_state(master, m, v, state, n, stream=None, check=True) -> int:
+    """Separate fp32 master, m, v [n] -> packed state [packed_floats(n)] (padding +0)."""
+    nn = max(int(n), 0)
+    rc = load_library().zs_pack_state(
+        ctypes.c_void_p(_dev(master, 4 * nn, "master")), ctypes.c_void_p(_dev(m, 4 * nn, "m")),
+        ctypes.c_void_p(_dev(v, 4 * nn, "v")),
+        ctypes.c_void_p(_dev(state, 4 * packed_floats(nn), "state")), int(n),
+        ctypes.c_void_p(_stream_handle(stream)))
+    if check and rc != ZS_OK:
+        raise ZsError(rc, "zs_pack_state")
+    return rc
+
+
+def zs_unpack_state(state, master, m, v, n, stream=None, check=True) -> int:
+    """Packed state [packed_floats(n)] -> separate fp32 master, m, v [n]."""
+    nn = max(int(n), 0)
+    rc = load_library().zs_unpack_state(
+        ctypes.c_void_p(_dev(state, 4 * packed_floats(nn), "state")),
+        ctypes.c_void_p(_dev(master, 4 * nn, "master")), ctypes.c_void_p(_dev(m, 4 * nn, "m")),
+        ctypes.c_void_p(_dev(v, 4 * nn, "v")), int(n), ctypes.c_void_p(_stream_handle(stream)))
+    if check and rc != ZS_OK:
+        raise ZsError(rc, "zs_unpack_state")
+    return rc
+
+
 class ShardStep:
     """One rank's step with its buffers fixed: the arguments are checked and
     marshalled once, and each call passes only the step t and the stream to
@@ -368,7 +425,8 @@ class ShardStep:
     zs_shard_step_cfg when ``cfg`` is given as a dict of ZsLaunchCfg fields),
     "q8ag" (needs ``param_q8`` and ``param_q8_scale``), "q8grad" (``grads``
     are the int8 partials, ``qscales`` their block scales) or "bf16mv" (m and
-    v are bf16).  The tensors are referenced for the object's lifetime."""
+    v are bf16) or "packed" (``master`` is the packed state, m and v are None).
+    The tensors are referenced for the object's lifetime."""
 
     def __init__(self, master, m, v, param_bf16, grads, n, seg_table_, hparams_,
                  variant="base", param_q8=None, param_q8_scale=None, qscales=None, cfg=None):
@@ -390,6 +448,17 @@ class ShardStep:
             head = [pm, pmm, pv, pp, ctypes.cast(qp, ctypes.c_void_p),
                     ctypes.cast(sp, ctypes.c_void_p)]
             fn = lib.zs_shard_step_q8grad
+        elif variant == "packed":
+            if m is not None or v is not None:
+                raise ValueError("the packed step takes its m and v inside the state")
+            gp = _ptr_array(grads, 2 * nn, "grads")
+            st = seg_table_ if isinstance(seg_table_, ZsSegTable) else seg_table(seg_table_)
+            hp = hparams_
+            self._c = (gp,)
+            head = [ctypes.c_void_p(_dev(master, 4 * packed_floats(nn), "state")),
+                    ctypes.c_void_p(_dev(param_bf16, 2 * nn, "param_bf16")),
+                    ctypes.cast(gp, ctypes.c_void_p)]
+            fn = lib.zs_shard_step_packed
         else:
             mv = 2 if variant == "bf16mv" else 4
             pm, pmm, pv, pp, pg, _, st, hp, gp = _marshal(master, m, v, param_bf16, grads, k, n,
@@ -428,7 +497,7 @@ class ShardStep:
 def algorithmic_bytes(variant: str, k: int, n: int) -> int:
     """HBM bytes one call moves by the algorithm, per entry point."""
     nb = -(-n // ZS_Q8_BLOCK)
-    if variant == "base":
+    if variant in ("base", "packed"):
         return (26 + 2 * k) * n
     if variant == "q8ag":
         return (26 + 2 * k) * n + n + 4 * nb

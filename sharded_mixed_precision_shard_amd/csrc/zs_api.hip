@@ -94,7 +94,8 @@ void launch_geometry(int variant, int64_t n, int chunk_tiles, int64_t *chunk_out
 int resolve_launch(int k, int64_t n, int variant, const zs_launch_cfg *cfg,
                    zs_launch_info *out, int *kernel_variant = nullptr) {
     if (k < 1 || k > ZS_MAX_K || n < 0 || n > INT64_MAX / 8) return ZS_ERR_INVALID_ARGUMENT;
-    if (variant != 0 && variant != kOutQ8 && variant != kGradQ8 && variant != kMvBf16)
+    if (variant != 0 && variant != kOutQ8 && variant != kGradQ8 && variant != kMvBf16 &&
+        variant != kPacked)
         return ZS_ERR_INVALID_ARGUMENT;
     // Streaming (non-temporal) loads and stores by default: nothing is
     // reused, and on MI355X they measured 5-10 % faster than cached access.
@@ -177,7 +178,8 @@ int validate_and_launch(const Request &r) {
     if (r.st->count < 1) return ZS_ERR_INVALID_ARGUMENT;
     if (r.st->count > ZS_MAX_SEGMENTS) return ZS_ERR_TOO_MANY_SEGMENTS;
     if (r.n == 0) return ZS_OK;
-    if (r.n > INT64_MAX / 8) return ZS_ERR_INVALID_ARGUMENT;
+    if (r.n > ((r.variant & kPacked) ? INT64_MAX / 16 : INT64_MAX / 8))
+        return ZS_ERR_INVALID_ARGUMENT;
     if (!r.st->segs) return ZS_ERR_INVALID_ARGUMENT;
     if ((uintptr_t)r.st->segs & 7u) return ZS_ERR_MISALIGNED;
 
@@ -186,9 +188,13 @@ int validate_and_launch(const Request &r) {
     const int64_t mv_bytes = (r.variant & kMvBf16) ? 2 * n : 4 * n;
     Span outs[6];
     int nouts = 0;
-    outs[nouts++] = {r.master, 4 * n, 16};
-    outs[nouts++] = {r.m, mv_bytes, 16};
-    outs[nouts++] = {r.v, mv_bytes, 16};
+    if (r.variant & kPacked) {
+        outs[nouts++] = {r.master, 4 * packed_floats(n), 16};  // the packed state
+    } else {
+        outs[nouts++] = {r.master, 4 * n, 16};
+        outs[nouts++] = {r.m, mv_bytes, 16};
+        outs[nouts++] = {r.v, mv_bytes, 16};
+    }
     outs[nouts++] = {r.param, 2 * n, 16};
     if (r.variant & kOutQ8) {
         outs[nouts++] = {r.q8, n, 16};
@@ -279,6 +285,36 @@ int validate_and_launch(const Request &r) {
     void *args[] = {&a};
     e = hipLaunchKernel((const void *)fn, dim3((unsigned)blocks), dim3(kThreads), args, dyn_lds,
                         (hipStream_t)r.stream);
+    if (e != hipSuccess) return device_error(e);
+    return ZS_OK;
+}
+
+// zs_pack_state / zs_unpack_state: validate, then one grid-stride launch.
+int layout_call(int dir, float *master, float *m, float *v, float *state, int64_t n,
+                void *stream) {
+    if (!g_initialized) return ZS_ERR_NOT_INITIALIZED;
+    if (n < 0 || n > INT64_MAX / 16) return ZS_ERR_INVALID_ARGUMENT;
+    if (n == 0) return ZS_OK;
+    const Span spans[4] = {{master, 4 * n, 16}, {m, 4 * n, 16}, {v, 4 * n, 16},
+                           {state, 4 * packed_floats(n), 16}};
+    for (const Span &x : spans)
+        if (!x.p) return ZS_ERR_INVALID_ARGUMENT;
+    for (const Span &x : spans)
+        if ((uintptr_t)x.p & (x.align - 1)) return ZS_ERR_MISALIGNED;
+    for (int x = 0; x < 4; ++x)
+        for (int y = x + 1; y < 4; ++y)
+            if (overlaps(spans[x].p, spans[x].bytes, spans[y].p, spans[y].bytes))
+                return ZS_ERR_ALIASING;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return device_error(e);
+    if (dev < 0 || dev >= kMaxDevices || !g_dev[dev].ready) return ZS_ERR_NOT_INITIALIZED;
+    // enough workgroups to fill the device; each loops over its share
+    const int64_t quads = packed_floats(n) / 3 / 4;
+    const int64_t want = (quads + kThreads - 1) / kThreads;
+    const int64_t fill = (int64_t)g_dev[dev].cus * 16;
+    e = launch_layout(dir, master, m, v, state, n, (int)(want < fill ? want : fill),
+                      (hipStream_t)stream);
     if (e != hipSuccess) return device_error(e);
     return ZS_OK;
 }
@@ -378,6 +414,27 @@ int zs_shard_step_bf16mv(float *master, uint16_t *m_bf16, uint16_t *v_bf16,
     r.grads = grads;
     r.variant = kMvBf16;
     return validate_and_launch(r);
+}
+
+int zs_shard_step_packed(float *state, uint16_t *param_bf16, const uint16_t *const *grads,
+                         int k, int64_t n, const zs_seg_table *seg_table,
+                         const zs_hparams *hparams, int64_t step, void *stream) {
+    Request r = base_request(state, nullptr, nullptr, param_bf16, k, n, seg_table, hparams, step,
+                             stream);
+    r.grads = grads;
+    r.variant = kPacked;
+    return validate_and_launch(r);
+}
+
+int zs_pack_state(const float *master, const float *m, const float *v, float *state, int64_t n,
+                  void *stream) {
+    return layout_call(kLayoutPack, const_cast<float *>(master), const_cast<float *>(m),
+                       const_cast<float *>(v), state, n, stream);
+}
+
+int zs_unpack_state(const float *state, float *master, float *m, float *v, int64_t n,
+                    void *stream) {
+    return layout_call(kLayoutUnpack, master, m, v, const_cast<float *>(state), n, stream);
 }
 
 int zs_fini(void) {

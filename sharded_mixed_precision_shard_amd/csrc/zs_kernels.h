@@ -26,11 +26,22 @@ constexpr int kSub = kWave * kQuad;           // 256: one dense instruction per 
 //   kMvBf16 - the moments m and v are stored as bf16 (12 bytes per parameter
 //             of optimizer state plus weight instead of 16).
 //   kWide   - two sub-windows per wave instead of one (launch-time choice for
-//             the bf16-moment step on the largest shards, see quads_for).
+//             the bf16-moment step on the largest shards, see quads_for);
+//   kPacked - master, m and v live in one fp32 array, packed per kSub-element
+//             block: block b holds the master values of elements kSub*b ..
+//             kSub*b + kSub-1, then their m, then their v (ZS packed layout).
 constexpr int kOutQ8 = 1;
 constexpr int kGradQ8 = 2;
 constexpr int kMvBf16 = 4;
 constexpr int kWide = 8;
+constexpr int kPacked = 16;
+
+// Packed layout: index of element i's master value (its m is kSub further,
+// its v 2*kSub further), and floats the packed state holds for n elements.
+__host__ __device__ constexpr int64_t packed_index(int64_t i) {
+    return (i / kSub) * (3 * kSub) + i % kSub;
+}
+constexpr int64_t packed_floats(int64_t n) { return 3 * kSub * ((n + kSub - 1) / kSub); }
 
 // Sub-windows (quads per lane) a wave handles per tile.  Measured on MI355X
 // with the per-wavefront segment lookup: one quad per lane, i.e. the fewest
@@ -50,8 +61,8 @@ constexpr int tile_for(int variant) { return (kThreads / kWave) * quads_for(vari
 static_assert(tile_for(0) == 1024 && tile_for(kMvBf16 | kWide) == 2048, "tile sizes");
 
 struct StepArgs {
-    float *master;
-    void *m;         // fp32 [n], or bf16 [n] in the bf16-moment variant
+    float *master;   // fp32 [n], or the packed state (kPacked)
+    void *m;         // fp32 [n], or bf16 [n] in the bf16-moment variant; unused with kPacked
     void *v;
     uint16_t *param;
     int8_t *q8;      // quantized parameter copy (variant with an int8 payload)
@@ -75,6 +86,15 @@ static_assert(kQ8Block == kSub, "a quantization block is one sub-window of a wav
 constexpr int64_t kStaticLds = (int64_t)(8 + 1) * kWave * (kThreads / kWave);
 
 typedef void (*kernel_fn)(const StepArgs);
+
+// Conversion between separate master, m, v arrays [n] and the packed state
+// (kPacked layout, packed_floats(n) floats): dir 0 packs (the padding past n
+// is written as +0), dir 1 unpacks (nothing past n is written).  A
+// grid-stride loop over `blocks` workgroups of kThreads.
+constexpr int kLayoutPack = 0;
+constexpr int kLayoutUnpack = 1;
+hipError_t launch_layout(int dir, float *master, float *m, float *v, float *state, int64_t n,
+                         int blocks, hipStream_t stream);
 
 // Most partials the wide (kWide) kernels are built for.
 constexpr int kWideMaxK = 4;

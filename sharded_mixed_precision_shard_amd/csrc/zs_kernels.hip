@@ -425,11 +425,18 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
 #pragma unroll
             for (int qd = 0; qd < kQuads; ++qd) {
                 const int64_t qi = e[qd] / kQuad;
-                wv[qd] = load<NT>(pw + qi);
-                if constexpr (V & kMvBf16) {
+                if constexpr (V & kPacked) {
+                    // one 3 KB run per wave: master, m, v of the sub-window
+                    const int64_t qs = packed_index(e[qd]) / kQuad;
+                    wv[qd] = load<NT>(pw + qs);
+                    mv[qd] = load<NT>(pw + qs + kWave);
+                    vv[qd] = load<NT>(pw + qs + 2 * kWave);
+                } else if constexpr (V & kMvBf16) {
+                    wv[qd] = load<NT>(pw + qi);
                     mv[qd] = bf16x4_to_f32x4(load<NT>(reinterpret_cast<const u32x2 *>(a.m) + qi));
                     vv[qd] = bf16x4_to_f32x4(load<NT>(reinterpret_cast<const u32x2 *>(a.v) + qi));
                 } else {
+                    wv[qd] = load<NT>(pw + qi);
                     mv[qd] = load<NT>(reinterpret_cast<const f32x4 *>(a.m) + qi);
                     vv[qd] = load<NT>(reinterpret_cast<const f32x4 *>(a.v) + qi);
                 }
@@ -443,11 +450,17 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
                 u32x2 pq;
                 quad_update<K, V, NT, (U & 1) != 0, (U & 2) != 0>(
                     wv[qd], mv[qd], vv[qd], gq[qd], (mask >> (kQuad * qd)) & 0xfu, a, pq);
-                store<NT>(pw + qi, wv[qd]);
-                if constexpr (V & kMvBf16) {
+                if constexpr (V & kPacked) {
+                    const int64_t qs = packed_index(e[qd]) / kQuad;
+                    store<NT>(pw + qs, wv[qd]);
+                    store<NT>(pw + qs + kWave, mv[qd]);
+                    store<NT>(pw + qs + 2 * kWave, vv[qd]);
+                } else if constexpr (V & kMvBf16) {
+                    store<NT>(pw + qi, wv[qd]);
                     store<NT>(reinterpret_cast<u32x2 *>(a.m) + qi, f32x4_to_bf16x4(mv[qd]));
                     store<NT>(reinterpret_cast<u32x2 *>(a.v) + qi, f32x4_to_bf16x4(vv[qd]));
                 } else {
+                    store<NT>(pw + qi, wv[qd]);
                     store<NT>(reinterpret_cast<f32x4 *>(a.m) + qi, mv[qd]);
                     store<NT>(reinterpret_cast<f32x4 *>(a.v) + qi, vv[qd]);
                 }
@@ -472,20 +485,33 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
                 if (i >= a.n) continue;
                 valid |= 1u << q;
                 const float g = scalar_grad<K, V>(a, i);
-                float wv = a.master[i], mvv, vvv;
-                if constexpr (V & kMvBf16) {
+                float wv, mvv, vvv;
+                if constexpr (V & kPacked) {
+                    const int64_t ps = packed_index(i);
+                    wv = a.master[ps];
+                    mvv = a.master[ps + kSub];
+                    vvv = a.master[ps + 2 * kSub];
+                } else if constexpr (V & kMvBf16) {
+                    wv = a.master[i];
                     mvv = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(a.m)[i] << 16);
                     vvv = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(a.v)[i] << 16);
                 } else {
+                    wv = a.master[i];
                     mvv = reinterpret_cast<const float *>(a.m)[i];
                     vvv = reinterpret_cast<const float *>(a.v)[i];
                 }
                 adamw<(U & 1) != 0, (U & 2) != 0>(wv, mvv, vvv, g, (mask >> q) & 1u, a);
-                a.master[i] = wv;
-                if constexpr (V & kMvBf16) {
+                if constexpr (V & kPacked) {
+                    const int64_t ps = packed_index(i);
+                    a.master[ps] = wv;
+                    a.master[ps + kSub] = mvv;
+                    a.master[ps + 2 * kSub] = vvv;
+                } else if constexpr (V & kMvBf16) {
+                    a.master[i] = wv;
                     reinterpret_cast<uint16_t *>(a.m)[i] = (uint16_t)to_bf16(mvv);
                     reinterpret_cast<uint16_t *>(a.v)[i] = (uint16_t)to_bf16(vvv);
                 } else {
+                    a.master[i] = wv;
                     reinterpret_cast<float *>(a.m)[i] = mvv;
                     reinterpret_cast<float *>(a.v)[i] = vvv;
                 }
@@ -513,7 +539,53 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
 
 static_assert(sizeof(WaveSlot) * (kThreads / kWave) == kStaticLds, "LDS per workgroup");
 
+// Quad q of the element space (elements 4q .. 4q+3, the last block's padding
+// included) between the separate arrays and its three quads in the packed
+// state; a quad that reaches past n goes element by element.
+__global__ __launch_bounds__(kThreads) void layout_kernel(int dir, float *master, float *m,
+                                                          float *v, float *state, int64_t n) {
+    const int64_t nq = packed_floats(n) / 3 / kQuad;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    f32x4 *const st4 = reinterpret_cast<f32x4 *>(state);
+    for (int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x; q < nq; q += stride) {
+        const int64_t i = q * kQuad;
+        const int64_t s = packed_index(i) / kQuad;
+        if (i + kQuad <= n) {
+            if (dir == kLayoutPack) {
+                st4[s] = reinterpret_cast<const f32x4 *>(master)[q];
+                st4[s + kWave] = reinterpret_cast<const f32x4 *>(m)[q];
+                st4[s + 2 * kWave] = reinterpret_cast<const f32x4 *>(v)[q];
+            } else {
+                reinterpret_cast<f32x4 *>(master)[q] = st4[s];
+                reinterpret_cast<f32x4 *>(m)[q] = st4[s + kWave];
+                reinterpret_cast<f32x4 *>(v)[q] = st4[s + 2 * kWave];
+            }
+            continue;
+        }
+        for (int j = 0; j < kQuad; ++j) {
+            const int64_t e = i + j;
+            const int64_t ps = packed_index(e);
+            if (dir == kLayoutPack) {
+                state[ps] = e < n ? master[e] : 0.0f;
+                state[ps + kSub] = e < n ? m[e] : 0.0f;
+                state[ps + 2 * kSub] = e < n ? v[e] : 0.0f;
+            } else if (e < n) {
+                master[e] = state[ps];
+                m[e] = state[ps + kSub];
+                v[e] = state[ps + 2 * kSub];
+            }
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_layout(int dir, float *master, float *m, float *v, float *state, int64_t n,
+                         int blocks, hipStream_t stream) {
+    hipLaunchKernelGGL(layout_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, dir,
+                       master, m, v, state, n);
+    return hipGetLastError();
+}
 
 template <int K, int V>
 kernel_fn pick_unit(int unit) {
@@ -531,6 +603,7 @@ kernel_fn pick_variant(int variant, int nt, int unit) {
         case kOutQ8: return pick_unit<K, kOutQ8>(unit);
         case kGradQ8: return pick_unit<K, kGradQ8>(unit);
         case kMvBf16: return pick_unit<K, kMvBf16>(unit);
+        case kPacked: return nt ? pick_unit<K, kPacked>(unit) : nullptr;
         case kMvBf16 | kWide:
             if constexpr (K <= kWideMaxK) return pick_unit<K, kMvBf16 | kWide>(unit);
             return nullptr;

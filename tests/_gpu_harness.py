@@ -22,13 +22,35 @@ def torch():
     return _t
 
 
-VARIANTS = ("base", "q8ag", "q8grad", "bf16mv")
+VARIANTS = ("base", "q8ag", "q8grad", "bf16mv", "packed")
+
+
+def pack_host(w, m, v):
+    """Packed optimizer state on the host, by reshaping: block b holds the
+    master values, then m, then v of elements 256b .. 256b + 255; the slots
+    past n are +0."""
+    n = w.size
+    nb = -(-n // 256)
+    out = np.zeros((nb, 3, 256), np.float32)
+    for j, x in enumerate((w, m, v)):
+        pad = np.zeros(nb * 256, np.float32)
+        pad[:n] = x
+        out[:, j, :] = pad.reshape(nb, 256)
+    return out.reshape(-1)
+
+
+def unpack_host(state, n):
+    """(master, m, v) [n] from a packed state (the inverse of pack_host)."""
+    blk = np.asarray(state).reshape(-1, 3, 256)
+    return tuple(blk[:, j, :].reshape(-1)[:n].copy() for j in range(3))
 
 
 class DeviceShard:
     """Device buffers of one rank's shard for a synth Workload, for one of the
     entry points: base (zs_shard_step), q8ag (also the int8 parameter copy),
-    q8grad (int8 partials) or bf16mv (bf16 moments)."""
+    q8grad (int8 partials), bf16mv (bf16 moments) or packed (master, m and v
+    in one array, per 256-element block; packed and read back here with torch
+    views, not with the library's conversion calls)."""
 
     def __init__(self, w: synth.Workload, variant="base", device="cuda:0"):
         t = torch()
@@ -38,10 +60,22 @@ class DeviceShard:
         nb = -(-n // zs.ZS_Q8_BLOCK)
         dev = t.device(device)
         mv_dtype = t.int16 if variant == "bf16mv" else t.float32
-        self.master = t.empty(n, dtype=t.float32, device=dev)
-        self.m = t.zeros(n, dtype=mv_dtype, device=dev)
-        self.v = t.zeros(n, dtype=mv_dtype, device=dev)
         self.param = t.zeros(n, dtype=t.int16, device=dev)
+        if variant == "packed":
+            self.state = t.zeros(zs.packed_floats(n), dtype=t.float32, device=dev)
+            master = t.empty(n, dtype=t.float32, device=dev)
+            synth.dev_master(w, master)
+            blocks = self.state.view(-1, 3, 256)
+            full = n // 256
+            blocks[:full, 0, :] = master[:full * 256].view(-1, 256)
+            if n % 256:
+                blocks[full, 0, :n % 256] = master[full * 256:]
+            del master
+            self.master = self.m = self.v = None
+        else:
+            self.master = t.empty(n, dtype=t.float32, device=dev)
+            self.m = t.zeros(n, dtype=mv_dtype, device=dev)
+            self.v = t.zeros(n, dtype=mv_dtype, device=dev)
         self.grads = self.qgrads = self.qscales = self.q8 = self.q8s = None
         if variant == "q8grad":
             self.qgrads = [t.empty(n, dtype=t.int8, device=dev) for _ in range(w.k)]
@@ -52,7 +86,8 @@ class DeviceShard:
             self.q8 = t.zeros(n, dtype=t.int8, device=dev)
             self.q8s = t.zeros(nb, dtype=t.float32, device=dev)
         self.table = segment_tensor(w.shard.segments, dev)
-        synth.dev_master(w, self.master)
+        if variant != "packed":
+            synth.dev_master(w, self.master)
 
     def fill_grads(self, step):
         if self.variant == "q8grad":
@@ -72,6 +107,9 @@ class DeviceShard:
         elif self.variant == "q8grad":
             zs.zs_shard_step_q8grad(self.master, self.m, self.v, self.param, self.qgrads,
                                     self.qscales, w.k, w.n, st, hp, t_step, s)
+        elif self.variant == "packed":
+            zs.zs_shard_step_packed(self.state, self.param, self.grads, w.k, w.n, st, hp, t_step,
+                                    s)
         elif self.variant == "bf16mv":
             zs.zs_shard_step_bf16mv(self.master, self.m, self.v, self.param, self.grads, w.k,
                                     w.n, st, hp, t_step, s)
@@ -84,6 +122,13 @@ class DeviceShard:
 
     def window(self, lo, hi):
         """(master, m, v, param[, q8, q8 scales of the covered blocks]) on [lo, hi)."""
+        if self.variant == "packed":
+            b0, b1 = lo // 256, (hi - 1) // 256 + 1
+            blk = self.state.view(-1, 3, 256)[b0:b1].cpu().numpy()
+            a, z = lo - b0 * 256, hi - b0 * 256
+            return (blk[:, 0, :].reshape(-1)[a:z].copy(), blk[:, 1, :].reshape(-1)[a:z].copy(),
+                    blk[:, 2, :].reshape(-1)[a:z].copy(),
+                    self.param[lo:hi].cpu().numpy().view(np.uint16))
         mv = (lambda x: x[lo:hi].cpu().numpy().view(np.uint16)) if self.variant == "bf16mv" \
             else (lambda x: x[lo:hi].cpu().numpy())
         out = (self.master[lo:hi].cpu().numpy(), mv(self.m), mv(self.v),
@@ -94,8 +139,8 @@ class DeviceShard:
         return out
 
     def free(self):
-        for name in ("master", "m", "v", "param", "grads", "qgrads", "qscales", "q8", "q8s",
-                     "table"):
+        for name in ("master", "m", "v", "state", "param", "grads", "qgrads", "qscales", "q8",
+                     "q8s", "table"):
             setattr(self, name, None)
         torch().cuda.empty_cache()
 

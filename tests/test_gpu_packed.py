@@ -1,0 +1,237 @@
+"""The packed-state step (zs_shard_step_packed) and the layout conversions
+(zs_pack_state, zs_unpack_state) through the C ABI.  The packed layout is
+built and read back here with numpy reshapes of (blocks, 3, 256), written
+independently of the library's conversion kernels; the step must equal the
+oracle, and zs_shard_step on the same inputs, bit for bit."""
+import numpy as np
+import pytest
+
+import oracle
+import sharded_mixed_precision_shard_amd as zs
+import synth
+from tests import _gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+F32 = np.float32
+SIZES = [1, 7, 255, 256, 257, 1023, 1024, 1025, 4097, 10007, 65539]
+
+
+@pytest.fixture(scope="module")
+def gpu():
+    import torch
+    assert torch.cuda.is_available()
+    torch.cuda.set_device(0)
+    assert zs.zs_init(0) == zs.ZS_OK
+    yield torch
+    torch.cuda.synchronize()
+
+
+pack = H.pack_host
+unpack = H.unpack_host
+
+
+def _dev(torch, a):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16).copy()).cuda()
+    return torch.from_numpy(a.copy()).cuda()
+
+
+def _segments(rng, n):
+    segs, a = [], 0
+    while a < n:
+        segs.append((a, bool(rng.random() < 0.5)))
+        a += int(rng.integers(1, 8)) if rng.random() < 0.4 else int(rng.integers(8, 3000))
+    return segs
+
+
+def _partials(rng, k, n, sigma=1e-2):
+    return [(rng.normal(0, sigma, n).astype(F32).view(np.uint32) >> 16).astype(np.uint16)
+            for _ in range(k)]
+
+
+def test_packed_floats_matches_the_header():
+    for n in (0, 1, 255, 256, 257, 10 ** 9 + 1):
+        assert zs.packed_floats(n) == 768 * (-(-n // 256))
+
+
+@pytest.mark.parametrize("n", SIZES)
+def test_pack_and_unpack(gpu, n):
+    """zs_pack_state writes the host packing (padding +0); zs_unpack_state
+    restores the arrays bit for bit and writes nothing past n."""
+    torch = gpu
+    rng = np.random.default_rng(n)
+    w, m, v = (rng.normal(0, 1, n).astype(F32) for _ in range(3))
+    w[::7] = -0.0
+    dstate = torch.full((zs.packed_floats(n),), 7.0, dtype=torch.float32, device="cuda")
+    zs.zs_pack_state(_dev(torch, w), _dev(torch, m), _dev(torch, v), dstate, n)
+    torch.cuda.synchronize()
+    got = dstate.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), pack(w, m, v).view(np.uint32))
+    guard = 5
+    outs = [torch.full((n + guard,), 3.0, dtype=torch.float32, device="cuda") for _ in range(3)]
+    zs.zs_unpack_state(dstate, *outs, n)
+    torch.cuda.synchronize()
+    for o, x in zip(outs, (w, m, v)):
+        h = o.cpu().numpy()
+        assert np.array_equal(h[:n].view(np.uint32), x.view(np.uint32))
+        assert np.all(h[n:] == 3.0)
+
+
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("k", [1, 2, 5, 16])
+def test_packed_step_matches_oracle_and_base(gpu, n, k):
+    torch = gpu
+    rng = np.random.default_rng(300 + n * 3 + k)
+    segs = _segments(rng, n)
+    w0 = rng.normal(0, 0.02, n).astype(F32)
+    ref = [w0.copy(), np.zeros(n, F32), np.zeros(n, F32), np.zeros(n, np.uint16)]
+    dstate = _dev(torch, pack(w0, ref[1], ref[2]))
+    dp = torch.zeros(n, dtype=torch.int16, device="cuda")
+    bw, bm, bv = _dev(torch, w0), _dev(torch, ref[1]), _dev(torch, ref[2])
+    bp = torch.zeros(n, dtype=torch.int16, device="cuda")
+    table = H.segment_tensor(segs, "cuda")
+    hpo, hpz = oracle.hparams(), zs.hparams()
+    s = torch.cuda.current_stream()
+    for t in range(1, 4):
+        gs = _partials(rng, k, n)
+        dgs = [_dev(torch, g) for g in gs]
+        zs.zs_shard_step_packed(dstate, dp, dgs, k, n, zs.seg_table(table), hpz, t, s)
+        zs.zs_shard_step(bw, bm, bv, bp, dgs, k, n, zs.seg_table(table), hpz, t, s)
+        assert oracle.shard_step(*ref, gs, segs, hpo, t) == 0
+    torch.cuda.synchronize()
+    state = dstate.cpu().numpy()
+    got = list(unpack(state, n)) + [dp.cpu().numpy().view(np.uint16)]
+    assert H.assert_parity(got, ref, "packed n=%d k=%d" % (n, k)), "not bitwise"
+    base = [bw.cpu().numpy(), bm.cpu().numpy(), bv.cpu().numpy(),
+            bp.cpu().numpy().view(np.uint16)]
+    for a, b in zip(got, base):
+        assert np.array_equal(np.ascontiguousarray(a).view(np.uint8), b.view(np.uint8))
+    # the step leaves the padding of the last block as it found it
+    pad = state.reshape(-1, 3, 256)[-1, :, n % 256:] if n % 256 else np.zeros(0, F32)
+    assert np.all(pad == 0.0)
+
+
+def test_packed_step_on_a_large_grid_equals_the_base_step(gpu):
+    """A shard above 2^26 elements (XCD chunk order, occupancy cap), many
+    segments and a ragged tail: packed and base steps agree bit for bit, and
+    a few windows agree with the oracle."""
+    torch = gpu
+    n, k = (1 << 26) + 12345, 2
+    rng = np.random.default_rng(26)
+    starts = np.concatenate([[0], np.sort(rng.choice(np.arange(1, n), 1969, replace=False))])
+    segs = [(int(a), bool(rng.random() < 0.5)) for a in starts]
+    assert zs.zs_launch_plan(k, n, "packed")["groups_per_cu"] == 5
+    w0 = synth.host_normal_f32(n, synth.stream_key(26, 1, 0, 0), 0, n, 0.02)
+    zeros = np.zeros(n, F32)
+    dstate = torch.zeros(zs.packed_floats(n), dtype=torch.float32, device="cuda")
+    zs.zs_pack_state(_dev(torch, w0), _dev(torch, zeros), _dev(torch, zeros), dstate, n)
+    bw, bm, bv = _dev(torch, w0), _dev(torch, zeros), _dev(torch, zeros)
+    dp = torch.zeros(n, dtype=torch.int16, device="cuda")
+    bp = torch.zeros(n, dtype=torch.int16, device="cuda")
+    table = H.segment_tensor(segs, "cuda")
+    hpz = zs.hparams()
+    s = torch.cuda.current_stream()
+    gs_all = []
+    for t in (1, 2):
+        gs = [synth.host_normal_bf16(n, synth.stream_key(26, 2, j, t), 0, n, 0.01)
+              for j in range(k)]
+        gs_all.append(gs)
+        dgs = [_dev(torch, g) for g in gs]
+        zs.zs_shard_step_packed(dstate, dp, dgs, k, n, zs.seg_table(table), hpz, t, s)
+        zs.zs_shard_step(bw, bm, bv, bp, dgs, k, n, zs.seg_table(table), hpz, t, s)
+    outs = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(3)]
+    zs.zs_unpack_state(dstate, *outs, n)
+    torch.cuda.synchronize()
+    for o, b in zip(outs + [dp], (bw, bm, bv, bp)):
+        assert torch.equal(o.view(torch.int32) if o.dtype == torch.float32 else o,
+                           b.view(torch.int32) if b.dtype == torch.float32 else b)
+    hpo = oracle.hparams()
+    for lo, hi in ((0, 4096), (n // 2 - 777, n // 2 + 1500), (n - 3000, n)):
+        ref = [w0[lo:hi].copy(), np.zeros(hi - lo, F32), np.zeros(hi - lo, F32),
+               np.zeros(hi - lo, np.uint16)]
+        wsegs = synth.clip_segments(segs, lo, hi)
+        for t, gs in zip((1, 2), gs_all):
+            assert oracle.shard_step(*ref, [g[lo:hi] for g in gs], wsegs, hpo, t) == 0
+        got = [outs[0][lo:hi].cpu().numpy(), outs[1][lo:hi].cpu().numpy(),
+               outs[2][lo:hi].cpu().numpy(), dp[lo:hi].cpu().numpy().view(np.uint16)]
+        assert H.assert_parity(got, ref, "window [%d,%d)" % (lo, hi)), "not bitwise"
+
+
+def test_prepared_packed_call_matches_the_plain_call(gpu):
+    torch = gpu
+    n, k = 70_001, 3
+    rng = np.random.default_rng(7)
+    segs = _segments(rng, n)
+    w0 = rng.normal(0, 0.02, n).astype(F32)
+    z = np.zeros(n, F32)
+    a = _dev(torch, pack(w0, z, z))
+    b = _dev(torch, pack(w0, z, z))
+    pa = torch.zeros(n, dtype=torch.int16, device="cuda")
+    pb = torch.zeros(n, dtype=torch.int16, device="cuda")
+    table = H.segment_tensor(segs, "cuda")
+    st, hp = zs.seg_table(table), zs.hparams()
+    gs = [_dev(torch, g) for g in _partials(rng, k, n)]
+    call = zs.ShardStep(a, None, None, pa, gs, n, st, hp, variant="packed")
+    for t in (1, 2, 3):
+        call(t)
+        zs.zs_shard_step_packed(b, pb, gs, k, n, st, hp, t)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32)) and torch.equal(pa, pb)
+
+
+def test_packed_argument_errors(gpu):
+    torch = gpu
+    n, k = 1000, 2
+    state = torch.zeros(zs.packed_floats(n) + 64, dtype=torch.float32, device="cuda")
+    p = torch.zeros(n, dtype=torch.int16, device="cuda")
+    g = [torch.zeros(n, dtype=torch.int16, device="cuda") for _ in range(k)]
+    table = H.segment_tensor([(0, True)], "cuda")
+    st, hp = zs.seg_table(table), zs.hparams()
+    sp, pp = state.data_ptr(), p.data_ptr()
+    gp = [x.data_ptr() for x in g]
+    call = lambda *a: zs.zs_shard_step_packed(*a, check=False)
+    assert call(sp, pp, gp, k, n, st, hp, 1) == zs.ZS_OK
+    assert call(0, pp, gp, k, n, st, hp, 1) == zs.ZS_ERR_INVALID_ARGUMENT
+    assert call(sp + 4, pp, gp, k, n, st, hp, 1) == zs.ZS_ERR_MISALIGNED
+    # the param copy, or a partial, inside the state
+    assert call(sp, sp + 4 * 1024, gp, k, n, st, hp, 1) == zs.ZS_ERR_ALIASING
+    assert call(sp, pp, [gp[0], sp + 4 * 2048], k, n, st, hp, 1) == zs.ZS_ERR_ALIASING
+    assert call(sp, pp, gp, k, 0, st, hp, 1) == zs.ZS_OK
+    assert call(sp, pp, gp, k, n, st, hp, 0) == zs.ZS_ERR_INVALID_ARGUMENT
+    arrs = [torch.zeros(n, dtype=torch.float32, device="cuda") for _ in range(3)]
+    ap = [x.data_ptr() for x in arrs]
+    pk = lambda *a: zs.zs_pack_state(*a, check=False)
+    up = lambda *a: zs.zs_unpack_state(*a, check=False)
+    assert pk(*ap, sp, n) == zs.ZS_OK and up(sp, *ap, n) == zs.ZS_OK
+    assert pk(ap[0], ap[1], ap[2], sp, 0) == zs.ZS_OK
+    assert pk(ap[0], ap[1], 0, sp, n) == zs.ZS_ERR_INVALID_ARGUMENT
+    assert pk(ap[0] + 4, ap[1], ap[2], sp, n) == zs.ZS_ERR_MISALIGNED
+    assert pk(ap[0], ap[0], ap[2], sp, n) == zs.ZS_ERR_ALIASING
+    assert up(sp, ap[0], ap[1], sp + 16, n) == zs.ZS_ERR_ALIASING
+    assert pk(*ap, sp, -1) == zs.ZS_ERR_INVALID_ARGUMENT
+    torch.cuda.synchronize()
+
+
+def test_70b_packed_windows(gpu):
+    """The 70B-shaped shard with packed state, t = 10000..10002: windows at
+    segment boundaries and at random equal the oracle bit for bit."""
+    torch = gpu
+    w = synth.workload("70b")
+    free, _ = torch.cuda.mem_get_info()
+    need = w.n * (12 + 4 + 2 + 2 * w.k) + (1 << 30)
+    if free < need:
+        pytest.skip("needs %.1f GB of free device memory" % (need / 1e9))
+    ts = w.step_ts()
+    ds = H.DeviceShard(w, "packed")
+    for t in ts:
+        ds.fill_grads(t)
+        ds.step(t)
+    torch.cuda.synchronize()
+    wins = H.boundary_windows(w, 1 << 14, max_boundaries=16, n_random=4, seed=5)
+    got = [ds.window(lo, hi) for lo, hi in wins]
+    ds.free()
+    for (lo, hi), g in zip(wins, got):
+        ref = H.oracle_window(w, lo, hi, ts)
+        assert H.assert_parity(g, ref, "70b packed [%d,%d)" % (lo, hi)), "not bitwise"
+    print("70b packed: %d windows bitwise equal" % len(wins), flush=True)

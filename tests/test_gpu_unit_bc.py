@@ -64,6 +64,7 @@ def test_unit_correction_kernels_are_bitwise(gpu, variant, span):
         m0, v0 = _bf16(m0), _bf16(v0)
     ref = [w0.copy(), m0.copy(), v0.copy(), np.zeros(n, np.uint16)]
     dw, dm, dv = _dev(torch, w0), _dev(torch, m0), _dev(torch, v0)
+    dstate = _dev(torch, H.pack_host(w0, m0, v0)) if variant == "packed" else None
     dp = torch.zeros(n, dtype=torch.int16, device="cuda")
     dq = torch.zeros(n, dtype=torch.int8, device="cuda")
     ds = torch.zeros(nb, dtype=torch.float32, device="cuda")
@@ -85,6 +86,8 @@ def test_unit_correction_kernels_are_bitwise(gpu, variant, span):
             zs.zs_shard_step_q8ag(dw, dm, dv, dp, dq, ds, dgs, k, n, st, hpz, t, s)
         elif variant == "bf16mv":
             zs.zs_shard_step_bf16mv(dw, dm, dv, dp, dgs, k, n, st, hpz, t, s)
+        elif variant == "packed":
+            zs.zs_shard_step_packed(dstate, dp, dgs, k, n, st, hpz, t, s)
         else:
             zs.zs_shard_step(dw, dm, dv, dp, dgs, k, n, st, hpz, t, s)
         step = oracle.shard_step_bf16mv if variant == "bf16mv" else oracle.shard_step
@@ -93,6 +96,8 @@ def test_unit_correction_kernels_are_bitwise(gpu, variant, span):
     mv = (lambda x: x.cpu().numpy().view(np.uint16)) if variant == "bf16mv" \
         else (lambda x: x.cpu().numpy())
     got = (dw.cpu().numpy(), mv(dm), mv(dv), dp.cpu().numpy().view(np.uint16))
+    if variant == "packed":
+        got = H.unpack_host(dstate.cpu().numpy(), n) + got[3:]
     want = tuple(ref)
     if variant == "q8ag":
         got += (dq.cpu().numpy(), ds.cpu().numpy())
