@@ -152,6 +152,77 @@ def snapshot(tensors, wins):
     return out
 
 
+def snapshot_packed(state, wins):
+    """The windows' master, m and v read out of a packed state (block b of 256
+    elements: their master values, then m, then v), as snapshot() gives them."""
+    blocks = state.view(-1, 3, 256)
+    out = {"master": [], "m": [], "v": []}
+    for a, b in wins:
+        b0, b1 = a // 256, (b - 1) // 256 + 1
+        blk = blocks[b0:b1].cpu().numpy()
+        lo, hi = a - b0 * 256, b - b0 * 256
+        for j, name in enumerate(("master", "m", "v")):
+            out[name].append(blk[:, j, :].reshape(-1)[lo:hi].copy())
+    return out
+
+
+def packed_leg(torch, w, pstate, master, m, v, param, grads, st, hp, stream, args,
+               bytes_per_step):
+    """zs_shard_step_packed on `pstate` (packed from the default step's state
+    before its warm-up), over the same steps with the same partials: GB/s per
+    launch (HIP events on the launch stream), its twin in its own launch, and
+    whether its final state and parameters equal the default step's bit for
+    bit on the parity windows."""
+    import numpy as np
+    import sharded_mixed_precision_shard_amd as zs
+    n, k = w.n, w.k
+    wins = parity_windows(w, n)
+    want = snapshot({"master": master, "m": m, "v": v, "param": param}, wins)
+    call = zs.ShardStep(pstate, None, None, param, grads, n, st, hp, variant="packed")
+    t = w.t0
+    for _ in range(args.warmup):
+        call(t, stream)
+        t += 1
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for i in range(args.steps):
+        starts[i].record(stream)
+        call(t, stream)
+        ends[i].record(stream)
+        t += 1
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    avg = sum(ms) / len(ms)
+    got = snapshot_packed(pstate, wins)
+    got.update(snapshot({"param": param}, wins))
+    same = all(np.array_equal(x.view(np.uint8), y.view(np.uint8))
+               for name in want for x, y in zip(got[name], want[name]))
+    plan = zs.zs_launch_plan(k, n, "packed")
+    achieved = bytes_per_step / (avg * 1e-3) / 1e9
+    out = {"entry_point": "zs_shard_step_packed", "launch": launch_key(plan),
+           "achieved": round(achieved, 2), "frac": round(achieved / HBM_PEAK_GBPS, 4),
+           "avg_launch_ms": round(avg, 4), "steps": args.steps,
+           "bitwise_equal_to_zs_shard_step": bool(same)}
+    if not args.no_twin:
+        twin = Twin(torch, "packed", dict(master=pstate, param=param, grads=grads), k, n, plan)
+        if twin.ok:
+            r = twin.rate("step", stream)
+            out["twin_step_gbps"] = round(r, 1)
+            out["pct_of_twin"] = round(100.0 * achieved / r, 2)
+    return out
+
+
+def _fill_packed_master(state, master, n):
+    """Write fp32 master [n] into the master slots of a packed state (torch
+    copies into strided views; m, v and the padding keep what they hold)."""
+    blocks = state.view(-1, 3, 256)
+    full = n // 256
+    blocks[:full, 0, :] = master[:full * 256].view(-1, 256)
+    if n % 256:
+        blocks[full, 0, :n % 256] = master[full * 256:]
+
+
 def block_slice(t, a, b):
     return t[a // 256:-(-b // 256)]
 
@@ -390,6 +461,7 @@ def twin_bytes(variant: str, k: int, n: int):
     """(read, written) bytes of the step's streams over n elements."""
     nb = -(-n // 256)
     return {"base": ((12 + 2 * k) * n, 14 * n),
+            "packed": ((12 + 2 * k) * n, 14 * n),
             "q8ag": ((12 + 2 * k) * n, 15 * n + 4 * nb),
             "q8grad": (12 * n + k * (n + 4 * nb), 14 * n),
             "bf16mv": ((8 + 2 * k) * n, 10 * n)}[variant]
@@ -404,7 +476,7 @@ class Twin:
     """The step's traffic without its arithmetic (libzs_ceiling.so), on the
     step's own buffers and in the step's own launch."""
     MODES = {"step": 0, "read": 1, "write": 2}
-    LAYOUT = {"base": 0, "q8ag": 1, "q8grad": 2, "bf16mv": 4}
+    LAYOUT = {"base": 0, "q8ag": 1, "q8grad": 2, "bf16mv": 4, "packed": 8}
 
     def __init__(self, torch, variant, bufs, k, n, plan):
         import ctypes
@@ -418,7 +490,8 @@ class Twin:
             self.chunk % (1024 * self.quads) == 0
         self.plan = plan
         ptr = lambda t: ctypes.c_void_p(t.data_ptr() if t is not None else 0)  # noqa: E731
-        self.head = [ptr(bufs["master"]), ptr(bufs["m"]), ptr(bufs["v"]), ptr(bufs["param"]),
+        self.head = [ptr(bufs["master"]), ptr(bufs.get("m")), ptr(bufs.get("v")),
+                     ptr(bufs["param"]),
                      ptr(bufs.get("q8")), ptr(bufs.get("q8s"))]
         gl = bufs.get("qgrads") if variant == "q8grad" else bufs["grads"]
         self.gp = (ctypes.c_void_p * k)(*[g.data_ptr() for g in gl])
@@ -672,9 +745,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="70b")
     ap.add_argument("--variant", default="base",
-                    choices=("base", "q8ag", "q8grad", "bf16mv", "offload"),
+                    choices=("base", "q8ag", "q8grad", "bf16mv", "packed", "offload"),
                     help="entry point: zs_shard_step (base), zs_shard_step_q8ag, "
-                         "zs_shard_step_q8grad, zs_shard_step_bf16mv, or the host "
+                         "zs_shard_step_q8grad, zs_shard_step_bf16mv, zs_shard_step_packed "
+                         "(master, m, v packed per 256-element block), or the host "
                          "(ZeRO-Offload) step zs_host_shard_step, which runs on the CPU "
                          "and needs no GPU")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -696,6 +770,10 @@ def main():
                     help="measure zs_shard_step_cfg's launch configurations (chunk order x "
                          "occupancy cap) on one set of buffers instead of the timed run")
     ap.add_argument("--rounds", type=int, default=3, help="rounds of --sweep")
+    ap.add_argument("--no-packed", action="store_true",
+                    help="skip the same-run measurement of zs_shard_step_packed (the same "
+                         "step on the state packed per 256-element block) beside the default "
+                         "zs_shard_step")
     args = ap.parse_args()
     if args.steps is None:
         args.steps = 200 if args.config in ("tiny", "gpt2-small") else 10
@@ -757,9 +835,14 @@ def main():
     dev = torch.device("cuda:0")
     nb = -(-n // zs.ZS_Q8_BLOCK)
     mv_dtype = torch.int16 if var == "bf16mv" else torch.float32
-    master = torch.empty(n, dtype=torch.float32, device=dev)
-    m = torch.zeros(n, dtype=mv_dtype, device=dev)
-    v = torch.zeros(n, dtype=mv_dtype, device=dev)
+    state = master = m = v = None
+    if var == "packed":
+        # master, m and v in one array, per 256-element block
+        state = torch.empty(zs.packed_floats(n), dtype=torch.float32, device=dev)
+    else:
+        master = torch.empty(n, dtype=torch.float32, device=dev)
+        m = torch.zeros(n, dtype=mv_dtype, device=dev)
+        v = torch.zeros(n, dtype=mv_dtype, device=dev)
     param = torch.zeros(n, dtype=torch.int16, device=dev)
     grads = qgrads = qscales = q8 = q8s = None
     if var == "q8grad":
@@ -783,13 +866,21 @@ def main():
     twin = None
     ceil = {}
     if not args.no_twin:
-        twin = Twin(torch, var, dict(master=master, m=m, v=v, param=param, q8=q8, q8s=q8s,
-                                     grads=grads, qgrads=qgrads, qscales=qscales), k, n, plan)
+        twin = Twin(torch, var, dict(master=state if var == "packed" else master, m=m, v=v,
+                                     param=param, q8=q8, q8s=q8s, grads=grads, qgrads=qgrads,
+                                     qscales=qscales), k, n, plan)
         if twin.ok:
             ceil["write"] = twin.rate("write", stream)
-    synth.dev_master(w, master)
-    m.zero_()
-    v.zero_()
+    if var == "packed":
+        state.zero_()
+        init = torch.empty(n, dtype=torch.float32, device=dev)
+        synth.dev_master(w, init)
+        _fill_packed_master(state, init, n)
+        del init
+    else:
+        synth.dev_master(w, master)
+        m.zero_()
+        v.zero_()
 
     # the call is checked and marshalled once; each step passes t and the stream
     if var == "q8grad":
@@ -800,6 +891,8 @@ def main():
                             param_q8=q8, param_q8_scale=q8s)
     elif var == "bf16mv":
         call = zs.ShardStep(master, m, v, param, grads, n, st, hp, variant="bf16mv")
+    elif var == "packed":
+        call = zs.ShardStep(state, None, None, param, grads, n, st, hp, variant="packed")
     else:
         call = zs.ShardStep(master, m, v, param, grads, n, st, hp, cfg=cfg)
 
@@ -843,7 +936,8 @@ def main():
     par = None
     if args.cpu_seconds > 0:
         wins = parity_windows(w, n)
-        before = snapshot({"master": master, "m": m, "v": v}, wins)
+        before = snapshot_packed(state, wins) if var == "packed" else \
+            snapshot({"master": master, "m": m, "v": v}, wins)
         if var == "q8grad":
             qg = [[q[a:b].cpu().numpy().copy() for a, b in wins] for q in qgrads]
             qs = [[block_slice(s, a, b).cpu().numpy().copy() for a, b in wins] for s in qscales]
@@ -851,6 +945,18 @@ def main():
         else:
             par = dict(grads=[[g[a:b].cpu().numpy().copy() for a, b in wins] for g in grads])
         par.update(windows=wins, before=before)
+
+    # the same step on the same state packed per 256-element block, timed after
+    # the default step from the state as it stands now (same t, same partials)
+    pstate, packed_skip = None, None
+    if var == "base" and cfg is None and not args.graph and not args.no_packed:
+        torch.cuda.empty_cache()
+        need = 4 * zs.packed_floats(n) + (1 << 30)
+        if torch.cuda.mem_get_info()[0] >= need:
+            pstate = torch.empty(zs.packed_floats(n), dtype=torch.float32, device=dev)
+            zs.zs_pack_state(master, m, v, pstate, n, stream)
+        else:
+            packed_skip = "needs %.1f GB more device memory" % (need / 1e9)
 
     t = w.t0
     for _ in range(args.warmup):
@@ -894,17 +1000,31 @@ def main():
     log("kernel ms per launch: avg %.4f min %.4f max %.4f" % (avg_ms, min(kernel_ms),
                                                               max(kernel_ms)))
     if par is not None:
-        after = snapshot({"master": master, "m": m, "v": v, "param": param, "q8": q8}, wins)
+        if var == "packed":
+            after = snapshot_packed(state, wins)
+            after.update(snapshot({"param": param}, wins))
+        else:
+            after = snapshot({"master": master, "m": m, "v": v, "param": param, "q8": q8}, wins)
         if var == "q8ag":
             after["q8s"] = [block_slice(q8s, a, b).cpu().numpy().copy() for a, b in wins]
         par.update(after=after, ts=list(range(w.t0, t)))
+
+    packed = None
+    if pstate is not None:
+        packed = packed_leg(torch, w, pstate, master, m, v, param, grads, st, hp, stream, args,
+                            bytes_per_step)
+        log("packed state: %.1f GB/s per launch, %s of its twin, bitwise equal to the "
+            "default step: %s" % (packed["achieved"], packed.get("pct_of_twin"),
+                                  packed["bitwise_equal_to_zs_shard_step"]))
+    elif packed_skip:
+        packed = {"skipped": packed_skip}
 
     value = bytes_per_step * args.steps / elapsed / 1e9
     achieved = bytes_per_step / (avg_ms * 1e-3) / 1e9
     traffic_key = args.config if var == "base" else "%s/%s" % (args.config, var)
     traffic = measured_traffic(traffic_key, key)
 
-    del master, m, v, param, grads, qgrads, qscales, q8, q8s, twin
+    del master, m, v, param, grads, qgrads, qscales, q8, q8s, twin, pstate
     torch.cuda.empty_cache()
 
     cpu = None
@@ -948,7 +1068,9 @@ def main():
         "storage": {"base": "f32 master/m/v, bf16 partials and param",
                     "q8ag": "f32 master/m/v, bf16 partials and param, int8 param copy",
                     "q8grad": "f32 master/m/v, int8 partials, bf16 param",
-                    "bf16mv": "f32 master, bf16 m/v, partials and param"}[var],
+                    "bf16mv": "f32 master, bf16 m/v, partials and param",
+                    "packed": "f32 master/m/v packed per 256-element block, bf16 partials and "
+                              "param"}[var],
         "data": "synthetic (seeded SplitMix64 / Irwin-Hall draws; partials of the first "
                 "measured step kept resident across timed steps)",
         "config": {
@@ -990,6 +1112,8 @@ def main():
             "single_thread": round(value / cpu["value"], 1),
             "threaded": round(value / cpu["threaded"]["value"], 1)},
     }
+    if packed is not None:
+        out["packed_state"] = packed
     print(json.dumps(out), flush=True)
 
 

@@ -48,6 +48,7 @@ constexpr int kLayoutBase = 0;    // f32 master/m/v, bf16 partials, bf16 param
 constexpr int kLayoutQ8Out = 1;   // + int8 parameter copy and one f32 scale per block
 constexpr int kLayoutQ8Grad = 2;  // int8 partials with one f32 scale per block each
 constexpr int kLayoutBf16Mv = 4;  // bf16 m and v
+constexpr int kLayoutPacked = 8;  // master, m, v packed per 256-element block in one array
 
 // Modes: 0 = the step's reads and writes, then
 constexpr int kModeRead = 1;   // its reads only
@@ -90,6 +91,7 @@ __global__ __launch_bounds__(kThreads) void twin_kernel(const TwinArgs a) {
     constexpr bool kMv16 = (L & kLayoutBf16Mv) != 0;
     constexpr bool kG8 = (L & kLayoutQ8Grad) != 0;
     constexpr bool kOut8 = (L & kLayoutQ8Out) != 0;
+    constexpr bool kPk = (L & kLayoutPacked) != 0;
     constexpr int64_t kTileQ = (int64_t)kTile * kQ;
     const int lane = (int)(threadIdx.x % kWave);
     const int wave = (int)(threadIdx.x / kWave);
@@ -105,20 +107,32 @@ __global__ __launch_bounds__(kThreads) void twin_kernel(const TwinArgs a) {
         const int64_t wv0 = t0 + (int64_t)wave * kSub * kQ;
         if (wv0 + kSub * kQ > c1) continue;  // whole windows only; the host sizes n to match
         int64_t qi[kQ];  // this lane's quad of each sub-window
+        int64_t iw[kQ], im[kQ], iv[kQ];  // its master, m and v quads
 #pragma unroll
-        for (int qd = 0; qd < kQ; ++qd) qi[qd] = (wv0 + (int64_t)qd * kSub) / kQuad + lane;
+        for (int qd = 0; qd < kQ; ++qd) {
+            qi[qd] = (wv0 + (int64_t)qd * kSub) / kQuad + lane;
+            if constexpr (kPk) {
+                iw[qd] = (wv0 + (int64_t)qd * kSub) / kSub * (3 * kWave) + lane;
+                im[qd] = iw[qd] + kWave;
+                iv[qd] = iw[qd] + 2 * kWave;
+            } else {
+                iw[qd] = im[qd] = iv[qd] = qi[qd];
+            }
+        }
+        void *const pm = kPk ? (void *)a.master : a.m;
+        void *const pv = kPk ? (void *)a.master : a.v;
         if (a.mode == kModeWrite) {
             const f32x4 z = {1.0f, 2.0f, 3.0f, 4.0f};
             const u32x2 h = {0x3f803f80u, 0x3f803f80u};
 #pragma unroll
             for (int qd = 0; qd < kQ; ++qd) {
-                st<f32x4>(a.master, qi[qd], z);
+                st<f32x4>(a.master, iw[qd], z);
                 if constexpr (kMv16) {
                     st<u32x2>(a.m, qi[qd], h);
                     st<u32x2>(a.v, qi[qd], h);
                 } else {
-                    st<f32x4>(a.m, qi[qd], z);
-                    st<f32x4>(a.v, qi[qd], z);
+                    st<f32x4>(pm, im[qd], z);
+                    st<f32x4>(pv, iv[qd], z);
                 }
                 st<u32x2>(a.param, qi[qd], h);
                 if constexpr (kOut8) {
@@ -136,13 +150,13 @@ __global__ __launch_bounds__(kThreads) void twin_kernel(const TwinArgs a) {
         float s[kQ][K];
 #pragma unroll
         for (int qd = 0; qd < kQ; ++qd) {
-            w[qd] = ld<f32x4>(a.master, qi[qd]);
+            w[qd] = ld<f32x4>(a.master, iw[qd]);
             if constexpr (kMv16) {
                 mh[qd] = ld<u32x2>(a.m, qi[qd]);
                 vh[qd] = ld<u32x2>(a.v, qi[qd]);
             } else {
-                m[qd] = ld<f32x4>(a.m, qi[qd]);
-                v[qd] = ld<f32x4>(a.v, qi[qd]);
+                m[qd] = ld<f32x4>(pm, im[qd]);
+                v[qd] = ld<f32x4>(pv, iv[qd]);
             }
 #pragma unroll
             for (int j = 0; j < K; ++j) {
@@ -191,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void twin_kernel(const TwinArgs a) {
                 }
             }
             opaque(w[qd]);
-            st<f32x4>(a.master, qi[qd], w[qd]);
+            st<f32x4>(a.master, iw[qd], w[qd]);
             if constexpr (kMv16) {
                 opaque(mh[qd]);
                 opaque(vh[qd]);
@@ -200,8 +214,8 @@ __global__ __launch_bounds__(kThreads) void twin_kernel(const TwinArgs a) {
             } else {
                 opaque(m[qd]);
                 opaque(v[qd]);
-                st<f32x4>(a.m, qi[qd], m[qd]);
-                st<f32x4>(a.v, qi[qd], v[qd]);
+                st<f32x4>(pm, im[qd], m[qd]);
+                st<f32x4>(pv, iv[qd], v[qd]);
             }
             u32x2 p;
             if constexpr (kG8) {
@@ -229,6 +243,7 @@ twin_fn pick_layout(int layout) {
         case kLayoutQ8Out: return twin_kernel<K, kLayoutQ8Out, Q>;
         case kLayoutQ8Grad: return twin_kernel<K, kLayoutQ8Grad, Q>;
         case kLayoutBf16Mv: return twin_kernel<K, kLayoutBf16Mv, Q>;
+        case kLayoutPacked: return twin_kernel<K, kLayoutPacked, Q>;
         default: return nullptr;
     }
 }
@@ -298,8 +313,9 @@ int zs_ceiling_copy(const void *src, void *dst, int64_t bytes, void *stream) {
 //         was; param and the int8 copy receive arbitrary bytes), 1 = its
 //         reads only, 2 = its writes only (state overwritten).
 //   layout: 0 = zs_shard_step, 1 = zs_shard_step_q8ag, 2 = zs_shard_step_q8grad,
-//         4 = zs_shard_step_bf16mv (the streams and element sizes that entry
-//         point moves).  grads holds k device pointers (int8 for layout 2,
+//         4 = zs_shard_step_bf16mv, 8 = zs_shard_step_packed (the streams and
+//         element sizes that entry point moves; with layout 8 master is the
+//         packed state and m, v are unused).  grads holds k device pointers (int8 for layout 2,
 //         bf16 otherwise); qscales (layout 2) k device pointers to one f32
 //         per 256 elements; q8 and q8_scale (layout 1) the int8 copy and its
 //         scales.
@@ -318,7 +334,7 @@ int zs_ceiling_twin(int mode, int layout, float *master, void *m, void *v, uint1
                     int block_order, int groups_per_cu, int quads, void *stream) {
     if (mode < 0 || mode > 2 || k < 1 || k > kMaxK || n < 0 || !grads) return -1;
     if (layout != kLayoutBase && layout != kLayoutQ8Out && layout != kLayoutQ8Grad &&
-        layout != kLayoutBf16Mv)
+        layout != kLayoutBf16Mv && layout != kLayoutPacked)
         return -1;
     if (quads != 1 && quads != 2) return -1;
     const int64_t tile = (int64_t)kTile * quads;
@@ -327,7 +343,7 @@ int zs_ceiling_twin(int mode, int layout, float *master, void *m, void *v, uint1
     if (groups_per_cu < 0 || groups_per_cu > 32) return -1;
     const twin_fn fn = pick_twin(k, layout, quads);
     if (!fn) return -1;
-    if (!master || !m || !v || !param) return -1;
+    if (!master || !param || (layout != kLayoutPacked && (!m || !v))) return -1;
     if ((layout & kLayoutQ8Out) && (!q8 || !q8_scale)) return -1;
     if ((layout & kLayoutQ8Grad) && !qscales) return -1;
     for (int j = 0; j < k; ++j)

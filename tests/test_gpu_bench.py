@@ -25,8 +25,9 @@ def _bench(*args):
 
 @pytest.mark.parametrize("extra", [[], ["--graph"], ["--variant", "q8ag"],
                                    ["--variant", "q8grad"], ["--variant", "bf16mv"],
+                                   ["--variant", "packed"],
                                    ["--block-order", "2", "--groups-per-cu", "4"]],
-                         ids=["base", "graph", "q8ag", "q8grad", "bf16mv", "cfg"])
+                         ids=["base", "graph", "q8ag", "q8grad", "bf16mv", "packed", "cfg"])
 def test_bench_line(extra):
     out = _bench(*extra)
     assert out["n_gpus"] == 1 and out["steps"] == 5 and out["warmup"] == 1
@@ -53,6 +54,13 @@ def test_bench_line(extra):
     assert par == cpu["parity"] and par["windows"] >= 1
     assert par["steps_replayed"] == 6  # one warm-up step and five timed ones
     assert par["within_tolerance"] and par["bitwise_equal"], par
+    pk = out.get("packed_state")
+    if variant == "base" and extra == []:
+        # the same steps on the packed state, beside the default step
+        assert pk["entry_point"] == "zs_shard_step_packed" and pk["achieved"] > 0
+        assert pk["bitwise_equal_to_zs_shard_step"] is True and pk["pct_of_twin"] > 0
+    else:
+        assert pk is None
 
 
 def test_streaming_copy_of_the_ceiling_library():
@@ -76,7 +84,8 @@ def test_streaming_copy_of_the_ceiling_library():
     assert lib.zs_ceiling_copy(src.data_ptr(), dst.data_ptr(), 0, s) == 0
 
 
-@pytest.mark.parametrize("variant", ["base", "q8ag", "q8grad", "bf16mv", "bf16mv-wide"])
+@pytest.mark.parametrize("variant", ["base", "q8ag", "q8grad", "bf16mv", "bf16mv-wide",
+                                     "packed"])
 def test_twin_moves_the_step_traffic_without_changing_the_state(variant):
     """The twin ceiling on a step's buffers: the whole-traffic mode writes the
     state back bit for bit, the read-only mode changes nothing, the
@@ -94,7 +103,10 @@ def test_twin_moves_the_step_traffic_without_changing_the_state(variant):
     rnd = lambda dt: torch.randint(-30000, 30000, (n,), generator=g, device="cuda",  # noqa
                                    dtype=torch.int32).to(dt)
     mvt = torch.int16 if variant == "bf16mv" else torch.float32
-    bufs = dict(master=torch.randn(n, device="cuda", generator=g), m=rnd(mvt), v=rnd(mvt),
+    packed = variant == "packed"
+    bufs = dict(master=torch.randn(zs.packed_floats(n) if packed else n, device="cuda",
+                                   generator=g),
+                m=None if packed else rnd(mvt), v=None if packed else rnd(mvt),
                 param=torch.zeros(n, dtype=torch.int16, device="cuda"),
                 q8=torch.zeros(n, dtype=torch.int8, device="cuda") if variant == "q8ag" else None,
                 q8s=torch.zeros(nb, device="cuda") if variant == "q8ag" else None)
@@ -110,7 +122,7 @@ def test_twin_moves_the_step_traffic_without_changing_the_state(variant):
                     groups_per_cu=5)
     twin = bench.Twin(torch, variant, bufs, k, n, plan)
     assert twin.ok and twin.n == n
-    keep = {x: bufs[x].clone() for x in ("master", "m", "v")}
+    keep = {x: bufs[x].clone() for x in ("master", "m", "v") if bufs[x] is not None}
     s = torch.cuda.current_stream()
     for mode in ("step", "read"):
         twin.launch(mode, s)
@@ -120,8 +132,8 @@ def test_twin_moves_the_step_traffic_without_changing_the_state(variant):
     assert twin.rate("step", s, reps=2) > 0
     twin.launch("write", s)
     torch.cuda.synchronize()
-    pattern = torch.tensor([1.0, 2.0, 3.0, 4.0], device="cuda").repeat(n // 4)
-    assert torch.equal(bufs["master"], pattern)
+    pattern = torch.tensor([1.0, 2.0, 3.0, 4.0], device="cuda").repeat(bufs["master"].numel() // 4)
+    assert torch.equal(bufs["master"], pattern)  # packed: master, m and v slots alike
 
 
 def test_launch_sweep_prints_every_configuration():
