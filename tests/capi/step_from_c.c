@@ -67,6 +67,17 @@ int main(void) {
     }
     zs_seg_table table = {dsegs, 4, 0};
 
+    /* the same steps on the packed state (master, m, v per 256-element block) */
+    float *dstate, *du[3];
+    uint16_t *dpp;
+    CHECK_HIP(hipMalloc((void **)&dstate, 4 * ZS_PACKED_FLOATS(n)));
+    CHECK_HIP(hipMalloc((void **)&dpp, 2 * n));
+    for (int x = 0; x < 3; ++x) CHECK_HIP(hipMalloc((void **)&du[x], 4 * n));
+    if (zs_pack_state(dw, dm, dv, dstate, n, s) != ZS_OK) {
+        fprintf(stderr, "zs_pack_state failed\n");
+        return 1;
+    }
+
     for (int64_t t = 1; t <= 3; ++t) {
         for (int j = 0; j < k; ++j) {
             for (int64_t i = 0; i < n; ++i) {
@@ -80,6 +91,11 @@ int main(void) {
         const uint16_t *const dgs[3] = {dg[0], dg[1], dg[2]};
         int rc = zs_shard_step(dw, dm, dv, dp, dgs, k, n, &table, &hp, t, s);
         if (rc != ZS_OK) { fprintf(stderr, "zs_shard_step: %s\n", zs_status_string(rc)); return 1; }
+        rc = zs_shard_step_packed(dstate, dpp, dgs, k, n, &table, &hp, t, s);
+        if (rc != ZS_OK) {
+            fprintf(stderr, "zs_shard_step_packed: %s\n", zs_status_string(rc));
+            return 1;
+        }
         CHECK_HIP(hipStreamSynchronize(s));
         const uint16_t *const hgs[3] = {g[0], g[1], g[2]};
         if (zs_oracle_shard_step(wr, mr, vr, pr, hgs, k, n, segs, 4, &hp, t) != 0) {
@@ -93,15 +109,29 @@ int main(void) {
     CHECK_HIP(hipMemcpy(p, dp, 2 * n, hipMemcpyDeviceToHost));
     int bad = memcmp(w, wr, 4 * n) != 0 || memcmp(m, mr, 4 * n) != 0 ||
               memcmp(v, vr, 4 * n) != 0 || memcmp(p, pr, 2 * n) != 0;
+    /* the packed state, unpacked on the device, against the oracle too */
+    if (zs_unpack_state(dstate, du[0], du[1], du[2], n, s) != ZS_OK) bad = 1;
+    CHECK_HIP(hipStreamSynchronize(s));
+    CHECK_HIP(hipMemcpy(w, du[0], 4 * n, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(m, du[1], 4 * n, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(v, du[2], 4 * n, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(p, dpp, 2 * n, hipMemcpyDeviceToHost));
+    if (memcmp(w, wr, 4 * n) != 0 || memcmp(m, mr, 4 * n) != 0 || memcmp(v, vr, 4 * n) != 0 ||
+        memcmp(p, pr, 2 * n) != 0) {
+        fprintf(stderr, "C ABI: the packed step differs from the oracle\n");
+        bad = 1;
+    }
     /* an argument error is reported synchronously, nothing enqueued */
     const uint16_t *const dgs[3] = {dg[0], dg[1], dg[2]};
     if (zs_shard_step(dw, dm, dv, dp, dgs, k, n, &table, &hp, 0, s) != ZS_ERR_INVALID_ARGUMENT)
         bad = 1;
     for (int j = 0; j < k; ++j) { hipFree(dg[j]); free(g[j]); }
     hipFree(dw); hipFree(dm); hipFree(dv); hipFree(dp); hipFree(dsegs);
+    hipFree(dstate); hipFree(dpp);
+    for (int x = 0; x < 3; ++x) hipFree(du[x]);
     hipStreamDestroy(s);
     zs_fini();
     if (bad) { fprintf(stderr, "C ABI: results differ from the oracle\n"); return 1; }
-    printf("C ABI: bitwise equal\n");
+    printf("C ABI: bitwise equal (separate and packed state)\n");
     return 0;
 }
