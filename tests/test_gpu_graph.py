@@ -26,7 +26,7 @@ def gpu():
     torch.cuda.synchronize()
 
 
-def _state(torch, w0, n, k, seed, q8):
+def _state(torch, w0, n, k, seed, entry):
     rng = np.random.default_rng(seed)
     f = lambda a: torch.from_numpy(a.copy()).cuda()  # noqa: E731
     st = dict(master=f(w0), m=torch.zeros(n, dtype=torch.float32, device="cuda"),
@@ -34,14 +34,21 @@ def _state(torch, w0, n, k, seed, q8):
               param=torch.zeros(n, dtype=torch.int16, device="cuda"),
               grads=[f((rng.normal(0, 1e-2, n).astype(np.float32).view(np.uint32) >> 16)
                        .astype(np.uint16).view(np.int16)) for _ in range(k)])
-    if q8:
+    if entry == "packed":
+        z = np.zeros(n, np.float32)
+        st["state"] = f(H.pack_host(w0, z, z))
+        del st["master"], st["m"], st["v"]
+    if entry == "q8ag":
         st["q8"] = torch.zeros(n, dtype=torch.int8, device="cuda")
         st["q8s"] = torch.zeros(-(-n // zs.ZS_Q8_BLOCK), dtype=torch.float32, device="cuda")
     return st
 
 
 def _call(st, k, n, table, hp, t, stream):
-    if "q8" in st:
+    if "state" in st:
+        zs.zs_shard_step_packed(st["state"], st["param"], st["grads"], k, n, zs.seg_table(table),
+                                hp, t, stream)
+    elif "q8" in st:
         zs.zs_shard_step_q8ag(st["master"], st["m"], st["v"], st["param"], st["q8"], st["q8s"],
                               st["grads"], k, n, zs.seg_table(table), hp, t, stream)
     else:
@@ -57,9 +64,10 @@ def _same(torch, a, b):
             assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), key
 
 
-@pytest.mark.parametrize("q8", [False, True], ids=["zs_shard_step", "zs_shard_step_q8ag"])
+@pytest.mark.parametrize("entry", ["base", "q8ag", "packed"],
+                         ids=["zs_shard_step", "zs_shard_step_q8ag", "zs_shard_step_packed"])
 @pytest.mark.parametrize("t", [7, 10000])
-def test_graph_replays_match_eager_calls(gpu, q8, t):
+def test_graph_replays_match_eager_calls(gpu, entry, t):
     torch = gpu
     n, k = 100_003, 3
     rng = np.random.default_rng(21)
@@ -70,15 +78,15 @@ def test_graph_replays_match_eager_calls(gpu, q8, t):
         a += int(rng.integers(1, 5000))
     table = H.segment_tensor(segs, "cuda")
     hp = zs.hparams(1e-3, 0.9, 0.95, 1e-8, 0.1, 1.0)
-    eager = _state(torch, w0, n, k, 5, q8)
-    graphed = _state(torch, w0, n, k, 5, q8)
+    eager = _state(torch, w0, n, k, 5, entry)
+    graphed = _state(torch, w0, n, k, 5, entry)
     torch.cuda.synchronize()
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         _call(graphed, k, n, table, hp, t, torch.cuda.current_stream())
     torch.cuda.synchronize()
-    _same(torch, graphed, _state(torch, w0, n, k, 5, q8))  # capture ran nothing
+    _same(torch, graphed, _state(torch, w0, n, k, 5, entry))  # capture ran nothing
 
     for rep in range(4):
         g.replay()
@@ -88,4 +96,6 @@ def test_graph_replays_match_eager_calls(gpu, q8, t):
         assert torch.isfinite((x * x).sum())  # unrelated eager work between replays
         torch.cuda.synchronize()
         _same(torch, graphed, eager)
-    assert not torch.equal(graphed["master"], torch.from_numpy(w0).cuda())
+    moved = graphed["state"].view(-1, 3, 256)[:, 0, :].reshape(-1)[:n] if entry == "packed" \
+        else graphed["master"]
+    assert not torch.equal(moved, torch.from_numpy(w0).cuda())
