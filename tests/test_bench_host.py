@@ -139,6 +139,7 @@ def test_launch_key_follows_the_resolved_launch():
     assert zs.zs_launch_plan(2, (1 << 32) - 1, "bf16mv")["window_quads"] == 1
     assert zs.zs_launch_plan(2, 1 << 32, "bf16mv")["window_quads"] == 2
     assert zs.zs_launch_plan(2, n70, "q8grad")["groups_per_cu"] == 5
+    assert zs.zs_launch_plan(2, n70, "packed") == p70  # the packed step launches as the step
     assert zs.zs_launch_plan(2, (1 << 32) - 1, "bf16mv")["groups_per_cu"] == 0
     assert zs.zs_launch_plan(2, 1 << 32, "bf16mv")["groups_per_cu"] == 5
     assert bench.launch_key(mv).endswith(",quads=2") and "quads" not in bench.launch_key(p70)
@@ -184,6 +185,14 @@ def test_twin_rejects_bad_arguments_before_any_device_call():
     assert call(layout=4, quads=2, chunk=1024) == -1  # chunk below the wide tile
     assert call(n=0) == 0                       # nothing to do
     assert call(n=0, layout=4, quads=2, chunk=2048) == 0
+    # the packed layout: m and v live in the state, so they may be null there only
+    def call_mv(layout, m, v, n=0):
+        return lib.zs_ceiling_twin(0, layout, P(4096), m, v, P(4096), None, None,
+                                   ctypes.cast(g, P), None, 2, n, 1024, 2, 0, 1, None)
+    assert call_mv(8, None, None) == 0 and call(layout=8, n=0) == 0
+    assert call_mv(0, None, None) == -1 and call_mv(4, P(4096), None) == -1
+    assert call(layout=8, quads=2, chunk=2048) == -1  # one sub-window per wave only
+    assert call(layout=12) == -1
 
 
 def test_parity_windows_cover_ends_and_boundaries():

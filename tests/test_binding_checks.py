@@ -169,3 +169,35 @@ def test_k_must_match_the_number_of_partials():
         zs.ZS_ERR_INVALID_ARGUMENT
     assert zs.zs_host_shard_step(w, m, v, p, [np.zeros(N, np.uint16)], None, N, [(0, True)],
                                  HP, 1) == zs.ZS_OK
+
+
+def test_packed_entry_points_check_their_buffers():
+    """zs_shard_step_packed sizes the state as ZS_PACKED_FLOATS(n) floats and
+    refuses host buffers; the conversions check all four buffers; the packed
+    ShardStep takes no separate m or v."""
+    nf = zs.packed_floats(N)
+    assert nf == 768 * 4  # 1000 elements: four 256-element blocks
+    st = zs.seg_table(FakeGpuTensor(16), 1)
+    g = [FakeGpuTensor(2 * N), FakeGpuTensor(2 * N)]
+    with pytest.raises(ValueError, match="state holds"):
+        zs.zs_shard_step_packed(FakeGpuTensor(4 * 3 * N), FakeGpuTensor(2 * N), g, 2, N, st,
+                                HP, 1)
+    with pytest.raises(TypeError, match="host"):
+        zs.zs_shard_step_packed(np.zeros(nf, np.float32), FakeGpuTensor(2 * N), g, 2, N, st,
+                                HP, 1)
+    with pytest.raises(ValueError, match="k=3 but 2 grads"):
+        zs.zs_shard_step_packed(FakeGpuTensor(4 * nf), FakeGpuTensor(2 * N), g, 3, N, st, HP, 1)
+    with pytest.raises(ValueError, match="state holds"):
+        zs.zs_pack_state(FakeGpuTensor(4 * N), FakeGpuTensor(4 * N), FakeGpuTensor(4 * N),
+                         FakeGpuTensor(4 * nf - 4), N)
+    with pytest.raises(ValueError, match="m holds"):
+        zs.zs_unpack_state(FakeGpuTensor(4 * nf), FakeGpuTensor(4 * N), FakeGpuTensor(4 * N - 4),
+                           FakeGpuTensor(4 * N), N)
+    with pytest.raises(TypeError, match="host"):
+        zs.zs_pack_state(np.zeros(N, np.float32), FakeGpuTensor(4 * N), FakeGpuTensor(4 * N),
+                         FakeGpuTensor(4 * nf), N)
+    with pytest.raises(ValueError, match="inside the state"):
+        zs.ShardStep(FakeGpuTensor(4 * nf), FakeGpuTensor(4 * N), None, FakeGpuTensor(2 * N),
+                     g, N, st, HP, variant="packed")
+    assert zs.algorithmic_bytes("packed", 2, N) == zs.algorithmic_bytes("base", 2, N)
+    assert zs.ZS_VARIANT["packed"] == 16
