@@ -462,6 +462,8 @@ def twin_bytes(variant: str, k: int, n: int):
     nb = -(-n // 256)
     return {"base": ((12 + 2 * k) * n, 14 * n),
             "packed": ((12 + 2 * k) * n, 14 * n),
+            "packed_q8ag": ((12 + 2 * k) * n, 15 * n + 4 * nb),
+            "packed_q8grad": (12 * n + k * (n + 4 * nb), 14 * n),
             "q8ag": ((12 + 2 * k) * n, 15 * n + 4 * nb),
             "q8grad": (12 * n + k * (n + 4 * nb), 14 * n),
             "bf16mv": ((8 + 2 * k) * n, 10 * n)}[variant]
@@ -476,7 +478,8 @@ class Twin:
     """The step's traffic without its arithmetic (libzs_ceiling.so), on the
     step's own buffers and in the step's own launch."""
     MODES = {"step": 0, "read": 1, "write": 2}
-    LAYOUT = {"base": 0, "q8ag": 1, "q8grad": 2, "bf16mv": 4, "packed": 8}
+    LAYOUT = {"base": 0, "q8ag": 1, "q8grad": 2, "bf16mv": 4, "packed": 8, "packed_q8ag": 9,
+              "packed_q8grad": 10}
 
     def __init__(self, torch, variant, bufs, k, n, plan):
         import ctypes
@@ -493,9 +496,10 @@ class Twin:
         self.head = [ptr(bufs["master"]), ptr(bufs.get("m")), ptr(bufs.get("v")),
                      ptr(bufs["param"]),
                      ptr(bufs.get("q8")), ptr(bufs.get("q8s"))]
-        gl = bufs.get("qgrads") if variant == "q8grad" else bufs["grads"]
+        q8g = variant in ("q8grad", "packed_q8grad")
+        gl = bufs.get("qgrads") if q8g else bufs["grads"]
         self.gp = (ctypes.c_void_p * k)(*[g.data_ptr() for g in gl])
-        sl = bufs.get("qscales") if variant == "q8grad" else None
+        sl = bufs.get("qscales") if q8g else None
         self.sp = (ctypes.c_void_p * k)(*[s.data_ptr() for s in sl]) if sl else None
 
     def launch(self, mode, stream):
@@ -745,10 +749,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="70b")
     ap.add_argument("--variant", default="base",
-                    choices=("base", "q8ag", "q8grad", "bf16mv", "packed", "offload"),
+                    choices=("base", "q8ag", "q8grad", "bf16mv", "packed", "packed_q8ag",
+                             "packed_q8grad", "offload"),
                     help="entry point: zs_shard_step (base), zs_shard_step_q8ag, "
                          "zs_shard_step_q8grad, zs_shard_step_bf16mv, zs_shard_step_packed "
-                         "(master, m, v packed per 256-element block), or the host "
+                         "(master, m, v packed per 256-element block), zs_shard_step_packed_q8ag, "
+                         "zs_shard_step_packed_q8grad, or the host "
                          "(ZeRO-Offload) step zs_host_shard_step, which runs on the CPU "
                          "and needs no GPU")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -835,8 +841,13 @@ def main():
     dev = torch.device("cuda:0")
     nb = -(-n // zs.ZS_Q8_BLOCK)
     mv_dtype = torch.int16 if var == "bf16mv" else torch.float32
+    packed_var = var.startswith("packed")
+    q8grad_var = var in ("q8grad", "packed_q8grad")
+    q8ag_var = var in ("q8ag", "packed_q8ag")
+    # the oracle arithmetic the variant computes (the packed forms compute their plain form's)
+    arith = {"packed": "base", "packed_q8ag": "q8ag", "packed_q8grad": "q8grad"}.get(var, var)
     state = master = m = v = None
-    if var == "packed":
+    if packed_var:
         # master, m and v in one array, per 256-element block
         state = torch.empty(zs.packed_floats(n), dtype=torch.float32, device=dev)
     else:
@@ -845,12 +856,12 @@ def main():
         v = torch.zeros(n, dtype=mv_dtype, device=dev)
     param = torch.zeros(n, dtype=torch.int16, device=dev)
     grads = qgrads = qscales = q8 = q8s = None
-    if var == "q8grad":
+    if q8grad_var:
         qgrads = [torch.empty(n, dtype=torch.int8, device=dev) for _ in range(k)]
         qscales = [torch.empty(nb, dtype=torch.float32, device=dev) for _ in range(k)]
     else:
         grads = [torch.empty(n, dtype=torch.int16, device=dev) for _ in range(k)]
-    if var == "q8ag":
+    if q8ag_var:
         q8 = torch.zeros(n, dtype=torch.int8, device=dev)
         q8s = torch.zeros(nb, dtype=torch.float32, device=dev)
     table = torch.tensor([[s, 1 if f else 0] for s, f in w.shard.segments], dtype=torch.int64,
@@ -866,12 +877,12 @@ def main():
     twin = None
     ceil = {}
     if not args.no_twin:
-        twin = Twin(torch, var, dict(master=state if var == "packed" else master, m=m, v=v,
+        twin = Twin(torch, var, dict(master=state if packed_var else master, m=m, v=v,
                                      param=param, q8=q8, q8s=q8s, grads=grads, qgrads=qgrads,
                                      qscales=qscales), k, n, plan)
         if twin.ok:
             ceil["write"] = twin.rate("write", stream)
-    if var == "packed":
+    if packed_var:
         state.zero_()
         init = torch.empty(n, dtype=torch.float32, device=dev)
         synth.dev_master(w, init)
@@ -893,6 +904,12 @@ def main():
         call = zs.ShardStep(master, m, v, param, grads, n, st, hp, variant="bf16mv")
     elif var == "packed":
         call = zs.ShardStep(state, None, None, param, grads, n, st, hp, variant="packed")
+    elif var == "packed_q8ag":
+        call = zs.ShardStep(state, None, None, param, grads, n, st, hp, variant=var,
+                            param_q8=q8, param_q8_scale=q8s)
+    elif var == "packed_q8grad":
+        call = zs.ShardStep(state, None, None, param, qgrads, n, st, hp, variant=var,
+                            qscales=qscales)
     else:
         call = zs.ShardStep(master, m, v, param, grads, n, st, hp, cfg=cfg)
 
@@ -900,7 +917,7 @@ def main():
         call(t, stream if on is None else on)
 
     def fill(t):
-        if var == "q8grad":
+        if q8grad_var:
             synth.dev_qgrads(w, t, qgrads, qscales)
         else:
             synth.dev_grads(w, t, grads)
@@ -936,9 +953,9 @@ def main():
     par = None
     if args.cpu_seconds > 0:
         wins = parity_windows(w, n)
-        before = snapshot_packed(state, wins) if var == "packed" else \
+        before = snapshot_packed(state, wins) if packed_var else \
             snapshot({"master": master, "m": m, "v": v}, wins)
-        if var == "q8grad":
+        if q8grad_var:
             qg = [[q[a:b].cpu().numpy().copy() for a, b in wins] for q in qgrads]
             qs = [[block_slice(s, a, b).cpu().numpy().copy() for a, b in wins] for s in qscales]
             par = dict(qgrads=qg, qscales=qs)
@@ -1000,12 +1017,12 @@ def main():
     log("kernel ms per launch: avg %.4f min %.4f max %.4f" % (avg_ms, min(kernel_ms),
                                                               max(kernel_ms)))
     if par is not None:
-        if var == "packed":
+        if packed_var:
             after = snapshot_packed(state, wins)
-            after.update(snapshot({"param": param}, wins))
+            after.update(snapshot({"param": param, "q8": q8}, wins))
         else:
             after = snapshot({"master": master, "m": m, "v": v, "param": param, "q8": q8}, wins)
-        if var == "q8ag":
+        if q8ag_var:
             after["q8s"] = [block_slice(q8s, a, b).cpu().numpy().copy() for a, b in wins]
         par.update(after=after, ts=list(range(w.t0, t)))
 
@@ -1029,7 +1046,7 @@ def main():
 
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, args.cpu_seconds, var, bpe, par)
+        cpu = cpu_baseline(w, args.cpu_seconds, arith, bpe, par)
         log("cpu oracle: %.3f GB/s (%s)" % (cpu["value"], cpu["sample"]))
         log("parity of the timed run: %s" % json.dumps(cpu["parity"]))
 
@@ -1070,7 +1087,11 @@ def main():
                     "q8grad": "f32 master/m/v, int8 partials, bf16 param",
                     "bf16mv": "f32 master, bf16 m/v, partials and param",
                     "packed": "f32 master/m/v packed per 256-element block, bf16 partials and "
-                              "param"}[var],
+                              "param",
+                    "packed_q8ag": "f32 master/m/v packed per 256-element block, bf16 partials "
+                                   "and param, int8 param copy",
+                    "packed_q8grad": "f32 master/m/v packed per 256-element block, int8 "
+                                     "partials, bf16 param"}[var],
         "data": "synthetic (seeded SplitMix64 / Irwin-Hall draws; partials of the first "
                 "measured step kept resident across timed steps)",
         "config": {

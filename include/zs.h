@@ -264,6 +264,21 @@ int zs_shard_step_packed(float *state, uint16_t *param_bf16, const uint16_t *con
                          const zs_hparams *hparams, int64_t step, void *stream);
 
 /*
+ * zs_shard_step_q8ag and zs_shard_step_q8grad on the packed state: the same
+ * outputs (the int8 parameter copy and its scales; the int8 partials and
+ * their scales read as there), bit for bit, with master, m and v in `state`
+ * as for zs_shard_step_packed.  Everything else as those entry points.
+ */
+int zs_shard_step_packed_q8ag(float *state, uint16_t *param_bf16, int8_t *param_q8,
+                              float *param_q8_scale, const uint16_t *const *grads, int k,
+                              int64_t n, const zs_seg_table *seg_table,
+                              const zs_hparams *hparams, int64_t step, void *stream);
+int zs_shard_step_packed_q8grad(float *state, uint16_t *param_bf16, const int8_t *const *qgrads,
+                                const float *const *qscales, int k, int64_t n,
+                                const zs_seg_table *seg_table, const zs_hparams *hparams,
+                                int64_t step, void *stream);
+
+/*
  * Convert, on `stream`, between separate master, m and v arrays (DEVICE fp32
  * [n] each) and the packed state of zs_shard_step_packed (DEVICE fp32
  * [ZS_PACKED_FLOATS(n)]).  zs_pack_state writes every slot of the state, the
@@ -306,6 +321,8 @@ int zs_launch_geometry(int k, int64_t n, const zs_launch_cfg *cfg, int64_t *work
 #define ZS_VARIANT_Q8GRAD 2 /* zs_shard_step_q8grad */
 #define ZS_VARIANT_BF16MV 4 /* zs_shard_step_bf16mv */
 #define ZS_VARIANT_PACKED 16 /* zs_shard_step_packed */
+#define ZS_VARIANT_PACKED_Q8AG 17   /* zs_shard_step_packed_q8ag */
+#define ZS_VARIANT_PACKED_Q8GRAD 18 /* zs_shard_step_packed_q8grad */
 
 /* The launch a step call resolves its defaults to. */
 typedef struct {

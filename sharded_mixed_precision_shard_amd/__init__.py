@@ -7,7 +7,8 @@ or as plain integer device addresses.  There is no CPU fallback: if
 
 Entry points keep the C names: :func:`zs_init`, :func:`zs_shard_step`,
 :func:`zs_shard_step_cfg`, :func:`zs_shard_step_q8ag`, :func:`zs_shard_step_q8grad`,
-:func:`zs_shard_step_bf16mv`, :func:`zs_shard_step_packed`, :func:`zs_pack_state`,
+:func:`zs_shard_step_bf16mv`, :func:`zs_shard_step_packed`,
+:func:`zs_shard_step_packed_q8ag`, :func:`zs_shard_step_packed_q8grad`, :func:`zs_pack_state`,
 :func:`zs_unpack_state`, :func:`zs_fini`, :func:`zs_status_string`,
 :func:`zs_last_device_error`, :func:`zs_algorithmic_bytes`,
 :func:`zs_launch_geometry`, :func:`zs_launch_plan`.
@@ -34,11 +35,13 @@ ZS_ERR_TOO_MANY_SEGMENTS = 4
 ZS_ERR_DEVICE = 5
 ZS_ERR_ALIASING = 6
 
-ZS_VARIANT = {"base": 0, "q8ag": 1, "q8grad": 2, "bf16mv": 4, "packed": 16}
+ZS_VARIANT = {"base": 0, "q8ag": 1, "q8grad": 2, "bf16mv": 4, "packed": 16, "packed_q8ag": 17,
+              "packed_q8grad": 18}
 
 # Symbols declared in include/zs.h.
 EXPORTS = ("zs_init", "zs_shard_step", "zs_shard_step_cfg", "zs_shard_step_q8ag",
            "zs_shard_step_q8grad", "zs_shard_step_bf16mv", "zs_shard_step_packed",
+           "zs_shard_step_packed_q8ag", "zs_shard_step_packed_q8grad",
            "zs_pack_state", "zs_unpack_state", "zs_fini", "zs_status_string",
            "zs_last_device_error", "zs_algorithmic_bytes", "zs_launch_geometry",
            "zs_launch_plan")
@@ -114,6 +117,12 @@ def load_library():
     lib.zs_shard_step_packed.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int64, P, P,
                                          ctypes.c_int64, P]
     lib.zs_shard_step_packed.restype = ctypes.c_int
+    lib.zs_shard_step_packed_q8ag.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int64, P, P,
+                                              ctypes.c_int64, P]
+    lib.zs_shard_step_packed_q8ag.restype = ctypes.c_int
+    lib.zs_shard_step_packed_q8grad.argtypes = [P, P, P, P, ctypes.c_int, ctypes.c_int64, P, P,
+                                                ctypes.c_int64, P]
+    lib.zs_shard_step_packed_q8grad.restype = ctypes.c_int
     lib.zs_pack_state.argtypes = [P, P, P, P, ctypes.c_int64, P]
     lib.zs_pack_state.restype = ctypes.c_int
     lib.zs_unpack_state.argtypes = [P, P, P, P, ctypes.c_int64, P]
@@ -392,6 +401,49 @@ def zs_shard_step_packed(state, param_bf16, grads, k, n, seg_table_, hparams_, s
     return rc
 
 
+def zs_shard_step_packed_q8ag(state, param_bf16, param_q8, param_q8_scale, grads, k, n,
+                              seg_table_, hparams_, step, stream=None, check=True) -> int:
+    """zs_shard_step_q8ag on the packed state."""
+    k = _check_k(k, grads, "grads")
+    nn = max(int(n), 0)
+    nb = -(-nn // ZS_Q8_BLOCK)
+    gp = _ptr_array(grads, 2 * nn, "grads")
+    st = seg_table_ if isinstance(seg_table_, ZsSegTable) else seg_table(seg_table_)
+    rc = load_library().zs_shard_step_packed_q8ag(
+        ctypes.c_void_p(_dev(state, 4 * packed_floats(nn), "state")),
+        ctypes.c_void_p(_dev(param_bf16, 2 * nn, "param_bf16")),
+        ctypes.c_void_p(_dev(param_q8, nn, "param_q8")),
+        ctypes.c_void_p(_dev(param_q8_scale, 4 * nb, "param_q8_scale")),
+        ctypes.cast(gp, ctypes.c_void_p), int(k), int(n), ctypes.byref(st),
+        ctypes.byref(hparams_), int(step), ctypes.c_void_p(_stream_handle(stream)))
+    if check and rc != ZS_OK:
+        raise ZsError(rc, "zs_shard_step_packed_q8ag")
+    return rc
+
+
+def zs_shard_step_packed_q8grad(state, param_bf16, qgrads, qscales, k, n, seg_table_, hparams_,
+                                step, stream=None, check=True) -> int:
+    """zs_shard_step_q8grad on the packed state."""
+    nn = max(int(n), 0)
+    nb = -(-nn // ZS_Q8_BLOCK)
+    k = _check_k(k, qgrads, "qgrads")
+    if len(qscales) != len(qgrads):
+        raise ValueError("%d qscales for %d qgrads: one scale array per int8 partial"
+                         % (len(qscales), len(qgrads)))
+    qp = _ptr_array(qgrads, nn, "qgrads")
+    sp = _ptr_array(qscales, 4 * nb, "qscales")
+    st = seg_table_ if isinstance(seg_table_, ZsSegTable) else seg_table(seg_table_)
+    rc = load_library().zs_shard_step_packed_q8grad(
+        ctypes.c_void_p(_dev(state, 4 * packed_floats(nn), "state")),
+        ctypes.c_void_p(_dev(param_bf16, 2 * nn, "param_bf16")),
+        ctypes.cast(qp, ctypes.c_void_p), ctypes.cast(sp, ctypes.c_void_p), int(k), int(n),
+        ctypes.byref(st), ctypes.byref(hparams_), int(step),
+        ctypes.c_void_p(_stream_handle(stream)))
+    if check and rc != ZS_OK:
+        raise ZsError(rc, "zs_shard_step_packed_q8grad")
+    return rc
+
+
 def zs_pack_state(master, m, v, state, n, stream=None, check=True) -> int:
     """Separate fp32 master, m, v [n] -> packed state [packed_floats(n)] (padding +0)."""
     nn = max(int(n), 0)
@@ -448,17 +500,31 @@ class ShardStep:
             head = [pm, pmm, pv, pp, ctypes.cast(qp, ctypes.c_void_p),
                     ctypes.cast(sp, ctypes.c_void_p)]
             fn = lib.zs_shard_step_q8grad
-        elif variant == "packed":
+        elif variant in ("packed", "packed_q8ag", "packed_q8grad"):
             if m is not None or v is not None:
                 raise ValueError("the packed step takes its m and v inside the state")
-            gp = _ptr_array(grads, 2 * nn, "grads")
             st = seg_table_ if isinstance(seg_table_, ZsSegTable) else seg_table(seg_table_)
             hp = hparams_
-            self._c = (gp,)
             head = [ctypes.c_void_p(_dev(master, 4 * packed_floats(nn), "state")),
-                    ctypes.c_void_p(_dev(param_bf16, 2 * nn, "param_bf16")),
-                    ctypes.cast(gp, ctypes.c_void_p)]
-            fn = lib.zs_shard_step_packed
+                    ctypes.c_void_p(_dev(param_bf16, 2 * nn, "param_bf16"))]
+            if variant == "packed_q8grad":
+                if len(qscales or []) != k:
+                    raise ValueError("q8grad needs one scale array per int8 partial")
+                qp = _ptr_array(grads, nn, "qgrads")
+                sp = _ptr_array(qscales, 4 * nb, "qscales")
+                self._c = (qp, sp)
+                head += [ctypes.cast(qp, ctypes.c_void_p), ctypes.cast(sp, ctypes.c_void_p)]
+                fn = lib.zs_shard_step_packed_q8grad
+            else:
+                gp = _ptr_array(grads, 2 * nn, "grads")
+                self._c = (gp,)
+                if variant == "packed_q8ag":
+                    head += [ctypes.c_void_p(_dev(param_q8, nn, "param_q8")),
+                             ctypes.c_void_p(_dev(param_q8_scale, 4 * nb, "param_q8_scale"))]
+                    fn = lib.zs_shard_step_packed_q8ag
+                else:
+                    fn = lib.zs_shard_step_packed
+                head.append(ctypes.cast(gp, ctypes.c_void_p))
         else:
             mv = 2 if variant == "bf16mv" else 4
             pm, pmm, pv, pp, pg, _, st, hp, gp = _marshal(master, m, v, param_bf16, grads, k, n,
@@ -499,9 +565,9 @@ def algorithmic_bytes(variant: str, k: int, n: int) -> int:
     nb = -(-n // ZS_Q8_BLOCK)
     if variant in ("base", "packed"):
         return (26 + 2 * k) * n
-    if variant == "q8ag":
+    if variant in ("q8ag", "packed_q8ag"):
         return (26 + 2 * k) * n + n + 4 * nb
-    if variant == "q8grad":
+    if variant in ("q8grad", "packed_q8grad"):
         return (12 + k + 14) * n + 4 * k * nb
     if variant == "bf16mv":
         return (18 + 2 * k) * n

@@ -95,7 +95,7 @@ int resolve_launch(int k, int64_t n, int variant, const zs_launch_cfg *cfg,
                    zs_launch_info *out, int *kernel_variant = nullptr) {
     if (k < 1 || k > ZS_MAX_K || n < 0 || n > INT64_MAX / 8) return ZS_ERR_INVALID_ARGUMENT;
     if (variant != 0 && variant != kOutQ8 && variant != kGradQ8 && variant != kMvBf16 &&
-        variant != kPacked)
+        variant != kPacked && variant != (kPacked | kOutQ8) && variant != (kPacked | kGradQ8))
         return ZS_ERR_INVALID_ARGUMENT;
     // Streaming (non-temporal) loads and stores by default: nothing is
     // reused, and on MI355X they measured 5-10 % faster than cached access.
@@ -423,6 +423,31 @@ int zs_shard_step_packed(float *state, uint16_t *param_bf16, const uint16_t *con
                              stream);
     r.grads = grads;
     r.variant = kPacked;
+    return validate_and_launch(r);
+}
+
+int zs_shard_step_packed_q8ag(float *state, uint16_t *param_bf16, int8_t *param_q8,
+                              float *param_q8_scale, const uint16_t *const *grads, int k,
+                              int64_t n, const zs_seg_table *seg_table,
+                              const zs_hparams *hparams, int64_t step, void *stream) {
+    Request r = base_request(state, nullptr, nullptr, param_bf16, k, n, seg_table, hparams, step,
+                             stream);
+    r.grads = grads;
+    r.q8 = param_q8;
+    r.q8_scale = param_q8_scale;
+    r.variant = kPacked | kOutQ8;
+    return validate_and_launch(r);
+}
+
+int zs_shard_step_packed_q8grad(float *state, uint16_t *param_bf16, const int8_t *const *qgrads,
+                                const float *const *qscales, int k, int64_t n,
+                                const zs_seg_table *seg_table, const zs_hparams *hparams,
+                                int64_t step, void *stream) {
+    Request r = base_request(state, nullptr, nullptr, param_bf16, k, n, seg_table, hparams, step,
+                             stream);
+    r.qgrads = qgrads;
+    r.qscales = qscales;
+    r.variant = kPacked | kGradQ8;
     return validate_and_launch(r);
 }
 

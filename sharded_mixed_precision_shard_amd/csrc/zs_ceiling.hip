@@ -244,6 +244,8 @@ twin_fn pick_layout(int layout) {
         case kLayoutQ8Grad: return twin_kernel<K, kLayoutQ8Grad, Q>;
         case kLayoutBf16Mv: return twin_kernel<K, kLayoutBf16Mv, Q>;
         case kLayoutPacked: return twin_kernel<K, kLayoutPacked, Q>;
+        case kLayoutPacked | kLayoutQ8Out: return twin_kernel<K, kLayoutPacked | kLayoutQ8Out, Q>;
+        case kLayoutPacked | kLayoutQ8Grad: return twin_kernel<K, kLayoutPacked | kLayoutQ8Grad, Q>;
         default: return nullptr;
     }
 }
@@ -313,9 +315,10 @@ int zs_ceiling_copy(const void *src, void *dst, int64_t bytes, void *stream) {
 //         was; param and the int8 copy receive arbitrary bytes), 1 = its
 //         reads only, 2 = its writes only (state overwritten).
 //   layout: 0 = zs_shard_step, 1 = zs_shard_step_q8ag, 2 = zs_shard_step_q8grad,
-//         4 = zs_shard_step_bf16mv, 8 = zs_shard_step_packed (the streams and
-//         element sizes that entry point moves; with layout 8 master is the
-//         packed state and m, v are unused).  grads holds k device pointers (int8 for layout 2,
+//         4 = zs_shard_step_bf16mv, 8 = zs_shard_step_packed, 9 and 10 = its
+//         int8-payload and int8-partial forms (the streams and element sizes
+//         that entry point moves; with layouts 8-10 master is the packed state
+//         and m, v are unused).  grads holds k device pointers (int8 for layout 2,
 //         bf16 otherwise); qscales (layout 2) k device pointers to one f32
 //         per 256 elements; q8 and q8_scale (layout 1) the int8 copy and its
 //         scales.
@@ -334,7 +337,8 @@ int zs_ceiling_twin(int mode, int layout, float *master, void *m, void *v, uint1
                     int block_order, int groups_per_cu, int quads, void *stream) {
     if (mode < 0 || mode > 2 || k < 1 || k > kMaxK || n < 0 || !grads) return -1;
     if (layout != kLayoutBase && layout != kLayoutQ8Out && layout != kLayoutQ8Grad &&
-        layout != kLayoutBf16Mv && layout != kLayoutPacked)
+        layout != kLayoutBf16Mv && layout != kLayoutPacked &&
+        layout != (kLayoutPacked | kLayoutQ8Out) && layout != (kLayoutPacked | kLayoutQ8Grad))
         return -1;
     if (quads != 1 && quads != 2) return -1;
     const int64_t tile = (int64_t)kTile * quads;
@@ -343,7 +347,7 @@ int zs_ceiling_twin(int mode, int layout, float *master, void *m, void *v, uint1
     if (groups_per_cu < 0 || groups_per_cu > 32) return -1;
     const twin_fn fn = pick_twin(k, layout, quads);
     if (!fn) return -1;
-    if (!master || !param || (layout != kLayoutPacked && (!m || !v))) return -1;
+    if (!master || !param || (!(layout & kLayoutPacked) && (!m || !v))) return -1;
     if ((layout & kLayoutQ8Out) && (!q8 || !q8_scale)) return -1;
     if ((layout & kLayoutQ8Grad) && !qscales) return -1;
     for (int j = 0; j < k; ++j)

@@ -604,6 +604,8 @@ kernel_fn pick_variant(int variant, int nt, int unit) {
         case kGradQ8: return pick_unit<K, kGradQ8>(unit);
         case kMvBf16: return pick_unit<K, kMvBf16>(unit);
         case kPacked: return nt ? pick_unit<K, kPacked>(unit) : nullptr;
+        case kPacked | kOutQ8: return nt ? pick_unit<K, kPacked | kOutQ8>(unit) : nullptr;
+        case kPacked | kGradQ8: return nt ? pick_unit<K, kPacked | kGradQ8>(unit) : nullptr;
         case kMvBf16 | kWide:
             if constexpr (K <= kWideMaxK) return pick_unit<K, kMvBf16 | kWide>(unit);
             return nullptr;

@@ -22,7 +22,7 @@ def torch():
     return _t
 
 
-VARIANTS = ("base", "q8ag", "q8grad", "bf16mv", "packed")
+VARIANTS = ("base", "q8ag", "q8grad", "bf16mv", "packed", "packed_q8ag", "packed_q8grad")
 
 
 def pack_host(w, m, v):

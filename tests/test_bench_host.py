@@ -140,6 +140,8 @@ def test_launch_key_follows_the_resolved_launch():
     assert zs.zs_launch_plan(2, 1 << 32, "bf16mv")["window_quads"] == 2
     assert zs.zs_launch_plan(2, n70, "q8grad")["groups_per_cu"] == 5
     assert zs.zs_launch_plan(2, n70, "packed") == p70  # the packed step launches as the step
+    assert zs.zs_launch_plan(2, n70, "packed_q8ag") == q8
+    assert zs.zs_launch_plan(2, n70, "packed_q8grad") == zs.zs_launch_plan(2, n70, "q8grad")
     assert zs.zs_launch_plan(2, (1 << 32) - 1, "bf16mv")["groups_per_cu"] == 0
     assert zs.zs_launch_plan(2, 1 << 32, "bf16mv")["groups_per_cu"] == 5
     assert bench.launch_key(mv).endswith(",quads=2") and "quads" not in bench.launch_key(p70)

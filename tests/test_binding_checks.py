@@ -200,4 +200,13 @@ def test_packed_entry_points_check_their_buffers():
         zs.ShardStep(FakeGpuTensor(4 * nf), FakeGpuTensor(4 * N), None, FakeGpuTensor(2 * N),
                      g, N, st, HP, variant="packed")
     assert zs.algorithmic_bytes("packed", 2, N) == zs.algorithmic_bytes("base", 2, N)
+    assert zs.algorithmic_bytes("packed_q8ag", 2, N) == zs.algorithmic_bytes("q8ag", 2, N)
+    assert zs.algorithmic_bytes("packed_q8grad", 2, N) == zs.algorithmic_bytes("q8grad", 2, N)
+    q = [FakeGpuTensor(N), FakeGpuTensor(N)]
+    with pytest.raises(ValueError, match="2 qscales for 2 qgrads|1 qscales for 2 qgrads"):
+        zs.zs_shard_step_packed_q8grad(FakeGpuTensor(4 * nf), FakeGpuTensor(2 * N), q,
+                                       [FakeGpuTensor(16)], 2, N, st, HP, 1)
+    with pytest.raises(ValueError, match="state holds"):
+        zs.zs_shard_step_packed_q8ag(FakeGpuTensor(4 * N), FakeGpuTensor(2 * N),
+                                     FakeGpuTensor(N), FakeGpuTensor(16), g, 2, N, st, HP, 1)
     assert zs.ZS_VARIANT["packed"] == 16

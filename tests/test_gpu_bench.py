@@ -25,9 +25,11 @@ def _bench(*args):
 
 @pytest.mark.parametrize("extra", [[], ["--graph"], ["--variant", "q8ag"],
                                    ["--variant", "q8grad"], ["--variant", "bf16mv"],
-                                   ["--variant", "packed"],
+                                   ["--variant", "packed"], ["--variant", "packed_q8ag"],
+                                   ["--variant", "packed_q8grad"],
                                    ["--block-order", "2", "--groups-per-cu", "4"]],
-                         ids=["base", "graph", "q8ag", "q8grad", "bf16mv", "packed", "cfg"])
+                         ids=["base", "graph", "q8ag", "q8grad", "bf16mv", "packed", "packed_q8ag",
+                              "packed_q8grad", "cfg"])
 def test_bench_line(extra):
     out = _bench(*extra)
     assert out["n_gpus"] == 1 and out["steps"] == 5 and out["warmup"] == 1
@@ -85,7 +87,7 @@ def test_streaming_copy_of_the_ceiling_library():
 
 
 @pytest.mark.parametrize("variant", ["base", "q8ag", "q8grad", "bf16mv", "bf16mv-wide",
-                                     "packed"])
+                                     "packed", "packed_q8ag", "packed_q8grad"])
 def test_twin_moves_the_step_traffic_without_changing_the_state(variant):
     """The twin ceiling on a step's buffers: the whole-traffic mode writes the
     state back bit for bit, the read-only mode changes nothing, the
@@ -103,14 +105,15 @@ def test_twin_moves_the_step_traffic_without_changing_the_state(variant):
     rnd = lambda dt: torch.randint(-30000, 30000, (n,), generator=g, device="cuda",  # noqa
                                    dtype=torch.int32).to(dt)
     mvt = torch.int16 if variant == "bf16mv" else torch.float32
-    packed = variant == "packed"
+    packed = variant.startswith("packed")
     bufs = dict(master=torch.randn(zs.packed_floats(n) if packed else n, device="cuda",
                                    generator=g),
                 m=None if packed else rnd(mvt), v=None if packed else rnd(mvt),
                 param=torch.zeros(n, dtype=torch.int16, device="cuda"),
-                q8=torch.zeros(n, dtype=torch.int8, device="cuda") if variant == "q8ag" else None,
-                q8s=torch.zeros(nb, device="cuda") if variant == "q8ag" else None)
-    if variant == "q8grad":
+                q8=torch.zeros(n, dtype=torch.int8, device="cuda")
+                if variant in ("q8ag", "packed_q8ag") else None,
+                q8s=torch.zeros(nb, device="cuda") if variant in ("q8ag", "packed_q8ag") else None)
+    if variant in ("q8grad", "packed_q8grad"):
         bufs["qgrads"] = [rnd(torch.int8) for _ in range(k)]
         bufs["qscales"] = [torch.rand(nb, device="cuda", generator=g) for _ in range(k)]
         bufs["grads"] = None

@@ -64,7 +64,8 @@ def test_unit_correction_kernels_are_bitwise(gpu, variant, span):
         m0, v0 = _bf16(m0), _bf16(v0)
     ref = [w0.copy(), m0.copy(), v0.copy(), np.zeros(n, np.uint16)]
     dw, dm, dv = _dev(torch, w0), _dev(torch, m0), _dev(torch, v0)
-    dstate = _dev(torch, H.pack_host(w0, m0, v0)) if variant == "packed" else None
+    packed = variant.startswith("packed")
+    dstate = _dev(torch, H.pack_host(w0, m0, v0)) if packed else None
     dp = torch.zeros(n, dtype=torch.int16, device="cuda")
     dq = torch.zeros(n, dtype=torch.int8, device="cuda")
     ds = torch.zeros(nb, dtype=torch.float32, device="cuda")
@@ -73,17 +74,22 @@ def test_unit_correction_kernels_are_bitwise(gpu, variant, span):
     hpz, hpo = zs.hparams(**HP), oracle.hparams(**HP)
     s = torch.cuda.current_stream()
     for t in RANGES[span]:
-        if variant == "q8grad":
+        if variant in ("q8grad", "packed_q8grad"):
             qs = [rng.integers(-127, 128, n).astype(np.int8) for _ in range(k)]
             ss = [(rng.random(nb) * 1e-4).astype(F32) for _ in range(k)]
-            zs.zs_shard_step_q8grad(dw, dm, dv, dp, [_dev(torch, q) for q in qs],
-                                    [_dev(torch, x) for x in ss], k, n, st, hpz, t, s)
+            dqs, dss = [_dev(torch, q) for q in qs], [_dev(torch, x) for x in ss]
+            if packed:
+                zs.zs_shard_step_packed_q8grad(dstate, dp, dqs, dss, k, n, st, hpz, t, s)
+            else:
+                zs.zs_shard_step_q8grad(dw, dm, dv, dp, dqs, dss, k, n, st, hpz, t, s)
             assert oracle.shard_step_q8grad(*ref, qs, ss, segs, hpo, t) == 0
             continue
         gs = [_bf16(rng.normal(0, 1e-3, n)) for _ in range(k)]
         dgs = [_dev(torch, g) for g in gs]
         if variant == "q8ag":
             zs.zs_shard_step_q8ag(dw, dm, dv, dp, dq, ds, dgs, k, n, st, hpz, t, s)
+        elif variant == "packed_q8ag":
+            zs.zs_shard_step_packed_q8ag(dstate, dp, dq, ds, dgs, k, n, st, hpz, t, s)
         elif variant == "bf16mv":
             zs.zs_shard_step_bf16mv(dw, dm, dv, dp, dgs, k, n, st, hpz, t, s)
         elif variant == "packed":
@@ -96,10 +102,10 @@ def test_unit_correction_kernels_are_bitwise(gpu, variant, span):
     mv = (lambda x: x.cpu().numpy().view(np.uint16)) if variant == "bf16mv" \
         else (lambda x: x.cpu().numpy())
     got = (dw.cpu().numpy(), mv(dm), mv(dv), dp.cpu().numpy().view(np.uint16))
-    if variant == "packed":
+    if packed:
         got = H.unpack_host(dstate.cpu().numpy(), n) + got[3:]
     want = tuple(ref)
-    if variant == "q8ag":
+    if variant in ("q8ag", "packed_q8ag"):
         got += (dq.cpu().numpy(), ds.cpu().numpy())
         want += oracle.q8_blocks(ref[3], zs.ZS_Q8_BLOCK)
     assert H.assert_parity(got, want, "%s %s" % (variant, span)), \
