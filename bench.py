@@ -166,19 +166,28 @@ def snapshot_packed(state, wins):
     return out
 
 
-def packed_leg(torch, w, pstate, master, m, v, param, grads, st, hp, stream, args,
-               bytes_per_step):
-    """zs_shard_step_packed on `pstate` (packed from the default step's state
-    before its warm-up), over the same steps with the same partials: GB/s per
-    launch (HIP events on the launch stream), its twin in its own launch, and
-    whether its final state and parameters equal the default step's bit for
-    bit on the parity windows."""
+# the packed-state form of each entry point that has one
+PACKED_FORM = {"base": "packed", "q8ag": "packed_q8ag", "q8grad": "packed_q8grad"}
+
+
+def packed_leg(torch, w, var, pstate, bufs, st, hp, stream, args, bytes_per_step):
+    """The packed-state form of entry point `var` on `pstate` (packed from the
+    separate-array step's state before its warm-up), over the same steps with
+    the same partials: GB/s per launch (HIP events on the launch stream), its
+    twin in its own launch, and whether its final state and outputs equal the
+    separate-array step's bit for bit on the parity windows."""
     import numpy as np
     import sharded_mixed_precision_shard_amd as zs
     n, k = w.n, w.k
+    pvar = PACKED_FORM[var]
+    param, q8, q8s = bufs["param"], bufs["q8"], bufs["q8s"]
     wins = parity_windows(w, n)
-    want = snapshot({"master": master, "m": m, "v": v, "param": param}, wins)
-    call = zs.ShardStep(pstate, None, None, param, grads, n, st, hp, variant="packed")
+    want = snapshot({name: bufs[name] for name in ("master", "m", "v", "param", "q8")}, wins)
+    if q8s is not None:
+        want["q8s"] = [block_slice(q8s, a, b).cpu().numpy().copy() for a, b in wins]
+    partials = bufs["qgrads"] if pvar == "packed_q8grad" else bufs["grads"]
+    call = zs.ShardStep(pstate, None, None, param, partials, n, st, hp, variant=pvar,
+                        param_q8=q8, param_q8_scale=q8s, qscales=bufs["qscales"])
     t = w.t0
     for _ in range(args.warmup):
         call(t, stream)
@@ -195,17 +204,20 @@ def packed_leg(torch, w, pstate, master, m, v, param, grads, st, hp, stream, arg
     ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
     avg = sum(ms) / len(ms)
     got = snapshot_packed(pstate, wins)
-    got.update(snapshot({"param": param}, wins))
+    got.update(snapshot({"param": param, "q8": q8}, wins))
+    if q8s is not None:
+        got["q8s"] = [block_slice(q8s, a, b).cpu().numpy().copy() for a, b in wins]
     same = all(np.array_equal(x.view(np.uint8), y.view(np.uint8))
                for name in want for x, y in zip(got[name], want[name]))
-    plan = zs.zs_launch_plan(k, n, "packed")
+    plan = zs.zs_launch_plan(k, n, pvar)
     achieved = bytes_per_step / (avg * 1e-3) / 1e9
-    out = {"entry_point": "zs_shard_step_packed", "launch": launch_key(plan),
+    out = {"entry_point": "zs_shard_step_" + pvar, "launch": launch_key(plan),
            "achieved": round(achieved, 2), "frac": round(achieved / HBM_PEAK_GBPS, 4),
            "avg_launch_ms": round(avg, 4), "steps": args.steps,
-           "bitwise_equal_to_zs_shard_step": bool(same)}
+           "separate_arrays_entry_point": "zs_shard_step" + ("" if var == "base" else "_" + var),
+           "bitwise_equal_to_separate_arrays": bool(same)}
     if not args.no_twin:
-        twin = Twin(torch, "packed", dict(master=pstate, param=param, grads=grads), k, n, plan)
+        twin = Twin(torch, pvar, dict(bufs, master=pstate, m=None, v=None), k, n, plan)
         if twin.ok:
             r = twin.rate("step", stream)
             out["twin_step_gbps"] = round(r, 1)
@@ -777,9 +789,10 @@ def main():
                          "occupancy cap) on one set of buffers instead of the timed run")
     ap.add_argument("--rounds", type=int, default=3, help="rounds of --sweep")
     ap.add_argument("--no-packed", action="store_true",
-                    help="skip the same-run measurement of zs_shard_step_packed (the same "
-                         "step on the state packed per 256-element block) beside the default "
-                         "zs_shard_step")
+                    help="skip the same-run measurement of the packed-state form "
+                         "(zs_shard_step_packed, _packed_q8ag, _packed_q8grad: the same step on "
+                         "the state packed per 256-element block) beside zs_shard_step, "
+                         "zs_shard_step_q8ag or zs_shard_step_q8grad")
     args = ap.parse_args()
     if args.steps is None:
         args.steps = 200 if args.config in ("tiny", "gpt2-small") else 10
@@ -966,7 +979,7 @@ def main():
     # the same step on the same state packed per 256-element block, timed after
     # the default step from the state as it stands now (same t, same partials)
     pstate, packed_skip = None, None
-    if var == "base" and cfg is None and not args.graph and not args.no_packed:
+    if var in PACKED_FORM and cfg is None and not args.graph and not args.no_packed:
         torch.cuda.empty_cache()
         need = 4 * zs.packed_floats(n) + (1 << 30)
         if torch.cuda.mem_get_info()[0] >= need:
@@ -1028,11 +1041,13 @@ def main():
 
     packed = None
     if pstate is not None:
-        packed = packed_leg(torch, w, pstate, master, m, v, param, grads, st, hp, stream, args,
-                            bytes_per_step)
+        packed = packed_leg(torch, w, var, pstate,
+                            dict(master=master, m=m, v=v, param=param, grads=grads, qgrads=qgrads,
+                                 qscales=qscales, q8=q8, q8s=q8s),
+                            st, hp, stream, args, bytes_per_step)
         log("packed state: %.1f GB/s per launch, %s of its twin, bitwise equal to the "
-            "default step: %s" % (packed["achieved"], packed.get("pct_of_twin"),
-                                  packed["bitwise_equal_to_zs_shard_step"]))
+            "separate-array step: %s" % (packed["achieved"], packed.get("pct_of_twin"),
+                                         packed["bitwise_equal_to_separate_arrays"]))
     elif packed_skip:
         packed = {"skipped": packed_skip}
 

@@ -477,7 +477,8 @@ class ShardStep:
     zs_shard_step_cfg when ``cfg`` is given as a dict of ZsLaunchCfg fields),
     "q8ag" (needs ``param_q8`` and ``param_q8_scale``), "q8grad" (``grads``
     are the int8 partials, ``qscales`` their block scales) or "bf16mv" (m and
-    v are bf16) or "packed" (``master`` is the packed state, m and v are None).
+    v are bf16) or "packed" (``master`` is the packed state, m and v are None),
+    and "packed_q8ag" / "packed_q8grad" (the int8 forms on the packed state).
     The tensors are referenced for the object's lifetime."""
 
     def __init__(self, master, m, v, param_bf16, grads, n, seg_table_, hparams_,

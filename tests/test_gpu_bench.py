@@ -57,10 +57,12 @@ def test_bench_line(extra):
     assert par["steps_replayed"] == 6  # one warm-up step and five timed ones
     assert par["within_tolerance"] and par["bitwise_equal"], par
     pk = out.get("packed_state")
-    if variant == "base" and extra == []:
-        # the same steps on the packed state, beside the default step
-        assert pk["entry_point"] == "zs_shard_step_packed" and pk["achieved"] > 0
-        assert pk["bitwise_equal_to_zs_shard_step"] is True and pk["pct_of_twin"] > 0
+    if extra in ([], ["--variant", "q8ag"], ["--variant", "q8grad"]):
+        # the same steps on the packed state, beside the separate-array step
+        pform = {"base": "packed", "q8ag": "packed_q8ag", "q8grad": "packed_q8grad"}[variant]
+        assert pk["entry_point"] == "zs_shard_step_" + pform and pk["achieved"] > 0
+        assert pk["separate_arrays_entry_point"] == want
+        assert pk["bitwise_equal_to_separate_arrays"] is True and pk["pct_of_twin"] > 0
     else:
         assert pk is None
 
