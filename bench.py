@@ -152,22 +152,36 @@ def snapshot(tensors, wins):
     return out
 
 
-def snapshot_packed(state, wins):
+def snapshot_packed(state, wins, mv16=False):
     """The windows' master, m and v read out of a packed state (block b of 256
-    elements: their master values, then m, then v), as snapshot() gives them."""
-    blocks = state.view(-1, 3, 256)
+    elements: their master values, then m, then v; with mv16 a block is 512
+    floats' room, 256 fp32 master values then 256 bf16 m and 256 bf16 v), as
+    snapshot() gives them."""
+    import numpy as np
+    blocks = state.view(-1, 512 if mv16 else 768)
+    cols = ((0, 256), (256, 384), (384, 512)) if mv16 else ((0, 256), (256, 512), (512, 768))
     out = {"master": [], "m": [], "v": []}
     for a, b in wins:
         b0, b1 = a // 256, (b - 1) // 256 + 1
         blk = blocks[b0:b1].cpu().numpy()
         lo, hi = a - b0 * 256, b - b0 * 256
         for j, name in enumerate(("master", "m", "v")):
-            out[name].append(blk[:, j, :].reshape(-1)[lo:hi].copy())
+            part = np.ascontiguousarray(blk[:, cols[j][0]:cols[j][1]])
+            if mv16 and j:
+                part = part.view(np.int16)  # as a bf16 array's snapshot reads
+            out[name].append(part.reshape(-1)[lo:hi].copy())
     return out
 
 
 # the packed-state form of each entry point that has one
-PACKED_FORM = {"base": "packed", "q8ag": "packed_q8ag", "q8grad": "packed_q8grad"}
+PACKED_FORM = {"base": "packed", "q8ag": "packed_q8ag", "q8grad": "packed_q8grad",
+               "bf16mv": "packed_bf16mv"}
+
+
+def packed_state_floats(var, n):
+    """Floats (or floats' room) of the packed state of entry point `var`."""
+    import sharded_mixed_precision_shard_amd as zs
+    return zs.packed_bf16mv_floats(n) if var.endswith("bf16mv") else zs.packed_floats(n)
 
 
 def packed_leg(torch, w, var, pstate, bufs, st, hp, stream, args, bytes_per_step):
@@ -203,7 +217,7 @@ def packed_leg(torch, w, var, pstate, bufs, st, hp, stream, args, bytes_per_step
     torch.cuda.synchronize()
     ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
     avg = sum(ms) / len(ms)
-    got = snapshot_packed(pstate, wins)
+    got = snapshot_packed(pstate, wins, mv16=pvar == "packed_bf16mv")
     got.update(snapshot({"param": param, "q8": q8}, wins))
     if q8s is not None:
         got["q8s"] = [block_slice(q8s, a, b).cpu().numpy().copy() for a, b in wins]
@@ -225,14 +239,15 @@ def packed_leg(torch, w, var, pstate, bufs, st, hp, stream, args, bytes_per_step
     return out
 
 
-def _fill_packed_master(state, master, n):
-    """Write fp32 master [n] into the master slots of a packed state (torch
+def _fill_packed_master(state, master, n, mv16=False):
+    """Write fp32 master [n] into the master slots of a packed state (the
+    first 256 floats of each block of 768, or of 512 with bf16 moments; torch
     copies into strided views; m, v and the padding keep what they hold)."""
-    blocks = state.view(-1, 3, 256)
+    blocks = state.view(-1, 512 if mv16 else 768)
     full = n // 256
-    blocks[:full, 0, :] = master[:full * 256].view(-1, 256)
+    blocks[:full, :256] = master[:full * 256].view(-1, 256)
     if n % 256:
-        blocks[full, 0, :n % 256] = master[full * 256:]
+        blocks[full, :n % 256] = master[full * 256:]
 
 
 def block_slice(t, a, b):
@@ -476,6 +491,7 @@ def twin_bytes(variant: str, k: int, n: int):
             "packed": ((12 + 2 * k) * n, 14 * n),
             "packed_q8ag": ((12 + 2 * k) * n, 15 * n + 4 * nb),
             "packed_q8grad": (12 * n + k * (n + 4 * nb), 14 * n),
+            "packed_bf16mv": ((8 + 2 * k) * n, 10 * n),
             "q8ag": ((12 + 2 * k) * n, 15 * n + 4 * nb),
             "q8grad": (12 * n + k * (n + 4 * nb), 14 * n),
             "bf16mv": ((8 + 2 * k) * n, 10 * n)}[variant]
@@ -491,7 +507,7 @@ class Twin:
     step's own buffers and in the step's own launch."""
     MODES = {"step": 0, "read": 1, "write": 2}
     LAYOUT = {"base": 0, "q8ag": 1, "q8grad": 2, "bf16mv": 4, "packed": 8, "packed_q8ag": 9,
-              "packed_q8grad": 10}
+              "packed_q8grad": 10, "packed_bf16mv": 12}
 
     def __init__(self, torch, variant, bufs, k, n, plan):
         import ctypes
@@ -762,11 +778,11 @@ def main():
     ap.add_argument("--config", default="70b")
     ap.add_argument("--variant", default="base",
                     choices=("base", "q8ag", "q8grad", "bf16mv", "packed", "packed_q8ag",
-                             "packed_q8grad", "offload"),
+                             "packed_q8grad", "packed_bf16mv", "offload"),
                     help="entry point: zs_shard_step (base), zs_shard_step_q8ag, "
                          "zs_shard_step_q8grad, zs_shard_step_bf16mv, zs_shard_step_packed "
                          "(master, m, v packed per 256-element block), zs_shard_step_packed_q8ag, "
-                         "zs_shard_step_packed_q8grad, or the host "
+                         "zs_shard_step_packed_q8grad, zs_shard_step_packed_bf16mv, or the host "
                          "(ZeRO-Offload) step zs_host_shard_step, which runs on the CPU "
                          "and needs no GPU")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -790,9 +806,10 @@ def main():
     ap.add_argument("--rounds", type=int, default=3, help="rounds of --sweep")
     ap.add_argument("--no-packed", action="store_true",
                     help="skip the same-run measurement of the packed-state form "
-                         "(zs_shard_step_packed, _packed_q8ag, _packed_q8grad: the same step on "
-                         "the state packed per 256-element block) beside zs_shard_step, "
-                         "zs_shard_step_q8ag or zs_shard_step_q8grad")
+                         "(zs_shard_step_packed, _packed_q8ag, _packed_q8grad, _packed_bf16mv: "
+                         "the same step on the state packed per 256-element block) beside "
+                         "zs_shard_step, zs_shard_step_q8ag, zs_shard_step_q8grad or "
+                         "zs_shard_step_bf16mv")
     args = ap.parse_args()
     if args.steps is None:
         args.steps = 200 if args.config in ("tiny", "gpt2-small") else 10
@@ -858,11 +875,13 @@ def main():
     q8grad_var = var in ("q8grad", "packed_q8grad")
     q8ag_var = var in ("q8ag", "packed_q8ag")
     # the oracle arithmetic the variant computes (the packed forms compute their plain form's)
-    arith = {"packed": "base", "packed_q8ag": "q8ag", "packed_q8grad": "q8grad"}.get(var, var)
+    arith = {"packed": "base", "packed_q8ag": "q8ag", "packed_q8grad": "q8grad",
+             "packed_bf16mv": "bf16mv"}.get(var, var)
+    mv16 = arith == "bf16mv"
     state = master = m = v = None
     if packed_var:
         # master, m and v in one array, per 256-element block
-        state = torch.empty(zs.packed_floats(n), dtype=torch.float32, device=dev)
+        state = torch.empty(packed_state_floats(var, n), dtype=torch.float32, device=dev)
     else:
         master = torch.empty(n, dtype=torch.float32, device=dev)
         m = torch.zeros(n, dtype=mv_dtype, device=dev)
@@ -899,7 +918,7 @@ def main():
         state.zero_()
         init = torch.empty(n, dtype=torch.float32, device=dev)
         synth.dev_master(w, init)
-        _fill_packed_master(state, init, n)
+        _fill_packed_master(state, init, n, mv16)
         del init
     else:
         synth.dev_master(w, master)
@@ -923,6 +942,8 @@ def main():
     elif var == "packed_q8grad":
         call = zs.ShardStep(state, None, None, param, qgrads, n, st, hp, variant=var,
                             qscales=qscales)
+    elif var == "packed_bf16mv":
+        call = zs.ShardStep(state, None, None, param, grads, n, st, hp, variant=var)
     else:
         call = zs.ShardStep(master, m, v, param, grads, n, st, hp, cfg=cfg)
 
@@ -966,7 +987,7 @@ def main():
     par = None
     if args.cpu_seconds > 0:
         wins = parity_windows(w, n)
-        before = snapshot_packed(state, wins) if packed_var else \
+        before = snapshot_packed(state, wins, mv16) if packed_var else \
             snapshot({"master": master, "m": m, "v": v}, wins)
         if q8grad_var:
             qg = [[q[a:b].cpu().numpy().copy() for a, b in wins] for q in qgrads]
@@ -981,10 +1002,12 @@ def main():
     pstate, packed_skip = None, None
     if var in PACKED_FORM and cfg is None and not args.graph and not args.no_packed:
         torch.cuda.empty_cache()
-        need = 4 * zs.packed_floats(n) + (1 << 30)
+        floats = packed_state_floats(var, n)
+        need = 4 * floats + (1 << 30)
         if torch.cuda.mem_get_info()[0] >= need:
-            pstate = torch.empty(zs.packed_floats(n), dtype=torch.float32, device=dev)
-            zs.zs_pack_state(master, m, v, pstate, n, stream)
+            pstate = torch.empty(floats, dtype=torch.float32, device=dev)
+            pack = zs.zs_pack_state_bf16mv if mv16 else zs.zs_pack_state
+            pack(master, m, v, pstate, n, stream)
         else:
             packed_skip = "needs %.1f GB more device memory" % (need / 1e9)
 
@@ -1031,7 +1054,7 @@ def main():
                                                               max(kernel_ms)))
     if par is not None:
         if packed_var:
-            after = snapshot_packed(state, wins)
+            after = snapshot_packed(state, wins, mv16)
             after.update(snapshot({"param": param, "q8": q8}, wins))
         else:
             after = snapshot({"master": master, "m": m, "v": v, "param": param, "q8": q8}, wins)
@@ -1106,7 +1129,9 @@ def main():
                     "packed_q8ag": "f32 master/m/v packed per 256-element block, bf16 partials "
                                    "and param, int8 param copy",
                     "packed_q8grad": "f32 master/m/v packed per 256-element block, int8 "
-                                     "partials, bf16 param"}[var],
+                                     "partials, bf16 param",
+                    "packed_bf16mv": "f32 master and bf16 m/v packed per 256-element block, "
+                                     "bf16 partials and param"}[var],
         "data": "synthetic (seeded SplitMix64 / Irwin-Hall draws; partials of the first "
                 "measured step kept resident across timed steps)",
         "config": {

@@ -108,9 +108,10 @@ typedef struct {
                               congestion on many physical placements of the arrays.
                               0 = default: none below 2^26 elements, a cap of 5
                               from 2^26 elements on, except for
-                              zs_shard_step_bf16mv below 2^32 elements or with
-                              k > 4 (no cap); from 2^32 elements with k <= 4 it
-                              takes two 256-element sub-windows per wavefront.
+                              zs_shard_step_bf16mv (and its packed form) below
+                              2^32 elements or with k > 4 (no cap); from 2^32
+                              elements with k <= 4 it takes two 256-element
+                              sub-windows per wavefront.
                               A cap whose LDS share exceeds the per-workgroup
                               limit returns ZS_ERR_INVALID_ARGUMENT. */
     int32_t block_order;  /* 0 = default, 1 = linear (workgroup b takes chunk b),
@@ -279,6 +280,31 @@ int zs_shard_step_packed_q8grad(float *state, uint16_t *param_bf16, const int8_t
                                 int64_t step, void *stream);
 
 /*
+ * zs_shard_step_bf16mv on packed state: the bf16-moment state of "Lecture 7:
+ * Parallelism I", section 8.4 (fp32 master weights, bf16 m and v) in one
+ * array, the rank's own to lay out as for zs_shard_step_packed.  Block b of
+ * 256 elements takes 2 KB: the fp32 master values of elements 256b .. 256b +
+ * 255, then their m and then their v as bf16.  In 16-bit units (state viewed
+ * as uint16_t, j = 0 .. 255):
+ *   state as fp32    [512 b + j]        = master[256 b + j]
+ *   state as uint16_t[1024 b + 512 + j] = m_bf16[256 b + j]
+ *   state as uint16_t[1024 b + 768 + j] = v_bf16[256 b + j]
+ * ZS_PACKED_BF16MV_FLOATS(n) floats in all (the last block's slots past n
+ * are padding the step neither reads nor writes).  The arithmetic and every
+ * output bit are zs_shard_step_bf16mv's.
+ *
+ *   state : DEVICE [ZS_PACKED_BF16MV_FLOATS(n) floats], read and updated in
+ *           place, 16-byte aligned
+ * Everything else as zs_shard_step_bf16mv.  HBM traffic: that of
+ * zs_shard_step_bf16mv.
+ */
+#define ZS_PACKED_BF16MV_FLOATS(n) (512 * (((int64_t)(n) + 255) / 256))
+int zs_shard_step_packed_bf16mv(float *state, uint16_t *param_bf16,
+                                const uint16_t *const *grads, int k, int64_t n,
+                                const zs_seg_table *seg_table, const zs_hparams *hparams,
+                                int64_t step, void *stream);
+
+/*
  * Convert, on `stream`, between separate master, m and v arrays (DEVICE fp32
  * [n] each) and the packed state of zs_shard_step_packed (DEVICE fp32
  * [ZS_PACKED_FLOATS(n)]).  zs_pack_state writes every slot of the state, the
@@ -293,6 +319,17 @@ int zs_pack_state(const float *master, const float *m, const float *v, float *st
                   void *stream);
 int zs_unpack_state(const float *state, float *master, float *m, float *v, int64_t n,
                     void *stream);
+
+/*
+ * The same conversions for the bf16-moment state: fp32 master [n] and bf16
+ * m_bf16, v_bf16 [n] (DEVICE) to and from the packed state of
+ * zs_shard_step_packed_bf16mv (DEVICE, ZS_PACKED_BF16MV_FLOATS(n) floats).
+ * Padding past n is written as zero bits.  Everything else as zs_pack_state.
+ */
+int zs_pack_state_bf16mv(const float *master, const uint16_t *m_bf16, const uint16_t *v_bf16,
+                         float *state, int64_t n, void *stream);
+int zs_unpack_state_bf16mv(const float *state, float *master, uint16_t *m_bf16, uint16_t *v_bf16,
+                           int64_t n, void *stream);
 
 /* Release what zs_init recorded.  Later calls return ZS_ERR_NOT_INITIALIZED
  * until zs_init is called again.  Always returns ZS_OK. */
@@ -323,6 +360,7 @@ int zs_launch_geometry(int k, int64_t n, const zs_launch_cfg *cfg, int64_t *work
 #define ZS_VARIANT_PACKED 16 /* zs_shard_step_packed */
 #define ZS_VARIANT_PACKED_Q8AG 17   /* zs_shard_step_packed_q8ag */
 #define ZS_VARIANT_PACKED_Q8GRAD 18 /* zs_shard_step_packed_q8grad */
+#define ZS_VARIANT_PACKED_BF16MV 20 /* zs_shard_step_packed_bf16mv */
 
 /* The launch a step call resolves its defaults to. */
 typedef struct {
@@ -335,8 +373,8 @@ typedef struct {
                                dropped at launch) */
     int32_t nontemporal;    /* 1 = streaming loads and stores, 0 = cached */
     int32_t window_quads;   /* 256-element sub-windows each wavefront takes per tile
-                               (1, or 2 for zs_shard_step_bf16mv on shards of at least
-                               2^32 elements with k <= 4) */
+                               (1, or 2 for zs_shard_step_bf16mv and its packed form on
+                               shards of at least 2^32 elements with k <= 4) */
 } zs_launch_info;
 
 /* The launch a call of entry point `variant` (ZS_VARIANT_*) over n elements

@@ -8,9 +8,10 @@ or as plain integer device addresses.  There is no CPU fallback: if
 Entry points keep the C names: :func:`zs_init`, :func:`zs_shard_step`,
 :func:`zs_shard_step_cfg`, :func:`zs_shard_step_q8ag`, :func:`zs_shard_step_q8grad`,
 :func:`zs_shard_step_bf16mv`, :func:`zs_shard_step_packed`,
-:func:`zs_shard_step_packed_q8ag`, :func:`zs_shard_step_packed_q8grad`, :func:`zs_pack_state`,
-:func:`zs_unpack_state`, :func:`zs_fini`, :func:`zs_status_string`,
-:func:`zs_last_device_error`, :func:`zs_algorithmic_bytes`,
+:func:`zs_shard_step_packed_q8ag`, :func:`zs_shard_step_packed_q8grad`,
+:func:`zs_shard_step_packed_bf16mv`, :func:`zs_pack_state`, :func:`zs_unpack_state`,
+:func:`zs_pack_state_bf16mv`, :func:`zs_unpack_state_bf16mv`, :func:`zs_fini`,
+:func:`zs_status_string`, :func:`zs_last_device_error`, :func:`zs_algorithmic_bytes`,
 :func:`zs_launch_geometry`, :func:`zs_launch_plan`.
 """
 from __future__ import annotations
@@ -36,13 +37,14 @@ ZS_ERR_DEVICE = 5
 ZS_ERR_ALIASING = 6
 
 ZS_VARIANT = {"base": 0, "q8ag": 1, "q8grad": 2, "bf16mv": 4, "packed": 16, "packed_q8ag": 17,
-              "packed_q8grad": 18}
+              "packed_q8grad": 18, "packed_bf16mv": 20}
 
 # Symbols declared in include/zs.h.
 EXPORTS = ("zs_init", "zs_shard_step", "zs_shard_step_cfg", "zs_shard_step_q8ag",
            "zs_shard_step_q8grad", "zs_shard_step_bf16mv", "zs_shard_step_packed",
            "zs_shard_step_packed_q8ag", "zs_shard_step_packed_q8grad",
-           "zs_pack_state", "zs_unpack_state", "zs_fini", "zs_status_string",
+           "zs_shard_step_packed_bf16mv", "zs_pack_state", "zs_unpack_state",
+           "zs_pack_state_bf16mv", "zs_unpack_state_bf16mv", "zs_fini", "zs_status_string",
            "zs_last_device_error", "zs_algorithmic_bytes", "zs_launch_geometry",
            "zs_launch_plan")
 
@@ -50,6 +52,12 @@ EXPORTS = ("zs_init", "zs_shard_step", "zs_shard_step_cfg", "zs_shard_step_q8ag"
 def packed_floats(n: int) -> int:
     """Floats of the packed optimizer state for n elements (ZS_PACKED_FLOATS)."""
     return 768 * ((int(n) + 255) // 256)
+
+
+def packed_bf16mv_floats(n: int) -> int:
+    """Floats' room of the packed bf16-moment state for n elements
+    (ZS_PACKED_BF16MV_FLOATS)."""
+    return 512 * ((int(n) + 255) // 256)
 
 
 class ZsHparams(ctypes.Structure):
@@ -123,6 +131,12 @@ def load_library():
     lib.zs_shard_step_packed_q8grad.argtypes = [P, P, P, P, ctypes.c_int, ctypes.c_int64, P, P,
                                                 ctypes.c_int64, P]
     lib.zs_shard_step_packed_q8grad.restype = ctypes.c_int
+    lib.zs_shard_step_packed_bf16mv.argtypes = lib.zs_shard_step_packed.argtypes
+    lib.zs_shard_step_packed_bf16mv.restype = ctypes.c_int
+    lib.zs_pack_state_bf16mv.argtypes = [P, P, P, P, ctypes.c_int64, P]
+    lib.zs_pack_state_bf16mv.restype = ctypes.c_int
+    lib.zs_unpack_state_bf16mv.argtypes = [P, P, P, P, ctypes.c_int64, P]
+    lib.zs_unpack_state_bf16mv.restype = ctypes.c_int
     lib.zs_pack_state.argtypes = [P, P, P, P, ctypes.c_int64, P]
     lib.zs_pack_state.restype = ctypes.c_int
     lib.zs_unpack_state.argtypes = [P, P, P, P, ctypes.c_int64, P]
@@ -262,8 +276,8 @@ def _check_k(k, arrays, name):
 
 
 def zs_launch_plan(k: int, n: int, variant: str = "base", cfg=None) -> dict:
-    """The launch a call of entry point ``variant`` ("base", "q8ag", "q8grad",
-    "bf16mv") would make: grid, chunk, chunk order, occupancy cap, cache
+    """The launch a call of entry point ``variant`` (a key of ZS_VARIANT:
+    "base", "q8ag", "q8grad", "bf16mv" or a packed form) would make: grid, chunk, chunk order, occupancy cap, cache
     policy and sub-windows per wavefront, as a dict of the zs_launch_info
     fields.  ``cfg`` (base only) is a dict of ZsLaunchCfg fields or None."""
     c = None
@@ -444,6 +458,24 @@ def zs_shard_step_packed_q8grad(state, param_bf16, qgrads, qscales, k, n, seg_ta
     return rc
 
 
+def zs_shard_step_packed_bf16mv(state, param_bf16, grads, k, n, seg_table_, hparams_, step,
+                                stream=None, check=True) -> int:
+    """zs_shard_step_bf16mv on the packed state (packed_bf16mv_floats(n)
+    floats: per 256-element block its fp32 master values, then bf16 m and v)."""
+    k = _check_k(k, grads, "grads")
+    nn = max(int(n), 0)
+    gp = _ptr_array(grads, 2 * nn, "grads")
+    st = seg_table_ if isinstance(seg_table_, ZsSegTable) else seg_table(seg_table_)
+    rc = load_library().zs_shard_step_packed_bf16mv(
+        ctypes.c_void_p(_dev(state, 4 * packed_bf16mv_floats(nn), "state")),
+        ctypes.c_void_p(_dev(param_bf16, 2 * nn, "param_bf16")), ctypes.cast(gp, ctypes.c_void_p),
+        int(k), int(n), ctypes.byref(st), ctypes.byref(hparams_), int(step),
+        ctypes.c_void_p(_stream_handle(stream)))
+    if check and rc != ZS_OK:
+        raise ZsError(rc, "zs_shard_step_packed_bf16mv")
+    return rc
+
+
 def zs_pack_state(master, m, v, state, n, stream=None, check=True) -> int:
     """Separate fp32 master, m, v [n] -> packed state [packed_floats(n)] (padding +0)."""
     nn = max(int(n), 0)
@@ -469,6 +501,34 @@ def zs_unpack_state(state, master, m, v, n, stream=None, check=True) -> int:
     return rc
 
 
+def zs_pack_state_bf16mv(master, m_bf16, v_bf16, state, n, stream=None, check=True) -> int:
+    """fp32 master, bf16 m, v [n] -> packed bf16-moment state (padding zero)."""
+    nn = max(int(n), 0)
+    rc = load_library().zs_pack_state_bf16mv(
+        ctypes.c_void_p(_dev(master, 4 * nn, "master")),
+        ctypes.c_void_p(_dev(m_bf16, 2 * nn, "m_bf16")),
+        ctypes.c_void_p(_dev(v_bf16, 2 * nn, "v_bf16")),
+        ctypes.c_void_p(_dev(state, 4 * packed_bf16mv_floats(nn), "state")), int(n),
+        ctypes.c_void_p(_stream_handle(stream)))
+    if check and rc != ZS_OK:
+        raise ZsError(rc, "zs_pack_state_bf16mv")
+    return rc
+
+
+def zs_unpack_state_bf16mv(state, master, m_bf16, v_bf16, n, stream=None, check=True) -> int:
+    """Packed bf16-moment state -> fp32 master, bf16 m, v [n]."""
+    nn = max(int(n), 0)
+    rc = load_library().zs_unpack_state_bf16mv(
+        ctypes.c_void_p(_dev(state, 4 * packed_bf16mv_floats(nn), "state")),
+        ctypes.c_void_p(_dev(master, 4 * nn, "master")),
+        ctypes.c_void_p(_dev(m_bf16, 2 * nn, "m_bf16")),
+        ctypes.c_void_p(_dev(v_bf16, 2 * nn, "v_bf16")), int(n),
+        ctypes.c_void_p(_stream_handle(stream)))
+    if check and rc != ZS_OK:
+        raise ZsError(rc, "zs_unpack_state_bf16mv")
+    return rc
+
+
 class ShardStep:
     """One rank's step with its buffers fixed: the arguments are checked and
     marshalled once, and each call passes only the step t and the stream to
@@ -478,7 +538,8 @@ class ShardStep:
     "q8ag" (needs ``param_q8`` and ``param_q8_scale``), "q8grad" (``grads``
     are the int8 partials, ``qscales`` their block scales) or "bf16mv" (m and
     v are bf16) or "packed" (``master`` is the packed state, m and v are None),
-    and "packed_q8ag" / "packed_q8grad" (the int8 forms on the packed state).
+    and "packed_q8ag" / "packed_q8grad" / "packed_bf16mv" (those forms on
+    their packed state).
     The tensors are referenced for the object's lifetime."""
 
     def __init__(self, master, m, v, param_bf16, grads, n, seg_table_, hparams_,
@@ -501,12 +562,13 @@ class ShardStep:
             head = [pm, pmm, pv, pp, ctypes.cast(qp, ctypes.c_void_p),
                     ctypes.cast(sp, ctypes.c_void_p)]
             fn = lib.zs_shard_step_q8grad
-        elif variant in ("packed", "packed_q8ag", "packed_q8grad"):
+        elif variant in ("packed", "packed_q8ag", "packed_q8grad", "packed_bf16mv"):
             if m is not None or v is not None:
                 raise ValueError("the packed step takes its m and v inside the state")
             st = seg_table_ if isinstance(seg_table_, ZsSegTable) else seg_table(seg_table_)
             hp = hparams_
-            head = [ctypes.c_void_p(_dev(master, 4 * packed_floats(nn), "state")),
+            floats = packed_bf16mv_floats(nn) if variant == "packed_bf16mv" else packed_floats(nn)
+            head = [ctypes.c_void_p(_dev(master, 4 * floats, "state")),
                     ctypes.c_void_p(_dev(param_bf16, 2 * nn, "param_bf16"))]
             if variant == "packed_q8grad":
                 if len(qscales or []) != k:
@@ -523,6 +585,8 @@ class ShardStep:
                     head += [ctypes.c_void_p(_dev(param_q8, nn, "param_q8")),
                              ctypes.c_void_p(_dev(param_q8_scale, 4 * nb, "param_q8_scale"))]
                     fn = lib.zs_shard_step_packed_q8ag
+                elif variant == "packed_bf16mv":
+                    fn = lib.zs_shard_step_packed_bf16mv
                 else:
                     fn = lib.zs_shard_step_packed
                 head.append(ctypes.cast(gp, ctypes.c_void_p))
@@ -570,7 +634,7 @@ def algorithmic_bytes(variant: str, k: int, n: int) -> int:
         return (26 + 2 * k) * n + n + 4 * nb
     if variant in ("q8grad", "packed_q8grad"):
         return (12 + k + 14) * n + 4 * k * nb
-    if variant == "bf16mv":
+    if variant in ("bf16mv", "packed_bf16mv"):
         return (18 + 2 * k) * n
     raise ValueError(variant)
 

@@ -95,7 +95,8 @@ int resolve_launch(int k, int64_t n, int variant, const zs_launch_cfg *cfg,
                    zs_launch_info *out, int *kernel_variant = nullptr) {
     if (k < 1 || k > ZS_MAX_K || n < 0 || n > INT64_MAX / 8) return ZS_ERR_INVALID_ARGUMENT;
     if (variant != 0 && variant != kOutQ8 && variant != kGradQ8 && variant != kMvBf16 &&
-        variant != kPacked && variant != (kPacked | kOutQ8) && variant != (kPacked | kGradQ8))
+        variant != kPacked && variant != (kPacked | kOutQ8) && variant != (kPacked | kGradQ8) &&
+        variant != (kPacked | kMvBf16))
         return ZS_ERR_INVALID_ARGUMENT;
     // Streaming (non-temporal) loads and stores by default: nothing is
     // reused, and on MI355X they measured 5-10 % faster than cached access.
@@ -112,13 +113,14 @@ int resolve_launch(int k, int64_t n, int variant, const zs_launch_cfg *cfg,
         groups_per_cu = cfg->groups_per_cu;
         block_order = cfg->block_order;
     }
-    const bool wide = variant == kMvBf16 && n >= kWideMinElems && k <= kWideMaxK;
+    const bool mv16 = (variant & kMvBf16) != 0;
+    const bool wide = mv16 && n >= kWideMinElems && k <= kWideMaxK;
     const int kv = wide ? (variant | kWide) : variant;
     int64_t chunk = 0, blocks = 0;
     if (n > 0) launch_geometry(kv, n, chunk_tiles, &chunk, &blocks);
     const bool xcd_order = block_order == 2 || (block_order == 0 && n >= kXcdOrderMinElems);
     // the default cap (negative: dropped where the device cannot hold it)
-    const int cap = (variant == kMvBf16 && !wide) ? 0 : kDefaultCap;
+    const int cap = (mv16 && !wide) ? 0 : kDefaultCap;
     if (groups_per_cu == 0 && n >= kXcdOrderMinElems && cap) groups_per_cu = -cap;
     out->workgroups = blocks;
     out->chunk_elements = chunk;
@@ -189,7 +191,9 @@ int validate_and_launch(const Request &r) {
     Span outs[6];
     int nouts = 0;
     if (r.variant & kPacked) {
-        outs[nouts++] = {r.master, 4 * packed_floats(n), 16};  // the packed state
+        // the packed state
+        const int64_t floats = (r.variant & kMvBf16) ? packed16_floats(n) : packed_floats(n);
+        outs[nouts++] = {r.master, 4 * floats, 16};
     } else {
         outs[nouts++] = {r.master, 4 * n, 16};
         outs[nouts++] = {r.m, mv_bytes, 16};
@@ -290,13 +294,15 @@ int validate_and_launch(const Request &r) {
 }
 
 // zs_pack_state / zs_unpack_state: validate, then one grid-stride launch.
-int layout_call(int dir, float *master, float *m, float *v, float *state, int64_t n,
+int layout_call(int dir, bool mv16, float *master, void *m, void *v, float *state, int64_t n,
                 void *stream) {
     if (!g_initialized) return ZS_ERR_NOT_INITIALIZED;
     if (n < 0 || n > INT64_MAX / 16) return ZS_ERR_INVALID_ARGUMENT;
     if (n == 0) return ZS_OK;
-    const Span spans[4] = {{master, 4 * n, 16}, {m, 4 * n, 16}, {v, 4 * n, 16},
-                           {state, 4 * packed_floats(n), 16}};
+    const int64_t mv_bytes = mv16 ? 2 * n : 4 * n;
+    const int64_t floats = mv16 ? packed16_floats(n) : packed_floats(n);
+    const Span spans[4] = {{master, 4 * n, 16}, {m, mv_bytes, 16}, {v, mv_bytes, 16},
+                           {state, 4 * floats, 16}};
     for (const Span &x : spans)
         if (!x.p) return ZS_ERR_INVALID_ARGUMENT;
     for (const Span &x : spans)
@@ -310,11 +316,14 @@ int layout_call(int dir, float *master, float *m, float *v, float *state, int64_
     if (e != hipSuccess) return device_error(e);
     if (dev < 0 || dev >= kMaxDevices || !g_dev[dev].ready) return ZS_ERR_NOT_INITIALIZED;
     // enough workgroups to fill the device; each loops over its share
-    const int64_t quads = packed_floats(n) / 3 / 4;
+    const int64_t quads = (n + kSub - 1) / kSub * (kSub / kQuad);
     const int64_t want = (quads + kThreads - 1) / kThreads;
     const int64_t fill = (int64_t)g_dev[dev].cus * 16;
-    e = launch_layout(dir, master, m, v, state, n, (int)(want < fill ? want : fill),
-                      (hipStream_t)stream);
+    const int blocks = (int)(want < fill ? want : fill);
+    e = mv16 ? launch_layout16(dir, master, (uint16_t *)m, (uint16_t *)v, state, n, blocks,
+                               (hipStream_t)stream)
+             : launch_layout(dir, master, (float *)m, (float *)v, state, n, blocks,
+                             (hipStream_t)stream);
     if (e != hipSuccess) return device_error(e);
     return ZS_OK;
 }
@@ -451,15 +460,39 @@ int zs_shard_step_packed_q8grad(float *state, uint16_t *param_bf16, const int8_t
     return validate_and_launch(r);
 }
 
+int zs_shard_step_packed_bf16mv(float *state, uint16_t *param_bf16,
+                                const uint16_t *const *grads, int k, int64_t n,
+                                const zs_seg_table *seg_table, const zs_hparams *hparams,
+                                int64_t step, void *stream) {
+    Request r = base_request(state, nullptr, nullptr, param_bf16, k, n, seg_table, hparams, step,
+                             stream);
+    r.grads = grads;
+    r.variant = kPacked | kMvBf16;
+    return validate_and_launch(r);
+}
+
 int zs_pack_state(const float *master, const float *m, const float *v, float *state, int64_t n,
                   void *stream) {
-    return layout_call(kLayoutPack, const_cast<float *>(master), const_cast<float *>(m),
+    return layout_call(kLayoutPack, false, const_cast<float *>(master), const_cast<float *>(m),
                        const_cast<float *>(v), state, n, stream);
 }
 
 int zs_unpack_state(const float *state, float *master, float *m, float *v, int64_t n,
                     void *stream) {
-    return layout_call(kLayoutUnpack, master, m, v, const_cast<float *>(state), n, stream);
+    return layout_call(kLayoutUnpack, false, master, m, v, const_cast<float *>(state), n, stream);
+}
+
+int zs_pack_state_bf16mv(const float *master, const uint16_t *m_bf16, const uint16_t *v_bf16,
+                         float *state, int64_t n, void *stream) {
+    return layout_call(kLayoutPack, true, const_cast<float *>(master),
+                       const_cast<uint16_t *>(m_bf16), const_cast<uint16_t *>(v_bf16), state, n,
+                       stream);
+}
+
+int zs_unpack_state_bf16mv(const float *state, float *master, uint16_t *m_bf16, uint16_t *v_bf16,
+                           int64_t n, void *stream) {
+    return layout_call(kLayoutUnpack, true, master, m_bf16, v_bf16, const_cast<float *>(state), n,
+                       stream);
 }
 
 int zs_fini(void) {

@@ -49,6 +49,7 @@ constexpr int kLayoutQ8Out = 1;   // + int8 parameter copy and one f32 scale per
 constexpr int kLayoutQ8Grad = 2;  // int8 partials with one f32 scale per block each
 constexpr int kLayoutBf16Mv = 4;  // bf16 m and v
 constexpr int kLayoutPacked = 8;  // master, m, v packed per 256-element block in one array
+                                  // (with kLayoutBf16Mv: fp32 master, then bf16 m and v)
 
 // Modes: 0 = the step's reads and writes, then
 constexpr int kModeRead = 1;   // its reads only
@@ -111,7 +112,13 @@ __global__ __launch_bounds__(kThreads) void twin_kernel(const TwinArgs a) {
 #pragma unroll
         for (int qd = 0; qd < kQ; ++qd) {
             qi[qd] = (wv0 + (int64_t)qd * kSub) / kQuad + lane;
-            if constexpr (kPk) {
+            if constexpr (kPk && kMv16) {
+                // 2 KB per block: 1 KB of fp32 quads, then 512 B each of bf16 m, v quads
+                const int64_t blk = (wv0 + (int64_t)qd * kSub) / kSub;
+                iw[qd] = blk * (2 * kWave) + lane;
+                im[qd] = blk * (4 * kWave) + 2 * kWave + lane;
+                iv[qd] = im[qd] + kWave;
+            } else if constexpr (kPk) {
                 iw[qd] = (wv0 + (int64_t)qd * kSub) / kSub * (3 * kWave) + lane;
                 im[qd] = iw[qd] + kWave;
                 iv[qd] = iw[qd] + 2 * kWave;
@@ -128,8 +135,8 @@ __global__ __launch_bounds__(kThreads) void twin_kernel(const TwinArgs a) {
             for (int qd = 0; qd < kQ; ++qd) {
                 st<f32x4>(a.master, iw[qd], z);
                 if constexpr (kMv16) {
-                    st<u32x2>(a.m, qi[qd], h);
-                    st<u32x2>(a.v, qi[qd], h);
+                    st<u32x2>(pm, im[qd], h);
+                    st<u32x2>(pv, iv[qd], h);
                 } else {
                     st<f32x4>(pm, im[qd], z);
                     st<f32x4>(pv, iv[qd], z);
@@ -152,8 +159,8 @@ __global__ __launch_bounds__(kThreads) void twin_kernel(const TwinArgs a) {
         for (int qd = 0; qd < kQ; ++qd) {
             w[qd] = ld<f32x4>(a.master, iw[qd]);
             if constexpr (kMv16) {
-                mh[qd] = ld<u32x2>(a.m, qi[qd]);
-                vh[qd] = ld<u32x2>(a.v, qi[qd]);
+                mh[qd] = ld<u32x2>(pm, im[qd]);
+                vh[qd] = ld<u32x2>(pv, iv[qd]);
             } else {
                 m[qd] = ld<f32x4>(pm, im[qd]);
                 v[qd] = ld<f32x4>(pv, iv[qd]);
@@ -209,8 +216,8 @@ __global__ __launch_bounds__(kThreads) void twin_kernel(const TwinArgs a) {
             if constexpr (kMv16) {
                 opaque(mh[qd]);
                 opaque(vh[qd]);
-                st<u32x2>(a.m, qi[qd], mh[qd]);
-                st<u32x2>(a.v, qi[qd], vh[qd]);
+                st<u32x2>(pm, im[qd], mh[qd]);
+                st<u32x2>(pv, iv[qd], vh[qd]);
             } else {
                 opaque(m[qd]);
                 opaque(v[qd]);
@@ -246,6 +253,7 @@ twin_fn pick_layout(int layout) {
         case kLayoutPacked: return twin_kernel<K, kLayoutPacked, Q>;
         case kLayoutPacked | kLayoutQ8Out: return twin_kernel<K, kLayoutPacked | kLayoutQ8Out, Q>;
         case kLayoutPacked | kLayoutQ8Grad: return twin_kernel<K, kLayoutPacked | kLayoutQ8Grad, Q>;
+        case kLayoutPacked | kLayoutBf16Mv: return twin_kernel<K, kLayoutPacked | kLayoutBf16Mv, Q>;
         default: return nullptr;
     }
 }
@@ -253,7 +261,7 @@ twin_fn pick_layout(int layout) {
 template <int K>
 twin_fn pick_quads(int layout, int quads) {
     // two sub-windows per wave only where the step has such a kernel
-    if (quads == 2) return layout == kLayoutBf16Mv ? pick_layout<K, 2>(layout) : nullptr;
+    if (quads == 2) return (layout & kLayoutBf16Mv) ? pick_layout<K, 2>(layout) : nullptr;
     return quads == 1 ? pick_layout<K, 1>(layout) : nullptr;
 }
 
@@ -316,9 +324,9 @@ int zs_ceiling_copy(const void *src, void *dst, int64_t bytes, void *stream) {
 //         reads only, 2 = its writes only (state overwritten).
 //   layout: 0 = zs_shard_step, 1 = zs_shard_step_q8ag, 2 = zs_shard_step_q8grad,
 //         4 = zs_shard_step_bf16mv, 8 = zs_shard_step_packed, 9 and 10 = its
-//         int8-payload and int8-partial forms (the streams and element sizes
-//         that entry point moves; with layouts 8-10 master is the packed state
-//         and m, v are unused).  grads holds k device pointers (int8 for layout 2,
+//         int8-payload and int8-partial forms, 12 = zs_shard_step_packed_bf16mv
+//         (the streams and element sizes that entry point moves; with layouts
+//         8-12 master is the packed state and m, v are unused).  grads holds k device pointers (int8 for layout 2,
 //         bf16 otherwise); qscales (layout 2) k device pointers to one f32
 //         per 256 elements; q8 and q8_scale (layout 1) the int8 copy and its
 //         scales.
@@ -326,7 +334,7 @@ int zs_ceiling_copy(const void *src, void *dst, int64_t bytes, void *stream) {
 //         sub-window of a wave: the twin covers whole windows only, so the host
 //         rounds a shard down to that).
 //   chunk, block_order (1 linear, 2 XCD-contiguous), groups_per_cu (0 =
-//         none), quads (sub-windows per wave: 1, or 2 with layout 4): the
+//         none), quads (sub-windows per wave: 1, or 2 with layouts 4 and 12): the
 //         launch zs_launch_plan reports for the step.
 // Every pointer is DEVICE memory sized for n elements, 16-byte aligned (the
 // scale arrays 4-byte).  Returns 0, -1 on a bad argument (nothing enqueued),
@@ -338,7 +346,8 @@ int zs_ceiling_twin(int mode, int layout, float *master, void *m, void *v, uint1
     if (mode < 0 || mode > 2 || k < 1 || k > kMaxK || n < 0 || !grads) return -1;
     if (layout != kLayoutBase && layout != kLayoutQ8Out && layout != kLayoutQ8Grad &&
         layout != kLayoutBf16Mv && layout != kLayoutPacked &&
-        layout != (kLayoutPacked | kLayoutQ8Out) && layout != (kLayoutPacked | kLayoutQ8Grad))
+        layout != (kLayoutPacked | kLayoutQ8Out) && layout != (kLayoutPacked | kLayoutQ8Grad) &&
+        layout != (kLayoutPacked | kLayoutBf16Mv))
         return -1;
     if (quads != 1 && quads != 2) return -1;
     const int64_t tile = (int64_t)kTile * quads;

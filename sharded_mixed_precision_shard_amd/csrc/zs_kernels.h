@@ -27,9 +27,10 @@ constexpr int kSub = kWave * kQuad;           // 256: one dense instruction per 
 //             of optimizer state plus weight instead of 16).
 //   kWide   - two sub-windows per wave instead of one (launch-time choice for
 //             the bf16-moment step on the largest shards, see quads_for);
-//   kPacked - master, m and v live in one fp32 array, packed per kSub-element
+//   kPacked - master, m and v live in one array, packed per kSub-element
 //             block: block b holds the master values of elements kSub*b ..
-//             kSub*b + kSub-1, then their m, then their v (ZS packed layout).
+//             kSub*b + kSub-1, then their m, then their v (ZS packed layout;
+//             with kMvBf16 the m and v runs are bf16, 2 KB per block).
 constexpr int kOutQ8 = 1;
 constexpr int kGradQ8 = 2;
 constexpr int kMvBf16 = 4;
@@ -42,6 +43,19 @@ __host__ __device__ constexpr int64_t packed_index(int64_t i) {
     return (i / kSub) * (3 * kSub) + i % kSub;
 }
 constexpr int64_t packed_floats(int64_t n) { return 3 * kSub * ((n + kSub - 1) / kSub); }
+
+// Packed layout with bf16 moments (kPacked | kMvBf16): block b holds kSub
+// fp32 master values, then their m and their v as bf16.  Float index of
+// element i's master value, 16-bit index of its m (its v is kSub further),
+// and floats the state holds for n elements.
+__host__ __device__ constexpr int64_t packed16_master(int64_t i) {
+    return (i / kSub) * (2 * kSub) + i % kSub;
+}
+__host__ __device__ constexpr int64_t packed16_m(int64_t i) {
+    return (i / kSub) * (4 * kSub) + 2 * kSub + i % kSub;
+}
+constexpr int64_t packed16_floats(int64_t n) { return 2 * kSub * ((n + kSub - 1) / kSub); }
+static_assert(packed16_m(kSub) == 2 * packed16_master(kSub) + 2 * kSub, "bf16 runs follow master");
 
 // Sub-windows (quads per lane) a wave handles per tile.  Measured on MI355X
 // with the per-wavefront segment lookup: one quad per lane, i.e. the fewest
@@ -61,7 +75,7 @@ constexpr int tile_for(int variant) { return (kThreads / kWave) * quads_for(vari
 static_assert(tile_for(0) == 1024 && tile_for(kMvBf16 | kWide) == 2048, "tile sizes");
 
 struct StepArgs {
-    float *master;   // fp32 [n], or the packed state (kPacked)
+    float *master;   // fp32 [n], or the packed state (kPacked; bf16 moments inside with kMvBf16)
     void *m;         // fp32 [n], or bf16 [n] in the bf16-moment variant; unused with kPacked
     void *v;
     uint16_t *param;
@@ -95,12 +109,16 @@ constexpr int kLayoutPack = 0;
 constexpr int kLayoutUnpack = 1;
 hipError_t launch_layout(int dir, float *master, float *m, float *v, float *state, int64_t n,
                          int blocks, hipStream_t stream);
+// The same between fp32 master, bf16 m and v [n] and the packed state with
+// bf16 moments (packed16_floats(n) floats).
+hipError_t launch_layout16(int dir, float *master, uint16_t *m, uint16_t *v, float *state,
+                           int64_t n, int blocks, hipStream_t stream);
 
 // Most partials the wide (kWide) kernels are built for.
 constexpr int kWideMaxK = 4;
 
 // The kernel for k partials, a variant (0 or one of the bits above; kWide
-// only with kMvBf16 and k <= kWideMaxK),
+// only with kMvBf16 and k <= kWideMaxK; kPacked only streaming),
 // streaming (nt = 1) or cached (nt = 0) access and the bias corrections that
 // are exactly 1.0f (unit_bc bit 0: bc1, bit 1: bc2; a streaming kernel then
 // leaves out that division); nullptr if there is none.

@@ -425,7 +425,14 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
 #pragma unroll
             for (int qd = 0; qd < kQuads; ++qd) {
                 const int64_t qi = e[qd] / kQuad;
-                if constexpr (V & kPacked) {
+                if constexpr ((V & kPacked) && (V & kMvBf16)) {
+                    // one 2 KB run per wave: master, then bf16 m and v
+                    const u32x2 *p16 = reinterpret_cast<const u32x2 *>(a.master);
+                    const int64_t qm = packed16_m(e[qd]) / kQuad;
+                    wv[qd] = load<NT>(pw + packed16_master(e[qd]) / kQuad);
+                    mv[qd] = bf16x4_to_f32x4(load<NT>(p16 + qm));
+                    vv[qd] = bf16x4_to_f32x4(load<NT>(p16 + qm + kWave));
+                } else if constexpr (V & kPacked) {
                     // one 3 KB run per wave: master, m, v of the sub-window
                     const int64_t qs = packed_index(e[qd]) / kQuad;
                     wv[qd] = load<NT>(pw + qs);
@@ -450,7 +457,13 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
                 u32x2 pq;
                 quad_update<K, V, NT, (U & 1) != 0, (U & 2) != 0>(
                     wv[qd], mv[qd], vv[qd], gq[qd], (mask >> (kQuad * qd)) & 0xfu, a, pq);
-                if constexpr (V & kPacked) {
+                if constexpr ((V & kPacked) && (V & kMvBf16)) {
+                    u32x2 *p16 = reinterpret_cast<u32x2 *>(a.master);
+                    const int64_t qm = packed16_m(e[qd]) / kQuad;
+                    store<NT>(pw + packed16_master(e[qd]) / kQuad, wv[qd]);
+                    store<NT>(p16 + qm, f32x4_to_bf16x4(mv[qd]));
+                    store<NT>(p16 + qm + kWave, f32x4_to_bf16x4(vv[qd]));
+                } else if constexpr (V & kPacked) {
                     const int64_t qs = packed_index(e[qd]) / kQuad;
                     store<NT>(pw + qs, wv[qd]);
                     store<NT>(pw + qs + kWave, mv[qd]);
@@ -486,7 +499,13 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
                 valid |= 1u << q;
                 const float g = scalar_grad<K, V>(a, i);
                 float wv, mvv, vvv;
-                if constexpr (V & kPacked) {
+                if constexpr ((V & kPacked) && (V & kMvBf16)) {
+                    const uint16_t *s16 = reinterpret_cast<const uint16_t *>(a.master);
+                    const int64_t pm = packed16_m(i);
+                    wv = a.master[packed16_master(i)];
+                    mvv = __uint_as_float((uint32_t)s16[pm] << 16);
+                    vvv = __uint_as_float((uint32_t)s16[pm + kSub] << 16);
+                } else if constexpr (V & kPacked) {
                     const int64_t ps = packed_index(i);
                     wv = a.master[ps];
                     mvv = a.master[ps + kSub];
@@ -501,7 +520,13 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
                     vvv = reinterpret_cast<const float *>(a.v)[i];
                 }
                 adamw<(U & 1) != 0, (U & 2) != 0>(wv, mvv, vvv, g, (mask >> q) & 1u, a);
-                if constexpr (V & kPacked) {
+                if constexpr ((V & kPacked) && (V & kMvBf16)) {
+                    uint16_t *s16 = reinterpret_cast<uint16_t *>(a.master);
+                    const int64_t pm = packed16_m(i);
+                    a.master[packed16_master(i)] = wv;
+                    s16[pm] = (uint16_t)to_bf16(mvv);
+                    s16[pm + kSub] = (uint16_t)to_bf16(vvv);
+                } else if constexpr (V & kPacked) {
                     const int64_t ps = packed_index(i);
                     a.master[ps] = wv;
                     a.master[ps + kSub] = mvv;
@@ -578,7 +603,56 @@ __global__ __launch_bounds__(kThreads) void layout_kernel(int dir, float *master
     }
 }
 
+// The same between fp32 master, bf16 m and v and the packed state with bf16
+// moments (packed16 layout): per quad, one 16-byte and two 8-byte moves.
+__global__ __launch_bounds__(kThreads) void layout16_kernel(int dir, float *master, uint16_t *m,
+                                                            uint16_t *v, float *state,
+                                                            int64_t n) {
+    const int64_t nq = packed16_floats(n) / 2 / kQuad;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    f32x4 *const st4 = reinterpret_cast<f32x4 *>(state);
+    u32x2 *const st2 = reinterpret_cast<u32x2 *>(state);
+    uint16_t *const s16 = reinterpret_cast<uint16_t *>(state);
+    for (int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x; q < nq; q += stride) {
+        const int64_t i = q * kQuad;
+        const int64_t sw = packed16_master(i) / kQuad;
+        const int64_t sm = packed16_m(i) / kQuad;
+        if (i + kQuad <= n) {
+            if (dir == kLayoutPack) {
+                st4[sw] = reinterpret_cast<const f32x4 *>(master)[q];
+                st2[sm] = reinterpret_cast<const u32x2 *>(m)[q];
+                st2[sm + kWave] = reinterpret_cast<const u32x2 *>(v)[q];
+            } else {
+                reinterpret_cast<f32x4 *>(master)[q] = st4[sw];
+                reinterpret_cast<u32x2 *>(m)[q] = st2[sm];
+                reinterpret_cast<u32x2 *>(v)[q] = st2[sm + kWave];
+            }
+            continue;
+        }
+        for (int j = 0; j < kQuad; ++j) {
+            const int64_t e = i + j;
+            const int64_t pw = packed16_master(e), pm = packed16_m(e);
+            if (dir == kLayoutPack) {
+                state[pw] = e < n ? master[e] : 0.0f;
+                s16[pm] = e < n ? m[e] : (uint16_t)0;
+                s16[pm + kSub] = e < n ? v[e] : (uint16_t)0;
+            } else if (e < n) {
+                master[e] = state[pw];
+                m[e] = s16[pm];
+                v[e] = s16[pm + kSub];
+            }
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_layout16(int dir, float *master, uint16_t *m, uint16_t *v, float *state,
+                           int64_t n, int blocks, hipStream_t stream) {
+    hipLaunchKernelGGL(layout16_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, dir,
+                       master, m, v, state, n);
+    return hipGetLastError();
+}
 
 hipError_t launch_layout(int dir, float *master, float *m, float *v, float *state, int64_t n,
                          int blocks, hipStream_t stream) {
@@ -606,8 +680,13 @@ kernel_fn pick_variant(int variant, int nt, int unit) {
         case kPacked: return nt ? pick_unit<K, kPacked>(unit) : nullptr;
         case kPacked | kOutQ8: return nt ? pick_unit<K, kPacked | kOutQ8>(unit) : nullptr;
         case kPacked | kGradQ8: return nt ? pick_unit<K, kPacked | kGradQ8>(unit) : nullptr;
+        case kPacked | kMvBf16: return nt ? pick_unit<K, kPacked | kMvBf16>(unit) : nullptr;
         case kMvBf16 | kWide:
             if constexpr (K <= kWideMaxK) return pick_unit<K, kMvBf16 | kWide>(unit);
+            return nullptr;
+        case kPacked | kMvBf16 | kWide:
+            if constexpr (K <= kWideMaxK)
+                return nt ? pick_unit<K, kPacked | kMvBf16 | kWide>(unit) : nullptr;
             return nullptr;
         default: return nullptr;
     }

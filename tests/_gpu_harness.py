@@ -22,7 +22,8 @@ def torch():
     return _t
 
 
-VARIANTS = ("base", "q8ag", "q8grad", "bf16mv", "packed", "packed_q8ag", "packed_q8grad")
+VARIANTS = ("base", "q8ag", "q8grad", "bf16mv", "packed", "packed_q8ag", "packed_q8grad",
+            "packed_bf16mv")
 
 
 def pack_host(w, m, v):
@@ -45,12 +46,39 @@ def unpack_host(state, n):
     return tuple(blk[:, j, :].reshape(-1)[:n].copy() for j in range(3))
 
 
+def pack16_host(w, m16, v16):
+    """Packed bf16-moment state on the host, by byte slices: block b is 2048
+    bytes, the fp32 master values of elements 256b .. 256b + 255 (1024
+    bytes), then their bf16 m (512 bytes), then their bf16 v; zero bytes past
+    n.  Returned as float32 (the state's declared type)."""
+    n = w.size
+    nb = -(-n // 256)
+    out = np.zeros((nb, 2048), np.uint8)
+    for x, dt, a, z in ((w, np.float32, 0, 1024), (m16, np.uint16, 1024, 1536),
+                        (v16, np.uint16, 1536, 2048)):
+        pad = np.zeros(nb * 256, dt)
+        pad[:n] = x
+        out[:, a:z] = pad.view(np.uint8).reshape(nb, z - a)
+    return out.reshape(-1).view(np.float32)
+
+
+def unpack16_host(state, n):
+    """(master fp32, m bf16 bits, v bf16 bits) [n] from a packed bf16-moment
+    state (the inverse of pack16_host)."""
+    blk = np.ascontiguousarray(state).view(np.uint8).reshape(-1, 2048)
+    w = np.ascontiguousarray(blk[:, :1024]).reshape(-1).view(np.float32)[:n].copy()
+    m = np.ascontiguousarray(blk[:, 1024:1536]).reshape(-1).view(np.uint16)[:n].copy()
+    v = np.ascontiguousarray(blk[:, 1536:]).reshape(-1).view(np.uint16)[:n].copy()
+    return w, m, v
+
+
 class DeviceShard:
     """Device buffers of one rank's shard for a synth Workload, for one of the
     entry points: base (zs_shard_step), q8ag (also the int8 parameter copy),
-    q8grad (int8 partials), bf16mv (bf16 moments) or packed (master, m and v
-    in one array, per 256-element block; packed and read back here with torch
-    views, not with the library's conversion calls)."""
+    q8grad (int8 partials), bf16mv (bf16 moments), packed (master, m and v
+    in one array, per 256-element block) or packed_bf16mv (the same with bf16
+    moments); packed states are filled and read back here with torch views,
+    not with the library's conversion calls."""
 
     def __init__(self, w: synth.Workload, variant="base", device="cuda:0"):
         t = torch()
@@ -61,15 +89,19 @@ class DeviceShard:
         dev = t.device(device)
         mv_dtype = t.int16 if variant == "bf16mv" else t.float32
         self.param = t.zeros(n, dtype=t.int16, device=dev)
-        if variant == "packed":
-            self.state = t.zeros(zs.packed_floats(n), dtype=t.float32, device=dev)
+        if variant in ("packed", "packed_bf16mv"):
+            # a block is 768 floats (master, m, v), or 512 floats' room
+            # (256 fp32 master values, then 256 bf16 m and 256 bf16 v)
+            mv16 = variant == "packed_bf16mv"
+            floats = zs.packed_bf16mv_floats(n) if mv16 else zs.packed_floats(n)
+            self.state = t.zeros(floats, dtype=t.float32, device=dev)
             master = t.empty(n, dtype=t.float32, device=dev)
             synth.dev_master(w, master)
-            blocks = self.state.view(-1, 3, 256)
+            blocks = self.state.view(-1, 512 if mv16 else 768)
             full = n // 256
-            blocks[:full, 0, :] = master[:full * 256].view(-1, 256)
+            blocks[:full, :256] = master[:full * 256].view(-1, 256)
             if n % 256:
-                blocks[full, 0, :n % 256] = master[full * 256:]
+                blocks[full, :n % 256] = master[full * 256:]
             del master
             self.master = self.m = self.v = None
         else:
@@ -86,7 +118,7 @@ class DeviceShard:
             self.q8 = t.zeros(n, dtype=t.int8, device=dev)
             self.q8s = t.zeros(nb, dtype=t.float32, device=dev)
         self.table = segment_tensor(w.shard.segments, dev)
-        if variant != "packed":
+        if self.master is not None:
             synth.dev_master(w, self.master)
 
     def fill_grads(self, step):
@@ -110,6 +142,9 @@ class DeviceShard:
         elif self.variant == "packed":
             zs.zs_shard_step_packed(self.state, self.param, self.grads, w.k, w.n, st, hp, t_step,
                                     s)
+        elif self.variant == "packed_bf16mv":
+            zs.zs_shard_step_packed_bf16mv(self.state, self.param, self.grads, w.k, w.n, st, hp,
+                                           t_step, s)
         elif self.variant == "bf16mv":
             zs.zs_shard_step_bf16mv(self.master, self.m, self.v, self.param, self.grads, w.k,
                                     w.n, st, hp, t_step, s)
@@ -128,6 +163,14 @@ class DeviceShard:
             a, z = lo - b0 * 256, hi - b0 * 256
             return (blk[:, 0, :].reshape(-1)[a:z].copy(), blk[:, 1, :].reshape(-1)[a:z].copy(),
                     blk[:, 2, :].reshape(-1)[a:z].copy(),
+                    self.param[lo:hi].cpu().numpy().view(np.uint16))
+        if self.variant == "packed_bf16mv":
+            b0, b1 = lo // 256, (hi - 1) // 256 + 1
+            blk = self.state.view(-1, 512)[b0:b1].cpu().numpy()
+            a, z = lo - b0 * 256, hi - b0 * 256
+            part = lambda c0, c1: np.ascontiguousarray(blk[:, c0:c1]).view(np.uint16)  # noqa
+            return (blk[:, :256].reshape(-1)[a:z].copy(), part(256, 384).reshape(-1)[a:z].copy(),
+                    part(384, 512).reshape(-1)[a:z].copy(),
                     self.param[lo:hi].cpu().numpy().view(np.uint16))
         mv = (lambda x: x[lo:hi].cpu().numpy().view(np.uint16)) if self.variant == "bf16mv" \
             else (lambda x: x[lo:hi].cpu().numpy())

@@ -142,6 +142,10 @@ def test_launch_key_follows_the_resolved_launch():
     assert zs.zs_launch_plan(2, n70, "packed") == p70  # the packed step launches as the step
     assert zs.zs_launch_plan(2, n70, "packed_q8ag") == q8
     assert zs.zs_launch_plan(2, n70, "packed_q8grad") == zs.zs_launch_plan(2, n70, "q8grad")
+    assert zs.zs_launch_plan(2, n70, "packed_bf16mv") == mv
+    for nn in ((1 << 32) - 1, 1 << 32, 10 ** 8, 5000):
+        for kk in (2, 8):
+            assert zs.zs_launch_plan(kk, nn, "packed_bf16mv") == zs.zs_launch_plan(kk, nn, "bf16mv")
     assert zs.zs_launch_plan(2, (1 << 32) - 1, "bf16mv")["groups_per_cu"] == 0
     assert zs.zs_launch_plan(2, 1 << 32, "bf16mv")["groups_per_cu"] == 5
     assert bench.launch_key(mv).endswith(",quads=2") and "quads" not in bench.launch_key(p70)
@@ -194,7 +198,10 @@ def test_twin_rejects_bad_arguments_before_any_device_call():
     assert call_mv(8, None, None) == 0 and call(layout=8, n=0) == 0
     assert call_mv(0, None, None) == -1 and call_mv(4, P(4096), None) == -1
     assert call(layout=8, quads=2, chunk=2048) == -1  # one sub-window per wave only
-    assert call(layout=12) == -1
+    assert call(layout=13) == -1 and call(layout=16) == -1
+    # the packed bf16-moment layout (12) takes one or two sub-windows per wave
+    assert call_mv(12, None, None) == 0 and call(layout=12, quads=2, chunk=2048, n=0) == 0
+    assert call(layout=12, quads=2, chunk=1024) == -1
 
 
 def test_parity_windows_cover_ends_and_boundaries():

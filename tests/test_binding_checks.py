@@ -210,3 +210,22 @@ def test_packed_entry_points_check_their_buffers():
         zs.zs_shard_step_packed_q8ag(FakeGpuTensor(4 * N), FakeGpuTensor(2 * N),
                                      FakeGpuTensor(N), FakeGpuTensor(16), g, 2, N, st, HP, 1)
     assert zs.ZS_VARIANT["packed"] == 16
+    # the bf16-moment state: 2 KB per 256-element block
+    nf16 = zs.packed_bf16mv_floats(N)
+    assert nf16 == 512 * 4 and zs.ZS_VARIANT["packed_bf16mv"] == 20
+    assert zs.algorithmic_bytes("packed_bf16mv", 2, N) == zs.algorithmic_bytes("bf16mv", 2, N)
+    with pytest.raises(ValueError, match="state holds"):
+        zs.zs_shard_step_packed_bf16mv(FakeGpuTensor(4 * nf16 - 16), FakeGpuTensor(2 * N), g, 2,
+                                       N, st, HP, 1)
+    with pytest.raises(ValueError, match="m_bf16 holds"):
+        zs.zs_pack_state_bf16mv(FakeGpuTensor(4 * N), FakeGpuTensor(2 * N - 2),
+                                FakeGpuTensor(2 * N), FakeGpuTensor(4 * nf16), N)
+    with pytest.raises(ValueError, match="state holds"):
+        zs.zs_unpack_state_bf16mv(FakeGpuTensor(4 * nf16 - 4), FakeGpuTensor(4 * N),
+                                  FakeGpuTensor(2 * N), FakeGpuTensor(2 * N), N)
+    with pytest.raises(ValueError, match="inside the state"):
+        zs.ShardStep(FakeGpuTensor(4 * nf16), None, FakeGpuTensor(2 * N), FakeGpuTensor(2 * N),
+                     g, N, st, HP, variant="packed_bf16mv")
+    with pytest.raises(ValueError, match="state holds"):
+        zs.ShardStep(FakeGpuTensor(4 * nf16 - 4), None, None, FakeGpuTensor(2 * N), g, N, st,
+                     HP, variant="packed_bf16mv")

@@ -26,10 +26,10 @@ def _bench(*args):
 @pytest.mark.parametrize("extra", [[], ["--graph"], ["--variant", "q8ag"],
                                    ["--variant", "q8grad"], ["--variant", "bf16mv"],
                                    ["--variant", "packed"], ["--variant", "packed_q8ag"],
-                                   ["--variant", "packed_q8grad"],
+                                   ["--variant", "packed_q8grad"], ["--variant", "packed_bf16mv"],
                                    ["--block-order", "2", "--groups-per-cu", "4"]],
                          ids=["base", "graph", "q8ag", "q8grad", "bf16mv", "packed", "packed_q8ag",
-                              "packed_q8grad", "cfg"])
+                              "packed_q8grad", "packed_bf16mv", "cfg"])
 def test_bench_line(extra):
     out = _bench(*extra)
     assert out["n_gpus"] == 1 and out["steps"] == 5 and out["warmup"] == 1
@@ -57,9 +57,10 @@ def test_bench_line(extra):
     assert par["steps_replayed"] == 6  # one warm-up step and five timed ones
     assert par["within_tolerance"] and par["bitwise_equal"], par
     pk = out.get("packed_state")
-    if extra in ([], ["--variant", "q8ag"], ["--variant", "q8grad"]):
+    if extra in ([], ["--variant", "q8ag"], ["--variant", "q8grad"], ["--variant", "bf16mv"]):
         # the same steps on the packed state, beside the separate-array step
-        pform = {"base": "packed", "q8ag": "packed_q8ag", "q8grad": "packed_q8grad"}[variant]
+        pform = {"base": "packed", "q8ag": "packed_q8ag", "q8grad": "packed_q8grad",
+                 "bf16mv": "packed_bf16mv"}[variant]
         assert pk["entry_point"] == "zs_shard_step_" + pform and pk["achieved"] > 0
         assert pk["separate_arrays_entry_point"] == want
         assert pk["bitwise_equal_to_separate_arrays"] is True and pk["pct_of_twin"] > 0
@@ -89,7 +90,8 @@ def test_streaming_copy_of_the_ceiling_library():
 
 
 @pytest.mark.parametrize("variant", ["base", "q8ag", "q8grad", "bf16mv", "bf16mv-wide",
-                                     "packed", "packed_q8ag", "packed_q8grad"])
+                                     "packed", "packed_q8ag", "packed_q8grad", "packed_bf16mv",
+                                     "packed_bf16mv-wide"])
 def test_twin_moves_the_step_traffic_without_changing_the_state(variant):
     """The twin ceiling on a step's buffers: the whole-traffic mode writes the
     state back bit for bit, the read-only mode changes nothing, the
@@ -99,8 +101,8 @@ def test_twin_moves_the_step_traffic_without_changing_the_state(variant):
     import bench
     import sharded_mixed_precision_shard_amd as zs
     torch.cuda.set_device(0)
-    wide = variant == "bf16mv-wide"
-    variant = "bf16mv" if wide else variant
+    wide = variant.endswith("-wide")
+    variant = variant[:-len("-wide")] if wide else variant
     k, n = 3, 1 << 16
     nb = n // 256
     g = torch.Generator(device="cuda").manual_seed(5)
@@ -108,8 +110,9 @@ def test_twin_moves_the_step_traffic_without_changing_the_state(variant):
                                    dtype=torch.int32).to(dt)
     mvt = torch.int16 if variant == "bf16mv" else torch.float32
     packed = variant.startswith("packed")
-    bufs = dict(master=torch.randn(zs.packed_floats(n) if packed else n, device="cuda",
-                                   generator=g),
+    mv16 = variant.endswith("bf16mv")
+    floats = (zs.packed_bf16mv_floats(n) if mv16 else zs.packed_floats(n)) if packed else n
+    bufs = dict(master=torch.randn(floats, device="cuda", generator=g),
                 m=None if packed else rnd(mvt), v=None if packed else rnd(mvt),
                 param=torch.zeros(n, dtype=torch.int16, device="cuda"),
                 q8=torch.zeros(n, dtype=torch.int8, device="cuda")
@@ -138,7 +141,13 @@ def test_twin_moves_the_step_traffic_without_changing_the_state(variant):
     twin.launch("write", s)
     torch.cuda.synchronize()
     pattern = torch.tensor([1.0, 2.0, 3.0, 4.0], device="cuda").repeat(bufs["master"].numel() // 4)
-    assert torch.equal(bufs["master"], pattern)  # packed: master, m and v slots alike
+    if packed and mv16:
+        # per 2 KB block: 256 fp32 master values, then bf16 m and v slots of 1.0 (0x3f80)
+        blk = pattern.view(-1, 512).clone()
+        blk[:, 256:] = torch.tensor([0x3f803f80], dtype=torch.int32, device="cuda").view(
+            torch.float32)
+        pattern = blk.view(-1)
+    assert torch.equal(bufs["master"].view(torch.int32), pattern.view(torch.int32))
 
 
 def test_launch_sweep_prints_every_configuration():

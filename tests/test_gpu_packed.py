@@ -1,8 +1,10 @@
-"""The packed-state step (zs_shard_step_packed) and the layout conversions
-(zs_pack_state, zs_unpack_state) through the C ABI.  The packed layout is
-built and read back here with numpy reshapes of (blocks, 3, 256), written
-independently of the library's conversion kernels; the step must equal the
-oracle, and zs_shard_step on the same inputs, bit for bit."""
+"""The packed-state steps (zs_shard_step_packed and its int8 and bf16-moment
+forms) and the layout conversions (zs_pack_state, zs_unpack_state and their
+bf16-moment forms) through the C ABI.  The packed layouts are built and read
+back here with numpy reshapes of (blocks, 3, 256) and byte slices of 2 KB
+blocks, written independently of the library's conversion kernels; each step
+must equal the oracle, and its separate-array entry point on the same inputs,
+bit for bit."""
 import numpy as np
 import pytest
 
@@ -356,3 +358,166 @@ def test_prepared_packed_q8_calls_match_the_plain_calls(gpu, variant):
     assert torch.equal(a.view(torch.int32), b.view(torch.int32)) and torch.equal(pa, pb)
     for x, y in extra:
         assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+
+
+# ---- the bf16-moment state packed per block (zs_shard_step_packed_bf16mv)
+
+pack16 = H.pack16_host
+unpack16 = H.unpack16_host
+
+
+def _bf16_bits(x):
+    return (x.astype(F32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_packed_bf16mv_floats_matches_the_header():
+    for n in (0, 1, 255, 256, 257, 10 ** 9 + 1):
+        assert zs.packed_bf16mv_floats(n) == 512 * (-(-n // 256))
+
+
+@pytest.mark.parametrize("n", SIZES)
+def test_pack_and_unpack_bf16mv(gpu, n):
+    """zs_pack_state_bf16mv writes the host packing (zero padding);
+    zs_unpack_state_bf16mv restores the arrays bit for bit and writes nothing
+    past n."""
+    torch = gpu
+    rng = np.random.default_rng(1000 + n)
+    w = rng.normal(0, 1, n).astype(F32)
+    m = rng.integers(0, 1 << 16, n).astype(np.uint16)
+    v = rng.integers(0, 1 << 16, n).astype(np.uint16)
+    dstate = torch.full((zs.packed_bf16mv_floats(n),), 7.0, dtype=torch.float32, device="cuda")
+    zs.zs_pack_state_bf16mv(_dev(torch, w), _dev(torch, m), _dev(torch, v), dstate, n)
+    torch.cuda.synchronize()
+    got = dstate.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), pack16(w, m, v).view(np.uint32))
+    guard = 5
+    ow = torch.full((n + guard,), 3.0, dtype=torch.float32, device="cuda")
+    om = torch.full((n + guard,), 77, dtype=torch.int16, device="cuda")
+    ov = torch.full((n + guard,), 77, dtype=torch.int16, device="cuda")
+    zs.zs_unpack_state_bf16mv(dstate, ow, om, ov, n)
+    torch.cuda.synchronize()
+    hw, hm, hv = ow.cpu().numpy(), om.cpu().numpy().view(np.uint16), ov.cpu().numpy().view(np.uint16)
+    assert np.array_equal(hw[:n].view(np.uint32), w.view(np.uint32)) and np.all(hw[n:] == 3.0)
+    assert np.array_equal(hm[:n], m) and np.all(hm[n:] == 77)
+    assert np.array_equal(hv[:n], v) and np.all(hv[n:] == 77)
+
+
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("k", [1, 3, 16])
+def test_packed_bf16mv_matches_oracle_and_bf16mv(gpu, n, k):
+    """Ten steps from non-zero bf16 moments: the oracle's bits, and
+    zs_shard_step_bf16mv's on the same inputs; the padding stays zero."""
+    torch = gpu
+    rng = np.random.default_rng(900 + n * 3 + k)
+    segs = _segments(rng, n)
+    w0 = rng.normal(0, 0.02, n).astype(F32)
+    m0 = _bf16_bits(rng.normal(0, 1e-3, n))
+    v0 = _bf16_bits(rng.normal(0, 1e-3, n) ** 2)
+    ref = [w0.copy(), m0.copy(), v0.copy(), np.zeros(n, np.uint16)]
+    dstate = _dev(torch, pack16(w0, m0, v0))
+    dp = torch.zeros(n, dtype=torch.int16, device="cuda")
+    bw, bm, bv = _dev(torch, w0), _dev(torch, m0), _dev(torch, v0)
+    bp = torch.zeros(n, dtype=torch.int16, device="cuda")
+    table = H.segment_tensor(segs, "cuda")
+    hpo, hpz = oracle.hparams(), zs.hparams()
+    s = torch.cuda.current_stream()
+    for t in range(1, 11):
+        gs = _partials(rng, k, n, 1e-3)
+        dgs = [_dev(torch, g) for g in gs]
+        zs.zs_shard_step_packed_bf16mv(dstate, dp, dgs, k, n, zs.seg_table(table), hpz, t, s)
+        zs.zs_shard_step_bf16mv(bw, bm, bv, bp, dgs, k, n, zs.seg_table(table), hpz, t, s)
+        assert oracle.shard_step_bf16mv(*ref, gs, segs, hpo, t) == 0
+    torch.cuda.synchronize()
+    state = dstate.cpu().numpy()
+    got = list(unpack16(state, n)) + [dp.cpu().numpy().view(np.uint16)]
+    assert H.assert_parity(got, ref, "packed bf16mv n=%d k=%d" % (n, k)), "not bitwise"
+    base = [bw.cpu().numpy(), bm.cpu().numpy().view(np.uint16), bv.cpu().numpy().view(np.uint16),
+            bp.cpu().numpy().view(np.uint16)]
+    for a, b in zip(got, base):
+        assert np.array_equal(np.ascontiguousarray(a).view(np.uint8), b.view(np.uint8))
+    if n % 256:
+        blk = state.view(np.uint8).reshape(-1, 2048)[-1]
+        r = n % 256
+        for a, z, size in ((0, 1024, 4), (1024, 1536, 2), (1536, 2048, 2)):
+            assert not blk[a + r * size:z].any()
+
+
+def test_prepared_packed_bf16mv_call_matches_the_plain_call(gpu):
+    torch = gpu
+    n, k = 70_001, 3
+    rng = np.random.default_rng(17)
+    segs = _segments(rng, n)
+    w0 = rng.normal(0, 0.02, n).astype(F32)
+    z = np.zeros(n, np.uint16)
+    a, b = _dev(torch, pack16(w0, z, z)), _dev(torch, pack16(w0, z, z))
+    pa = torch.zeros(n, dtype=torch.int16, device="cuda")
+    pb = torch.zeros(n, dtype=torch.int16, device="cuda")
+    table = H.segment_tensor(segs, "cuda")
+    st, hp = zs.seg_table(table), zs.hparams()
+    gs = [_dev(torch, g) for g in _partials(rng, k, n)]
+    call = zs.ShardStep(a, None, None, pa, gs, n, st, hp, variant="packed_bf16mv")
+    for t in (1, 2, 3):
+        call(t)
+        zs.zs_shard_step_packed_bf16mv(b, pb, gs, k, n, st, hp, t)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32)) and torch.equal(pa, pb)
+
+
+def test_packed_bf16mv_argument_errors(gpu):
+    torch = gpu
+    n, k = 1000, 2
+    state = torch.zeros(zs.packed_bf16mv_floats(n) + 64, dtype=torch.float32, device="cuda")
+    p = torch.zeros(n, dtype=torch.int16, device="cuda")
+    g = [torch.zeros(n, dtype=torch.int16, device="cuda") for _ in range(k)]
+    table = H.segment_tensor([(0, True)], "cuda")
+    st, hp = zs.seg_table(table), zs.hparams()
+    sp, pp = state.data_ptr(), p.data_ptr()
+    gp = [x.data_ptr() for x in g]
+    call = lambda *a: zs.zs_shard_step_packed_bf16mv(*a, check=False)  # noqa: E731
+    assert call(sp, pp, gp, k, n, st, hp, 1) == zs.ZS_OK
+    assert call(0, pp, gp, k, n, st, hp, 1) == zs.ZS_ERR_INVALID_ARGUMENT
+    assert call(sp + 8, pp, gp, k, n, st, hp, 1) == zs.ZS_ERR_MISALIGNED
+    # the state spans 2 KB per 256 elements: a param copy 3 KB in overlaps it
+    assert call(sp, sp + 3 * 1024, gp, k, n, st, hp, 1) == zs.ZS_ERR_ALIASING
+    assert call(sp, pp, [gp[0], sp + 4 * 1024], k, n, st, hp, 1) == zs.ZS_ERR_ALIASING
+    assert call(sp, pp, gp, k, 0, st, hp, 1) == zs.ZS_OK
+    w = torch.zeros(n, dtype=torch.float32, device="cuda")
+    m = torch.zeros(n, dtype=torch.int16, device="cuda")
+    v = torch.zeros(n, dtype=torch.int16, device="cuda")
+    wp, mp, vp = w.data_ptr(), m.data_ptr(), v.data_ptr()
+    pk = lambda *a: zs.zs_pack_state_bf16mv(*a, check=False)  # noqa: E731
+    up = lambda *a: zs.zs_unpack_state_bf16mv(*a, check=False)  # noqa: E731
+    assert pk(wp, mp, vp, sp, n) == zs.ZS_OK and up(sp, wp, mp, vp, n) == zs.ZS_OK
+    assert pk(wp, mp, vp, sp, 0) == zs.ZS_OK
+    assert pk(wp, mp, 0, sp, n) == zs.ZS_ERR_INVALID_ARGUMENT
+    assert pk(wp, mp + 2, vp, sp, n) == zs.ZS_ERR_MISALIGNED
+    assert pk(wp, mp, mp, sp, n) == zs.ZS_ERR_ALIASING
+    assert up(sp, wp, mp, sp + 16, n) == zs.ZS_ERR_ALIASING
+    assert pk(wp, mp, vp, sp, -1) == zs.ZS_ERR_INVALID_ARGUMENT
+    torch.cuda.synchronize()
+
+
+def test_70b_packed_bf16mv_windows(gpu):
+    """The 70B-shaped shard with the packed bf16-moment state, which takes the
+    wide launch (two sub-windows per wave), t = 10000..10002: windows at
+    segment boundaries and at random equal the oracle bit for bit."""
+    torch = gpu
+    w = synth.workload("70b")
+    assert zs.zs_launch_plan(w.k, w.n, "packed_bf16mv")["window_quads"] == 2
+    free, _ = torch.cuda.mem_get_info()
+    need = w.n * (8 + 4 + 2 + 2 * w.k) + (1 << 30)
+    if free < need:
+        pytest.skip("needs %.1f GB of free device memory" % (need / 1e9))
+    ts = w.step_ts()
+    ds = H.DeviceShard(w, "packed_bf16mv")
+    for t in ts:
+        ds.fill_grads(t)
+        ds.step(t)
+    torch.cuda.synchronize()
+    wins = H.boundary_windows(w, 1 << 14, max_boundaries=16, n_random=4, seed=6)
+    got = [ds.window(lo, hi) for lo, hi in wins]
+    ds.free()
+    for (lo, hi), g in zip(wins, got):
+        ref = H.oracle_window(w, lo, hi, ts, variant="bf16mv")
+        assert H.assert_parity(g, ref, "70b packed bf16mv [%d,%d)" % (lo, hi)), "not bitwise"
+    print("70b packed bf16mv: %d windows bitwise equal" % len(wins), flush=True)

@@ -60,12 +60,14 @@ def test_unit_correction_kernels_are_bitwise(gpu, variant, span):
     w0 = rng.normal(0, 0.02, n).astype(F32)
     m0 = rng.normal(0, 1e-3, n).astype(F32)
     v0 = (rng.normal(0, 1e-3, n) ** 2).astype(F32)
-    if variant == "bf16mv":
+    mv16 = variant in ("bf16mv", "packed_bf16mv")
+    if mv16:
         m0, v0 = _bf16(m0), _bf16(v0)
     ref = [w0.copy(), m0.copy(), v0.copy(), np.zeros(n, np.uint16)]
     dw, dm, dv = _dev(torch, w0), _dev(torch, m0), _dev(torch, v0)
     packed = variant.startswith("packed")
-    dstate = _dev(torch, H.pack_host(w0, m0, v0)) if packed else None
+    pack = H.pack16_host if mv16 else H.pack_host
+    dstate = _dev(torch, pack(w0, m0, v0)) if packed else None
     dp = torch.zeros(n, dtype=torch.int16, device="cuda")
     dq = torch.zeros(n, dtype=torch.int8, device="cuda")
     ds = torch.zeros(nb, dtype=torch.float32, device="cuda")
@@ -94,16 +96,18 @@ def test_unit_correction_kernels_are_bitwise(gpu, variant, span):
             zs.zs_shard_step_bf16mv(dw, dm, dv, dp, dgs, k, n, st, hpz, t, s)
         elif variant == "packed":
             zs.zs_shard_step_packed(dstate, dp, dgs, k, n, st, hpz, t, s)
+        elif variant == "packed_bf16mv":
+            zs.zs_shard_step_packed_bf16mv(dstate, dp, dgs, k, n, st, hpz, t, s)
         else:
             zs.zs_shard_step(dw, dm, dv, dp, dgs, k, n, st, hpz, t, s)
-        step = oracle.shard_step_bf16mv if variant == "bf16mv" else oracle.shard_step
+        step = oracle.shard_step_bf16mv if mv16 else oracle.shard_step
         assert step(*ref, gs, segs, hpo, t) == 0
     torch.cuda.synchronize()
-    mv = (lambda x: x.cpu().numpy().view(np.uint16)) if variant == "bf16mv" \
-        else (lambda x: x.cpu().numpy())
+    mv = (lambda x: x.cpu().numpy().view(np.uint16)) if mv16 else (lambda x: x.cpu().numpy())
     got = (dw.cpu().numpy(), mv(dm), mv(dv), dp.cpu().numpy().view(np.uint16))
     if packed:
-        got = H.unpack_host(dstate.cpu().numpy(), n) + got[3:]
+        unpack = H.unpack16_host if mv16 else H.unpack_host
+        got = unpack(dstate.cpu().numpy(), n) + got[3:]
     want = tuple(ref)
     if variant in ("q8ag", "packed_q8ag"):
         got += (dq.cpu().numpy(), ds.cpu().numpy())
