@@ -34,9 +34,13 @@ def _state(torch, w0, n, k, seed, entry):
               param=torch.zeros(n, dtype=torch.int16, device="cuda"),
               grads=[f((rng.normal(0, 1e-2, n).astype(np.float32).view(np.uint32) >> 16)
                        .astype(np.uint16).view(np.int16)) for _ in range(k)])
-    if entry == "packed":
-        z = np.zeros(n, np.float32)
-        st["state"] = f(H.pack_host(w0, z, z))
+    if entry in ("bf16mv", "packed_bf16mv"):
+        st["m"] = torch.zeros(n, dtype=torch.int16, device="cuda")
+        st["v"] = torch.zeros(n, dtype=torch.int16, device="cuda")
+    if entry in ("packed", "packed_bf16mv"):
+        z = np.zeros(n, np.uint16 if entry == "packed_bf16mv" else np.float32)
+        pack = H.pack16_host if entry == "packed_bf16mv" else H.pack_host
+        st["state"] = f(pack(w0, z, z))
         del st["master"], st["m"], st["v"]
     if entry == "q8ag":
         st["q8"] = torch.zeros(n, dtype=torch.int8, device="cuda")
@@ -44,11 +48,17 @@ def _state(torch, w0, n, k, seed, entry):
     return st
 
 
-def _call(st, k, n, table, hp, t, stream):
-    if "state" in st:
+def _call(entry, st, k, n, table, hp, t, stream):
+    if entry == "packed":
         zs.zs_shard_step_packed(st["state"], st["param"], st["grads"], k, n, zs.seg_table(table),
                                 hp, t, stream)
-    elif "q8" in st:
+    elif entry == "packed_bf16mv":
+        zs.zs_shard_step_packed_bf16mv(st["state"], st["param"], st["grads"], k, n,
+                                       zs.seg_table(table), hp, t, stream)
+    elif entry == "bf16mv":
+        zs.zs_shard_step_bf16mv(st["master"], st["m"], st["v"], st["param"], st["grads"], k, n,
+                                zs.seg_table(table), hp, t, stream)
+    elif entry == "q8ag":
         zs.zs_shard_step_q8ag(st["master"], st["m"], st["v"], st["param"], st["q8"], st["q8s"],
                               st["grads"], k, n, zs.seg_table(table), hp, t, stream)
     else:
@@ -64,8 +74,9 @@ def _same(torch, a, b):
             assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), key
 
 
-@pytest.mark.parametrize("entry", ["base", "q8ag", "packed"],
-                         ids=["zs_shard_step", "zs_shard_step_q8ag", "zs_shard_step_packed"])
+@pytest.mark.parametrize("entry", ["base", "q8ag", "bf16mv", "packed", "packed_bf16mv"],
+                         ids=["zs_shard_step", "zs_shard_step_q8ag", "zs_shard_step_bf16mv",
+                              "zs_shard_step_packed", "zs_shard_step_packed_bf16mv"])
 @pytest.mark.parametrize("t", [7, 10000])
 def test_graph_replays_match_eager_calls(gpu, entry, t):
     torch = gpu
@@ -84,18 +95,21 @@ def test_graph_replays_match_eager_calls(gpu, entry, t):
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        _call(graphed, k, n, table, hp, t, torch.cuda.current_stream())
+        _call(entry, graphed, k, n, table, hp, t, torch.cuda.current_stream())
     torch.cuda.synchronize()
     _same(torch, graphed, _state(torch, w0, n, k, 5, entry))  # capture ran nothing
 
     for rep in range(4):
         g.replay()
-        _call(eager, k, n, table, hp, t, torch.cuda.current_stream())
+        _call(entry, eager, k, n, table, hp, t, torch.cuda.current_stream())
         torch.cuda.synchronize()
         x = torch.randn(4096, device="cuda")
         assert torch.isfinite((x * x).sum())  # unrelated eager work between replays
         torch.cuda.synchronize()
         _same(torch, graphed, eager)
-    moved = graphed["state"].view(-1, 3, 256)[:, 0, :].reshape(-1)[:n] if entry == "packed" \
-        else graphed["master"]
+    if entry in ("packed", "packed_bf16mv"):
+        block = 512 if entry == "packed_bf16mv" else 768
+        moved = graphed["state"].view(-1, block)[:, :256].reshape(-1)[:n]
+    else:
+        moved = graphed["master"]
     assert not torch.equal(moved, torch.from_numpy(w0).cuda())
