@@ -30,6 +30,9 @@
 //     window inside one segment takes that segment's flag, a window with
 //     segment boundaries stages the 64 entries around it in the wave's LDS
 //     slot and each lane walks them for its own elements;
+//   * the optimizer state may instead be packed per 256-element block in one
+//     array (master, then m, then v: one 3 KB run per wavefront, or 2 KB with
+//     bf16 moments); the arithmetic is the same;
 //   * 64-bit element indices throughout (shards exceed 2^31 elements).
 //
 // Numerics follow the header: binary32, no contraction, correctly rounded
