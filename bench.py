@@ -113,7 +113,7 @@ def oracle_threads() -> int:
 
 # ---------------------------------------------------------------- parity windows
 
-PARITY_WINDOW = 1 << 16
+PARITY_WINDOW = 1 << 20
 
 
 def parity_windows(w, n: int, count: int = 10):

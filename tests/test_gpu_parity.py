@@ -628,16 +628,20 @@ def _large_config(torch, name, window, max_boundaries):
 
 def test_7b_rank0_windows(gpu):
     """7B-shaped rank 0 of 8 (805M elements, k = 8, 1% heavy-tailed partials):
-    100 pre-warm steps then 10 measured steps, windowed comparison."""
+    100 pre-warm steps then 10 measured steps, windowed comparison (windows of
+    2^13 elements: the oracle regenerates and replays all 110 steps of eight
+    partials for each)."""
     _large_config(gpu, "7b", 1 << 13, 40)
 
 
 def test_175b_rank0_windows(gpu):
-    """GPT-3-175B-shaped rank 0 of 64 (2.72e9 elements, k = 2), 5 steps."""
-    _large_config(gpu, "175b", 1 << 16, 32)
+    """GPT-3-175B-shaped rank 0 of 64 (2.72e9 elements, k = 2), 5 steps:
+    windows of 2^20 elements at every segment boundary, both ends and random."""
+    _large_config(gpu, "175b", 1 << 20, 32)
 
 
 def test_70b_rank0_windows(gpu):
     """70B-shaped rank 0 of 8 (8.05e9 elements, 1970 segments, k = 2) at
-    t = 10000..10002, windowed comparison."""
-    _large_config(gpu, "70b", 1 << 15, 64)
+    t = 10000..10002: windows of 2^20 elements at 64 of the segment
+    boundaries, both ends and random."""
+    _large_config(gpu, "70b", 1 << 20, 64)
