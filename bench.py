@@ -1160,6 +1160,9 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
+            # the counted bytes (rocprofv3 counters of this kernel source and
+            # launch) over this run's average launch time
+            "traffic_gbps": round(traffic / (avg_ms * 1e-3) / 1e9, 2) if traffic else None,
             "kernel": "shard_step_kernel<K=%d,%s>" % (k, var),
             "avg_launch_ms": round(avg_ms, 4),
             "timing": "one HIP graph of the timed steps, average per step" if args.graph

@@ -39,6 +39,10 @@ def test_bench_line(extra):
     r = out["roofline"]
     assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["unit"] == "GB/s"
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
+    if r["traffic"] is None:
+        assert r["traffic_gbps"] is None
+    else:
+        assert abs(r["traffic_gbps"] - r["traffic"] / (r["avg_launch_ms"] * 1e-3) / 1e9) < 1
     assert out["kernel_ms"]["min"] <= out["kernel_ms"]["median"] <= out["kernel_ms"]["max"]
     cpu = out["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["cores"] == 1 and cpu["value"] > 0
