@@ -277,9 +277,10 @@ def _check_k(k, arrays, name):
 
 def zs_launch_plan(k: int, n: int, variant: str = "base", cfg=None) -> dict:
     """The launch a call of entry point ``variant`` (a key of ZS_VARIANT:
-    "base", "q8ag", "q8grad", "bf16mv" or a packed form) would make: grid, chunk, chunk order, occupancy cap, cache
-    policy and sub-windows per wavefront, as a dict of the zs_launch_info
-    fields.  ``cfg`` (base only) is a dict of ZsLaunchCfg fields or None."""
+    "base", "q8ag", "q8grad", "bf16mv" or a packed form) would make: grid,
+    chunk, chunk order, occupancy cap, cache policy and sub-windows per
+    wavefront, as a dict of the zs_launch_info fields.  ``cfg`` (base only)
+    is a dict of ZsLaunchCfg fields or None."""
     c = None
     if cfg:
         c = ZsLaunchCfg(**{f: int(cfg.get(f, 0)) for f, _ in ZsLaunchCfg._fields_})

@@ -326,10 +326,10 @@ int zs_ceiling_copy(const void *src, void *dst, int64_t bytes, void *stream) {
 //         4 = zs_shard_step_bf16mv, 8 = zs_shard_step_packed, 9 and 10 = its
 //         int8-payload and int8-partial forms, 12 = zs_shard_step_packed_bf16mv
 //         (the streams and element sizes that entry point moves; with layouts
-//         8-12 master is the packed state and m, v are unused).  grads holds k device pointers (int8 for layout 2,
-//         bf16 otherwise); qscales (layout 2) k device pointers to one f32
-//         per 256 elements; q8 and q8_scale (layout 1) the int8 copy and its
-//         scales.
+//         8-12 master is the packed state and m, v are unused).  grads holds
+//         k device pointers (int8 with bit 2, bf16 otherwise); qscales (bit
+//         2) k device pointers to one f32 per 256 elements; q8 and q8_scale
+//         (bit 1) the int8 copy and its scales.
 //   n: elements; a multiple of chunk and of the tile (1024 elements per
 //         sub-window of a wave: the twin covers whole windows only, so the host
 //         rounds a shard down to that).

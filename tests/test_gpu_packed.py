@@ -396,7 +396,8 @@ def test_pack_and_unpack_bf16mv(gpu, n):
     ov = torch.full((n + guard,), 77, dtype=torch.int16, device="cuda")
     zs.zs_unpack_state_bf16mv(dstate, ow, om, ov, n)
     torch.cuda.synchronize()
-    hw, hm, hv = ow.cpu().numpy(), om.cpu().numpy().view(np.uint16), ov.cpu().numpy().view(np.uint16)
+    hw = ow.cpu().numpy()
+    hm, hv = om.cpu().numpy().view(np.uint16), ov.cpu().numpy().view(np.uint16)
     assert np.array_equal(hw[:n].view(np.uint32), w.view(np.uint32)) and np.all(hw[n:] == 3.0)
     assert np.array_equal(hm[:n], m) and np.all(hm[n:] == 77)
     assert np.array_equal(hv[:n], v) and np.all(hv[n:] == 77)
