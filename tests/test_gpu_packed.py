@@ -215,28 +215,49 @@ def test_packed_argument_errors(gpu):
     torch.cuda.synchronize()
 
 
-def test_70b_packed_windows(gpu):
-    """The 70B-shaped shard with packed state, t = 10000..10002: windows at
-    segment boundaries and at random equal the oracle bit for bit."""
-    torch = gpu
-    w = synth.workload("70b")
+def _packed_shard_windows(torch, name, variant, window, max_boundaries):
+    """A model-shaped shard with packed state over its workload's steps (the
+    pre-warm steps included): windows at segment boundaries, both ends and at
+    random equal the oracle bit for bit."""
+    w = synth.workload(name)
     free, _ = torch.cuda.mem_get_info()
-    need = w.n * (12 + 4 + 2 + 2 * w.k) + (1 << 30)
+    state = 8 if variant == "packed_bf16mv" else 12
+    need = w.n * (state + 4 + 2 + 2 * w.k) + (1 << 30)
     if free < need:
         pytest.skip("needs %.1f GB of free device memory" % (need / 1e9))
-    ts = w.step_ts()
-    ds = H.DeviceShard(w, "packed")
+    ts = list(range(1, w.prewarm_steps + 1)) + w.step_ts()
+    ds = H.DeviceShard(w, variant)
     for t in ts:
         ds.fill_grads(t)
         ds.step(t)
     torch.cuda.synchronize()
-    wins = H.boundary_windows(w, 1 << 14, max_boundaries=16, n_random=4, seed=5)
+    wins = H.boundary_windows(w, window, max_boundaries=max_boundaries, n_random=4, seed=5)
     got = [ds.window(lo, hi) for lo, hi in wins]
     ds.free()
+    arith = "bf16mv" if variant == "packed_bf16mv" else "base"
     for (lo, hi), g in zip(wins, got):
-        ref = H.oracle_window(w, lo, hi, ts)
-        assert H.assert_parity(g, ref, "70b packed [%d,%d)" % (lo, hi)), "not bitwise"
-    print("70b packed: %d windows bitwise equal" % len(wins), flush=True)
+        ref = H.oracle_window(w, lo, hi, ts, variant=arith)
+        assert H.assert_parity(g, ref, "%s %s [%d,%d)" % (name, variant, lo, hi)), "not bitwise"
+    print("%s %s: %d windows bitwise equal" % (name, variant, len(wins)), flush=True)
+
+
+def test_70b_packed_windows(gpu):
+    """The 70B-shaped shard with packed state, t = 10000..10002."""
+    _packed_shard_windows(gpu, "70b", "packed", 1 << 14, 16)
+
+
+@pytest.mark.parametrize("variant", ["packed", "packed_bf16mv"])
+def test_175b_packed_windows(gpu, variant):
+    """The 175B-shaped shard (13 segments, k = 2, five steps) with packed state:
+    windows of 2^20 elements."""
+    _packed_shard_windows(gpu, "175b", variant, 1 << 20, 16)
+
+
+@pytest.mark.parametrize("variant", ["packed", "packed_bf16mv"])
+def test_7b_packed_windows(gpu, variant):
+    """The 7B-shaped shard (k = 8, heavy-tailed partials, 100 pre-warm steps
+    then 10) with packed state."""
+    _packed_shard_windows(gpu, "7b", variant, 1 << 12, 12)
 
 
 @pytest.mark.parametrize("n", SIZES)
@@ -500,25 +521,7 @@ def test_packed_bf16mv_argument_errors(gpu):
 
 def test_70b_packed_bf16mv_windows(gpu):
     """The 70B-shaped shard with the packed bf16-moment state, which takes the
-    wide launch (two sub-windows per wave), t = 10000..10002: windows at
-    segment boundaries and at random equal the oracle bit for bit."""
-    torch = gpu
+    wide launch (two sub-windows per wave), t = 10000..10002."""
     w = synth.workload("70b")
     assert zs.zs_launch_plan(w.k, w.n, "packed_bf16mv")["window_quads"] == 2
-    free, _ = torch.cuda.mem_get_info()
-    need = w.n * (8 + 4 + 2 + 2 * w.k) + (1 << 30)
-    if free < need:
-        pytest.skip("needs %.1f GB of free device memory" % (need / 1e9))
-    ts = w.step_ts()
-    ds = H.DeviceShard(w, "packed_bf16mv")
-    for t in ts:
-        ds.fill_grads(t)
-        ds.step(t)
-    torch.cuda.synchronize()
-    wins = H.boundary_windows(w, 1 << 14, max_boundaries=16, n_random=4, seed=6)
-    got = [ds.window(lo, hi) for lo, hi in wins]
-    ds.free()
-    for (lo, hi), g in zip(wins, got):
-        ref = H.oracle_window(w, lo, hi, ts, variant="bf16mv")
-        assert H.assert_parity(g, ref, "70b packed bf16mv [%d,%d)" % (lo, hi)), "not bitwise"
-    print("70b packed bf16mv: %d windows bitwise equal" % len(wins), flush=True)
+    _packed_shard_windows(gpu, "70b", "packed_bf16mv", 1 << 14, 16)
