@@ -84,6 +84,17 @@ def load_library(path: str):
     lib.zs_oracle_shard_step_bf16mv.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int64,
                                                 P, ctypes.c_int32, P, ctypes.c_int64]
     lib.zs_oracle_shard_step_bf16mv.restype = ctypes.c_int
+    lib.zs_oracle_splitmix64.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+    lib.zs_oracle_splitmix64.restype = ctypes.c_uint64
+    lib.zs_oracle_bf16_sr_array.argtypes = [P, P, P, ctypes.c_int64]
+    lib.zs_oracle_bf16_sr_array.restype = None
+    lib.zs_oracle_sr_bits.argtypes = [ctypes.c_uint64, ctypes.c_int64, ctypes.c_int,
+                                      ctypes.c_int64]
+    lib.zs_oracle_sr_bits.restype = ctypes.c_uint32
+    lib.zs_oracle_shard_step_bf16mv_sr.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int64,
+                                                   P, ctypes.c_int32, P, ctypes.c_int64,
+                                                   ctypes.c_uint64]
+    lib.zs_oracle_shard_step_bf16mv_sr.restype = ctypes.c_int
     return lib
 
 
@@ -227,3 +238,46 @@ def shard_step_bf16mv(master, m_bf16, v_bf16, param_bf16, grads, segs, hp: Hpara
         _ptr(master), _ptr(m_bf16), _ptr(v_bf16), _ptr(param_bf16),
         ctypes.cast(gp, ctypes.c_void_p), k, n, ctypes.cast(seg_arr, ctypes.c_void_p),
         len(seg_arr), ctypes.byref(hp), int(step))
+
+
+def splitmix64(key: int, i: int) -> int:
+    """Output i of the SplitMix64 stream with key `key` (counter-style)."""
+    return int(_load().zs_oracle_splitmix64(key & (2 ** 64 - 1), i & (2 ** 64 - 1)))
+
+
+def bf16_sr(x: np.ndarray, r: np.ndarray) -> np.ndarray:
+    """Stochastic fp32 -> bf16 of each x with its 16 random bits r (low 16
+    bits of uint32); uint16 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    r = np.ascontiguousarray(r, dtype=np.uint32)
+    if x.shape != r.shape:
+        raise ValueError("x and r differ in shape")
+    out = np.empty(x.shape, np.uint16)
+    _load().zs_oracle_bf16_sr_array(_ptr(x), _ptr(r), _ptr(out), x.size)
+    return out
+
+
+def sr_bits(seed: int, step: int, which: int, i: int) -> int:
+    """The 16 random bits the stochastic step uses for element i's m
+    (which = 0) or v (which = 1) at step t."""
+    return int(_load().zs_oracle_sr_bits(seed & (2 ** 64 - 1), int(step), int(which), int(i)))
+
+
+def shard_step_bf16mv_sr(master, m_bf16, v_bf16, param_bf16, grads, segs, hp: Hparams,
+                         step: int, seed: int) -> int:
+    """Oracle step with bf16 moments rounded stochastically (uint16 bit
+    patterns, updated in place); `seed` selects the random streams."""
+    n = master.shape[0]
+    _check(master, np.float32, n, "master")
+    _check(m_bf16, np.uint16, n, "m")
+    _check(v_bf16, np.uint16, n, "v")
+    _check(param_bf16, np.uint16, n, "param_bf16")
+    for g in grads:
+        _check(g, np.uint16, n, "grad")
+    k = len(grads)
+    gp = (ctypes.c_void_p * max(k, 1))(*[g.ctypes.data for g in grads])
+    seg_arr = segs if isinstance(segs, ctypes.Array) else segments_array(segs)
+    return _load().zs_oracle_shard_step_bf16mv_sr(
+        _ptr(master), _ptr(m_bf16), _ptr(v_bf16), _ptr(param_bf16),
+        ctypes.cast(gp, ctypes.c_void_p), k, n, ctypes.cast(seg_arr, ctypes.c_void_p),
+        len(seg_arr), ctypes.byref(hp), int(step), seed & (2 ** 64 - 1))

@@ -369,3 +369,94 @@ int zs_oracle_shard_step_bf16mv(float *master, uint16_t *m, uint16_t *v, uint16_
     }
     return ZO_OK;
 }
+
+/*
+ * Stochastic rounding of the bf16 moments: the other reading of "Lecture 7:
+ * Parallelism I", section 8.4 (bf16 m and v), whose text does not say how
+ * the moments are rounded.  A value is rounded down to the bf16 below it in
+ * magnitude or up to the one above with probability equal to its distance
+ * from the lower one, so that the expectation of the rounded value is the
+ * value itself.  The 16 random bits per rounding come from SplitMix64
+ * (Steele, Lea and Flood, "Fast splittable pseudorandom number generators",
+ * OOPSLA 2014), used counter-style: output i of the stream with key K is
+ * mix64(K + (i + 1) * 0x9E3779B97F4A7C15).
+ */
+static uint64_t sm64_mix(uint64_t z)
+{
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+uint64_t zs_oracle_splitmix64(uint64_t key, uint64_t i)
+{
+    return sm64_mix(key + (i + 1u) * 0x9E3779B97F4A7C15ull);
+}
+
+/* fp32 -> bf16 with the 16 random bits r: adding r below the kept bits and
+ * dropping them rounds the magnitude up exactly when r >= 65536 - (dropped
+ * bits), i.e. with probability (dropped bits) / 65536.  The sign bit is not
+ * touched (the carry stays inside the magnitude; the largest finite value
+ * can round up to infinity).  NaN -> 0x7FC0; infinities stay. */
+uint16_t zs_oracle_bf16_sr(float x, uint32_t r)
+{
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)0x7FC0u;
+    return (uint16_t)((u + (r & 0xffffu)) >> 16);
+}
+
+void zs_oracle_bf16_sr_array(const float *x, const uint32_t *r, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = zs_oracle_bf16_sr(x[i], r[i]);
+}
+
+/* The random bits of element i for moment `which` (0 = m, 1 = v) at step
+ * t: the stream key is output 2t + which of the caller's seed; word i / 4 of
+ * that stream holds the bits of elements 4(i/4) .. 4(i/4) + 3, 16 each, the
+ * lowest for the first. */
+uint32_t zs_oracle_sr_bits(uint64_t seed, int64_t step, int which, int64_t i)
+{
+    uint64_t key = zs_oracle_splitmix64(seed, 2u * (uint64_t)step + (uint64_t)which);
+    uint64_t word = zs_oracle_splitmix64(key, (uint64_t)i / 4u);
+    return (uint32_t)((word >> (16 * (i % 4))) & 0xffffu);
+}
+
+/*
+ * Shard step with bf16 moments rounded stochastically: exactly
+ * zs_oracle_shard_step_bf16mv except that the new m and v are stored with
+ * zs_oracle_bf16_sr, each with its own random bits (the parameter copy is
+ * still rounded to nearest even).  `seed` selects the random streams; a
+ * rank would pass its own.
+ */
+int zs_oracle_shard_step_bf16mv_sr(float *master, uint16_t *m, uint16_t *v, uint16_t *param_bf16,
+                                   const uint16_t *const *grads, int k, int64_t n,
+                                   const zo_segment *segs, int32_t nseg, const zo_hparams *hp,
+                                   int64_t step, uint64_t seed)
+{
+    if (k < 1 || n < 0 || step < 1 || !hparams_ok(hp)) return ZO_ERR_INVALID;
+    if (!segs_ok(segs, nseg)) return ZO_ERR_INVALID;
+    if (n == 0) return ZO_OK;
+    if (!master || !m || !v || !param_bf16 || !grads) return ZO_ERR_INVALID;
+    for (int j = 0; j < k; ++j)
+        if (!grads[j]) return ZO_ERR_INVALID;
+    zo_scalars sc = make_scalars(hp, step);
+    int32_t seg = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        while (seg + 1 < nseg && segs[seg + 1].start <= i)
+            ++seg;
+        float g = bf16_to_f32(grads[0][i]);
+        for (int j = 1; j < k; ++j)
+            g = g + bf16_to_f32(grads[j][i]);
+        g = g * hp->grad_scale;
+        float mf = bf16_to_f32(m[i]);
+        float vf = bf16_to_f32(v[i]);
+        adamw_element(&master[i], &mf, &vf, g, segs[seg].wd_on != 0, hp, &sc);
+        m[i] = zs_oracle_bf16_sr(mf, zs_oracle_sr_bits(seed, step, 0, i));
+        v[i] = zs_oracle_bf16_sr(vf, zs_oracle_sr_bits(seed, step, 1, i));
+        param_bf16[i] = zs_oracle_bf16_rne(master[i]);
+    }
+    return ZO_OK;
+}

@@ -28,6 +28,10 @@ int zs_oracle_shard_step_q8grad(float *, float *, float *, uint16_t *, const int
 int zs_oracle_shard_step_bf16mv(float *, uint16_t *, uint16_t *, uint16_t *,
                                 const uint16_t *const *, int, int64_t, const seg_t *, int32_t,
                                 const hp_t *, int64_t);
+int zs_oracle_shard_step_bf16mv_sr(float *, uint16_t *, uint16_t *, uint16_t *,
+                                   const uint16_t *const *, int, int64_t, const seg_t *, int32_t,
+                                   const hp_t *, int64_t, uint64_t);
+void zs_oracle_bf16_sr_array(const float *, const uint32_t *, uint16_t *, int64_t);
 
 static uint64_t rng_state = 0x9E3779B97F4A7C15ull;
 static uint32_t rnd(void)
@@ -105,6 +109,9 @@ int main(void)
                 failures += zs_oracle_shard_step_bf16mv(w, mb, vb, p,
                                                         (const uint16_t *const *)g, k, n, segs,
                                                         nseg, &hp, t) != 0;
+                failures += zs_oracle_shard_step_bf16mv_sr(w, mb, vb, p,
+                                                           (const uint16_t *const *)g, k, n,
+                                                           segs, nseg, &hp, t, 77u + t) != 0;
             }
             /* argument errors touch nothing */
             failures += zs_oracle_shard_step(w, m, v, p, (const uint16_t *const *)g, k, n, segs,
@@ -122,6 +129,10 @@ int main(void)
             for (int64_t i = 0; i < n; ++i) { mask[i] = (uint8_t)(rnd() & 1); gf[i] = rndf(0.01f); }
             failures += zs_oracle_adamw_unsharded(w, m, v, p, gf, mask, n, &hp, 1) != 0;
             zs_oracle_bf16_rne_array(w, p, n);
+            uint32_t *rb = xmalloc(4 * (size_t)n);
+            for (int64_t i = 0; i < n; ++i) rb[i] = rnd();
+            zs_oracle_bf16_sr_array(w, rb, p, n);
+            free(rb);
             float s5[5];
             zs_oracle_scalars(&hp, 10000, s5);
             free(pq); free(ps); free(back); free(mask); free(gf); free(segs);

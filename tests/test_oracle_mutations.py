@@ -16,6 +16,7 @@ import oracle
 from tests import test_oracle_pins as P
 from tests import test_oracle_q8 as Q
 from tests import test_oracle_sharding as S
+from tests import test_oracle_sr as R
 from tests import test_oracle_variants as V
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "zs_oracle.c")
@@ -103,6 +104,35 @@ VARIANT_MUTATIONS = [
      "          m[i] = (uint16_t)(cm.u >> 16); v[i] = (uint16_t)(cv.u >> 16); }"),
 ]
 
+# Mistakes in the stochastic rounding of the bf16 moments: caught by its pins.
+SR_MUTATIONS = [
+    ("SR truncates",
+     "return (uint16_t)((u + (r & 0xffffu)) >> 16);", "return (uint16_t)(u >> 16);"),
+    ("SR rounds up once too often",
+     "return (uint16_t)((u + (r & 0xffffu)) >> 16);",
+     "return (uint16_t)((u + (r & 0xffffu) + 1u) >> 16);"),
+    ("SR carries NaN payloads",
+     "    if ((u & 0x7fffffffu) > 0x7f800000u)\n        return (uint16_t)0x7FC0u;\n"
+     "    return (uint16_t)((u + (r & 0xffffu)) >> 16);",
+     "    return (uint16_t)((u + (r & 0xffffu)) >> 16);"),
+    ("SR m and v share one stream",
+     "zs_oracle_sr_bits(seed, step, 1, i)", "zs_oracle_sr_bits(seed, step, 0, i)"),
+    ("SR one random field for a whole quad",
+     "(word >> (16 * (i % 4))) & 0xffffu", "word & 0xffffu"),
+    ("SR streams not keyed by the step",
+     "2u * (uint64_t)step + (uint64_t)which", "(uint64_t)which"),
+    ("SR streams not keyed by the seed",
+     "uint64_t key = zs_oracle_splitmix64(seed,", "uint64_t key = zs_oracle_splitmix64(0,"),
+    ("SR generator's increment wrong",
+     "return sm64_mix(key + (i + 1u) * 0x9E3779B97F4A7C15ull);",
+     "return sm64_mix(key + i * 0x9E3779B97F4A7C15ull);"),
+]
+
+SR_BATTERY = [R.test_generator_is_the_published_splitmix64, R.test_rounding_distribution_is_exact,
+              R.test_specials, R.test_first_step_matches_round_to_nearest_step,
+              R.test_first_step_is_unbiased, R.test_random_streams_are_independent,
+              R.test_random_bits_are_uniform]
+
 VARIANT_BATTERY = [Q.test_hand_worked_block_with_ties, Q.test_zero_block_and_single_element,
                    Q.test_nonfinite_blocks_only_poison_themselves,
                    lambda: Q.test_error_bound_and_extremes(7),
@@ -152,6 +182,7 @@ def test_unmutated_copy_passes_the_battery():
         lib = oracle.load_library(_compile(open(SRC).read(), d))
         assert _first_failing_pin(lib) is None
         assert _first_failing_pin(lib, VARIANT_BATTERY) is None
+        assert _first_failing_pin(lib, SR_BATTERY) is None
 
 
 @pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
@@ -174,5 +205,17 @@ def test_planted_variant_mistake_is_caught(name, old, new):
     with tempfile.TemporaryDirectory() as d:
         lib = oracle.load_library(_compile(mutated, d))
         caught = _first_failing_pin(lib, VARIANT_BATTERY)
+    assert caught is not None, "no pin catches: %s" % name
+    print("%-50s caught by %s" % (name, caught))
+
+
+@pytest.mark.parametrize("name,old,new", SR_MUTATIONS, ids=[m[0] for m in SR_MUTATIONS])
+def test_planted_rounding_mistake_is_caught(name, old, new):
+    text = open(SRC).read()
+    assert text.count(old) == 1, "mutation site not found once: %s" % name
+    mutated = text.replace(old, new, 1)
+    with tempfile.TemporaryDirectory() as d:
+        lib = oracle.load_library(_compile(mutated, d))
+        caught = _first_failing_pin(lib, SR_BATTERY)
     assert caught is not None, "no pin catches: %s" % name
     print("%-50s caught by %s" % (name, caught))
