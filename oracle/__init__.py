@@ -93,7 +93,7 @@ def load_library(path: str):
     lib.zs_oracle_sr_bits.restype = ctypes.c_uint32
     lib.zs_oracle_shard_step_bf16mv_sr.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int64,
                                                    P, ctypes.c_int32, P, ctypes.c_int64,
-                                                   ctypes.c_uint64]
+                                                   ctypes.c_uint64, ctypes.c_int64]
     lib.zs_oracle_shard_step_bf16mv_sr.restype = ctypes.c_int
     return lib
 
@@ -264,9 +264,10 @@ def sr_bits(seed: int, step: int, which: int, i: int) -> int:
 
 
 def shard_step_bf16mv_sr(master, m_bf16, v_bf16, param_bf16, grads, segs, hp: Hparams,
-                         step: int, seed: int) -> int:
+                         step: int, seed: int, index0: int = 0) -> int:
     """Oracle step with bf16 moments rounded stochastically (uint16 bit
-    patterns, updated in place); `seed` selects the random streams."""
+    patterns, updated in place); `seed` selects the random streams and the
+    arrays hold shard elements index0 .. index0 + n - 1."""
     n = master.shape[0]
     _check(master, np.float32, n, "master")
     _check(m_bf16, np.uint16, n, "m")
@@ -280,4 +281,4 @@ def shard_step_bf16mv_sr(master, m_bf16, v_bf16, param_bf16, grads, segs, hp: Hp
     return _load().zs_oracle_shard_step_bf16mv_sr(
         _ptr(master), _ptr(m_bf16), _ptr(v_bf16), _ptr(param_bf16),
         ctypes.cast(gp, ctypes.c_void_p), k, n, ctypes.cast(seg_arr, ctypes.c_void_p),
-        len(seg_arr), ctypes.byref(hp), int(step), seed & (2 ** 64 - 1))
+        len(seg_arr), ctypes.byref(hp), int(step), seed & (2 ** 64 - 1), int(index0))

@@ -429,13 +429,16 @@ uint32_t zs_oracle_sr_bits(uint64_t seed, int64_t step, int which, int64_t i)
  * zs_oracle_shard_step_bf16mv except that the new m and v are stored with
  * zs_oracle_bf16_sr, each with its own random bits (the parameter copy is
  * still rounded to nearest even).  `seed` selects the random streams; a
- * rank would pass its own.
+ * rank would pass its own.  The arrays hold shard elements index0 ..
+ * index0 + n - 1 (a window of the shard; index0 = 0 for the whole shard),
+ * whose random bits are those of their place in the shard.
  */
 int zs_oracle_shard_step_bf16mv_sr(float *master, uint16_t *m, uint16_t *v, uint16_t *param_bf16,
                                    const uint16_t *const *grads, int k, int64_t n,
                                    const zo_segment *segs, int32_t nseg, const zo_hparams *hp,
-                                   int64_t step, uint64_t seed)
+                                   int64_t step, uint64_t seed, int64_t index0)
 {
+    if (index0 < 0) return ZO_ERR_INVALID;
     if (k < 1 || n < 0 || step < 1 || !hparams_ok(hp)) return ZO_ERR_INVALID;
     if (!segs_ok(segs, nseg)) return ZO_ERR_INVALID;
     if (n == 0) return ZO_OK;
@@ -454,8 +457,8 @@ int zs_oracle_shard_step_bf16mv_sr(float *master, uint16_t *m, uint16_t *v, uint
         float mf = bf16_to_f32(m[i]);
         float vf = bf16_to_f32(v[i]);
         adamw_element(&master[i], &mf, &vf, g, segs[seg].wd_on != 0, hp, &sc);
-        m[i] = zs_oracle_bf16_sr(mf, zs_oracle_sr_bits(seed, step, 0, i));
-        v[i] = zs_oracle_bf16_sr(vf, zs_oracle_sr_bits(seed, step, 1, i));
+        m[i] = zs_oracle_bf16_sr(mf, zs_oracle_sr_bits(seed, step, 0, index0 + i));
+        v[i] = zs_oracle_bf16_sr(vf, zs_oracle_sr_bits(seed, step, 1, index0 + i));
         param_bf16[i] = zs_oracle_bf16_rne(master[i]);
     }
     return ZO_OK;

@@ -30,7 +30,7 @@ int zs_oracle_shard_step_bf16mv(float *, uint16_t *, uint16_t *, uint16_t *,
                                 const hp_t *, int64_t);
 int zs_oracle_shard_step_bf16mv_sr(float *, uint16_t *, uint16_t *, uint16_t *,
                                    const uint16_t *const *, int, int64_t, const seg_t *, int32_t,
-                                   const hp_t *, int64_t, uint64_t);
+                                   const hp_t *, int64_t, uint64_t, int64_t);
 void zs_oracle_bf16_sr_array(const float *, const uint32_t *, uint16_t *, int64_t);
 
 static uint64_t rng_state = 0x9E3779B97F4A7C15ull;
@@ -111,7 +111,8 @@ int main(void)
                                                         nseg, &hp, t) != 0;
                 failures += zs_oracle_shard_step_bf16mv_sr(w, mb, vb, p,
                                                            (const uint16_t *const *)g, k, n,
-                                                           segs, nseg, &hp, t, 77u + t) != 0;
+                                                           segs, nseg, &hp, t, 77u + t,
+                                                           (int64_t)(t * 3)) != 0;
             }
             /* argument errors touch nothing */
             failures += zs_oracle_shard_step(w, m, v, p, (const uint16_t *const *)g, k, n, segs,

@@ -116,13 +116,15 @@ SR_MUTATIONS = [
      "    return (uint16_t)((u + (r & 0xffffu)) >> 16);",
      "    return (uint16_t)((u + (r & 0xffffu)) >> 16);"),
     ("SR m and v share one stream",
-     "zs_oracle_sr_bits(seed, step, 1, i)", "zs_oracle_sr_bits(seed, step, 0, i)"),
+     "zs_oracle_sr_bits(seed, step, 1, index0 + i)", "zs_oracle_sr_bits(seed, step, 0, index0 + i)"),
     ("SR one random field for a whole quad",
      "(word >> (16 * (i % 4))) & 0xffffu", "word & 0xffffu"),
     ("SR streams not keyed by the step",
      "2u * (uint64_t)step + (uint64_t)which", "(uint64_t)which"),
     ("SR streams not keyed by the seed",
      "uint64_t key = zs_oracle_splitmix64(seed,", "uint64_t key = zs_oracle_splitmix64(0,"),
+    ("SR window bits taken from the window's own index",
+     "zs_oracle_sr_bits(seed, step, 0, index0 + i)", "zs_oracle_sr_bits(seed, step, 0, i)"),
     ("SR generator's increment wrong",
      "return sm64_mix(key + (i + 1u) * 0x9E3779B97F4A7C15ull);",
      "return sm64_mix(key + i * 0x9E3779B97F4A7C15ull);"),
@@ -131,7 +133,8 @@ SR_MUTATIONS = [
 SR_BATTERY = [R.test_generator_is_the_published_splitmix64, R.test_rounding_distribution_is_exact,
               R.test_specials, R.test_first_step_matches_round_to_nearest_step,
               R.test_first_step_is_unbiased, R.test_random_streams_are_independent,
-              R.test_random_bits_are_uniform]
+              R.test_random_bits_are_uniform,
+              R.test_a_window_takes_the_bits_of_its_place_in_the_shard]
 
 VARIANT_BATTERY = [Q.test_hand_worked_block_with_ties, Q.test_zero_block_and_single_element,
                    Q.test_nonfinite_blocks_only_poison_themselves,
@@ -199,8 +202,10 @@ def test_planted_mistake_is_caught(name, old, new):
 
 @pytest.mark.parametrize("name,old,new", VARIANT_MUTATIONS, ids=[m[0] for m in VARIANT_MUTATIONS])
 def test_planted_variant_mistake_is_caught(name, old, new):
+    # the first occurrence is the routine the variant pins cover (the
+    # stochastic-rounding step repeats some of its lines further down)
     text = open(SRC).read()
-    assert text.count(old) == 1, "mutation site not found once: %s" % name
+    assert text.count(old) >= 1, "mutation site not found: %s" % name
     mutated = text.replace(old, new, 1)
     with tempfile.TemporaryDirectory() as d:
         lib = oracle.load_library(_compile(mutated, d))

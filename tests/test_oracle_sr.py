@@ -182,3 +182,27 @@ def test_random_bits_are_uniform():
     counts = np.bincount(r >> 12, minlength=16)
     sd = np.sqrt(n / 16 * (1 - 1 / 16))
     assert np.all(np.abs(counts - n / 16) < 5 * sd), counts
+
+
+def test_a_window_takes_the_bits_of_its_place_in_the_shard():
+    """Replaying elements [lo, hi) alone, with index0 = lo, gives exactly the
+    whole run's values there (the step is elementwise and each element's
+    random bits depend on its shard index); with index0 = 0 it does not."""
+    n, lo, hi = 40_000, 12_345, 23_457
+    rng = np.random.default_rng(8)
+    w0 = rng.normal(0, 0.02, n).astype(F32)
+    g = [(rng.normal(0, 1e-3, n).astype(F32).view(np.uint32) >> 16).astype(np.uint16)]
+    segs = [(0, True), (20_000, False)]
+    hp = oracle.hparams()
+    full = [w0.copy(), np.zeros(n, np.uint16), np.zeros(n, np.uint16), np.zeros(n, np.uint16)]
+    win = [w0[lo:hi].copy(), np.zeros(hi - lo, np.uint16), np.zeros(hi - lo, np.uint16),
+           np.zeros(hi - lo, np.uint16)]
+    shifted = [x.copy() for x in win]
+    wsegs = [(0, True), (20_000 - lo, False)]
+    for t in (1, 2, 3):
+        assert oracle.shard_step_bf16mv_sr(*full, g, segs, hp, t, 31) == 0
+        assert oracle.shard_step_bf16mv_sr(*win, [g[0][lo:hi]], wsegs, hp, t, 31, lo) == 0
+        assert oracle.shard_step_bf16mv_sr(*shifted, [g[0][lo:hi]], wsegs, hp, t, 31, 0) == 0
+    for a, b in zip(full, win):
+        assert np.array_equal(a[lo:hi].view(np.uint8), b.view(np.uint8))
+    assert not np.array_equal(shifted[1], win[1])
