@@ -111,6 +111,15 @@ def oracle_threads() -> int:
     return max(1, min(len(os.sched_getaffinity(0)), HOST_THREAD_CAP))
 
 
+# the arithmetic families with bf16 moments
+MV16 = ("bf16mv", "bf16mv_sr")
+
+
+def sr_seed(w) -> int:
+    """The random-stream seed the stochastic-rounding steps use on a workload."""
+    return (w.seed * 0x9E3779B1 + 17) & (2 ** 64 - 1)
+
+
 # ---------------------------------------------------------------- parity windows
 
 PARITY_WINDOW = 1 << 20
@@ -175,13 +184,13 @@ def snapshot_packed(state, wins, mv16=False):
 
 # the packed-state form of each entry point that has one
 PACKED_FORM = {"base": "packed", "q8ag": "packed_q8ag", "q8grad": "packed_q8grad",
-               "bf16mv": "packed_bf16mv"}
+               "bf16mv": "packed_bf16mv", "bf16mv_sr": "packed_bf16mv_sr"}
 
 
 def packed_state_floats(var, n):
     """Floats (or floats' room) of the packed state of entry point `var`."""
     import sharded_mixed_precision_shard_amd as zs
-    return zs.packed_bf16mv_floats(n) if var.endswith("bf16mv") else zs.packed_floats(n)
+    return zs.packed_bf16mv_floats(n) if "bf16mv" in var else zs.packed_floats(n)
 
 
 def packed_leg(torch, w, var, pstate, bufs, st, hp, stream, args, bytes_per_step):
@@ -201,7 +210,8 @@ def packed_leg(torch, w, var, pstate, bufs, st, hp, stream, args, bytes_per_step
         want["q8s"] = [block_slice(q8s, a, b).cpu().numpy().copy() for a, b in wins]
     partials = bufs["qgrads"] if pvar == "packed_q8grad" else bufs["grads"]
     call = zs.ShardStep(pstate, None, None, param, partials, n, st, hp, variant=pvar,
-                        param_q8=q8, param_q8_scale=q8s, qscales=bufs["qscales"])
+                        param_q8=q8, param_q8_scale=q8s, qscales=bufs["qscales"],
+                        seed=sr_seed(w) if pvar.endswith("_sr") else None)
     t = w.t0
     for _ in range(args.warmup):
         call(t, stream)
@@ -217,7 +227,7 @@ def packed_leg(torch, w, var, pstate, bufs, st, hp, stream, args, bytes_per_step
     torch.cuda.synchronize()
     ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
     avg = sum(ms) / len(ms)
-    got = snapshot_packed(pstate, wins, mv16=pvar == "packed_bf16mv")
+    got = snapshot_packed(pstate, wins, mv16="bf16mv" in pvar)
     got.update(snapshot({"param": param, "q8": q8}, wins))
     if q8s is not None:
         got["q8s"] = [block_slice(q8s, a, b).cpu().numpy().copy() for a, b in wins]
@@ -322,6 +332,10 @@ def _parity_replay(w, variant, par):
                 rc = oracle.shard_step_bf16mv(master, m.view(np.uint16), v.view(np.uint16), p,
                                               [g[i].view(np.uint16) for g in par["grads"]],
                                               segs, hp, t)
+            elif variant == "bf16mv_sr":
+                rc = oracle.shard_step_bf16mv_sr(master, m.view(np.uint16), v.view(np.uint16),
+                                                 p, [g[i].view(np.uint16) for g in par["grads"]],
+                                                 segs, hp, t, sr_seed(w), a)
             else:
                 rc = oracle.shard_step(master, m, v, p,
                                        [g[i].view(np.uint16) for g in par["grads"]], segs, hp, t)
@@ -331,7 +345,7 @@ def _parity_replay(w, variant, par):
         exact &= gm.tobytes() == master.tobytes() and gmm.tobytes() == m.tobytes() and \
             gv.tobytes() == v.tobytes() and gp.tobytes() == p.tobytes()
         errs["master"] = max(errs["master"], _rel_err(gm, master))
-        if variant == "bf16mv":
+        if variant in MV16:
             ulp_mv = max(ulp_mv, _bf16_ulp(gmm, m), _bf16_ulp(gv, v))
         else:
             errs["m"] = max(errs["m"], _rel_err(gmm, m))
@@ -347,10 +361,10 @@ def _parity_replay(w, variant, par):
     out = {"windows": len(wins), "window_elements": elems, "steps_replayed": len(ts),
            "first_t": ts[0], "last_t": ts[-1],
            "max_rel_err": {k: float("%.3g" % e) for k, e in errs.items()
-                           if not (variant == "bf16mv" and k != "master")},
+                           if not (variant in MV16 and k != "master")},
            "max_param_bf16_ulp": ulp_p, "bitwise_equal": bool(exact),
            "oracle_seconds": round(elapsed, 3)}
-    if variant == "bf16mv":
+    if variant in MV16:
         out["max_moment_bf16_ulp"] = ulp_mv
     if variant == "q8ag":
         out["max_q8_code_diff"] = dq
@@ -369,7 +383,7 @@ def _throughput_sample(w, seconds, variant, bytes_per_elem):
     n = min(w.n, 1 << 27)
     threads = oracle_threads()
     master = synth.host_master(w, 0, n, threads=threads)
-    mv_dtype = np.uint16 if variant == "bf16mv" else np.float32
+    mv_dtype = np.uint16 if variant in MV16 else np.float32
     m = np.zeros(n, mv_dtype)
     v = np.zeros(n, mv_dtype)
     p = np.zeros(n, np.uint16)
@@ -389,6 +403,8 @@ def _throughput_sample(w, seconds, variant, bytes_per_elem):
             rc = oracle.shard_step_q8grad(master, m, v, p, qgrads, qscales, segs, hp, t)
         elif variant == "bf16mv":
             rc = oracle.shard_step_bf16mv(master, m, v, p, grads, segs, hp, t)
+        elif variant == "bf16mv_sr":
+            rc = oracle.shard_step_bf16mv_sr(master, m, v, p, grads, segs, hp, t, sr_seed(w))
         else:
             rc = oracle.shard_step(master, m, v, p, grads, segs, hp, t)
             if variant == "q8ag":
@@ -403,7 +419,7 @@ def _throughput_sample(w, seconds, variant, bytes_per_elem):
     threaded = _threaded_oracle(master, m, v, p, grads if variant != "q8grad" else None,
                                 segs, hp, t, variant, bytes_per_elem, threads,
                                 qgrads if variant == "q8grad" else None,
-                                qscales if variant == "q8grad" else None)
+                                qscales if variant == "q8grad" else None, seed=sr_seed(w))
     return {
         "value": round(n * steps * bytes_per_elem / elapsed / 1e9, 4),
         "unit": "GB/s",
@@ -420,7 +436,7 @@ def _throughput_sample(w, seconds, variant, bytes_per_elem):
 
 
 def _threaded_oracle(master, m, v, p, grads, segs, hp, t, variant, bytes_per_elem, threads,
-                     qgrads=None, qscales=None, seconds=3.0):
+                     qgrads=None, qscales=None, seconds=3.0, seed=0):
     """The same oracle driven from T threads over T contiguous ranges of the
     window (the step is elementwise, so the split does not change a bit);
     T = the CPUs this process may use, at most HOST_THREAD_CAP."""
@@ -446,6 +462,10 @@ def _threaded_oracle(master, m, v, p, grads, segs, hp, t, variant, bytes_per_ele
         if variant == "bf16mv":
             return oracle.shard_step_bf16mv(master[a:b], m[a:b], v[a:b], p[a:b],
                                             [g[a:b] for g in grads], tabs[i], hp, step)
+        if variant == "bf16mv_sr":
+            return oracle.shard_step_bf16mv_sr(master[a:b], m[a:b], v[a:b], p[a:b],
+                                               [g[a:b] for g in grads], tabs[i], hp, step,
+                                               seed, a)
         rc = oracle.shard_step(master[a:b], m[a:b], v[a:b], p[a:b], [g[a:b] for g in grads],
                                tabs[i], hp, step)
         if variant == "q8ag":
@@ -492,6 +512,8 @@ def twin_bytes(variant: str, k: int, n: int):
             "packed_q8ag": ((12 + 2 * k) * n, 15 * n + 4 * nb),
             "packed_q8grad": (12 * n + k * (n + 4 * nb), 14 * n),
             "packed_bf16mv": ((8 + 2 * k) * n, 10 * n),
+            "bf16mv_sr": ((8 + 2 * k) * n, 10 * n),
+            "packed_bf16mv_sr": ((8 + 2 * k) * n, 10 * n),
             "q8ag": ((12 + 2 * k) * n, 15 * n + 4 * nb),
             "q8grad": (12 * n + k * (n + 4 * nb), 14 * n),
             "bf16mv": ((8 + 2 * k) * n, 10 * n)}[variant]
@@ -507,7 +529,7 @@ class Twin:
     step's own buffers and in the step's own launch."""
     MODES = {"step": 0, "read": 1, "write": 2}
     LAYOUT = {"base": 0, "q8ag": 1, "q8grad": 2, "bf16mv": 4, "packed": 8, "packed_q8ag": 9,
-              "packed_q8grad": 10, "packed_bf16mv": 12}
+              "packed_q8grad": 10, "packed_bf16mv": 12, "bf16mv_sr": 4, "packed_bf16mv_sr": 12}
 
     def __init__(self, torch, variant, bufs, k, n, plan):
         import ctypes
@@ -778,11 +800,14 @@ def main():
     ap.add_argument("--config", default="70b")
     ap.add_argument("--variant", default="base",
                     choices=("base", "q8ag", "q8grad", "bf16mv", "packed", "packed_q8ag",
-                             "packed_q8grad", "packed_bf16mv", "offload"),
+                             "packed_q8grad", "packed_bf16mv", "bf16mv_sr", "packed_bf16mv_sr",
+                             "offload"),
                     help="entry point: zs_shard_step (base), zs_shard_step_q8ag, "
                          "zs_shard_step_q8grad, zs_shard_step_bf16mv, zs_shard_step_packed "
                          "(master, m, v packed per 256-element block), zs_shard_step_packed_q8ag, "
-                         "zs_shard_step_packed_q8grad, zs_shard_step_packed_bf16mv, or the host "
+                         "zs_shard_step_packed_q8grad, zs_shard_step_packed_bf16mv, "
+                         "zs_shard_step_bf16mv_sr and zs_shard_step_packed_bf16mv_sr (bf16 "
+                         "moments rounded stochastically), or the host "
                          "(ZeRO-Offload) step zs_host_shard_step, which runs on the CPU "
                          "and needs no GPU")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -870,14 +895,14 @@ def main():
 
     dev = torch.device("cuda:0")
     nb = -(-n // zs.ZS_Q8_BLOCK)
-    mv_dtype = torch.int16 if var == "bf16mv" else torch.float32
+    mv_dtype = torch.int16 if var in MV16 else torch.float32
     packed_var = var.startswith("packed")
     q8grad_var = var in ("q8grad", "packed_q8grad")
     q8ag_var = var in ("q8ag", "packed_q8ag")
     # the oracle arithmetic the variant computes (the packed forms compute their plain form's)
     arith = {"packed": "base", "packed_q8ag": "q8ag", "packed_q8grad": "q8grad",
-             "packed_bf16mv": "bf16mv"}.get(var, var)
-    mv16 = arith == "bf16mv"
+             "packed_bf16mv": "bf16mv", "packed_bf16mv_sr": "bf16mv_sr"}.get(var, var)
+    mv16 = arith in MV16
     state = master = m = v = None
     if packed_var:
         # master, m and v in one array, per 256-element block
@@ -944,6 +969,11 @@ def main():
                             qscales=qscales)
     elif var == "packed_bf16mv":
         call = zs.ShardStep(state, None, None, param, grads, n, st, hp, variant=var)
+    elif var == "packed_bf16mv_sr":
+        call = zs.ShardStep(state, None, None, param, grads, n, st, hp, variant=var,
+                            seed=sr_seed(w))
+    elif var == "bf16mv_sr":
+        call = zs.ShardStep(master, m, v, param, grads, n, st, hp, variant=var, seed=sr_seed(w))
     else:
         call = zs.ShardStep(master, m, v, param, grads, n, st, hp, cfg=cfg)
 
@@ -1131,7 +1161,12 @@ def main():
                     "packed_q8grad": "f32 master/m/v packed per 256-element block, int8 "
                                      "partials, bf16 param",
                     "packed_bf16mv": "f32 master and bf16 m/v packed per 256-element block, "
-                                     "bf16 partials and param"}[var],
+                                     "bf16 partials and param",
+                    "bf16mv_sr": "f32 master, bf16 m/v (stochastically rounded), partials and "
+                                 "param",
+                    "packed_bf16mv_sr": "f32 master and bf16 m/v (stochastically rounded) "
+                                        "packed per 256-element block, bf16 partials and "
+                                        "param"}[var],
         "data": "synthetic (seeded SplitMix64 / Irwin-Hall draws; partials of the first "
                 "measured step kept resident across timed steps)",
         "config": {

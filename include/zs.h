@@ -108,10 +108,11 @@ typedef struct {
                               congestion on many physical placements of the arrays.
                               0 = default: none below 2^26 elements, a cap of 5
                               from 2^26 elements on, except for
-                              zs_shard_step_bf16mv (and its packed form) below
-                              2^32 elements or with k > 4 (no cap); from 2^32
-                              elements with k <= 4 it takes two 256-element
-                              sub-windows per wavefront.
+                              zs_shard_step_bf16mv (and its packed and
+                              stochastic forms) below 2^32 elements or with
+                              k > 4 (no cap); from 2^32 elements with k <= 4
+                              it takes two 256-element sub-windows per
+                              wavefront.
                               A cap whose LDS share exceeds the per-workgroup
                               limit returns ZS_ERR_INVALID_ARGUMENT. */
     int32_t block_order;  /* 0 = default, 1 = linear (workgroup b takes chunk b),
@@ -305,6 +306,37 @@ int zs_shard_step_packed_bf16mv(float *state, uint16_t *param_bf16,
                                 int64_t step, void *stream);
 
 /*
+ * zs_shard_step_bf16mv (and its packed form) with the new m and v rounded to
+ * bf16 stochastically instead of to nearest: the other reading of "Lecture 7:
+ * Parallelism I", section 8.4, which keeps the moments in bf16 without saying
+ * how they are rounded.  Each moment's magnitude is rounded up to the next
+ * bf16 with probability (its 16 dropped bits) / 2^16 and down otherwise, so
+ * the stored moment equals the exact one in expectation; NaN -> 0x7FC0,
+ * infinities stay, the largest finite value may round up to infinity.  The
+ * master update uses the unrounded moments and the parameter copy is rounded
+ * to nearest even, as in zs_shard_step_bf16mv.
+ *
+ * Random bits: SplitMix64 (Steele, Lea and Flood, "Fast splittable
+ * pseudorandom number generators", OOPSLA 2014) used counter-style, output i
+ * of key K being mix64(K + (i + 1) * 0x9E3779B97F4A7C15).  At step t the key
+ * of m's stream is output 2t of `seed`, that of v's output 2t + 1; element i
+ * (shard-local) takes bits 16 (i mod 4) .. 16 (i mod 4) + 15 of output i / 4
+ * of the stream.  The result is a function of (inputs, step, seed) alone,
+ * whatever the launch; ranks should pass different seeds.
+ *
+ * Arguments, layout, errors and traffic as zs_shard_step_bf16mv and
+ * zs_shard_step_packed_bf16mv, plus `seed`.
+ */
+int zs_shard_step_bf16mv_sr(float *master, uint16_t *m_bf16, uint16_t *v_bf16,
+                            uint16_t *param_bf16, const uint16_t *const *grads, int k, int64_t n,
+                            const zs_seg_table *seg_table, const zs_hparams *hparams,
+                            int64_t step, uint64_t seed, void *stream);
+int zs_shard_step_packed_bf16mv_sr(float *state, uint16_t *param_bf16,
+                                   const uint16_t *const *grads, int k, int64_t n,
+                                   const zs_seg_table *seg_table, const zs_hparams *hparams,
+                                   int64_t step, uint64_t seed, void *stream);
+
+/*
  * Convert, on `stream`, between separate master, m and v arrays (DEVICE fp32
  * [n] each) and the packed state of zs_shard_step_packed (DEVICE fp32
  * [ZS_PACKED_FLOATS(n)]).  zs_pack_state writes every slot of the state, the
@@ -361,6 +393,8 @@ int zs_launch_geometry(int k, int64_t n, const zs_launch_cfg *cfg, int64_t *work
 #define ZS_VARIANT_PACKED_Q8AG 17   /* zs_shard_step_packed_q8ag */
 #define ZS_VARIANT_PACKED_Q8GRAD 18 /* zs_shard_step_packed_q8grad */
 #define ZS_VARIANT_PACKED_BF16MV 20 /* zs_shard_step_packed_bf16mv */
+#define ZS_VARIANT_BF16MV_SR 36     /* zs_shard_step_bf16mv_sr */
+#define ZS_VARIANT_PACKED_BF16MV_SR 52 /* zs_shard_step_packed_bf16mv_sr */
 
 /* The launch a step call resolves its defaults to. */
 typedef struct {
@@ -373,8 +407,9 @@ typedef struct {
                                dropped at launch) */
     int32_t nontemporal;    /* 1 = streaming loads and stores, 0 = cached */
     int32_t window_quads;   /* 256-element sub-windows each wavefront takes per tile
-                               (1, or 2 for zs_shard_step_bf16mv and its packed form on
-                               shards of at least 2^32 elements with k <= 4) */
+                               (1, or 2 for zs_shard_step_bf16mv and its packed and
+                               stochastic forms on shards of at least 2^32 elements
+                               with k <= 4) */
 } zs_launch_info;
 
 /* The launch a call of entry point `variant` (ZS_VARIANT_*) over n elements

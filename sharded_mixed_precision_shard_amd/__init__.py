@@ -9,7 +9,8 @@ Entry points keep the C names: :func:`zs_init`, :func:`zs_shard_step`,
 :func:`zs_shard_step_cfg`, :func:`zs_shard_step_q8ag`, :func:`zs_shard_step_q8grad`,
 :func:`zs_shard_step_bf16mv`, :func:`zs_shard_step_packed`,
 :func:`zs_shard_step_packed_q8ag`, :func:`zs_shard_step_packed_q8grad`,
-:func:`zs_shard_step_packed_bf16mv`, :func:`zs_pack_state`, :func:`zs_unpack_state`,
+:func:`zs_shard_step_packed_bf16mv`, :func:`zs_shard_step_bf16mv_sr`,
+:func:`zs_shard_step_packed_bf16mv_sr`, :func:`zs_pack_state`, :func:`zs_unpack_state`,
 :func:`zs_pack_state_bf16mv`, :func:`zs_unpack_state_bf16mv`, :func:`zs_fini`,
 :func:`zs_status_string`, :func:`zs_last_device_error`, :func:`zs_algorithmic_bytes`,
 :func:`zs_launch_geometry`, :func:`zs_launch_plan`.
@@ -37,13 +38,14 @@ ZS_ERR_DEVICE = 5
 ZS_ERR_ALIASING = 6
 
 ZS_VARIANT = {"base": 0, "q8ag": 1, "q8grad": 2, "bf16mv": 4, "packed": 16, "packed_q8ag": 17,
-              "packed_q8grad": 18, "packed_bf16mv": 20}
+              "packed_q8grad": 18, "packed_bf16mv": 20, "bf16mv_sr": 36, "packed_bf16mv_sr": 52}
 
 # Symbols declared in include/zs.h.
 EXPORTS = ("zs_init", "zs_shard_step", "zs_shard_step_cfg", "zs_shard_step_q8ag",
            "zs_shard_step_q8grad", "zs_shard_step_bf16mv", "zs_shard_step_packed",
            "zs_shard_step_packed_q8ag", "zs_shard_step_packed_q8grad",
-           "zs_shard_step_packed_bf16mv", "zs_pack_state", "zs_unpack_state",
+           "zs_shard_step_packed_bf16mv", "zs_shard_step_bf16mv_sr",
+           "zs_shard_step_packed_bf16mv_sr", "zs_pack_state", "zs_unpack_state",
            "zs_pack_state_bf16mv", "zs_unpack_state_bf16mv", "zs_fini", "zs_status_string",
            "zs_last_device_error", "zs_algorithmic_bytes", "zs_launch_geometry",
            "zs_launch_plan")
@@ -133,6 +135,11 @@ def load_library():
     lib.zs_shard_step_packed_q8grad.restype = ctypes.c_int
     lib.zs_shard_step_packed_bf16mv.argtypes = lib.zs_shard_step_packed.argtypes
     lib.zs_shard_step_packed_bf16mv.restype = ctypes.c_int
+    lib.zs_shard_step_bf16mv_sr.argtypes = step_args[:-1] + [ctypes.c_uint64, P]
+    lib.zs_shard_step_bf16mv_sr.restype = ctypes.c_int
+    lib.zs_shard_step_packed_bf16mv_sr.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int64, P, P,
+                                                   ctypes.c_int64, ctypes.c_uint64, P]
+    lib.zs_shard_step_packed_bf16mv_sr.restype = ctypes.c_int
     lib.zs_pack_state_bf16mv.argtypes = [P, P, P, P, ctypes.c_int64, P]
     lib.zs_pack_state_bf16mv.restype = ctypes.c_int
     lib.zs_unpack_state_bf16mv.argtypes = [P, P, P, P, ctypes.c_int64, P]
@@ -398,6 +405,28 @@ def zs_shard_step_bf16mv(master, m_bf16, v_bf16, param_bf16, grads, k, n, seg_ta
     return rc
 
 
+def zs_shard_step_bf16mv_sr(master, m_bf16, v_bf16, param_bf16, grads, k, n, seg_table_,
+                            hparams_, step, seed, stream=None, check=True) -> int:
+    """zs_shard_step_bf16mv with m and v rounded stochastically; `seed`
+    (uint64) selects the random streams."""
+    pm, pmm, pv, pp, pg, kk, st, hp, keep = _marshal(master, m_bf16, v_bf16, param_bf16, grads,
+                                                     k, n, seg_table_, hparams_, mv_size=2)
+    rc = load_library().zs_shard_step_bf16mv_sr(pm, pmm, pv, pp, pg, kk, int(n), ctypes.byref(st),
+                                                ctypes.byref(hp), int(step), _seed(seed),
+                                                ctypes.c_void_p(_stream_handle(stream)))
+    del keep
+    if check and rc != ZS_OK:
+        raise ZsError(rc, "zs_shard_step_bf16mv_sr")
+    return rc
+
+
+def _seed(seed) -> int:
+    s = int(seed)
+    if not 0 <= s < 2 ** 64:
+        raise ValueError("seed must be an unsigned 64-bit integer, got %d" % s)
+    return s
+
+
 def zs_shard_step_packed(state, param_bf16, grads, k, n, seg_table_, hparams_, step,
                          stream=None, check=True) -> int:
     """zs_shard_step on the packed optimizer state (fp32 [packed_floats(n)]:
@@ -502,6 +531,23 @@ def zs_unpack_state(state, master, m, v, n, stream=None, check=True) -> int:
     return rc
 
 
+def zs_shard_step_packed_bf16mv_sr(state, param_bf16, grads, k, n, seg_table_, hparams_, step,
+                                   seed, stream=None, check=True) -> int:
+    """zs_shard_step_packed_bf16mv with m and v rounded stochastically."""
+    k = _check_k(k, grads, "grads")
+    nn = max(int(n), 0)
+    gp = _ptr_array(grads, 2 * nn, "grads")
+    st = seg_table_ if isinstance(seg_table_, ZsSegTable) else seg_table(seg_table_)
+    rc = load_library().zs_shard_step_packed_bf16mv_sr(
+        ctypes.c_void_p(_dev(state, 4 * packed_bf16mv_floats(nn), "state")),
+        ctypes.c_void_p(_dev(param_bf16, 2 * nn, "param_bf16")), ctypes.cast(gp, ctypes.c_void_p),
+        int(k), int(n), ctypes.byref(st), ctypes.byref(hparams_), int(step), _seed(seed),
+        ctypes.c_void_p(_stream_handle(stream)))
+    if check and rc != ZS_OK:
+        raise ZsError(rc, "zs_shard_step_packed_bf16mv_sr")
+    return rc
+
+
 def zs_pack_state_bf16mv(master, m_bf16, v_bf16, state, n, stream=None, check=True) -> int:
     """fp32 master, bf16 m, v [n] -> packed bf16-moment state (padding zero)."""
     nn = max(int(n), 0)
@@ -540,12 +586,22 @@ class ShardStep:
     are the int8 partials, ``qscales`` their block scales) or "bf16mv" (m and
     v are bf16) or "packed" (``master`` is the packed state, m and v are None),
     and "packed_q8ag" / "packed_q8grad" / "packed_bf16mv" (those forms on
-    their packed state).
+    their packed state); "bf16mv_sr" and "packed_bf16mv_sr" round the bf16
+    moments stochastically with the random streams of ``seed``.
     The tensors are referenced for the object's lifetime."""
 
     def __init__(self, master, m, v, param_bf16, grads, n, seg_table_, hparams_,
-                 variant="base", param_q8=None, param_q8_scale=None, qscales=None, cfg=None):
+                 variant="base", param_q8=None, param_q8_scale=None, qscales=None, cfg=None,
+                 seed=None):
         lib = load_library()
+        # the stochastic forms take the seed between the step and the stream
+        self._mid = []
+        if variant.endswith("_sr"):
+            if seed is None:
+                raise ValueError("%s needs a seed" % variant)
+            self._mid = [_seed(seed)]
+        elif seed is not None:
+            raise ValueError("a seed applies to the stochastic-rounding forms only")
         self._keep = [master, m, v, param_bf16, list(grads), seg_table_, param_q8,
                       param_q8_scale, qscales]
         self.n = int(n)
@@ -563,12 +619,14 @@ class ShardStep:
             head = [pm, pmm, pv, pp, ctypes.cast(qp, ctypes.c_void_p),
                     ctypes.cast(sp, ctypes.c_void_p)]
             fn = lib.zs_shard_step_q8grad
-        elif variant in ("packed", "packed_q8ag", "packed_q8grad", "packed_bf16mv"):
+        elif variant in ("packed", "packed_q8ag", "packed_q8grad", "packed_bf16mv",
+                         "packed_bf16mv_sr"):
             if m is not None or v is not None:
                 raise ValueError("the packed step takes its m and v inside the state")
             st = seg_table_ if isinstance(seg_table_, ZsSegTable) else seg_table(seg_table_)
             hp = hparams_
-            floats = packed_bf16mv_floats(nn) if variant == "packed_bf16mv" else packed_floats(nn)
+            floats = packed_bf16mv_floats(nn) if variant.startswith("packed_bf16mv") \
+                else packed_floats(nn)
             head = [ctypes.c_void_p(_dev(master, 4 * floats, "state")),
                     ctypes.c_void_p(_dev(param_bf16, 2 * nn, "param_bf16"))]
             if variant == "packed_q8grad":
@@ -588,11 +646,13 @@ class ShardStep:
                     fn = lib.zs_shard_step_packed_q8ag
                 elif variant == "packed_bf16mv":
                     fn = lib.zs_shard_step_packed_bf16mv
+                elif variant == "packed_bf16mv_sr":
+                    fn = lib.zs_shard_step_packed_bf16mv_sr
                 else:
                     fn = lib.zs_shard_step_packed
                 head.append(ctypes.cast(gp, ctypes.c_void_p))
         else:
-            mv = 2 if variant == "bf16mv" else 4
+            mv = 2 if variant in ("bf16mv", "bf16mv_sr") else 4
             pm, pmm, pv, pp, pg, _, st, hp, gp = _marshal(master, m, v, param_bf16, grads, k, n,
                                                           seg_table_, hparams_, mv_size=mv)
             self._c = (gp,)
@@ -602,6 +662,8 @@ class ShardStep:
                 fn = lib.zs_shard_step_q8ag
             elif variant == "bf16mv":
                 head, fn = [pm, pmm, pv, pp, pg], lib.zs_shard_step_bf16mv
+            elif variant == "bf16mv_sr":
+                head, fn = [pm, pmm, pv, pp, pg], lib.zs_shard_step_bf16mv_sr
             elif variant == "base":
                 head = [pm, pmm, pv, pp, pg]
                 fn = lib.zs_shard_step_cfg if cfg else lib.zs_shard_step
@@ -619,8 +681,8 @@ class ShardStep:
         self.variant = variant
 
     def __call__(self, step, stream=None, check=True) -> int:
-        rc = self._fn(*self._head, int(step), ctypes.c_void_p(_stream_handle(stream)),
-                      *self._tail)
+        rc = self._fn(*self._head, int(step), *self._mid,
+                      ctypes.c_void_p(_stream_handle(stream)), *self._tail)
         if check and rc != ZS_OK:
             raise ZsError(rc, "ShardStep(%s)" % self.variant)
         return rc
@@ -635,7 +697,7 @@ def algorithmic_bytes(variant: str, k: int, n: int) -> int:
         return (26 + 2 * k) * n + n + 4 * nb
     if variant in ("q8grad", "packed_q8grad"):
         return (12 + k + 14) * n + 4 * k * nb
-    if variant in ("bf16mv", "packed_bf16mv"):
+    if variant in ("bf16mv", "packed_bf16mv", "bf16mv_sr", "packed_bf16mv_sr"):
         return (18 + 2 * k) * n
     raise ValueError(variant)
 

@@ -96,7 +96,8 @@ int resolve_launch(int k, int64_t n, int variant, const zs_launch_cfg *cfg,
     if (k < 1 || k > ZS_MAX_K || n < 0 || n > INT64_MAX / 8) return ZS_ERR_INVALID_ARGUMENT;
     if (variant != 0 && variant != kOutQ8 && variant != kGradQ8 && variant != kMvBf16 &&
         variant != kPacked && variant != (kPacked | kOutQ8) && variant != (kPacked | kGradQ8) &&
-        variant != (kPacked | kMvBf16))
+        variant != (kPacked | kMvBf16) && variant != (kMvBf16 | kSR) &&
+        variant != (kPacked | kMvBf16 | kSR))
         return ZS_ERR_INVALID_ARGUMENT;
     // Streaming (non-temporal) loads and stores by default: nothing is
     // reused, and on MI355X they measured 5-10 % faster than cached access.
@@ -151,6 +152,7 @@ struct Request {
     void *stream = nullptr;
     const zs_launch_cfg *cfg = nullptr;
     int variant = 0;
+    uint64_t seed = 0;  // kSR: the caller's seed of the random streams
 };
 
 struct Span {
@@ -262,6 +264,9 @@ int validate_and_launch(const Request &r) {
         a.df = 1.0f - lrwd;
     }
     a.gscale = hp->grad_scale;
+    // kSR: the stream keys of this step's m and v roundings
+    a.sr_key_m = sr_word(r.seed, 2u * (uint64_t)r.step);
+    a.sr_key_v = sr_word(r.seed, 2u * (uint64_t)r.step + 1u);
 
     const int64_t blocks = plan.workgroups;
     a.chunk = plan.chunk_elements;
@@ -468,6 +473,30 @@ int zs_shard_step_packed_bf16mv(float *state, uint16_t *param_bf16,
                              stream);
     r.grads = grads;
     r.variant = kPacked | kMvBf16;
+    return validate_and_launch(r);
+}
+
+int zs_shard_step_bf16mv_sr(float *master, uint16_t *m_bf16, uint16_t *v_bf16,
+                            uint16_t *param_bf16, const uint16_t *const *grads, int k, int64_t n,
+                            const zs_seg_table *seg_table, const zs_hparams *hparams,
+                            int64_t step, uint64_t seed, void *stream) {
+    Request r = base_request(master, m_bf16, v_bf16, param_bf16, k, n, seg_table, hparams, step,
+                             stream);
+    r.grads = grads;
+    r.variant = kMvBf16 | kSR;
+    r.seed = seed;
+    return validate_and_launch(r);
+}
+
+int zs_shard_step_packed_bf16mv_sr(float *state, uint16_t *param_bf16,
+                                   const uint16_t *const *grads, int k, int64_t n,
+                                   const zs_seg_table *seg_table, const zs_hparams *hparams,
+                                   int64_t step, uint64_t seed, void *stream) {
+    Request r = base_request(state, nullptr, nullptr, param_bf16, k, n, seg_table, hparams, step,
+                             stream);
+    r.grads = grads;
+    r.variant = kPacked | kMvBf16 | kSR;
+    r.seed = seed;
     return validate_and_launch(r);
 }
 

@@ -27,6 +27,10 @@ constexpr int kSub = kWave * kQuad;           // 256: one dense instruction per 
 //             of optimizer state plus weight instead of 16).
 //   kWide   - two sub-windows per wave instead of one (launch-time choice for
 //             the bf16-moment step on the largest shards, see quads_for);
+//   kSR     - with kMvBf16: m and v are rounded to bf16 stochastically (the
+//             magnitude rounds up with probability equal to the dropped
+//             bits over 2^16), with 16 random bits per rounding from
+//             SplitMix64 streams keyed per step and moment (see sr_word);
 //   kPacked - master, m and v live in one array, packed per kSub-element
 //             block: block b holds the master values of elements kSub*b ..
 //             kSub*b + kSub-1, then their m, then their v (ZS packed layout;
@@ -36,6 +40,20 @@ constexpr int kGradQ8 = 2;
 constexpr int kMvBf16 = 4;
 constexpr int kWide = 8;
 constexpr int kPacked = 16;
+constexpr int kSR = 32;
+
+// SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+// generators", OOPSLA 2014) used counter-style: output i of the stream with
+// key `key`.  The stochastic step's stream for moment w (0 = m, 1 = v) at
+// step t has key sr_word(seed, 2t + w); element i takes the 16 bits
+// 16 (i mod 4) .. 16 (i mod 4) + 15 of its output i / 4.
+__host__ __device__ constexpr uint64_t sr_word(uint64_t key, uint64_t i) {
+    uint64_t z = key + (i + 1u) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+static_assert(sr_word(0, 0) == 0xE220A8397B1DCDAFull, "SplitMix64's first output for seed 0");
 
 // Packed layout: index of element i's master value (its m is kSub further,
 // its v 2*kSub further), and floats the packed state holds for n elements.
@@ -90,6 +108,7 @@ struct StepArgs {
     int32_t nseg;
     int32_t xcds;   // XCDs the dispatcher deals workgroups to in turn; 1 = linear order
     float lr, b1, b2, c1, c2, bc1, bc2, eps, df, gscale;
+    uint64_t sr_key_m, sr_key_v;  // kSR: the step's stream keys for m and v
 };
 
 constexpr int kQ8Block = ZS_Q8_BLOCK;

@@ -233,6 +233,44 @@ __device__ __forceinline__ u32x2 f32x4_to_bf16x4(f32x4 x) {
     return r;
 }
 
+// Stochastic fp32 -> bf16 with the 16 random bits r: adding r below the
+// kept bits and dropping them rounds the magnitude up with probability
+// (dropped bits) / 2^16 (the carry stays inside the magnitude; the largest
+// finite value can round up to infinity); NaN -> 0x7FC0, infinities stay.
+__device__ __forceinline__ uint32_t to_bf16_sr(float x, uint32_t r) {
+    const uint32_t u = __float_as_uint(x);
+    return ((u & 0x7fffffffu) > 0x7f800000u) ? 0x7fc0u : ((u + r) >> 16);
+}
+
+// A moment quad (elements 4 qi .. 4 qi + 3) to bf16: to nearest even, or
+// stochastically (kSR) with the 64-bit word qi of the stream `key`, 16 bits
+// per element, the lowest for the first.
+template <int V>
+__device__ __forceinline__ u32x2 moment_bf16x4(f32x4 x, uint64_t key, int64_t qi) {
+    if constexpr ((V & kSR) != 0) {
+        const uint64_t w = sr_word(key, (uint64_t)qi);
+        u32x2 r;
+        r[0] = to_bf16_sr(x[0], (uint32_t)w & 0xffffu) |
+               (to_bf16_sr(x[1], (uint32_t)(w >> 16) & 0xffffu) << 16);
+        r[1] = to_bf16_sr(x[2], (uint32_t)(w >> 32) & 0xffffu) |
+               (to_bf16_sr(x[3], (uint32_t)(w >> 48)) << 16);
+        return r;
+    } else {
+        return f32x4_to_bf16x4(x);
+    }
+}
+
+// One moment element i to bf16, as moment_bf16x4 does it for its quad.
+template <int V>
+__device__ __forceinline__ uint32_t moment_bf16(float x, uint64_t key, int64_t i) {
+    if constexpr ((V & kSR) != 0) {
+        const uint64_t w = sr_word(key, (uint64_t)(i / kQuad));
+        return to_bf16_sr(x, (uint32_t)(w >> (16 * (i % kQuad))) & 0xffffu);
+    } else {
+        return to_bf16(x);
+    }
+}
+
 __device__ __forceinline__ float i8_at(uint32_t word, int byte) {
     return (float)(int32_t)(int8_t)(uint8_t)(word >> (8 * byte));
 }
@@ -464,8 +502,8 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
                     u32x2 *p16 = reinterpret_cast<u32x2 *>(a.master);
                     const int64_t qm = packed16_m(e[qd]) / kQuad;
                     store<NT>(pw + packed16_master(e[qd]) / kQuad, wv[qd]);
-                    store<NT>(p16 + qm, f32x4_to_bf16x4(mv[qd]));
-                    store<NT>(p16 + qm + kWave, f32x4_to_bf16x4(vv[qd]));
+                    store<NT>(p16 + qm, moment_bf16x4<V>(mv[qd], a.sr_key_m, qi));
+                    store<NT>(p16 + qm + kWave, moment_bf16x4<V>(vv[qd], a.sr_key_v, qi));
                 } else if constexpr (V & kPacked) {
                     const int64_t qs = packed_index(e[qd]) / kQuad;
                     store<NT>(pw + qs, wv[qd]);
@@ -473,8 +511,10 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
                     store<NT>(pw + qs + 2 * kWave, vv[qd]);
                 } else if constexpr (V & kMvBf16) {
                     store<NT>(pw + qi, wv[qd]);
-                    store<NT>(reinterpret_cast<u32x2 *>(a.m) + qi, f32x4_to_bf16x4(mv[qd]));
-                    store<NT>(reinterpret_cast<u32x2 *>(a.v) + qi, f32x4_to_bf16x4(vv[qd]));
+                    store<NT>(reinterpret_cast<u32x2 *>(a.m) + qi,
+                              moment_bf16x4<V>(mv[qd], a.sr_key_m, qi));
+                    store<NT>(reinterpret_cast<u32x2 *>(a.v) + qi,
+                              moment_bf16x4<V>(vv[qd], a.sr_key_v, qi));
                 } else {
                     store<NT>(pw + qi, wv[qd]);
                     store<NT>(reinterpret_cast<f32x4 *>(a.m) + qi, mv[qd]);
@@ -527,8 +567,8 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
                     uint16_t *s16 = reinterpret_cast<uint16_t *>(a.master);
                     const int64_t pm = packed16_m(i);
                     a.master[packed16_master(i)] = wv;
-                    s16[pm] = (uint16_t)to_bf16(mvv);
-                    s16[pm + kSub] = (uint16_t)to_bf16(vvv);
+                    s16[pm] = (uint16_t)moment_bf16<V>(mvv, a.sr_key_m, i);
+                    s16[pm + kSub] = (uint16_t)moment_bf16<V>(vvv, a.sr_key_v, i);
                 } else if constexpr (V & kPacked) {
                     const int64_t ps = packed_index(i);
                     a.master[ps] = wv;
@@ -536,8 +576,10 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
                     a.master[ps + 2 * kSub] = vvv;
                 } else if constexpr (V & kMvBf16) {
                     a.master[i] = wv;
-                    reinterpret_cast<uint16_t *>(a.m)[i] = (uint16_t)to_bf16(mvv);
-                    reinterpret_cast<uint16_t *>(a.v)[i] = (uint16_t)to_bf16(vvv);
+                    uint16_t *m16 = reinterpret_cast<uint16_t *>(a.m);
+                    uint16_t *v16 = reinterpret_cast<uint16_t *>(a.v);
+                    m16[i] = (uint16_t)moment_bf16<V>(mvv, a.sr_key_m, i);
+                    v16[i] = (uint16_t)moment_bf16<V>(vvv, a.sr_key_v, i);
                 } else {
                     a.master[i] = wv;
                     reinterpret_cast<float *>(a.m)[i] = mvv;
@@ -690,6 +732,16 @@ kernel_fn pick_variant(int variant, int nt, int unit) {
         case kPacked | kMvBf16 | kWide:
             if constexpr (K <= kWideMaxK)
                 return nt ? pick_unit<K, kPacked | kMvBf16 | kWide>(unit) : nullptr;
+            return nullptr;
+        case kMvBf16 | kSR: return pick_unit<K, kMvBf16 | kSR>(unit);
+        case kMvBf16 | kSR | kWide:
+            if constexpr (K <= kWideMaxK) return pick_unit<K, kMvBf16 | kSR | kWide>(unit);
+            return nullptr;
+        case kPacked | kMvBf16 | kSR:
+            return nt ? pick_unit<K, kPacked | kMvBf16 | kSR>(unit) : nullptr;
+        case kPacked | kMvBf16 | kSR | kWide:
+            if constexpr (K <= kWideMaxK)
+                return nt ? pick_unit<K, kPacked | kMvBf16 | kSR | kWide>(unit) : nullptr;
             return nullptr;
         default: return nullptr;
     }

@@ -23,7 +23,12 @@ def torch():
 
 
 VARIANTS = ("base", "q8ag", "q8grad", "bf16mv", "packed", "packed_q8ag", "packed_q8grad",
-            "packed_bf16mv")
+            "packed_bf16mv", "bf16mv_sr", "packed_bf16mv_sr")
+
+
+def sr_seed(w: synth.Workload) -> int:
+    """The random-stream seed the stochastic-rounding steps use for a workload."""
+    return (w.seed * 0x9E3779B1 + 17) & (2 ** 64 - 1)
 
 
 def pack_host(w, m, v):
@@ -87,12 +92,13 @@ class DeviceShard:
         n = w.n
         nb = -(-n // zs.ZS_Q8_BLOCK)
         dev = t.device(device)
-        mv_dtype = t.int16 if variant == "bf16mv" else t.float32
+        self.seed = sr_seed(w)
+        mv_dtype = t.int16 if variant in ("bf16mv", "bf16mv_sr") else t.float32
         self.param = t.zeros(n, dtype=t.int16, device=dev)
-        if variant in ("packed", "packed_bf16mv"):
+        if variant in ("packed", "packed_bf16mv", "packed_bf16mv_sr"):
             # a block is 768 floats (master, m, v), or 512 floats' room
             # (256 fp32 master values, then 256 bf16 m and 256 bf16 v)
-            mv16 = variant == "packed_bf16mv"
+            mv16 = variant != "packed"
             floats = zs.packed_bf16mv_floats(n) if mv16 else zs.packed_floats(n)
             self.state = t.zeros(floats, dtype=t.float32, device=dev)
             master = t.empty(n, dtype=t.float32, device=dev)
@@ -142,6 +148,12 @@ class DeviceShard:
         elif self.variant == "packed":
             zs.zs_shard_step_packed(self.state, self.param, self.grads, w.k, w.n, st, hp, t_step,
                                     s)
+        elif self.variant == "packed_bf16mv_sr":
+            zs.zs_shard_step_packed_bf16mv_sr(self.state, self.param, self.grads, w.k, w.n, st,
+                                              hp, t_step, self.seed, s)
+        elif self.variant == "bf16mv_sr":
+            zs.zs_shard_step_bf16mv_sr(self.master, self.m, self.v, self.param, self.grads, w.k,
+                                       w.n, st, hp, t_step, self.seed, s)
         elif self.variant == "packed_bf16mv":
             zs.zs_shard_step_packed_bf16mv(self.state, self.param, self.grads, w.k, w.n, st, hp,
                                            t_step, s)
@@ -164,7 +176,7 @@ class DeviceShard:
             return (blk[:, 0, :].reshape(-1)[a:z].copy(), blk[:, 1, :].reshape(-1)[a:z].copy(),
                     blk[:, 2, :].reshape(-1)[a:z].copy(),
                     self.param[lo:hi].cpu().numpy().view(np.uint16))
-        if self.variant == "packed_bf16mv":
+        if self.variant in ("packed_bf16mv", "packed_bf16mv_sr"):
             b0, b1 = lo // 256, (hi - 1) // 256 + 1
             blk = self.state.view(-1, 512)[b0:b1].cpu().numpy()
             a, z = lo - b0 * 256, hi - b0 * 256
@@ -172,7 +184,8 @@ class DeviceShard:
             return (blk[:, :256].reshape(-1)[a:z].copy(), part(256, 384).reshape(-1)[a:z].copy(),
                     part(384, 512).reshape(-1)[a:z].copy(),
                     self.param[lo:hi].cpu().numpy().view(np.uint16))
-        mv = (lambda x: x[lo:hi].cpu().numpy().view(np.uint16)) if self.variant == "bf16mv" \
+        mv = (lambda x: x[lo:hi].cpu().numpy().view(np.uint16)) \
+            if self.variant in ("bf16mv", "bf16mv_sr") \
             else (lambda x: x[lo:hi].cpu().numpy())
         out = (self.master[lo:hi].cpu().numpy(), mv(self.m), mv(self.v),
                self.param[lo:hi].cpu().numpy().view(np.uint16))
@@ -200,7 +213,7 @@ def oracle_window(w: synth.Workload, lo, hi, steps, variant="base"):
     Quantized variants need lo on a block boundary and hi on one or at n."""
     n = hi - lo
     master = synth.host_master(w, lo, hi)
-    mv_dtype = np.uint16 if variant == "bf16mv" else F32
+    mv_dtype = np.uint16 if variant in ("bf16mv", "bf16mv_sr") else F32
     m = np.zeros(n, mv_dtype)
     v = np.zeros(n, mv_dtype)
     p = np.zeros(n, np.uint16)
@@ -213,6 +226,9 @@ def oracle_window(w: synth.Workload, lo, hi, steps, variant="base"):
         elif variant == "bf16mv":
             rc = oracle.shard_step_bf16mv(master, m, v, p, synth.host_grads(w, t, lo, hi), segs,
                                           hp, t)
+        elif variant == "bf16mv_sr":
+            rc = oracle.shard_step_bf16mv_sr(master, m, v, p, synth.host_grads(w, t, lo, hi),
+                                             segs, hp, t, sr_seed(w), lo)
         else:
             rc = oracle.shard_step(master, m, v, p, synth.host_grads(w, t, lo, hi), segs, hp, t)
         assert rc == 0

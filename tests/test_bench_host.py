@@ -143,9 +143,12 @@ def test_launch_key_follows_the_resolved_launch():
     assert zs.zs_launch_plan(2, n70, "packed_q8ag") == q8
     assert zs.zs_launch_plan(2, n70, "packed_q8grad") == zs.zs_launch_plan(2, n70, "q8grad")
     assert zs.zs_launch_plan(2, n70, "packed_bf16mv") == mv
+    assert zs.zs_launch_plan(2, n70, "bf16mv_sr") == mv
+    assert zs.zs_launch_plan(2, n70, "packed_bf16mv_sr") == mv
     for nn in ((1 << 32) - 1, 1 << 32, 10 ** 8, 5000):
         for kk in (2, 8):
-            assert zs.zs_launch_plan(kk, nn, "packed_bf16mv") == zs.zs_launch_plan(kk, nn, "bf16mv")
+            for form in ("packed_bf16mv", "bf16mv_sr", "packed_bf16mv_sr"):
+                assert zs.zs_launch_plan(kk, nn, form) == zs.zs_launch_plan(kk, nn, "bf16mv")
     assert zs.zs_launch_plan(2, (1 << 32) - 1, "bf16mv")["groups_per_cu"] == 0
     assert zs.zs_launch_plan(2, 1 << 32, "bf16mv")["groups_per_cu"] == 5
     assert bench.launch_key(mv).endswith(",quads=2") and "quads" not in bench.launch_key(p70)

@@ -229,3 +229,17 @@ def test_packed_entry_points_check_their_buffers():
     with pytest.raises(ValueError, match="state holds"):
         zs.ShardStep(FakeGpuTensor(4 * nf16 - 4), None, None, FakeGpuTensor(2 * N), g, N, st,
                      HP, variant="packed_bf16mv")
+    # stochastic rounding: the same buffers, plus an unsigned 64-bit seed
+    assert zs.ZS_VARIANT["bf16mv_sr"] == 36 and zs.ZS_VARIANT["packed_bf16mv_sr"] == 52
+    assert zs.algorithmic_bytes("bf16mv_sr", 2, N) == zs.algorithmic_bytes("bf16mv", 2, N)
+    assert zs.algorithmic_bytes("packed_bf16mv_sr", 2, N) == zs.algorithmic_bytes("bf16mv", 2, N)
+    with pytest.raises(ValueError, match="unsigned 64-bit"):
+        zs.zs_shard_step_packed_bf16mv_sr(FakeGpuTensor(4 * nf16), FakeGpuTensor(2 * N), g, 2, N,
+                                          st, HP, 1, -5)
+    with pytest.raises(ValueError, match="m holds"):
+        zs.zs_shard_step_bf16mv_sr(FakeGpuTensor(4 * N), FakeGpuTensor(2 * N - 2),
+                                   FakeGpuTensor(2 * N), FakeGpuTensor(2 * N), g, 2, N, st, HP, 1,
+                                   7)
+    with pytest.raises(ValueError, match="needs a seed"):
+        zs.ShardStep(FakeGpuTensor(4 * nf16), None, None, FakeGpuTensor(2 * N), g, N, st, HP,
+                     variant="packed_bf16mv_sr")

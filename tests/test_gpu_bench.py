@@ -27,9 +27,11 @@ def _bench(*args):
                                    ["--variant", "q8grad"], ["--variant", "bf16mv"],
                                    ["--variant", "packed"], ["--variant", "packed_q8ag"],
                                    ["--variant", "packed_q8grad"], ["--variant", "packed_bf16mv"],
+                                   ["--variant", "bf16mv_sr"], ["--variant", "packed_bf16mv_sr"],
                                    ["--block-order", "2", "--groups-per-cu", "4"]],
                          ids=["base", "graph", "q8ag", "q8grad", "bf16mv", "packed", "packed_q8ag",
-                              "packed_q8grad", "packed_bf16mv", "cfg"])
+                              "packed_q8grad", "packed_bf16mv", "bf16mv_sr", "packed_bf16mv_sr",
+                              "cfg"])
 def test_bench_line(extra):
     out = _bench(*extra)
     assert out["n_gpus"] == 1 and out["steps"] == 5 and out["warmup"] == 1
@@ -61,10 +63,11 @@ def test_bench_line(extra):
     assert par["steps_replayed"] == 6  # one warm-up step and five timed ones
     assert par["within_tolerance"] and par["bitwise_equal"], par
     pk = out.get("packed_state")
-    if extra in ([], ["--variant", "q8ag"], ["--variant", "q8grad"], ["--variant", "bf16mv"]):
+    if extra in ([], ["--variant", "q8ag"], ["--variant", "q8grad"], ["--variant", "bf16mv"],
+                 ["--variant", "bf16mv_sr"]):
         # the same steps on the packed state, beside the separate-array step
         pform = {"base": "packed", "q8ag": "packed_q8ag", "q8grad": "packed_q8grad",
-                 "bf16mv": "packed_bf16mv"}[variant]
+                 "bf16mv": "packed_bf16mv", "bf16mv_sr": "packed_bf16mv_sr"}[variant]
         assert pk["entry_point"] == "zs_shard_step_" + pform and pk["achieved"] > 0
         assert pk["separate_arrays_entry_point"] == want
         assert pk["bitwise_equal_to_separate_arrays"] is True and pk["pct_of_twin"] > 0

@@ -39,7 +39,8 @@ def _bf16(x):
     return (x.astype(F32).view(np.uint32) >> 16).astype(np.uint16)
 
 
-@pytest.mark.parametrize("variant", ["base", "bf16mv", "q8grad", "packed", "packed_bf16mv"])
+@pytest.mark.parametrize("variant", ["base", "bf16mv", "q8grad", "packed", "packed_bf16mv",
+                                     "bf16mv_sr"])
 def test_thousand_steps_stay_bitwise(gpu, variant):
     torch = gpu
     rng = np.random.default_rng(4242)
@@ -49,7 +50,8 @@ def test_thousand_steps_stay_bitwise(gpu, variant):
     while a < n:
         segs.append((a, bool(rng.random() < 0.6)))
         a += int(rng.integers(1, 9)) if rng.random() < 0.3 else int(rng.integers(9, 3000))
-    mv16 = variant in ("bf16mv", "packed_bf16mv")
+    mv16 = variant in ("bf16mv", "packed_bf16mv", "bf16mv_sr")
+    seed = 987654321
     packed = variant.startswith("packed")
     w0 = rng.normal(0, 0.02, n).astype(F32)
     mz = np.zeros(n, np.uint16 if mv16 else F32)
@@ -80,10 +82,15 @@ def test_thousand_steps_stay_bitwise(gpu, variant):
                 zs.zs_shard_step_bf16mv(dw, dm, dv, dp, dgs, k, n, st, hpz, t, s)
             elif variant == "packed":
                 zs.zs_shard_step_packed(state, dp, dgs, k, n, st, hpz, t, s)
+            elif variant == "bf16mv_sr":
+                zs.zs_shard_step_bf16mv_sr(dw, dm, dv, dp, dgs, k, n, st, hpz, t, seed, s)
             else:
                 zs.zs_shard_step_packed_bf16mv(state, dp, dgs, k, n, st, hpz, t, s)
-            step = oracle.shard_step_bf16mv if mv16 else oracle.shard_step
-            assert step(*ref, gs, segs, hpo, t) == 0
+            if variant == "bf16mv_sr":
+                assert oracle.shard_step_bf16mv_sr(*ref, gs, segs, hpo, t, seed) == 0
+            else:
+                step = oracle.shard_step_bf16mv if mv16 else oracle.shard_step
+                assert step(*ref, gs, segs, hpo, t) == 0
         if t % 100 == 0:
             torch.cuda.synchronize()
             if packed:

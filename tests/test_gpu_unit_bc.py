@@ -60,7 +60,8 @@ def test_unit_correction_kernels_are_bitwise(gpu, variant, span):
     w0 = rng.normal(0, 0.02, n).astype(F32)
     m0 = rng.normal(0, 1e-3, n).astype(F32)
     v0 = (rng.normal(0, 1e-3, n) ** 2).astype(F32)
-    mv16 = variant in ("bf16mv", "packed_bf16mv")
+    mv16 = variant in ("bf16mv", "packed_bf16mv", "bf16mv_sr", "packed_bf16mv_sr")
+    seed = 0x5EED + len(variant)
     if mv16:
         m0, v0 = _bf16(m0), _bf16(v0)
     ref = [w0.copy(), m0.copy(), v0.copy(), np.zeros(n, np.uint16)]
@@ -98,10 +99,17 @@ def test_unit_correction_kernels_are_bitwise(gpu, variant, span):
             zs.zs_shard_step_packed(dstate, dp, dgs, k, n, st, hpz, t, s)
         elif variant == "packed_bf16mv":
             zs.zs_shard_step_packed_bf16mv(dstate, dp, dgs, k, n, st, hpz, t, s)
+        elif variant == "bf16mv_sr":
+            zs.zs_shard_step_bf16mv_sr(dw, dm, dv, dp, dgs, k, n, st, hpz, t, seed, s)
+        elif variant == "packed_bf16mv_sr":
+            zs.zs_shard_step_packed_bf16mv_sr(dstate, dp, dgs, k, n, st, hpz, t, seed, s)
         else:
             zs.zs_shard_step(dw, dm, dv, dp, dgs, k, n, st, hpz, t, s)
-        step = oracle.shard_step_bf16mv if mv16 else oracle.shard_step
-        assert step(*ref, gs, segs, hpo, t) == 0
+        if variant.endswith("_sr"):
+            assert oracle.shard_step_bf16mv_sr(*ref, gs, segs, hpo, t, seed) == 0
+        else:
+            step = oracle.shard_step_bf16mv if mv16 else oracle.shard_step
+            assert step(*ref, gs, segs, hpo, t) == 0
     torch.cuda.synchronize()
     mv = (lambda x: x.cpu().numpy().view(np.uint16)) if mv16 else (lambda x: x.cpu().numpy())
     got = (dw.cpu().numpy(), mv(dm), mv(dv), dp.cpu().numpy().view(np.uint16))
