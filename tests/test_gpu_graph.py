@@ -34,7 +34,7 @@ def _state(torch, w0, n, k, seed, entry):
               param=torch.zeros(n, dtype=torch.int16, device="cuda"),
               grads=[f((rng.normal(0, 1e-2, n).astype(np.float32).view(np.uint32) >> 16)
                        .astype(np.uint16).view(np.int16)) for _ in range(k)])
-    if entry in ("bf16mv", "packed_bf16mv"):
+    if entry in ("bf16mv", "packed_bf16mv", "bf16mv_sr"):
         st["m"] = torch.zeros(n, dtype=torch.int16, device="cuda")
         st["v"] = torch.zeros(n, dtype=torch.int16, device="cuda")
     if entry in ("packed", "packed_bf16mv"):
@@ -55,6 +55,9 @@ def _call(entry, st, k, n, table, hp, t, stream):
     elif entry == "packed_bf16mv":
         zs.zs_shard_step_packed_bf16mv(st["state"], st["param"], st["grads"], k, n,
                                        zs.seg_table(table), hp, t, stream)
+    elif entry == "bf16mv_sr":
+        zs.zs_shard_step_bf16mv_sr(st["master"], st["m"], st["v"], st["param"], st["grads"], k,
+                                   n, zs.seg_table(table), hp, t, 0xC0FFEE, stream)
     elif entry == "bf16mv":
         zs.zs_shard_step_bf16mv(st["master"], st["m"], st["v"], st["param"], st["grads"], k, n,
                                 zs.seg_table(table), hp, t, stream)
@@ -74,9 +77,11 @@ def _same(torch, a, b):
             assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), key
 
 
-@pytest.mark.parametrize("entry", ["base", "q8ag", "bf16mv", "packed", "packed_bf16mv"],
+@pytest.mark.parametrize("entry", ["base", "q8ag", "bf16mv", "packed", "packed_bf16mv",
+                                   "bf16mv_sr"],
                          ids=["zs_shard_step", "zs_shard_step_q8ag", "zs_shard_step_bf16mv",
-                              "zs_shard_step_packed", "zs_shard_step_packed_bf16mv"])
+                              "zs_shard_step_packed", "zs_shard_step_packed_bf16mv",
+                              "zs_shard_step_bf16mv_sr"])
 @pytest.mark.parametrize("t", [7, 10000])
 def test_graph_replays_match_eager_calls(gpu, entry, t):
     torch = gpu
