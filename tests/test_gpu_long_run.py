@@ -40,7 +40,7 @@ def _bf16(x):
 
 
 @pytest.mark.parametrize("variant", ["base", "bf16mv", "q8grad", "packed", "packed_bf16mv",
-                                     "bf16mv_sr"])
+                                     "bf16mv_sr", "packed_bf16mv_sr"])
 def test_thousand_steps_stay_bitwise(gpu, variant):
     torch = gpu
     rng = np.random.default_rng(4242)
@@ -50,7 +50,7 @@ def test_thousand_steps_stay_bitwise(gpu, variant):
     while a < n:
         segs.append((a, bool(rng.random() < 0.6)))
         a += int(rng.integers(1, 9)) if rng.random() < 0.3 else int(rng.integers(9, 3000))
-    mv16 = variant in ("bf16mv", "packed_bf16mv", "bf16mv_sr")
+    mv16 = variant in ("bf16mv", "packed_bf16mv", "bf16mv_sr", "packed_bf16mv_sr")
     seed = 987654321
     packed = variant.startswith("packed")
     w0 = rng.normal(0, 0.02, n).astype(F32)
@@ -84,9 +84,11 @@ def test_thousand_steps_stay_bitwise(gpu, variant):
                 zs.zs_shard_step_packed(state, dp, dgs, k, n, st, hpz, t, s)
             elif variant == "bf16mv_sr":
                 zs.zs_shard_step_bf16mv_sr(dw, dm, dv, dp, dgs, k, n, st, hpz, t, seed, s)
+            elif variant == "packed_bf16mv_sr":
+                zs.zs_shard_step_packed_bf16mv_sr(state, dp, dgs, k, n, st, hpz, t, seed, s)
             else:
                 zs.zs_shard_step_packed_bf16mv(state, dp, dgs, k, n, st, hpz, t, s)
-            if variant == "bf16mv_sr":
+            if variant.endswith("_sr"):
                 assert oracle.shard_step_bf16mv_sr(*ref, gs, segs, hpo, t, seed) == 0
             else:
                 step = oracle.shard_step_bf16mv if mv16 else oracle.shard_step
