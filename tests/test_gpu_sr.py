@@ -115,31 +115,51 @@ def test_seed_and_rounding_change_only_what_they_should(gpu):
         assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
 
 
-@pytest.mark.parametrize("variant", ["bf16mv_sr", "packed_bf16mv_sr"])
-def test_70b_sr_windows(gpu, variant):
-    """The 70B-shaped shard (two sub-windows per wavefront), t = 10000..10002:
-    windows at segment boundaries and at random equal the oracle replaying
-    them with their shard indices."""
-    torch = gpu
-    w = synth.workload("70b")
-    assert zs.zs_launch_plan(w.k, w.n, variant)["window_quads"] == 2
+def _sr_shard_windows(torch, name, variant, window, max_boundaries):
+    """A model-shaped shard over its workload's steps (pre-warm included):
+    windows at segment boundaries, both ends and at random equal the oracle
+    replaying them with their shard indices."""
+    w = synth.workload(name)
     free, _ = torch.cuda.mem_get_info()
     need = w.n * (8 + 4 + 2 + 2 * w.k) + (1 << 30)
     if free < need:
         pytest.skip("needs %.1f GB of free device memory" % (need / 1e9))
-    ts = w.step_ts()
+    ts = list(range(1, w.prewarm_steps + 1)) + w.step_ts()
     ds = H.DeviceShard(w, variant)
     for t in ts:
         ds.fill_grads(t)
         ds.step(t)
     torch.cuda.synchronize()
-    wins = H.boundary_windows(w, 1 << 14, max_boundaries=16, n_random=4, seed=9)
+    wins = H.boundary_windows(w, window, max_boundaries=max_boundaries, n_random=4, seed=9)
     got = [ds.window(lo, hi) for lo, hi in wins]
     ds.free()
     for (lo, hi), g in zip(wins, got):
         ref = H.oracle_window(w, lo, hi, ts, variant="bf16mv_sr")
-        assert H.assert_parity(g, ref, "70b %s [%d,%d)" % (variant, lo, hi)), "not bitwise"
-    print("70b %s: %d windows bitwise equal" % (variant, len(wins)), flush=True)
+        assert H.assert_parity(g, ref, "%s %s [%d,%d)" % (name, variant, lo, hi)), "not bitwise"
+    print("%s %s: %d windows bitwise equal" % (name, variant, len(wins)), flush=True)
+
+
+@pytest.mark.parametrize("variant", ["bf16mv_sr", "packed_bf16mv_sr"])
+def test_70b_sr_windows(gpu, variant):
+    """The 70B-shaped shard (two sub-windows per wavefront), t = 10000..10002."""
+    w = synth.workload("70b")
+    assert zs.zs_launch_plan(w.k, w.n, variant)["window_quads"] == 2
+    _sr_shard_windows(gpu, "70b", variant, 1 << 14, 16)
+
+
+@pytest.mark.parametrize("variant", ["bf16mv_sr", "packed_bf16mv_sr"])
+def test_175b_sr_windows(gpu, variant):
+    """The 175B-shaped shard (one sub-window per wavefront, k = 2, t = 1..5)."""
+    w = synth.workload("175b")
+    assert zs.zs_launch_plan(w.k, w.n, variant)["window_quads"] == 1
+    _sr_shard_windows(gpu, "175b", variant, 1 << 18, 16)
+
+
+@pytest.mark.parametrize("variant", ["bf16mv_sr", "packed_bf16mv_sr"])
+def test_7b_sr_windows(gpu, variant):
+    """The 7B-shaped shard (k = 8, heavy-tailed partials, 100 pre-warm steps
+    then 10)."""
+    _sr_shard_windows(gpu, "7b", variant, 1 << 12, 12)
 
 
 @pytest.mark.parametrize("variant", ["bf16mv_sr", "packed_bf16mv_sr"])
