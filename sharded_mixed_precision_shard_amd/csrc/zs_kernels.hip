@@ -39,6 +39,8 @@
 // divide and square root, denormals kept, bf16 round-to-nearest-even with
 // NaN -> 0x7FC0.
 
+#include <type_traits>
+
 #include "zs_kernels.h"
 
 namespace zs_detail {
@@ -403,6 +405,59 @@ __device__ __forceinline__ uint32_t quantize_block(const uint32_t bits[4], uint3
     return word;
 }
 
+// Where element e's optimizer state lives.  Separate arrays: index e of
+// master, m and v (m, v fp32, or bf16 with kMvBf16).  Packed (kPacked): in
+// the one state array, the block of e holds its kSub master values, then its
+// kSub m and its kSub v (fp32, or bf16 with kMvBf16).  For a quad's first
+// element (e a multiple of kQuad) the pointers are also the quad's.
+template <int V>
+struct StateAt {
+    static constexpr bool kMv16 = (V & kMvBf16) != 0;
+    typedef typename std::conditional<kMv16, uint16_t, float>::type Moment;
+    float *w;
+    Moment *m;
+    Moment *v;
+
+    __device__ __forceinline__ StateAt(const StepArgs &a, int64_t e) {
+        if constexpr ((V & kPacked) && kMv16) {
+            w = a.master + packed16_master(e);
+            m = reinterpret_cast<uint16_t *>(a.master) + packed16_m(e);
+            v = m + kSub;
+        } else if constexpr ((V & kPacked) != 0) {
+            w = a.master + packed_index(e);
+            m = w + kSub;
+            v = w + 2 * kSub;
+        } else {
+            w = a.master + e;
+            m = reinterpret_cast<Moment *>(a.m) + e;
+            v = reinterpret_cast<Moment *>(a.v) + e;
+        }
+    }
+
+    // A moment quad widened to fp32, and stored back (bf16: rounded as the
+    // variant says, moment_bf16x4).
+    template <int NT>
+    __device__ __forceinline__ static f32x4 load_quad(const Moment *p) {
+        if constexpr (kMv16) return bf16x4_to_f32x4(load<NT>(reinterpret_cast<const u32x2 *>(p)));
+        else return load<NT>(reinterpret_cast<const f32x4 *>(p));
+    }
+    template <int NT>
+    __device__ __forceinline__ static void store_quad(Moment *p, f32x4 x, uint64_t key,
+                                                      int64_t qi) {
+        if constexpr (kMv16) store<NT>(reinterpret_cast<u32x2 *>(p), moment_bf16x4<V>(x, key, qi));
+        else store<NT>(reinterpret_cast<f32x4 *>(p), x);
+    }
+    // One moment element, the same way.
+    __device__ __forceinline__ static float load_one(const Moment *p) {
+        if constexpr (kMv16) return __uint_as_float((uint32_t)*p << 16);
+        else return *p;
+    }
+    __device__ __forceinline__ static void store_one(Moment *p, float x, uint64_t key, int64_t i) {
+        if constexpr (kMv16) *p = (uint16_t)moment_bf16<V>(x, key, i);
+        else *p = x;
+    }
+};
+
 // Reduce, update and pack one lane's quad.  mask bit e = decay of element e.
 template <int K, int V, int NT, bool U1, bool U2>
 __device__ __forceinline__ void quad_update(f32x4 &w, f32x4 &m, f32x4 &v,
@@ -460,34 +515,17 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
         if (w0 + kWindow <= a.n) {
             // Whole window in range: dense vector traffic only.  The loads are
             // issued first, so the segment search below overlaps them.
-            f32x4 *pw = reinterpret_cast<f32x4 *>(a.master);
+            // (packed: the wave's state is one run, 3 KB, or 2 KB with bf16 moments)
+            typedef StateAt<V> S;
             f32x4 wv[kQuads], mv[kQuads], vv[kQuads];
             QuadGrads<K, V, NT> gq[kQuads];
 #pragma unroll
             for (int qd = 0; qd < kQuads; ++qd) {
                 const int64_t qi = e[qd] / kQuad;
-                if constexpr ((V & kPacked) && (V & kMvBf16)) {
-                    // one 2 KB run per wave: master, then bf16 m and v
-                    const u32x2 *p16 = reinterpret_cast<const u32x2 *>(a.master);
-                    const int64_t qm = packed16_m(e[qd]) / kQuad;
-                    wv[qd] = load<NT>(pw + packed16_master(e[qd]) / kQuad);
-                    mv[qd] = bf16x4_to_f32x4(load<NT>(p16 + qm));
-                    vv[qd] = bf16x4_to_f32x4(load<NT>(p16 + qm + kWave));
-                } else if constexpr (V & kPacked) {
-                    // one 3 KB run per wave: master, m, v of the sub-window
-                    const int64_t qs = packed_index(e[qd]) / kQuad;
-                    wv[qd] = load<NT>(pw + qs);
-                    mv[qd] = load<NT>(pw + qs + kWave);
-                    vv[qd] = load<NT>(pw + qs + 2 * kWave);
-                } else if constexpr (V & kMvBf16) {
-                    wv[qd] = load<NT>(pw + qi);
-                    mv[qd] = bf16x4_to_f32x4(load<NT>(reinterpret_cast<const u32x2 *>(a.m) + qi));
-                    vv[qd] = bf16x4_to_f32x4(load<NT>(reinterpret_cast<const u32x2 *>(a.v) + qi));
-                } else {
-                    wv[qd] = load<NT>(pw + qi);
-                    mv[qd] = load<NT>(reinterpret_cast<const f32x4 *>(a.m) + qi);
-                    vv[qd] = load<NT>(reinterpret_cast<const f32x4 *>(a.v) + qi);
-                }
+                const S st(a, e[qd]);
+                wv[qd] = load<NT>(reinterpret_cast<const f32x4 *>(st.w));
+                mv[qd] = S::template load_quad<NT>(st.m);
+                vv[qd] = S::template load_quad<NT>(st.v);
                 gq[qd].load_from(a, qi);
             }
             // Decay flags: bit 4*qd + j for element e[qd] + j.
@@ -498,28 +536,10 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
                 u32x2 pq;
                 quad_update<K, V, NT, (U & 1) != 0, (U & 2) != 0>(
                     wv[qd], mv[qd], vv[qd], gq[qd], (mask >> (kQuad * qd)) & 0xfu, a, pq);
-                if constexpr ((V & kPacked) && (V & kMvBf16)) {
-                    u32x2 *p16 = reinterpret_cast<u32x2 *>(a.master);
-                    const int64_t qm = packed16_m(e[qd]) / kQuad;
-                    store<NT>(pw + packed16_master(e[qd]) / kQuad, wv[qd]);
-                    store<NT>(p16 + qm, moment_bf16x4<V>(mv[qd], a.sr_key_m, qi));
-                    store<NT>(p16 + qm + kWave, moment_bf16x4<V>(vv[qd], a.sr_key_v, qi));
-                } else if constexpr (V & kPacked) {
-                    const int64_t qs = packed_index(e[qd]) / kQuad;
-                    store<NT>(pw + qs, wv[qd]);
-                    store<NT>(pw + qs + kWave, mv[qd]);
-                    store<NT>(pw + qs + 2 * kWave, vv[qd]);
-                } else if constexpr (V & kMvBf16) {
-                    store<NT>(pw + qi, wv[qd]);
-                    store<NT>(reinterpret_cast<u32x2 *>(a.m) + qi,
-                              moment_bf16x4<V>(mv[qd], a.sr_key_m, qi));
-                    store<NT>(reinterpret_cast<u32x2 *>(a.v) + qi,
-                              moment_bf16x4<V>(vv[qd], a.sr_key_v, qi));
-                } else {
-                    store<NT>(pw + qi, wv[qd]);
-                    store<NT>(reinterpret_cast<f32x4 *>(a.m) + qi, mv[qd]);
-                    store<NT>(reinterpret_cast<f32x4 *>(a.v) + qi, vv[qd]);
-                }
+                const S st(a, e[qd]);
+                store<NT>(reinterpret_cast<f32x4 *>(st.w), wv[qd]);
+                S::template store_quad<NT>(st.m, mv[qd], a.sr_key_m, qi);
+                S::template store_quad<NT>(st.v, vv[qd], a.sr_key_v, qi);
                 store<NT>(reinterpret_cast<u32x2 *>(a.param) + qi, pq);
                 if constexpr (V & kOutQ8) {
                     const uint32_t bits[4] = {pq[0] << 16, pq[0] & 0xffff0000u, pq[1] << 16,
@@ -541,50 +561,13 @@ __global__ __launch_bounds__(kThreads) void shard_step_kernel(const StepArgs a) 
                 if (i >= a.n) continue;
                 valid |= 1u << q;
                 const float g = scalar_grad<K, V>(a, i);
-                float wv, mvv, vvv;
-                if constexpr ((V & kPacked) && (V & kMvBf16)) {
-                    const uint16_t *s16 = reinterpret_cast<const uint16_t *>(a.master);
-                    const int64_t pm = packed16_m(i);
-                    wv = a.master[packed16_master(i)];
-                    mvv = __uint_as_float((uint32_t)s16[pm] << 16);
-                    vvv = __uint_as_float((uint32_t)s16[pm + kSub] << 16);
-                } else if constexpr (V & kPacked) {
-                    const int64_t ps = packed_index(i);
-                    wv = a.master[ps];
-                    mvv = a.master[ps + kSub];
-                    vvv = a.master[ps + 2 * kSub];
-                } else if constexpr (V & kMvBf16) {
-                    wv = a.master[i];
-                    mvv = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(a.m)[i] << 16);
-                    vvv = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(a.v)[i] << 16);
-                } else {
-                    wv = a.master[i];
-                    mvv = reinterpret_cast<const float *>(a.m)[i];
-                    vvv = reinterpret_cast<const float *>(a.v)[i];
-                }
+                typedef StateAt<V> S;
+                const S st(a, i);
+                float wv = *st.w, mvv = S::load_one(st.m), vvv = S::load_one(st.v);
                 adamw<(U & 1) != 0, (U & 2) != 0>(wv, mvv, vvv, g, (mask >> q) & 1u, a);
-                if constexpr ((V & kPacked) && (V & kMvBf16)) {
-                    uint16_t *s16 = reinterpret_cast<uint16_t *>(a.master);
-                    const int64_t pm = packed16_m(i);
-                    a.master[packed16_master(i)] = wv;
-                    s16[pm] = (uint16_t)moment_bf16<V>(mvv, a.sr_key_m, i);
-                    s16[pm + kSub] = (uint16_t)moment_bf16<V>(vvv, a.sr_key_v, i);
-                } else if constexpr (V & kPacked) {
-                    const int64_t ps = packed_index(i);
-                    a.master[ps] = wv;
-                    a.master[ps + kSub] = mvv;
-                    a.master[ps + 2 * kSub] = vvv;
-                } else if constexpr (V & kMvBf16) {
-                    a.master[i] = wv;
-                    uint16_t *m16 = reinterpret_cast<uint16_t *>(a.m);
-                    uint16_t *v16 = reinterpret_cast<uint16_t *>(a.v);
-                    m16[i] = (uint16_t)moment_bf16<V>(mvv, a.sr_key_m, i);
-                    v16[i] = (uint16_t)moment_bf16<V>(vvv, a.sr_key_v, i);
-                } else {
-                    a.master[i] = wv;
-                    reinterpret_cast<float *>(a.m)[i] = mvv;
-                    reinterpret_cast<float *>(a.v)[i] = vvv;
-                }
+                *st.w = wv;
+                S::store_one(st.m, mvv, a.sr_key_m, i);
+                S::store_one(st.v, vvv, a.sr_key_v, i);
                 const uint32_t pbf = to_bf16(wv);
                 a.param[i] = (uint16_t)pbf;
                 pbits[q] = pbf << 16;
