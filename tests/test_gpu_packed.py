@@ -525,3 +525,48 @@ def test_70b_packed_bf16mv_windows(gpu):
     w = synth.workload("70b")
     assert zs.zs_launch_plan(w.k, w.n, "packed_bf16mv")["window_quads"] == 2
     _packed_shard_windows(gpu, "70b", "packed_bf16mv", 1 << 14, 16)
+
+
+def test_packed_bf16mv_on_a_large_grid_equals_the_bf16mv_step(gpu):
+    """A shard above 2^26 elements (XCD chunk order) with a ragged tail: the
+    device conversions of the bf16-moment state both ways and the packed
+    step (nearest and stochastic rounding) agree bit for bit with the
+    separate-array steps."""
+    torch = gpu
+    n, k = (1 << 26) + 4321, 2
+    rng = np.random.default_rng(27)
+    starts = np.concatenate([[0], np.sort(rng.choice(np.arange(1, n), 999, replace=False))])
+    segs = [(int(a), bool(rng.random() < 0.5)) for a in starts]
+    w0 = synth.host_normal_f32(n, synth.stream_key(27, 1, 0, 0), 0, n, 0.02)
+    m0 = _bf16_bits(synth.host_normal_f32(n, synth.stream_key(27, 1, 1, 0), 0, n, 1e-3))
+    v0 = _bf16_bits(synth.host_normal_f32(n, synth.stream_key(27, 1, 2, 0), 0, n, 1e-3) ** 2)
+    table = H.segment_tensor(segs, "cuda")
+    st, hp = zs.seg_table(table), zs.hparams()
+    s = torch.cuda.current_stream()
+    for sr in (False, True):
+        bw, bm, bv = _dev(torch, w0), _dev(torch, m0), _dev(torch, v0)
+        state = torch.empty(zs.packed_bf16mv_floats(n), dtype=torch.float32, device="cuda")
+        zs.zs_pack_state_bf16mv(bw, bm, bv, state, n)
+        bp = torch.zeros(n, dtype=torch.int16, device="cuda")
+        pp = torch.zeros(n, dtype=torch.int16, device="cuda")
+        for t in (1, 2):
+            gs = [_dev(torch, synth.host_normal_bf16(n, synth.stream_key(27, 2, j, t), 0, n, 0.01))
+                  for j in range(k)]
+            if sr:
+                zs.zs_shard_step_packed_bf16mv_sr(state, pp, gs, k, n, st, hp, t, 77, s)
+                zs.zs_shard_step_bf16mv_sr(bw, bm, bv, bp, gs, k, n, st, hp, t, 77, s)
+            else:
+                zs.zs_shard_step_packed_bf16mv(state, pp, gs, k, n, st, hp, t, s)
+                zs.zs_shard_step_bf16mv(bw, bm, bv, bp, gs, k, n, st, hp, t, s)
+        ow = torch.empty(n, dtype=torch.float32, device="cuda")
+        om = torch.empty(n, dtype=torch.int16, device="cuda")
+        ov = torch.empty(n, dtype=torch.int16, device="cuda")
+        zs.zs_unpack_state_bf16mv(state, ow, om, ov, n)
+        torch.cuda.synchronize()
+        assert torch.equal(ow.view(torch.int32), bw.view(torch.int32))
+        assert torch.equal(om, bm) and torch.equal(ov, bv) and torch.equal(pp, bp)
+        # the host packing of the separate arrays equals the device state
+        hs = state.cpu().numpy()
+        assert np.array_equal(hs.view(np.uint32), H.pack16_host(
+            bw.cpu().numpy(), bm.cpu().numpy().view(np.uint16),
+            bv.cpu().numpy().view(np.uint16)).view(np.uint32))
