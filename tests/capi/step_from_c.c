@@ -15,6 +15,9 @@
 /* the oracle's own declarations (it has no header; same field layout) */
 int zs_oracle_shard_step(float *, float *, float *, uint16_t *, const uint16_t *const *, int,
                          int64_t, const zs_segment *, int32_t, const zs_hparams *, int64_t);
+int zs_oracle_shard_step_bf16mv_sr(float *, uint16_t *, uint16_t *, uint16_t *,
+                                   const uint16_t *const *, int, int64_t, const zs_segment *,
+                                   int32_t, const zs_hparams *, int64_t, uint64_t, int64_t);
 
 #define CHECK_HIP(x)                                                                  \
     do {                                                                              \
@@ -121,6 +124,59 @@ int main(void) {
         fprintf(stderr, "C ABI: the packed step differs from the oracle\n");
         bad = 1;
     }
+    /* bf16 moments rounded stochastically, with a full 64-bit seed */
+    {
+        const uint64_t seed = 0xFEDCBA9876543210ull;
+        float *w2 = malloc(4 * n), *dw2;
+        uint16_t *mb = calloc(n, 2), *vb = calloc(n, 2), *pb = calloc(n, 2);
+        uint16_t *mbr = calloc(n, 2), *vbr = calloc(n, 2), *pbr = calloc(n, 2);
+        uint16_t *dmb, *dvb, *dpb;
+        float *wr2 = malloc(4 * n);
+        for (int64_t i = 0; i < n; ++i) wr2[i] = w2[i] = rndf(0.02f);
+        CHECK_HIP(hipMalloc((void **)&dw2, 4 * n));
+        CHECK_HIP(hipMalloc((void **)&dmb, 2 * n));
+        CHECK_HIP(hipMalloc((void **)&dvb, 2 * n));
+        CHECK_HIP(hipMalloc((void **)&dpb, 2 * n));
+        CHECK_HIP(hipMemcpy(dw2, w2, 4 * n, hipMemcpyHostToDevice));
+        CHECK_HIP(hipMemcpy(dmb, mb, 2 * n, hipMemcpyHostToDevice));
+        CHECK_HIP(hipMemcpy(dvb, vb, 2 * n, hipMemcpyHostToDevice));
+        for (int64_t t = 1; t <= 3; ++t) {
+            for (int j = 0; j < k; ++j) {
+                for (int64_t i = 0; i < n; ++i) {
+                    float f = rndf(0.001f);
+                    uint32_t u;
+                    memcpy(&u, &f, 4);
+                    g[j][i] = (uint16_t)(u >> 16);
+                }
+                CHECK_HIP(hipMemcpy(dg[j], g[j], 2 * n, hipMemcpyHostToDevice));
+            }
+            const uint16_t *const dgs2[3] = {dg[0], dg[1], dg[2]};
+            int rc = zs_shard_step_bf16mv_sr(dw2, dmb, dvb, dpb, dgs2, k, n, &table, &hp, t, seed,
+                                             s);
+            if (rc != ZS_OK) {
+                fprintf(stderr, "zs_shard_step_bf16mv_sr: %s\n", zs_status_string(rc));
+                return 1;
+            }
+            CHECK_HIP(hipStreamSynchronize(s));
+            const uint16_t *const hgs[3] = {g[0], g[1], g[2]};
+            if (zs_oracle_shard_step_bf16mv_sr(wr2, mbr, vbr, pbr, hgs, k, n, segs, 4, &hp, t, seed,
+                                               0) != 0) {
+                fprintf(stderr, "oracle refused the stochastic step\n");
+                return 1;
+            }
+        }
+        CHECK_HIP(hipMemcpy(w2, dw2, 4 * n, hipMemcpyDeviceToHost));
+        CHECK_HIP(hipMemcpy(mb, dmb, 2 * n, hipMemcpyDeviceToHost));
+        CHECK_HIP(hipMemcpy(vb, dvb, 2 * n, hipMemcpyDeviceToHost));
+        CHECK_HIP(hipMemcpy(pb, dpb, 2 * n, hipMemcpyDeviceToHost));
+        if (memcmp(w2, wr2, 4 * n) != 0 || memcmp(mb, mbr, 2 * n) != 0 ||
+            memcmp(vb, vbr, 2 * n) != 0 || memcmp(pb, pbr, 2 * n) != 0) {
+            fprintf(stderr, "C ABI: the stochastic step differs from the oracle\n");
+            bad = 1;
+        }
+        hipFree(dw2); hipFree(dmb); hipFree(dvb); hipFree(dpb);
+        free(w2); free(wr2); free(mb); free(vb); free(pb); free(mbr); free(vbr); free(pbr);
+    }
     /* an argument error is reported synchronously, nothing enqueued */
     const uint16_t *const dgs[3] = {dg[0], dg[1], dg[2]};
     if (zs_shard_step(dw, dm, dv, dp, dgs, k, n, &table, &hp, 0, s) != ZS_ERR_INVALID_ARGUMENT)
@@ -132,6 +188,6 @@ int main(void) {
     hipStreamDestroy(s);
     zs_fini();
     if (bad) { fprintf(stderr, "C ABI: results differ from the oracle\n"); return 1; }
-    printf("C ABI: bitwise equal (separate and packed state)\n");
+    printf("C ABI: bitwise equal (separate and packed state, stochastic bf16 moments)\n");
     return 0;
 }
