@@ -250,9 +250,10 @@ int zs_shard_step_bf16mv(float *master, uint16_t *m_bf16, uint16_t *v_bf16,
  * ZS_PACKED_FLOATS(n) floats in all; the slots past n in the last block are
  * padding, which the step neither reads nor writes.  Each wavefront then
  * moves its state as one 3 KB run instead of three 1 KB runs in three
- * arrays: about 2 % faster on MI355X on the 70B-shaped shard once the
- * placement of the arrays in memory is accounted for (which alone moves
- * either layout by up to 3 %).  The arithmetic and every output bit are
+ * arrays: on MI355X about 2 % faster on average on the 70B-shaped shard,
+ * though a single run can go either way (the placement of the arrays in
+ * physical memory alone moves either layout by up to 3 %), and 2-7 % on
+ * the smaller shards measured.  The arithmetic and every output bit are
  * zs_shard_step's.
  *
  *   state : DEVICE fp32 [ZS_PACKED_FLOATS(n)], read and updated in place,
