@@ -102,8 +102,8 @@ def host_info():
             "usable_cpus": len(os.sched_getaffinity(0))}
 
 
-# A one-GPU share of the GPU hosts is 16 CPUs: the threaded oracle uses at most
-# that many threads, whatever the host has online.
+# The threaded oracle uses at most 16 threads, one GPU's share of the CPUs of
+# an eight-GPU MI355X host, whatever the host has online.
 HOST_THREAD_CAP = 16
 
 
@@ -999,7 +999,7 @@ def main():
         log("twin of the step's traffic: whole %.1f GB/s, reads %.1f GB/s, writes %.1f GB/s"
             % (ceil["step"], ceil["read"], ceil["write"]))
         # the same traffic in other launch shapes (chunk order x occupancy cap):
-        # the best of them is what this box delivers for it
+        # the best of them is what this machine delivers for it
         best = (ceil["step"], key)
         for order, cap in TWIN_SHAPES:
             alt = dict(plan, block_order=order, groups_per_cu=cap)

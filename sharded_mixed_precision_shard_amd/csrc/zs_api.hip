@@ -38,7 +38,7 @@ constexpr int64_t kXcdOrderMinElems = int64_t(1) << 26;
 // 5 resident workgroups per CU.  On MI355X it measured 0-8 % faster on shards
 // of 0.8-3 x 10^9 elements (most on placements where DRAM queues congest) and
 // 1.3-1.6 % faster for every entry point on the 8 x 10^9-element 70B shard
-// (same process, two boxes; 4 is as good, 6 and more or none slower).  The
+// (same process, two machines; 4 is as good, 6 and more or none slower).  The
 // bf16-moment step with one sub-window per wavefront keeps no default cap
 // (0-1 % slower under it below 2^32 elements, 9-11 % above).
 constexpr int kDefaultCap = 5;

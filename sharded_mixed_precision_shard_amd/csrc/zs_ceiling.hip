@@ -13,7 +13,7 @@
 //    left as it was; the output arrays get arbitrary bytes), the read streams
 //    alone, or the write streams alone (which overwrites the state).  Its
 //    rate is what the memory system delivers for exactly this traffic on
-//    this box and this physical placement of the arrays.
+//    this machine and this physical placement of the arrays.
 
 #include <hip/hip_runtime.h>
 

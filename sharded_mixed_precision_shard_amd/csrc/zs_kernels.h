@@ -84,7 +84,7 @@ static_assert(packed16_m(kSub) == 2 * packed16_master(kSub) + 2 * kSub, "bf16 ru
 // 70B- and 175B-shaped shards for the base and bf16-moment steps, same
 // process).  The exception is kWide: on shards of 2^32 elements and more the
 // bf16-moment step with two quads per lane under an occupancy cap of 5 moved
-// 1.3-1.9 % more than with one quad uncapped (same process, three boxes),
+// 1.3-1.9 % more than with one quad uncapped (same process, three machines),
 // while one quad under that cap lost 9-11 %: fewer waves, each with twice
 // the loads in flight across its arithmetic.
 constexpr int quads_for(int variant) { return (variant & kWide) ? 2 : 1; }

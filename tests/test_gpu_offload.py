@@ -1,4 +1,4 @@
-"""The ZeRO-Offload host step (include/zs_host.h) on the GPU host's own CPUs,
+"""The ZeRO-Offload host step (include/zs_host.h) on the CPUs of the machine that holds the GPU,
 bit for bit against the oracle and against the GPU step (zs_shard_step) on
 the same seeded inputs: GPT-2-small rank 0 over its 10 steps on the whole
 shard, and windows of the 70B-shaped shard at t = 10000..10002.
