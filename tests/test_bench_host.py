@@ -273,3 +273,23 @@ def test_parity_replay_reports_equality_and_planted_differences():
     r = bench._parity_replay(w, "base", par)
     assert not r["bitwise_equal"] and r["within_tolerance"]
     assert r["max_param_bf16_ulp"] == 1
+
+
+def test_every_entry_point_is_benchable_and_its_bytes_agree():
+    """Each entry point the binding names has a bench variant, a twin layout
+    and a byte count, and the bench's stream bytes add up to the binding's
+    algorithmic bytes; each packed form maps back to its separate form."""
+    import sharded_mixed_precision_shard_amd as zs
+    help_text = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"],
+                               capture_output=True, text=True, timeout=60, cwd=ROOT).stdout
+    help_text = " ".join(help_text.split())
+    for var in zs.ZS_VARIANT:
+        assert var in bench.Twin.LAYOUT, var
+        assert var in help_text, var
+        for k, n in ((1, 1), (2, 1000), (8, 10 ** 6 + 3), (16, 257)):
+            r, w = bench.twin_bytes(var, k, n)
+            assert r + w == zs.algorithmic_bytes(var, k, n), (var, k, n)
+    for sep, packed in bench.PACKED_FORM.items():
+        assert sep in zs.ZS_VARIANT and packed in zs.ZS_VARIANT
+        assert zs.algorithmic_bytes(sep, 2, 999) == zs.algorithmic_bytes(packed, 2, 999)
+        assert bench.Twin.LAYOUT[packed] == bench.Twin.LAYOUT[sep] | 8
