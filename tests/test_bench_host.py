@@ -293,3 +293,17 @@ def test_every_entry_point_is_benchable_and_its_bytes_agree():
         assert sep in zs.ZS_VARIANT and packed in zs.ZS_VARIANT
         assert zs.algorithmic_bytes(sep, 2, 999) == zs.algorithmic_bytes(packed, 2, 999)
         assert bench.Twin.LAYOUT[packed] == bench.Twin.LAYOUT[sep] | 8
+
+
+def test_committed_traffic_matches_the_current_kernels():
+    """profiles/traffic.json holds counted bytes for the current kernel source
+    and the default launch of the headline workload (so the bench line's
+    roofline.traffic is not null), within 0.1 % of the algorithmic bytes."""
+    import sharded_mixed_precision_shard_amd as zs
+    w = synth.workload("70b")
+    key = bench.launch_key(zs.zs_launch_plan(w.k, w.n))
+    traffic = bench.measured_traffic("70b", key)
+    assert traffic is not None, "re-take the rocprofv3 counters for kernel %s" % (
+        bench.kernel_source_hash())
+    alg = zs.algorithmic_bytes("base", w.k, w.n)
+    assert abs(traffic / alg - 1) < 1e-3
